@@ -1,0 +1,348 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- a library routine, a closed form, an exact-arithmetic invariant, a
+hand-derived golden case or brute force -- so that a dropped term, a wrong
+sign or index, or a transposed operand in the oracle fails here.
+
+Sources: convrot-mlx README ("What is included": normalized Hadamard rotation
+for groups 64/256, rowwise absmax INT4 in [-7, 7], reversible N x packed-K and
+K x packed-N layouts); comfy-quants issue "convrot is ... QuaRot Stage 1c",
+section 1 (R = I_G (x) H, X.R = [X_1 H, ..., X_G H], Y = sum_i RHT(X_i)RHT(W_i)^T).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from w4a4_rotated_bit_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits_of(values_f32):
+    return synth.to_bf16_bits(np.asarray(values_f32, dtype=np.float32))
+
+
+def _exact_bf16(values):
+    """bf16 bits for values that must be exactly representable."""
+    f = np.asarray(values, dtype=np.float64)
+    bits = _bits_of(f.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(bits).astype(np.float64), f), "value not bf16-exact"
+    return bits
+
+
+# --------------------------------------------------------------------------
+# Hadamard matrix
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_sylvester_matches_scipy(g):
+    # scipy.linalg.hadamard builds the Sylvester matrix in natural order.
+    assert np.array_equal(oracle.sylvester(g).astype(np.int64), scipy.linalg.hadamard(g).astype(np.int64))
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_sylvester_closed_form_and_orthogonality(g):
+    H = oracle.sylvester(g).astype(np.int64)
+    i = np.arange(g)[:, None]
+    j = np.arange(g)[None, :]
+    popc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(H, np.where(popc % 2 == 0, 1, -1))
+    assert np.array_equal(H @ H.T, g * np.eye(g, dtype=np.int64))      # H H^T = g I
+    assert np.array_equal(H, H.T)
+    assert np.all(H[0] == 1) and np.all(H[:, 0] == 1)                   # H . 1 = g e_0
+    # normalized: (H/sqrt g)(H/sqrt g)^T = I exactly in binary64 for g = 4^k
+    Hn = H.astype(np.float64) / np.sqrt(g)
+    assert np.array_equal(Hn @ Hn.T, np.eye(g))
+
+
+# --------------------------------------------------------------------------
+# Grouped rotation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g,K", [(64, 64), (64, 320), (256, 256), (256, 1024)])
+def test_rotation_equals_kronecker_operator(g, K):
+    """r = x (I_G (x) H_g)/sqrt(g), computed here as one dense product with
+    numpy's Kronecker product of scipy's Hadamard; must equal the oracle's
+    group-by-group result after one rounding to binary32."""
+    x = synth.random_bf16((5, K), seed=11, outliers=3)
+    R = np.kron(np.eye(K // g), scipy.linalg.hadamard(g)).astype(np.float64) / np.sqrt(g)
+    ref = (synth.bf16_bits_to_f32(x).astype(np.float64) @ R).astype(np.float32)
+    got = oracle.rotate_rows(x, g)
+    assert np.array_equal(got, ref)
+
+
+def _fwht_inplace(v):
+    """Independent fast Walsh-Hadamard transform (butterflies, unnormalized)."""
+    v = v.copy()
+    h = 1
+    n = v.shape[-1]
+    while h < n:
+        for s in range(0, n, 2 * h):
+            a = v[..., s:s + h].copy()
+            b = v[..., s + h:s + 2 * h].copy()
+            v[..., s:s + h] = a + b
+            v[..., s + h:s + 2 * h] = a - b
+        h *= 2
+    return v
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_rotation_equals_independent_fwht(g):
+    x = synth.random_bf16((3, 4 * g), seed=12, outliers=2)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64).reshape(3, 4, g)
+    ref = (_fwht_inplace(xf) / np.sqrt(g)).reshape(3, 4 * g).astype(np.float32)
+    assert np.array_equal(oracle.rotate_rows(x, g), ref)
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_rotation_basis_vectors_give_hadamard_rows(g):
+    K = 2 * g
+    eye = np.zeros((K, K), dtype=np.float32)
+    eye[np.arange(K), np.arange(K)] = 1.0
+    r = oracle.rotate_rows(_bits_of(eye), g).astype(np.float64)
+    H = scipy.linalg.hadamard(g) / np.sqrt(g)
+    assert np.array_equal(r[:g, :g], H) and np.array_equal(r[g:, g:], H)
+    assert np.all(r[:g, g:] == 0) and np.all(r[g:, :g] == 0)            # block diagonal
+
+
+@pytest.mark.parametrize("g,K", [(64, 192), (256, 512)])
+def test_rotation_invariance_exact_on_integers(g, K):
+    """(XR)(WR)^T = X W^T exactly: small integers make every rotated value a
+    multiple of 1/sqrt(g) and every sum exact in binary64."""
+    rng = np.random.default_rng(5)
+    X = rng.integers(-8, 9, size=(7, K)).astype(np.float32)
+    W = rng.integers(-8, 9, size=(9, K)).astype(np.float32)
+    RX = oracle.rotate_rows(_bits_of(X), g).astype(np.float64)
+    RW = oracle.rotate_rows(_bits_of(W), g).astype(np.float64)
+    lhs = RX @ RW.T
+    rhs = X.astype(np.int64) @ W.astype(np.int64).T
+    assert np.array_equal(lhs, rhs.astype(np.float64))
+    # chunked form: sum over groups of RHT(X_i) RHT(W_i)^T
+    chunked = sum(RX[:, i:i + g] @ RW[:, i:i + g].T for i in range(0, K, g))
+    assert np.array_equal(chunked, rhs.astype(np.float64))
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_rotation_preserves_group_norms(g):
+    x = synth.random_bf16((4, 3 * g), seed=13, outliers=4)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64).reshape(4, 3, g)
+    r = oracle.rotate_rows(x, g).astype(np.float64).reshape(4, 3, g)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(xf, axis=-1), rtol=1e-6)
+
+
+def test_rotation_rejects_bad_group():
+    x = synth.random_bf16((2, 100), seed=1)
+    with pytest.raises(ValueError):
+        oracle.rotate_rows(x, 64)      # K not a multiple of g
+    with pytest.raises(ValueError):
+        oracle.rotate_rows(synth.random_bf16((2, 96), seed=1), 48)  # not a power of two
+
+
+# --------------------------------------------------------------------------
+# Quantization
+# --------------------------------------------------------------------------
+
+def _golden_quant_cases():
+    with open(os.path.join(GOLDEN, "quant_ties.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_quant_cases(), ids=lambda c: c["name"])
+def test_quantizer_golden_ties(case):
+    g, K = case["g"], case["K"]
+    x = np.zeros((K,), dtype=np.float64)
+    for gi, grp in enumerate(case["groups"]):
+        xe, xo = float(Fraction(grp["x_even"])), float(Fraction(grp["x_odd"]))
+        x[gi * g:(gi + 1) * g:2] = xe
+        x[gi * g + 1:(gi + 1) * g:2] = xo
+    bits = _exact_bf16(x)[None, :]
+    q, s, r = oracle.prepare_rows(bits, g, want_rotated=True)
+    want_r = np.zeros((K,), dtype=np.float64)
+    for k, v in case["rot_nonzero"].items():
+        want_r[int(k)] = float(Fraction(v))
+    assert np.array_equal(r[0].astype(np.float64), want_r)
+    assert float(s[0]) == float(Fraction(case["scale"]))
+    want_q = np.zeros((K,), dtype=np.int8)
+    for k, v in case["codes_nonzero"].items():
+        want_q[int(k)] = v
+    assert np.array_equal(q[0], want_q)
+
+
+def test_quantizer_properties_random():
+    x = synth.random_bf16((64, 1024), seed=21, outliers=8)
+    q, s, r = oracle.prepare_rows(x, 256, want_rotated=True)
+    assert q.min() >= -7 and q.max() <= 7
+    assert np.all(np.abs(q).max(axis=1) == 7)                          # every nonzero row reaches 7
+    a = np.abs(r).max(axis=1)
+    np.testing.assert_array_equal(s, (a / np.float32(7)).astype(np.float32))
+    # nearest grid point: |r - q s| <= s/2 (with one ulp of slack for r/s rounding)
+    err = np.abs(r.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-6))
+    # and no other code is closer
+    for d in (-1, 1):
+        alt = np.clip(q.astype(np.int64) + d, -7, 7)
+        err_alt = np.abs(r.astype(np.float64) - alt * s[:, None].astype(np.float64))
+        assert np.all(err <= err_alt * (1 + 1e-6) + 1e-30)
+
+
+def test_quantizer_zero_rows():
+    x = synth.random_bf16((4, 512), seed=22)
+    x[1] = 0
+    x[3] = 0x8000  # negative zeros
+    q, s = oracle.prepare_rows(x, 64)
+    assert s[1] == 0 and s[3] == 0 and np.all(q[1] == 0) and np.all(q[3] == 0)
+    assert s[0] > 0 and s[2] > 0
+
+
+# --------------------------------------------------------------------------
+# Packing
+# --------------------------------------------------------------------------
+
+def test_pack_exhaustive_pairs():
+    vals = np.arange(-7, 8, dtype=np.int8)
+    a, b = np.meshgrid(vals, vals, indexing="ij")
+    codes = np.stack([a.ravel(), b.ravel()], axis=1)                   # [225, 2]
+    p = oracle.pack_nk(codes)
+    lo = p[:, 0] & 0x0F
+    hi = p[:, 0] >> 4
+    to_signed = lambda v: np.where(v >= 8, v.astype(np.int16) - 16, v.astype(np.int16))
+    assert np.array_equal(to_signed(lo), codes[:, 0]) and np.array_equal(to_signed(hi), codes[:, 1])
+    assert len(np.unique(p)) == 225                                     # injective
+    assert np.array_equal(oracle.unpack_nk(p, 2), codes)
+    assert not np.any(lo == 8) and not np.any(hi == 8)                  # code -8 never appears
+
+
+def test_nk_kn_round_trip_and_transpose():
+    rng = np.random.default_rng(3)
+    N, K = 48, 96
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    nk = oracle.pack_nk(codes)
+    kn = oracle.nk_to_kn(nk, N, K)
+    assert kn.shape == (K, N // 2)
+    # K x packed-N is the N x packed-K packing of the transposed codes
+    assert np.array_equal(kn, oracle.pack_nk(codes.T.copy()))
+    assert np.array_equal(oracle.kn_to_nk(kn, N, K), nk)
+
+
+# --------------------------------------------------------------------------
+# Integer products
+# --------------------------------------------------------------------------
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(4)
+    M, N, K = 5, 6, 40
+    a = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    b = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    acc = oracle.gemm_i32(a, b)
+    for m in range(M):
+        for n in range(N):
+            assert acc[m, n] == sum(int(a[m, k]) * int(b[n, k]) for k in range(K))
+
+
+@pytest.mark.parametrize("K", [256, 12288])
+def test_gemm_integer_edges(K):
+    plus = np.full((2, K), 7, dtype=np.int8)
+    minus = np.full((1, K), -7, dtype=np.int8)
+    acc = oracle.gemm_i32(plus, np.concatenate([plus[:1], minus]))
+    assert acc[0, 0] == 49 * K and acc[0, 1] == -49 * K
+
+
+def test_gemm_matches_numpy_int64():
+    rng = np.random.default_rng(8)
+    a = rng.integers(-7, 8, size=(33, 512)).astype(np.int8)
+    b = rng.integers(-7, 8, size=(47, 512)).astype(np.int8)
+    assert np.array_equal(oracle.gemm_i32(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+# --------------------------------------------------------------------------
+# bf16 and the epilogue
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_golden():
+    with open(os.path.join(GOLDEN, "bf16_rounding.json")) as f:
+        cases = json.load(f)["cases"]
+    src = np.array([int(a, 16) for a, _ in cases], dtype=np.uint32).view(np.float32)
+    want = np.array([int(b, 16) for _, b in cases], dtype=np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16(src), want)
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16(v), ref)
+
+
+def _round_to_f32_exact(fr: Fraction) -> np.float32:
+    """Correctly rounded binary32 of an exact rational, ties to even, by
+    checking the neighbours of a candidate."""
+    c = np.float32(float(fr))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (int(np.float32(cand).view(np.uint32)) & 1) == 0):
+            best = (d, cand)
+    return np.float32(best[1])
+
+
+def test_epilogue_exact_rational():
+    rng = np.random.default_rng(10)
+    M, N = 6, 7
+    acc = rng.integers(-600000, 600000, size=(M, N)).astype(np.int32)
+    sx = (rng.uniform(0.1, 5, M)).astype(np.float32)
+    sw = (rng.uniform(1e-3, 1e-2, N)).astype(np.float32)
+    bias = _bits_of(rng.standard_normal(N) * 0.01)
+    y = oracle.epilogue(acc, sx, sw, bias)
+    bf = synth.bf16_bits_to_f32(bias)
+    for m in range(M):
+        for n in range(N):
+            t = np.float32(np.float32(acc[m, n]) * sx[m])            # binary32 product, rounded
+            exact = Fraction(float(t)) * Fraction(float(sw[n])) + Fraction(float(bf[n]))
+            yf = _round_to_f32_exact(exact)                          # one rounding: the fma
+            assert y[m, n] == oracle.f32_to_bf16(np.array([yf]))[0]
+
+
+def test_epilogue_zero_row_gives_bias():
+    acc = np.zeros((2, 5), dtype=np.int32)
+    bias = _bits_of(np.array([0.5, -0.25, 1.0, 0.0, -3.0]))
+    y = oracle.epilogue(acc, np.zeros(2, np.float32), np.ones(5, np.float32), bias)
+    assert np.array_equal(y, np.stack([bias, bias]))
+    assert np.array_equal(oracle.epilogue(acc, np.ones(2, np.float32), np.ones(5, np.float32), None),
+                          np.zeros((2, 5), np.uint16))
+
+
+# --------------------------------------------------------------------------
+# The whole linear
+# --------------------------------------------------------------------------
+
+def test_linear_composes_steps_and_tracks_dense():
+    inp = synth.make("tiny_m64_k1024_n1024_g256")
+    g = 256
+    qw, sw = oracle.prepare_weight(inp["w"], g)
+    y, parts = oracle.linear(inp["x"], qw, sw, inp["bias"], g, want_parts=True)
+    qx, sx = oracle.prepare_rows(inp["x"], g)
+    assert np.array_equal(parts["qx"], qx) and np.array_equal(parts["sx"], sx)
+    acc = oracle.gemm_i32(qx, qw)
+    assert np.array_equal(parts["acc"], acc)
+    assert np.array_equal(y, oracle.epilogue(acc, sx, sw, inp["bias"]))
+    # informational accuracy against the dense product: 4-bit rowwise
+    # quantization of rotated Gaussian rows stays well inside 25% relative error
+    X = synth.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    W = synth.bf16_bits_to_f32(inp["w"]).astype(np.float64)
+    dense = X @ W.T
+    yf = synth.bf16_bits_to_f32(y).astype(np.float64)
+    rel = np.linalg.norm(yf - dense) / np.linalg.norm(dense)
+    assert rel < 0.25, rel
+
+
+def test_linear_thread_count_does_not_change_result():
+    inp = synth.make("g64_m128_k2048_n2048", M=16)
+    qw, sw = oracle.prepare_weight(inp["w"][:256], 64, threads=3)
+    y1 = oracle.linear(inp["x"], qw, sw, inp["bias"][:256], 64, threads=1)
+    y7 = oracle.linear(inp["x"], qw, sw, inp["bias"][:256], 64, threads=7)
+    assert np.array_equal(y1, y7)
