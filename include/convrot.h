@@ -1,0 +1,178 @@
+/*
+ * convrot.h -- C ABI of the ConvRot W4A4 rotated linear for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (convrot-mlx README, "What is included"; comfy-quants issue
+ * "convrot is ... QuaRot Stage 1c", section 1):
+ *   Y[M,N] = bf16( (Q(X R) . Q(W R)^T) * sx[m] * sw[n] + bias[n] )
+ * where R = I_G (x) H_g / sqrt(g) is the block-diagonal normalized Sylvester
+ * Hadamard rotation over contiguous groups of g in {64, 256} input channels,
+ * and Q quantizes each rotated row symmetrically to signed 4-bit codes in
+ * [-7, 7] with one scale s = absmax(row) / 7 per row (codes rint(r / s),
+ * ties to even; an all-zero row has s = 0 and codes 0).  The product is an
+ * exact integer dot product; the epilogue is fmaf(float(acc) * sx[m], sw[n],
+ * bias[n]) rounded to bf16 (nearest even).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are dense row-major; X is [M][K] and W is [N][K] (a weight row
+ *     is an output channel), Y is [M][N].  bf16 tensors are passed as raw
+ *     16-bit storage.
+ *   - Pointers named *_dev are device pointers; pointers named *_host are host
+ *     pointers.  The library never allocates, frees or retains device memory
+ *     and keeps no state between calls: the caller owns every buffer.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Device
+ *     entry points only enqueue work on it and return; nothing is synchronised.
+ *   - Device buffers must be 16-byte aligned except sw/sx/bias (4/4/2 bytes).
+ *   - Sizes: 1 <= K <= 16384 with K % g == 0; 0 <= M, N <= 16777216.  M == 0 or
+ *     N == 0 is a no-op that returns CONVROT_OK.
+ *   - All arguments are checked before anything is launched; on any error
+ *     nothing is enqueued and an error status is returned.  There is no
+ *     fallback path of any kind.
+ *   - Calls on different streams may run concurrently; calls sharing a
+ *     workspace must be ordered by the caller.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define CONVROT_OK 0
+#define CONVROT_EINVAL 1     /* bad size, group, null or misaligned pointer   */
+#define CONVROT_EWORKSPACE 2 /* workspace smaller than convrot_workspace_bytes */
+#define CONVROT_EHIP 3       /* the HIP runtime reported an error at launch   */
+#define CONVROT_EDEVICE 4    /* current device is not a gfx950 GPU            */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* convrot_status_string(int status);
+
+/* Library version string, e.g. "convrot-gfx950 1.0". */
+const char* convrot_version(void);
+
+/* ---- sizes (host only, no HIP call) ----------------------------------- */
+
+/* Bytes of the packed INT4 weight image for an N x K weight:
+ * round_up(N, 32) * round_up(K, 128) / 2.  Layout: 32-column x 128-K units
+ * in MFMA fragment order (convrot-mlx README, "What is included": the K x
+ * packed-N family of layouts, here tiled for CDNA4 matrix cores).  g must be
+ * 64 or 256 and K % g == 0.  Returns CONVROT_OK or CONVROT_EINVAL. */
+int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
+
+/* Bytes of workspace convrot_linear needs: the activation-code image
+ * (round_up(M, 32) * round_up(K, 128) bytes, INT8 codes) followed, at the
+ * next 256-byte boundary, by the activation scales sx (round_up(M, 32)
+ * floats).  Returns CONVROT_OK or CONVROT_EINVAL. */
+int convrot_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
+
+/* ---- argument checks (host only, no HIP call) ------------------------- */
+
+/* The checks convrot_prepare_weight performs.  Returns a status code. */
+int convrot_validate_weight(const void* W_dev, int64_t N, int64_t K, int g, const void* image_dev,
+                            const float* sw_dev);
+
+/* The checks convrot_linear performs.  Returns a status code. */
+int convrot_validate_linear(const void* X_dev, int64_t M, int64_t K, const void* image_dev,
+                            const float* sw_dev, const void* bias_dev, int64_t N, int g, const void* Y_dev,
+                            const void* workspace_dev, size_t ws_bytes);
+
+/* ---- offline weight preparation --------------------------------------- */
+
+/* Rotate every weight row by I_G (x) H_g / sqrt(g), quantize it rowwise to
+ * INT4 codes in [-7, 7] with scale sw[n] = absmax / 7, and write the codes as
+ * the packed weight image (convrot-mlx README, "Install and test": the
+ * weight conversion step quantize_convrot_weight followed by the repack for
+ * the matrix-core layout).
+ *   W_dev     bf16 [N][K], read only.
+ *   image_dev convrot_weight_image_bytes(N, K, g) bytes, fully written
+ *             (padding included).  Valid only for this (N, K); the caller keeps
+ *             g beside it and passes the same g to convrot_linear.
+ *   sw_dev    float [N], written.
+ */
+int convrot_prepare_weight(const void* W_dev, int64_t N, int64_t K, int g, void* image_dev, float* sw_dev,
+                           void* stream);
+
+/* The same rotation and quantization, writing the portable N x packed-K form
+ * (convrot-mlx README, "What is included": reversible N x packed-K layout):
+ * qweight_nk_dev is uint8 [N][K/2], byte j of row n holding code 2j in its low
+ * nibble and code 2j+1 in its high nibble (two's complement).  sw_dev float [N]. */
+int convrot_quantize_weight(const void* W_dev, int64_t N, int64_t K, int g, uint8_t* qweight_nk_dev,
+                            float* sw_dev, void* stream);
+
+/* Lossless repack of N x packed-K codes into the weight image (the analogue
+ * of the pages' repack_nk_weight_for_mpp, convrot-mlx README, "Install and
+ * test").  image_dev: convrot_weight_image_bytes(N, K, 64) bytes. */
+int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t K, void* image_dev,
+                               void* stream);
+
+/* ---- the linear ------------------------------------------------------- */
+
+/* Y = the ConvRot W4A4 linear of X with a prepared weight (convrot-mlx
+ * README, "Install and test": the complete path is rotation, activation
+ * quantization, integer product, scaling and bias).
+ *   X_dev      bf16 [M][K].
+ *   image_dev  from convrot_prepare_weight / convrot_repack_nk_to_image with
+ *              the same N, K (and g for prepare_weight).
+ *   sw_dev     float [N].
+ *   bias_dev   bf16 [N], or NULL for no bias.
+ *   Y_dev      bf16 [M][N], written.
+ *   workspace_dev / ws_bytes: at least convrot_workspace_bytes(M, K, g); its
+ *              contents on entry are ignored and on exit hold the activation
+ *              codes and scales of X.
+ */
+int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_dev, const float* sw_dev,
+                   const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
+                   void* stream);
+
+/* The two halves of convrot_linear, for callers that want to time or reuse
+ * them separately.  convrot_prepare_activations writes the activation codes
+ * and scales of X into the workspace (rotation, row absmax, quantization);
+ * convrot_gemm consumes that workspace: integer products against the weight
+ * image, then the scale + bias epilogue into Y.  Same arguments and rules as
+ * convrot_linear. */
+int convrot_prepare_activations(const void* X_dev, int64_t M, int64_t K, int g, void* workspace_dev,
+                                size_t ws_bytes, void* stream);
+int convrot_gemm(const void* workspace_dev, size_t ws_bytes, int64_t M, int64_t K, const void* image_dev,
+                 const float* sw_dev, const void* bias_dev, int64_t N, void* Y_dev, void* stream);
+
+/* ---- parity hooks (same kernels, exposed intermediate results) ---------- */
+
+/* Rotation + row absmax + quantization of `rows` bf16 rows, with plain
+ * row-major outputs: codes_dev int8 [rows][K], scales_dev float [rows], and,
+ * if rotated_dev is not NULL, the rotated rows as float [rows][K] (convrot-mlx
+ * README, "What is included": the rotation and the rowwise quantizer). */
+int convrot_prepare_rows(const void* X_dev, int64_t rows, int64_t K, int g, int8_t* codes_dev, float* scales_dev,
+                         float* rotated_dev, void* stream);
+
+/* The integer product alone: acc_dev int32 [M][N] = qx . codes(image)^T for
+ * activation codes qx_dev int8 [M][K] (values in [-7, 7]).  The codes are first
+ * re-laid-out into the workspace (convrot_workspace_bytes(M, K, 64) bytes),
+ * then the GEMM kernel of convrot_linear runs with its epilogue replaced by
+ * an int32 store. */
+int convrot_gemm_i32(const int8_t* qx_dev, int64_t M, int64_t K, const void* image_dev, int64_t N,
+                     int32_t* acc_dev, void* workspace_dev, size_t ws_bytes, void* stream);
+
+/* ---- host layout tools (host memory, no HIP call) ----------------------- */
+
+/* int8 codes [N][K] <-> N x packed-K uint8 [N][K/2] (low nibble = even k). */
+int convrot_host_pack_nk(const int8_t* codes_host, int64_t N, int64_t K, uint8_t* nk_host);
+int convrot_host_unpack_nk(const uint8_t* nk_host, int64_t N, int64_t K, int8_t* codes_host);
+/* N x packed-K [N][K/2] <-> K x packed-N [K][N/2] (low nibble = even n);
+ * N and K even. */
+int convrot_host_nk_to_kn(const uint8_t* nk_host, int64_t N, int64_t K, uint8_t* kn_host);
+int convrot_host_kn_to_nk(const uint8_t* kn_host, int64_t N, int64_t K, uint8_t* nk_host);
+/* N x packed-K <-> weight image (convrot_weight_image_bytes(N, K, 64) bytes);
+ * image_to_nk ignores the padding. */
+int convrot_host_nk_to_image(const uint8_t* nk_host, int64_t N, int64_t K, uint8_t* image_host);
+int convrot_host_image_to_nk(const uint8_t* image_host, int64_t N, int64_t K, uint8_t* nk_host);
+/* Activation-code image (workspace head) -> int8 codes [M][K]. */
+int convrot_host_act_image_to_codes(const uint8_t* image_host, int64_t M, int64_t K, int8_t* codes_host);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONVROT_H */

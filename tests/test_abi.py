@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI, runnable without a GPU: the library loads and
+exports every function include/convrot.h declares; sizes, argument checks and
+status codes; the host layout tools against the oracle's packing (convrot-mlx
+README, "What is included": reversible N x packed-K and K x packed-N layouts).
+No device entry point is called here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from w4a4_rotated_bit_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = _declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding knows the signature of each one
+    assert set(names) == set(B._SIGNATURES), set(names) ^ set(B._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert B.convrot_version().startswith("convrot-gfx950")
+    for code in (0, 1, 2, 3, 4):
+        assert B.convrot_status_string(code)
+    assert B.convrot_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K,g,want", [
+    (1024, 1024, 256, 1024 * 1024 // 2),
+    (9216, 3072, 256, 9216 * 3072 // 2),
+    (33, 192, 64, 64 * 256 // 2),        # N padded to 64, K to 256
+])
+def test_weight_image_bytes(N, K, g, want):
+    assert B.convrot_weight_image_bytes(N, K, g) == want
+
+
+def test_workspace_bytes():
+    # activation image (M up to 32 rows, K up to 128) + 256-aligned scales
+    assert B.convrot_workspace_bytes(1, 3072, 256) == 32 * 3072 + 32 * 4
+    assert B.convrot_workspace_bytes(1536, 3072, 256) == 1536 * 3072 + 1536 * 4
+    assert B.convrot_workspace_bytes(5, 192, 64) == 32 * 256 + 32 * 4
+
+
+@pytest.mark.parametrize("N,K,g", [(16, 100, 64), (16, 512, 128), (16, 0, 64), (-1, 256, 256), (16, 32768, 256)])
+def test_size_queries_reject_bad_shapes(N, K, g):
+    with pytest.raises(B.ConvRotError) as e:
+        B.convrot_weight_image_bytes(N, K, g)
+    assert e.value.status == B.CONVROT_EINVAL
+
+
+def _validate_linear(**over):
+    args = dict(X=4096, M=64, K=1024, image=8192, sw=16384, bias=0, N=1024, g=256, Y=32768, ws=65536,
+                ws_bytes=B.convrot_workspace_bytes(64, 1024, 256))
+    args.update(over)
+    return B.convrot_validate_linear(args["X"], args["M"], args["K"], args["image"], args["sw"], args["bias"],
+                                     args["N"], args["g"], args["Y"], args["ws"], args["ws_bytes"])
+
+
+def test_validate_linear_statuses():
+    assert _validate_linear() == B.CONVROT_OK
+    assert _validate_linear(bias=2) == B.CONVROT_OK
+    assert _validate_linear(g=128) == B.CONVROT_EINVAL
+    assert _validate_linear(K=1000) == B.CONVROT_EINVAL
+    assert _validate_linear(X=0) == B.CONVROT_EINVAL
+    assert _validate_linear(Y=0) == B.CONVROT_EINVAL
+    assert _validate_linear(image=0) == B.CONVROT_EINVAL
+    assert _validate_linear(X=4100) == B.CONVROT_EINVAL           # misaligned
+    assert _validate_linear(sw=16386) == B.CONVROT_EINVAL         # misaligned
+    assert _validate_linear(bias=3) == B.CONVROT_EINVAL           # misaligned
+    assert _validate_linear(ws_bytes=1000) == B.CONVROT_EWORKSPACE
+    assert _validate_linear(M=0, X=0, Y=0) == B.CONVROT_OK        # empty input is a no-op
+    assert _validate_linear(N=0) == B.CONVROT_OK
+    assert _validate_linear(M=-1) == B.CONVROT_EINVAL
+
+
+def test_validate_weight_statuses():
+    assert B.convrot_validate_weight(4096, 1024, 1024, 256, 8192, 16384) == B.CONVROT_OK
+    assert B.convrot_validate_weight(4096, 1024, 1024, 32, 8192, 16384) == B.CONVROT_EINVAL
+    assert B.convrot_validate_weight(0, 1024, 1024, 256, 8192, 16384) == B.CONVROT_EINVAL
+    assert B.convrot_validate_weight(4096, 1024, 1000, 64, 8192, 16384) == B.CONVROT_EINVAL
+    assert B.convrot_validate_weight(0, 0, 1024, 256, 0, 0) == B.CONVROT_OK
+
+
+# --------------------------------------------------------------------------
+# host layout tools vs the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(32, 128), (48, 256), (70, 192), (1, 64)])
+def test_host_pack_and_transpose_match_oracle(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    nk = B.convrot_host_pack_nk(codes)
+    assert np.array_equal(nk, oracle.pack_nk(codes))
+    assert np.array_equal(B.convrot_host_unpack_nk(nk, K), codes)
+    if N % 2 == 0:
+        kn = B.convrot_host_nk_to_kn(nk, N, K)
+        assert np.array_equal(kn, oracle.nk_to_kn(nk, N, K))
+        assert np.array_equal(B.convrot_host_kn_to_nk(kn, N, K), nk)
+
+
+@pytest.mark.parametrize("N,K", [(32, 128), (64, 384), (70, 192), (5, 64), (96, 1024)])
+def test_host_image_round_trip(N, K):
+    rng = np.random.default_rng(7 + N + K)
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    nk = oracle.pack_nk(codes)
+    image = B.convrot_host_nk_to_image(nk, N, K)
+    assert image.size == B.convrot_weight_image_bytes(N, K, 64)
+    assert np.array_equal(B.convrot_host_image_to_nk(image, N, K), nk)
+    # every code lands somewhere and the padding is zero: the image holds
+    # exactly the nibbles of nk (as a multiset) plus zeros
+    nz_img = np.count_nonzero(np.concatenate([image & 0xF, image >> 4]))
+    nz_nk = np.count_nonzero(np.concatenate([nk & 0xF, nk >> 4]))
+    assert nz_img == nz_nk
+
+
+def test_host_image_widening_property():
+    """Inside the image, (word << 4) & 0xF0F0F0F0 and word & 0xF0F0F0F0 are
+    16 x the codes k..k+3 and k+4..k+7 as signed bytes (checked on a unit)."""
+    N, K = 32, 128
+    rng = np.random.default_rng(1)
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = B.convrot_host_nk_to_image(oracle.pack_nk(codes), N, K)
+    words = image.view(np.uint32)
+    lo = ((words << 4) & 0xF0F0F0F0).astype(np.uint32).view(np.int8).astype(np.int32)
+    hi = (words & 0xF0F0F0F0).astype(np.uint32).view(np.int8).astype(np.int32)
+    assert np.all(lo % 16 == 0) and np.all(hi % 16 == 0)
+    got = np.sort(np.concatenate([lo, hi]) // 16)
+    assert np.array_equal(got, np.sort(codes.ravel().astype(np.int32)))

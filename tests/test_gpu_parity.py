@@ -1,0 +1,249 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded
+synthetic inputs.  Small shapes are compared element by element and span
+several tiles with ragged tails; the full diffusion-transformer shapes are
+compared on sampled rows and columns plus properties that hold at any size.
+
+Method: convrot-mlx README, "What is included" (grouped normalized Hadamard
+rotation for g = 64/256, symmetric rowwise absmax INT4 in [-7, 7],
+reversible packed layouts), "Install and test" (rotation, activation
+quantization, integer product, scaling, bias); comfy-quants issue "convrot
+is ... QuaRot Stage 1c", section 1 (R = I_G (x) H)."""
+import numpy as np
+import pytest
+
+import oracle
+from w4a4_rotated_bit_amd import synth
+
+from ._parity import compare_codes, compare_rotated, compare_y
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _host_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# rotation + quantization (K1)
+# --------------------------------------------------------------------------
+
+PREP_SHAPES = [
+    (5, 256, 256), (37, 1024, 256), (64, 3072, 256), (3, 12288, 256), (2, 16384, 256),
+    (7, 192, 64), (128, 2048, 64), (1, 64, 64), (33, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("rows,K,g", PREP_SHAPES)
+def test_prepare_rows_parity(gpu, rows, K, g):
+    x = synth.random_bf16((rows, K), seed=rows * 7 + K + g, outliers=max(1, K // 200))
+    x[0, :] = 0  # an all-zero row
+    q, s, r = gpu.convrot_prepare_rows(_dev(x), g, want_rotated=True)
+    oq, os_, orr = oracle.prepare_rows(x, g, want_rotated=True)
+    gq, gs, gr = q.cpu().numpy(), s.cpu().numpy(), r.cpu().numpy()
+    compare_rotated(gr, orr)
+    assert np.array_equal(gs, os_), "scales differ"
+    compare_codes(gq, oq, orr, os_)
+    assert gs[0] == 0 and np.all(gq[0] == 0)
+
+
+def test_prepare_rows_golden_ties(gpu):
+    import json
+    import os
+    from fractions import Fraction
+    with open(os.path.join(os.path.dirname(__file__), "golden", "quant_ties.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        g, K = case["g"], case["K"]
+        x = np.zeros((K,), dtype=np.float32)
+        for gi, grp in enumerate(case["groups"]):
+            x[gi * g:(gi + 1) * g:2] = float(Fraction(grp["x_even"]))
+            x[gi * g + 1:(gi + 1) * g:2] = float(Fraction(grp["x_odd"]))
+        q, s, _ = gpu.convrot_prepare_rows(_dev(synth.to_bf16_bits(x)[None, :]), g)
+        want = np.zeros((K,), np.int8)
+        for k, v in case["codes_nonzero"].items():
+            want[int(k)] = v
+        assert np.array_equal(q.cpu().numpy()[0], want), case["name"]
+        assert float(s.cpu().numpy()[0]) == float(Fraction(case["scale"])), case["name"]
+
+
+# --------------------------------------------------------------------------
+# weight preparation and layouts (K1 + K3)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,g", [(70, 512, 256), (32, 256, 256), (45, 192, 64), (256, 1024, 64)])
+def test_weight_image_and_nk_parity(gpu, N, K, g):
+    w = synth.random_bf16((N, K), seed=N + K, std=0.02)
+    oq, osw = oracle.prepare_weight(w, g)
+    onk = oracle.pack_nk(oq)
+    W = _dev(w)
+    image, sw = gpu.convrot_prepare_weight(W, g)
+    nk, sw2 = gpu.convrot_quantize_weight(W, g)
+    osr = oracle.rotate_rows(w, g)
+    assert np.array_equal(sw.cpu().numpy(), osw) and np.array_equal(sw2.cpu().numpy(), osw)
+    img = image.cpu().numpy()
+    compare_codes(oracle.unpack_nk(gpu.convrot_host_image_to_nk(img, N, K), K), oq, osr, osw, "image codes")
+    compare_codes(oracle.unpack_nk(nk.cpu().numpy(), K), oq, osr, osw, "nk codes")
+    # the device repack of N x packed-K is byte-identical to the direct image
+    image2 = gpu.convrot_repack_nk_to_image(nk, N, K)
+    assert np.array_equal(image2.cpu().numpy(), img)
+    # and so is the host repack (layout definition shared by host and device)
+    assert np.array_equal(gpu.convrot_host_nk_to_image(nk.cpu().numpy(), N, K), img)
+    # lossless round trip through K x packed-N
+    if N % 2 == 0:
+        kn = gpu.convrot_host_nk_to_kn(nk.cpu().numpy(), N, K)
+        assert np.array_equal(kn, oracle.nk_to_kn(onk, N, K))
+        assert np.array_equal(gpu.convrot_host_kn_to_nk(kn, N, K), onk)
+
+
+# --------------------------------------------------------------------------
+# integer product (K2 without the epilogue)
+# --------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
+               (513, 257, 256), (17, 33, 12288)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_bit_exact(gpu, M, N, K):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), N, K))
+    acc = gpu.convrot_gemm_i32(_dev(qx), image, N).cpu().numpy()
+    assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
+
+
+def test_gemm_i32_integer_edges(gpu):
+    K = 12288
+    qx = np.stack([np.full(K, 7, np.int8), np.full(K, -7, np.int8), np.zeros(K, np.int8)])
+    qw = np.stack([np.full(K, 7, np.int8), np.full(K, -7, np.int8)] * 16)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), 32, K))
+    acc = gpu.convrot_gemm_i32(_dev(qx), image, 32).cpu().numpy()
+    assert acc[0, 0] == 49 * K and acc[0, 1] == -49 * K and acc[1, 0] == -49 * K and acc[1, 1] == 49 * K
+    assert np.all(acc[2] == 0)
+    assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
+
+
+# --------------------------------------------------------------------------
+# the whole linear
+# --------------------------------------------------------------------------
+
+def _linear_parity(gpu, x, w, bias, g):
+    N, K = w.shape
+    oq_w, osw = oracle.prepare_weight(w, g)
+    y_or, parts = oracle.linear(x, oq_w, osw, bias, g, want_parts=True)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), g)
+    ws = gpu.new_workspace(x.shape[0], K, g)
+    Y = gpu.convrot_linear(_dev(x), image, sw, None if bias is None else _dev(bias), N, g, workspace=ws)
+    gy = _host_bits(Y)
+    # codes of X (from the workspace) and of W (from the image)
+    M = x.shape[0]
+    qx = gpu.convrot_host_act_image_to_codes(ws.cpu().numpy(), M, K)
+    orx = oracle.rotate_rows(x, g)
+    compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
+    qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
+    compare_codes(qw, oq_w, oracle.rotate_rows(w, g), osw, "weight codes")
+    rows_ok = np.all(qx == parts["qx"], axis=1) & bool(np.array_equal(qw, oq_w))
+    compare_y(gy, y_or, rows_ok)
+    return gy, y_or
+
+
+@pytest.mark.parametrize("name", ["tiny_m64_k1024_n1024_g256", "g64_m128_k2048_n2048"])
+def test_linear_small_workloads_full(gpu, name):
+    inp = synth.make(name)
+    wl = inp["workload"]
+    _linear_parity(gpu, inp["x"], inp["w"], inp["bias"], wl.g)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 96, 256, 256), (37, 70, 512, 256), (300, 520, 1280, 256),
+                                     (33, 64, 192, 64), (257, 300, 2048, 64), (2, 2, 64, 64)])
+def test_linear_ragged_shapes(gpu, M, N, K, g):
+    x = synth.random_bf16((M, K), seed=M + N, outliers=3)
+    w = synth.random_bf16((N, K), seed=N + K, std=0.02)
+    b = synth.random_bf16((N,), seed=K, std=0.01)
+    _linear_parity(gpu, x, w, b, g)
+
+
+def test_linear_no_bias_and_zero_rows(gpu):
+    M, N, K, g = 40, 64, 512, 256
+    x = synth.random_bf16((M, K), seed=3, outliers=2)
+    x[5] = 0
+    x[39] = 0
+    w = synth.random_bf16((N, K), seed=4, std=0.02)
+    gy, _ = _linear_parity(gpu, x, w, None, g)
+    assert np.all(gy[5] == 0) and np.all(gy[39] == 0)
+    b = synth.random_bf16((N,), seed=5, std=0.01)
+    gy, _ = _linear_parity(gpu, x, w, b, g)
+    assert np.array_equal(gy[5], b) and np.array_equal(gy[39], b)
+
+
+def test_linear_empty_is_noop(gpu):
+    import torch
+    w = synth.random_bf16((32, 256), seed=1, std=0.02)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), 256)
+    X = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    Y = gpu.convrot_linear(X, image, sw, None, 32, 256, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert Y.shape == (0, 32)
+
+
+def test_linear_rejects_bad_arguments(gpu):
+    import torch
+    w = synth.random_bf16((32, 256), seed=1, std=0.02)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), 256)
+    X = _dev(synth.random_bf16((4, 256), seed=2))
+    with pytest.raises(gpu.ConvRotError) as e:
+        gpu.convrot_linear(X, image, sw, None, 32, 128)
+    assert e.value.status == gpu.CONVROT_EINVAL
+    with pytest.raises(gpu.ConvRotError) as e:
+        gpu.convrot_linear(X, image, sw, None, 32, 256, workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == gpu.CONVROT_EWORKSPACE
+
+
+FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_mlp_down_m1536_k12288_n3072",
+        "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_linear_full_size_sampled(gpu, name):
+    """Full shapes, the launch configuration the benchmark times; the oracle
+    recomputes sampled rows x sampled columns from scratch."""
+    import torch
+    inp = synth.make(name)
+    wl = inp["workload"]
+    M, N, K, g = wl.M, wl.N, wl.K, wl.g
+    W = _dev(inp["w"])
+    image, sw = gpu.convrot_prepare_weight(W, g)
+    ws = gpu.new_workspace(M, K, g)
+    Y = gpu.convrot_linear(_dev(inp["x"]), image, sw, _dev(inp["bias"]), N, g, workspace=ws)
+    Y2 = gpu.convrot_linear(_dev(inp["x"]), image, sw, _dev(inp["bias"]), N, g)
+    torch.cuda.synchronize()
+    gy = _host_bits(Y)
+    assert np.array_equal(gy, _host_bits(Y2)), "two runs differ"
+    assert np.all(np.isfinite(synth.bf16_bits_to_f32(gy)))
+    rng = np.random.default_rng(2024)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 24), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=192, replace=False)]))
+    oq_x, osx, orx = oracle.prepare_rows(inp["x"][rows], g, want_rotated=True)
+    oq_w, osw, orw = oracle.prepare_rows(inp["w"][cols], g, want_rotated=True)
+    # scales and codes
+    assert np.array_equal(sw.cpu().numpy()[cols], osw)
+    wsh = ws.cpu().numpy()
+    gq_x = gpu.convrot_host_act_image_to_codes(wsh, M, K)[rows]
+    n_x = compare_codes(gq_x, oq_x, orx, osx, "activation codes")
+    qw_all = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
+    assert qw_all.min() >= -7 and qw_all.max() <= 7
+    assert np.all(np.abs(qw_all).max(axis=1) == 7)
+    n_w = compare_codes(qw_all[cols], oq_w, orw, osw, "weight codes")
+    y_or = oracle.epilogue(oracle.gemm_i32(oq_x, oq_w), osx, osw, inp["bias"][cols])
+    rows_ok = np.all(gq_x == oq_x, axis=1) & (n_w == 0)
+    compare_y(gy[np.ix_(rows, cols)], y_or, rows_ok)
+    print(f"{name}: code mismatches x={n_x} w={n_w}")

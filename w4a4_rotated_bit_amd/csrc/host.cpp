@@ -1,0 +1,195 @@
+// host.cpp -- size queries, argument checks and host layout tools of the
+// ConvRot C ABI.  Pure C++: nothing here calls the HIP runtime, so every
+// function works on a machine without a GPU.
+#include <string.h>
+
+#include "../../include/convrot.h"
+#include "internal.h"
+#include "layout.h"
+
+using namespace convrot;
+
+namespace convrot {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_shape(int64_t rows, int64_t K, int g)
+{
+    if (g != 64 && g != 256) return CONVROT_EINVAL;
+    if (K < 1 || K > kMaxK || K % g != 0) return CONVROT_EINVAL;
+    if (rows < 0 || rows > kMaxRows) return CONVROT_EINVAL;
+    return CONVROT_OK;
+}
+
+size_t act_image_bytes(int64_t M, int64_t K) { return (size_t)round_up(M, kTileRows) * (size_t)round_up(K, kTileK); }
+
+size_t workspace_sx_offset(int64_t M, int64_t K) { return (size_t)round_up((int64_t)act_image_bytes(M, K), 256); }
+
+size_t workspace_bytes(int64_t M, int64_t K)
+{
+    return workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows);
+}
+
+size_t weight_image_bytes(int64_t N, int64_t K) { return (size_t)round_up(N, kTileRows) * (size_t)round_up(K, kTileK) / 2; }
+
+}  // namespace convrot
+
+extern "C" {
+
+const char* convrot_status_string(int status)
+{
+    switch (status) {
+        case CONVROT_OK: return "ok";
+        case CONVROT_EINVAL: return "invalid argument (size, group, null or misaligned pointer)";
+        case CONVROT_EWORKSPACE: return "workspace too small";
+        case CONVROT_EHIP: return "HIP runtime error at launch";
+        case CONVROT_EDEVICE: return "current device is not a gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+const char* convrot_version(void) { return "convrot-gfx950 1.0"; }
+
+int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
+{
+    if (!bytes) return CONVROT_EINVAL;
+    int rc = check_shape(N, K, g);
+    if (rc) return rc;
+    *bytes = weight_image_bytes(N, K);
+    return CONVROT_OK;
+}
+
+int convrot_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes)
+{
+    if (!bytes) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, g);
+    if (rc) return rc;
+    *bytes = workspace_bytes(M, K);
+    return CONVROT_OK;
+}
+
+int convrot_validate_weight(const void* W, int64_t N, int64_t K, int g, const void* image, const float* sw)
+{
+    int rc = check_shape(N, K, g);
+    if (rc) return rc;
+    if (N == 0) return CONVROT_OK;
+    if (!W || !image || !sw) return CONVROT_EINVAL;
+    if (!aligned(W, 16) || !aligned(image, 16) || !aligned(sw, 4)) return CONVROT_EINVAL;
+    return CONVROT_OK;
+}
+
+int convrot_validate_linear(const void* X, int64_t M, int64_t K, const void* image, const float* sw,
+                            const void* bias, int64_t N, int g, const void* Y, const void* ws, size_t ws_bytes)
+{
+    int rc = check_shape(M, K, g);
+    if (rc) return rc;
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if (!X || !image || !sw || !Y || !ws) return CONVROT_EINVAL;
+    if (!aligned(X, 16) || !aligned(image, 16) || !aligned(Y, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
+    if (!aligned(sw, 4) || (bias && !aligned(bias, 2))) return CONVROT_EINVAL;
+    if (ws_bytes < workspace_bytes(M, K)) return CONVROT_EWORKSPACE;
+    return CONVROT_OK;
+}
+
+// ---- host layout tools ---------------------------------------------------
+
+static inline uint8_t lo4(int8_t q) { return (uint8_t)q & 0x0F; }
+static inline int8_t sext4(uint8_t v) { return (int8_t)((int8_t)(v << 4) >> 4); }
+
+int convrot_host_pack_nk(const int8_t* codes, int64_t N, int64_t K, uint8_t* nk)
+{
+    if (!codes || !nk || N < 0 || K < 2 || K % 2) return CONVROT_EINVAL;
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t* q = codes + n * K;
+        uint8_t* p = nk + n * (K / 2);
+        for (int64_t j = 0; j < K / 2; ++j) p[j] = (uint8_t)(lo4(q[2 * j]) | (lo4(q[2 * j + 1]) << 4));
+    }
+    return CONVROT_OK;
+}
+
+int convrot_host_unpack_nk(const uint8_t* nk, int64_t N, int64_t K, int8_t* codes)
+{
+    if (!codes || !nk || N < 0 || K < 2 || K % 2) return CONVROT_EINVAL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j) {
+            uint8_t b = nk[n * (K / 2) + j];
+            codes[n * K + 2 * j] = sext4(b & 0x0F);
+            codes[n * K + 2 * j + 1] = sext4(b >> 4);
+        }
+    return CONVROT_OK;
+}
+
+// Nibble of code (n, k) in an N x packed-K buffer.
+static inline uint8_t nk_nib(const uint8_t* nk, int64_t K, int64_t n, int64_t k)
+{
+    uint8_t b = nk[n * (K / 2) + k / 2];
+    return (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+}
+
+int convrot_host_nk_to_kn(const uint8_t* nk, int64_t N, int64_t K, uint8_t* kn)
+{
+    if (!nk || !kn || N < 2 || K < 2 || N % 2 || K % 2) return CONVROT_EINVAL;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N / 2; ++j)
+            kn[k * (N / 2) + j] = (uint8_t)(nk_nib(nk, K, 2 * j, k) | (nk_nib(nk, K, 2 * j + 1, k) << 4));
+    return CONVROT_OK;
+}
+
+int convrot_host_kn_to_nk(const uint8_t* kn, int64_t N, int64_t K, uint8_t* nk)
+{
+    if (!nk || !kn || N < 2 || K < 2 || N % 2 || K % 2) return CONVROT_EINVAL;
+    // K x packed-N is N x packed-K with the roles of N and K swapped
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j)
+            nk[n * (K / 2) + j] = (uint8_t)(nk_nib(kn, N, 2 * j, n) | (nk_nib(kn, N, 2 * j + 1, n) << 4));
+    return CONVROT_OK;
+}
+
+int convrot_host_nk_to_image(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image)
+{
+    if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
+    const int64_t K_pad = round_up(K, kTileK);
+    memset(image, 0, weight_image_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; k += 8) {
+            uint32_t word = 0;
+            for (int b = 0; b < 4; ++b)
+                word |= (uint32_t)(nk_nib(nk, K, n, k + b) | (nk_nib(nk, K, n, k + 4 + b) << 4)) << (8 * b);
+            memcpy(image + wgt_word_offset(n, k, K_pad), &word, 4);
+        }
+    return CONVROT_OK;
+}
+
+int convrot_host_image_to_nk(const uint8_t* image, int64_t N, int64_t K, uint8_t* nk)
+{
+    if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
+    const int64_t K_pad = round_up(K, kTileK);
+    memset(nk, 0, (size_t)N * (size_t)(K / 2));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; k += 8) {
+            uint32_t word;
+            memcpy(&word, image + wgt_word_offset(n, k, K_pad), 4);
+            uint8_t* p = nk + n * (K / 2) + k / 2;
+            for (int b = 0; b < 4; ++b) {
+                uint8_t byte = (uint8_t)(word >> (8 * b));
+                uint8_t c_lo = byte & 0x0F;   // code k + b
+                uint8_t c_hi = byte >> 4;     // code k + 4 + b
+                int e0 = b, e1 = 4 + b;       // positions within the 8 codes
+                p[e0 / 2] |= (e0 & 1) ? (uint8_t)(c_lo << 4) : c_lo;
+                p[e1 / 2] |= (e1 & 1) ? (uint8_t)(c_hi << 4) : c_hi;
+            }
+        }
+    return CONVROT_OK;
+}
+
+int convrot_host_act_image_to_codes(const uint8_t* image, int64_t M, int64_t K, int8_t* codes)
+{
+    if (!image || !codes || M < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
+    const int64_t K_pad = round_up(K, kTileK);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; k += 16) memcpy(codes + m * K + k, image + act_chunk_offset(m, k, K_pad), 16);
+    return CONVROT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// kernels.h -- launch interface between the C ABI and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+enum PrepOut { OUT_ACT_IMAGE = 0, OUT_WGT_IMAGE = 1, OUT_ROWMAJOR = 2, OUT_NK = 3 };
+enum GemmOut { GEMM_OUT_BF16 = 0, GEMM_OUT_I32 = 1 };
+
+struct PrepArgs {
+    const uint16_t* X;   // bf16 [rows][K]
+    int64_t rows;        // rows holding data
+    int64_t rows_pad;    // rows written (image modes: rows rounded up to 32)
+    int64_t K, K_pad;    // K_pad = K rounded up to 128 (image modes)
+    uint8_t* out;        // codes in the layout of the mode
+    float* scales;       // [rows]
+    float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
+    int team;            // lanes per row (set by launch_prep)
+    int slices_pad;      // K_pad / 64 (set by launch_prep)
+};
+
+struct GemmArgs {
+    const uint8_t* act;  // activation image
+    const uint8_t* wgt;  // weight image
+    const float* sx;     // [M]
+    const float* sw;     // [N]
+    const uint16_t* bias;  // bf16 [N] or nullptr
+    void* out;           // bf16 or int32 [M][N]
+    int64_t M, N;
+    int MT, NT, KB;      // 32-row tiles, 32-column tiles, 128-K blocks
+    int tiles_m, tiles_n;  // set by launch_gemm
+};
+
+void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
+void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
+void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, hipStream_t s);
+void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s);
+
+}  // namespace convrot
