@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the ConvRot W4A4 linear on one MI355X.
+
+One step = one complete ``convrot_linear`` call (rotation, row absmax and
+INT4 quantization of the activations, INT8-MFMA product against the packed
+INT4 weight image, scale + bias epilogue to bf16) over one batch of seeded
+synthetic input already resident in HBM.  The weight is prepared once before
+timing (an offline step; its time is reported separately).  Steps cycle
+through enough independent buffer sets (>= 512 MiB in total) that the 256 MiB
+Infinity Cache cannot serve the weights from a previous step.
+
+Prints one JSON line on stdout.  ``value`` is effective TOPS = 2*M*N*K per
+step time.  ``roofline`` rates the GEMM kernel (the dominant one) from its
+average launch duration, measured with HIP events on the launch stream,
+against the dense INT8 matrix-core peak.  ``cpu_baseline`` is the CPU oracle
+timed on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ConvRot W4A4 linear effective TOPS + GB/s and % of roofline, FLUX shapes"
+DEFAULT_WORKLOAD = "flux_qkv_m1536_k3072_n9216"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 matrix-core peak, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCE = os.path.join(ROOT, "w4a4_rotated_bit_amd", "csrc", "kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, gemm_ops_unit_launches: int):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, target_s: float):
+    """The oracle's linear on a bounded sample of rows (weight prepared by the
+    oracle beforehand, untimed, like the GPU's offline weight step)."""
+    import oracle
+    wl = inp["workload"]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    qw, sw = oracle.prepare_weight(inp["w"], wl.g, threads=threads)
+    log(f"cpu baseline: oracle weight preparation {time.perf_counter() - t0:.1f} s (untimed)")
+    probe = min(wl.M, 8)
+    t0 = time.perf_counter()
+    oracle.linear(inp["x"][:probe], qw, sw, inp["bias"], wl.g, threads=threads)
+    dt = time.perf_counter() - t0
+    rows = int(max(probe, min(wl.M, probe * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], wl.g, threads=threads)
+    dt = time.perf_counter() - t0
+    tops = 2.0 * rows * wl.N * wl.K / dt / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} rows of X against the full {wl.N}x{wl.K} weight "
+                      f"(complete linear: rotation, quantization, int64 dot products, epilogue), "
+                      f"{dt:.2f} s"}
+
+
+def copy_probe(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-bytes", type=float, default=512 * 2**20, help="total bytes of rotating buffer sets")
+    ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from w4a4_rotated_bit_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 10)
+        return
+
+    binding.load()
+    inp = synth.make(args.workload)
+    wl = inp["workload"]
+    M, N, K, g = wl.M, wl.N, wl.K, wl.g
+    log(f"workload {wl.name}: M={M} N={N} K={K} g={g}")
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    X0, W0, B0 = dev_bf16(inp["x"]), dev_bf16(inp["w"]), dev_bf16(inp["bias"])
+    # offline weight preparation (timed separately, informational)
+    image0, sw0 = binding.convrot_prepare_weight(W0, g)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(3):
+        binding.convrot_prepare_weight(W0, g, image=image0, sw=sw0)
+    ev1.record()
+    torch.cuda.synchronize()
+    weight_prep_ms = ev0.elapsed_time(ev1) / 3
+
+    ws_bytes = binding.convrot_workspace_bytes(M, K, g)
+    set_bytes = X0.numel() * 2 + image0.numel() + sw0.numel() * 4 + B0.numel() * 2 + M * N * 2 + ws_bytes
+    n_sets = int(min(64, max(1, -(-args.cold_bytes // set_bytes))))
+    sets = []
+    for i in range(n_sets):
+        sets.append(dict(X=X0.clone(), image=image0.clone(), sw=sw0.clone(), bias=B0.clone(),
+                         Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                         ws=torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")))
+    del W0
+    torch.cuda.synchronize()
+    log(f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB each")
+
+    def step(i):
+        s = sets[i % n_sets]
+        binding.convrot_linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # GEMM kernel alone: per-launch HIP events on the launch stream, same cold rotation
+    n_gemm = max(10, min(args.steps, 200))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_gemm)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_gemm)]
+    for i in range(n_gemm):
+        s = sets[i % n_sets]
+        binding.convrot_prepare_activations(s["X"], g, s["ws"])
+        starts[i].record()
+        binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
+        ends[i].record()
+    torch.cuda.synchronize()
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    # activation preparation alone, the same way
+    for i in range(n_gemm):
+        s = sets[i % n_sets]
+        starts[i].record()
+        binding.convrot_prepare_activations(s["X"], g, s["ws"])
+        ends[i].record()
+    torch.cuda.synchronize()
+    prep_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    gbs = wl.bytes_alg / (ms_per_step * 1e-3) / 1e9
+    traffic = read_traffic(wl.name, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": g, "x_kind": wl.x_kind,
+                   "outlier_channels": wl.outlier_count, "cold_buffer_sets": n_sets},
+        "gbps": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "int8_frac": round(value / PEAK_INT8_TOPS, 4),
+        "kernel_us": {"prep": round(prep_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)},
+        "weight_prep_ms": round(weight_prep_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

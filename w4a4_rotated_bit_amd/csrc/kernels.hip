@@ -49,22 +49,43 @@ __device__ inline double quad_xor(double v)
     return __hiloint2double(hi, lo);
 }
 
-// Code = clamp(rint(fl32(r / s)), -7, 7).  Fast path: y = r * rcp(s) is within
-// 2 ulp of r / s (|y| < 8, so 2 ulp <= 2^-20); whenever y is farther than
-// 2^-18 from a half-integer, rint(y) equals rint(fl32(r / s)) because no
-// rounding boundary lies between them.  Near a half-integer (or when s is not
-// a normal number) the correctly rounded binary32 division decides.
-__device__ inline int8_t quantize_one(float r, float s, float inv, bool exact_only)
+// Codes = clamp(rint(fl32(r / s)), -7, 7) for the 8 x 8 values of a lane.
+// Fast path: y = r * rcp(s) is within 2 ulp of r / s (|y| < 8, so the error is
+// below 2^-20); whenever y is farther than 2^-18 from a half-integer, rint(y)
+// equals rint(fl32(r / s)) because no rounding boundary lies between them.
+// Elements near a half-integer (and rows whose s is not a normal number) take
+// the correctly rounded binary32 division, in a branch that is skipped unless
+// some lane of the wave needs it.
+__device__ inline void quantize_lane(const float (&r)[8][8], float s, bool zero_row, int8_t (&q)[8][8])
 {
-    float q;
-    const float y = r * inv;
-    const float ry = rintf(y);
-    if (exact_only || fabsf(fabsf(y - ry) - 0.5f) < 0x1p-18f)
-        q = rintf(r / s);  // IEEE binary32 division, round half to even
-    else
-        q = ry;
-    q = fminf(fmaxf(q, -7.0f), 7.0f);
-    return (int8_t)q;
+    const bool exact_only = !(s >= 0x1p-126f);
+    const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
+    float qf[8][8];
+    bool need = exact_only && !zero_row;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = r[j][e] * inv;
+            const float ry = rintf(y);
+            need |= fabsf(fabsf(y - ry) - 0.5f) < 0x1p-18f;
+            qf[j][e] = ry;
+        }
+    if (need && !zero_row) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = r[j][e] * inv;
+                if (exact_only || fabsf(fabsf(y - rintf(y)) - 0.5f) < 0x1p-18f)
+                    qf[j][e] = rintf(r[j][e] / s);  // IEEE binary32 division, round half to even
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            q[j][e] = zero_row ? (int8_t)0 : (int8_t)(int)fminf(fmaxf(qf[j][e], -7.0f), 7.0f);
 }
 
 __device__ inline uint32_t nib(int8_t q) { return (uint32_t)(uint8_t)q & 0xFu; }
@@ -206,8 +227,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     }
     const bool zero_row = !(amax > 0.0f);
     const float s = zero_row ? 0.0f : amax / 7.0f;  // IEEE binary32 division
-    const bool exact_only = !(s >= 0x1p-126f);      // s not a normal number
-    const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
 
     if (!row_in) return;
     if (row_valid && slice == 0) a.scales[row] = s;
@@ -215,12 +234,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     const bool write_slice = (MODE == OUT_ACT_IMAGE || MODE == OUT_WGT_IMAGE) ? (slice < a.slices_pad) : has_data;
     if (!write_slice) return;
 
+    int8_t qa[8][8];
+    quantize_lane(r, s, zero_row, qa);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int64_t k = slice_k<G>(slice, j);
-        int8_t q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = zero_row ? (int8_t)0 : quantize_one(r[j][e], s, inv, exact_only);
+        const int8_t* q = qa[j];
         if constexpr (MODE == OUT_ACT_IMAGE) {
             uint2 w;
             w.x = pack4_i8(q);
@@ -253,64 +272,70 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 // ---------------------------------------------------------------------------
 // gemm_kernel
 //
-// Block tile 256 (M) x 256 (N), K stepped 128 at a time through a double
-// buffer in LDS: 8 activation units (4 KB each) + 8 weight units (2 KB each)
-// = 48 KB per stage, copied global -> LDS with global_load_lds_dwordx4 (the
-// images are stored in exactly the LDS order, so every copy is a straight
-// 1 KB run per wave instruction).  Four waves in a 2 x 2 arrangement each own
-// a 128 x 128 output tile = 4 x 4 MFMA 32x32x32 tiles.  Weight nibbles are
-// widened to INT8 x 16 in registers right after the LDS read; the int32
-// accumulators are divided by 16 (exact) in the epilogue.
+// Block tile 256 (M) x 256 (N); K advances 128 at a time through a ring of
+// three LDS stages, each holding 8 activation units (4 KB each) and 8 weight
+// units (2 KB each) = 48 KB.  The images are stored in exactly the LDS order,
+// so every global -> LDS copy is a straight 1 KB run per wave instruction
+// (global_load_lds_dwordx4, 16 bytes per lane, no registers involved); the
+// copy of stage k+2 is in flight while stage k feeds the matrix cores.  The
+// three stages are three distinct arrays and the main loop is unrolled by
+// three, so every LDS read names a stage that no copy in flight targets.
+// Eight waves, two per SIMD, each own a 128 (M) x 64 (N) output tile: 4 x 2
+// MFMA 32x32x32 tiles computed as W . X^T, so that each lane ends up holding
+// four consecutive output columns of one row (8-byte stores).  Weight nibbles
+// are widened to INT8 x 16 in registers right after the LDS read; the int32
+// sums are divided by 16 (exact) in the epilogue.
 // ---------------------------------------------------------------------------
 
 constexpr int kBM = 256, kBN = 256;
+constexpr int kWaves = 8;
 constexpr int kStageA = 8 * kActUnitBytes;   // 32 KB
 constexpr int kStageB = 8 * kWgtUnitBytes;   // 16 KB
 constexpr int kStage = kStageA + kStageB;    // 48 KB
 
-// Global -> register half of a stage copy: each wave moves 8 KB of
-// activation units and 4 KB of weight units, 16 bytes per lane per load.
-struct StageRegs {
-    uint4 a[8];
-    uint4 b[4];
-};
-
-__device__ inline void load_stage(const GemmArgs& a, StageRegs& st, int mt0, int nt0, int kb, int wave, int lane)
+// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
+// M0 + 16 l.  Written as inline asm so that the compiler neither tracks the
+// copy (and waits for it before unrelated LDS reads) nor needs registers for
+// it: nothing is returned, the address VGPRs are consumed at issue, and the
+// LDS side is ordered by the explicit vmcnt waits below.
+__device__ inline void lds_copy16(const uint8_t* g, uint8_t* l)
 {
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-        const int mt = mt0 + 2 * wave + u2;
-        const uint8_t* src = a.act + ((size_t)mt * a.KB + kb) * kActUnitBytes + lane * 16;
-        const bool ok = mt < a.MT;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            st.a[u2 * 4 + p] = ok ? *(const uint4*)(src + p * 1024) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-        const int nt = nt0 + 2 * wave + u2;
-        const uint8_t* src = a.wgt + ((size_t)nt * a.KB + kb) * kWgtUnitBytes + lane * 16;
-        const bool ok = nt < a.NT;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            st.b[u2 * 2 + p] = ok ? *(const uint4*)(src + p * 1024) : make_uint4(0, 0, 0, 0);
-    }
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
 }
 
-// Register -> LDS half: the images are stored in LDS order, so lane l of a
-// wave writes bytes [16 l, 16 l + 16) of each 1 KB piece.
-__device__ inline void store_stage(uint8_t* stage, const StageRegs& st, int wave, int lane)
+// Wait until at most one stage of copies (6 per wave: 4 x 1 KB activation +
+// 2 x 1 KB weight) is in flight, then
+// synchronise the workgroup.  No fence: the only memory traffic to order is
+// LDS (all reads of the released stage were consumed before this point) and
+// the copies (ordered by vmcnt).
+__device__ inline void wait_stage_and_barrier()
 {
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+}
+__device__ inline void wait_all_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wave w copies activation unit w (4 KB) and weight unit w (2 KB) of stage kb.
+// Units past the end of the matrix are re-read from the last valid unit (their
+// products land in rows/columns that are never stored), which keeps the
+// number of copies in flight per wave constant.
+__device__ inline void issue_stage(const GemmArgs& a, uint8_t* stage, int mt0, int nt0, int kb, int wave, int lane)
+{
+    const int mt = min(mt0 + wave, a.MT - 1), nt = min(nt0 + wave, a.NT - 1);
+    const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kActUnitBytes + lane * 16;
+    const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kWgtUnitBytes + lane * 16;
+    uint8_t* da = stage + wave * kActUnitBytes;
+    uint8_t* db = stage + kStageA + wave * kWgtUnitBytes;
 #pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2)
+    for (int p = 0; p < 4; ++p) lds_copy16(sa + p * 1024, da + p * 1024);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            *(uint4*)(stage + (2 * wave + u2) * kActUnitBytes + p * 1024 + lane * 16) = st.a[u2 * 4 + p];
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            *(uint4*)(stage + kStageA + (2 * wave + u2) * kWgtUnitBytes + p * 1024 + lane * 16) = st.b[u2 * 2 + p];
+    for (int p = 0; p < 2; ++p) lds_copy16(sb + p * 1024, db + p * 1024);
 }
 
 __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
@@ -323,53 +348,48 @@ __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
     return r;
 }
 
-// One 128-K stage of MFMAs out of LDS.  Fragments for the next k-step are
-// read before the current k-step's MFMAs are issued.
-__device__ inline void compute_stage(const uint8_t* stage, int wm, int wn, int r32, int h, v16i (&acc)[4][4])
+// One 128-K stage of MFMAs out of LDS for a 128 (M) x 64 (N) wave tile;
+// acc[j][i] accumulates D = W_j . X_i^T (rows n, columns m).
+__device__ inline void compute_stage(const uint8_t* stage, int wm, int wn, int r32, int h, v16i (&acc)[2][4])
 {
     const uint8_t* sa = stage + (wm * 4) * kActUnitBytes + r32 * 128;
-    const uint8_t* sb = stage + kStageA + (wn * 4) * kWgtUnitBytes + r32 * 64;
-    const int swz_a = r32 & 7, swz_b = (r32 >> 1) & 3;
-    uint4 bq[2][4];
-    v4i af[2][4];
+    const uint8_t* sb = stage + kStageA + (wn * 2) * kWgtUnitBytes + r32 * 64;
+    const int swz_a = act_swizzle(r32), swz_b = wgt_swizzle(r32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bq[0][j] = *(const uint4*)(sb + j * kWgtUnitBytes + ((h ^ swz_b) * 16));
+    for (int pr = 0; pr < 2; ++pr) {
+        uint4 bq[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[0][i] = *(const v4i*)(sa + i * kActUnitBytes + ((h ^ swz_a) * 16));
+        for (int j = 0; j < 2; ++j) bq[j] = *(const uint4*)(sb + j * kWgtUnitBytes + (((2 * pr + h) ^ swz_b) * 16));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks + 1 < 4) {
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ks = 2 * pr + kk;
+            v4i af[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[nxt][i] = *(const v4i*)(sa + i * kActUnitBytes + (((2 * (ks + 1) + h) ^ swz_a) * 16));
+                af[i] = *(const v4i*)(sa + i * kActUnitBytes + (((2 * ks + h) ^ swz_a) * 16));
+            v4i bf[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bf[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[j][i], 0, 0, 0);
         }
-        if (ks == 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bq[1][j] = *(const uint4*)(sb + j * kWgtUnitBytes + (((2 + h) ^ swz_b) * 16));
-        }
-        const int pr = ks >> 1;
-        v4i bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = (ks & 1) == 0 ? widen_lo_hi(bq[pr][j].x, bq[pr][j].y) : widen_lo_hi(bq[pr][j].z, bq[pr][j].w);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[j], acc[i][j], 0, 0, 0);
     }
 }
 
 template <int OUT>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a)
+__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t s0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t s1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t s2[kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves of 128 x 64
 
     // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous range of tiles (row tiles fastest) so tiles sharing weight
@@ -382,67 +402,154 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a)
     const int tm = vid % a.tiles_m, tn = vid / a.tiles_m;
     const int mt0 = tm * (kBM / 32), nt0 = tn * (kBN / 32);
 
-    v16i acc[4][4];
+    v16i acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
     const int r32 = lane & 31, h = lane >> 5;
+    const int KB = a.KB;
 
-    StageRegs st;
-    load_stage(a, st, mt0, nt0, 0, wave, lane);
-    store_stage(smem, st, wave, lane);
-    __syncthreads();
+    issue_stage(a, s0, mt0, nt0, 0, wave, lane);
+    if (KB > 1) {
+        issue_stage(a, s1, mt0, nt0, 1, wave, lane);
+        wait_stage_and_barrier();
+    } else {
+        wait_all_and_barrier();
+    }
 
-    for (int kb = 0; kb < a.KB; ++kb) {
-        const bool more = kb + 1 < a.KB;
-        if (more) load_stage(a, st, mt0, nt0, kb + 1, wave, lane);  // in flight during the MFMAs
-        compute_stage(smem + (kb & 1) * kStage, wm, wn, r32, h, acc);
-        if (more) store_stage(smem + ((kb + 1) & 1) * kStage, st, wave, lane);
+    int kb = 0;
+    for (; kb + 3 <= KB; kb += 3) {
+        // stage kb in s0, kb+1 in s1 (possibly in flight); kb+2 -> s2
+        if (kb + 2 < KB) issue_stage(a, s2, mt0, nt0, kb + 2, wave, lane);
+        compute_stage(s0, wm, wn, r32, h, acc);
+        if (kb + 2 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
+
+        if (kb + 3 < KB) issue_stage(a, s0, mt0, nt0, kb + 3, wave, lane);
+        compute_stage(s1, wm, wn, r32, h, acc);
+        if (kb + 3 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
+
+        if (kb + 4 < KB) issue_stage(a, s1, mt0, nt0, kb + 4, wave, lane);
+        compute_stage(s2, wm, wn, r32, h, acc);
+        if (kb + 4 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
+    }
+    // 0, 1 or 2 stages left: stage kb in s0, kb+1 in s1 (both already issued)
+    if (kb < KB) {
+        compute_stage(s0, wm, wn, r32, h, acc);
+        if (kb + 1 < KB) {
+            wait_all_and_barrier();
+            compute_stage(s1, wm, wn, r32, h, acc);
+        }
+    }
+
+    // epilogue: D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
+    // register (row / 8) * 4 + row % 4; here rows are output columns n and
+    // columns are output rows m, so lane l holds row m = l % 32 and, per group
+    // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
+    const int64_t m_base = (int64_t)tm * kBM + wm * 128;
+    const int64_t n_base = (int64_t)tn * kBN + wn * 64;
+    const bool vec_ok = (a.N % 4) == 0;
+
+    // The block's 256 column scales and biases and 256 row scales go through
+    // LDS (free again once every wave has finished its last stage): one
+    // cooperative load instead of per-lane scattered loads.
+    float* p_sw = (float*)s0;
+    float* p_b = p_sw + kBN;
+    float* p_sx = p_b + kBN;
+    if constexpr (OUT == GEMM_OUT_BF16) {
+        __syncthreads();
+        if (tid < kBN) {
+            const int64_t n = (int64_t)tn * kBN + tid;
+            const int64_t nc = n < a.N ? n : a.N - 1;
+            p_sw[tid] = a.sw[nc];
+            p_b[tid] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
+        } else if (tid < kBN + kBM) {
+            const int64_t m = (int64_t)tm * kBM + (tid - kBN);
+            p_sx[tid - kBN] = a.sx[m < a.M ? m : a.M - 1];
+        }
         __syncthreads();
     }
 
-    // epilogue: D[i][j] of a 32x32 MFMA tile sits in lane (j + 32 * ((i / 4) % 2)),
-    // register (i / 8) * 4 + i % 4.
-    const int64_t m_base = (int64_t)tm * kBM + wm * 128;
-    const int64_t n_base = (int64_t)tn * kBN + wn * 128;
-    float swn[4], bn[4];
-    bool n_ok[4];
+    // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
+    // register (row / 8) * 4 + row % 4; here rows are output columns n and
+    // columns are output rows m, so lane l holds row m = l % 32 and, per group
+    // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
+    if constexpr (OUT == GEMM_OUT_I32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n_base + 32 * j + r32;
-        n_ok[j] = n < a.N;
-        swn[j] = 0.0f;
-        bn[j] = 0.0f;
-        if (OUT == GEMM_OUT_BF16 && n_ok[j]) {
-            swn[j] = a.sw[n];
-            bn[j] = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m_base + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m_base + 32 * i + r32;
             if (m >= a.M) continue;
-            const float sxm = (OUT == GEMM_OUT_BF16) ? a.sx[m] : 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!n_ok[j]) continue;
-                const int64_t n = n_base + 32 * j + r32;
-                const int32_t v = acc[i][j][r] >> 4;  // weights entered as 16 * code
-                if constexpr (OUT == GEMM_OUT_I32) {
-                    ((int32_t*)a.out)[m * a.N + n] = v;
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t n0 = n_base + 32 * j + 8 * t + 4 * h;
+                    if (n0 >= a.N) continue;
+                    int32_t v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * t + u] >> 4;  // weights entered as 16 * code
+                    int32_t* dst = (int32_t*)a.out + m * a.N + n0;
+                    if (vec_ok) {
+                        *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
+                    } else {
+                        for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
+                    }
+                }
+        }
+    } else {
+        // bf16 output through a per-wave LDS tile of 32 rows x 64 columns
+        // (row pitch 144 bytes: the 8-byte writes of 16 consecutive lanes hit
+        // distinct banks), one 32-row MFMA tile row at a time; then every lane
+        // stores 16 bytes and 8 lanes cover one 128-byte row segment.
+        constexpr int kPitch = 144;
+        static_assert(kWaves * 32 * kPitch <= kStage, "output staging must fit one stage buffer");
+        uint8_t* tile = s1 + wave * (32 * kPitch);
+        const bool vec8 = (a.N % 8) == 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sxm = p_sx[wm * 128 + 32 * i + r32];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
+                    const float4 sw4 = *(const float4*)(p_sw + wn * 64 + nl);
+                    const float4 b4 = *(const float4*)(p_b + wn * 64 + nl);
+                    const float sc[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                    uint16_t y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int32_t v = acc[j][i][4 * t + u] >> 4;  // weights entered as 16 * code
+                        y[u] = f32_to_bf16_rne(__builtin_fmaf((float)v * sxm, sc[u], bb[u]));
+                    }
+                    uint2 w;
+                    w.x = (uint32_t)y[0] | ((uint32_t)y[1] << 16);
+                    w.y = (uint32_t)y[2] | ((uint32_t)y[3] << 16);
+                    *(uint2*)(tile + r32 * kPitch + nl * 2) = w;
+                }
+            // read back row segments: lane l takes 16-byte chunk (l & 7) of rows (l >> 3) + 8 s
+#pragma unroll
+            for (int sr = 0; sr < 4; ++sr) {
+                const int rho = (lane >> 3) + 8 * sr;
+                const int c = lane & 7;
+                const uint4 w = *(const uint4*)(tile + rho * kPitch + c * 16);
+                const int64_t m = m_base + 32 * i + rho;
+                const int64_t n = n_base + 8 * c;
+                if (m >= a.M || n >= a.N) continue;
+                uint16_t* dst = (uint16_t*)a.out + m * a.N + n;
+                if (vec8 && n + 8 <= a.N) {
+                    *(uint4*)dst = w;
                 } else {
-                    const float t = (float)v * sxm;
-                    const float y = __builtin_fmaf(t, swn[j], bn[j]);
-                    ((uint16_t*)a.out)[m * a.N + n] = f32_to_bf16_rne(y);
+                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                    for (int u = 0; u < 8 && n + u < a.N; ++u) dst[u] = (uint16_t)(ww[u >> 1] >> (16 * (u & 1)));
                 }
             }
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -534,7 +641,7 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
 {
     a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
     a.tiles_n = (a.NT + kBN / 32 - 1) / (kBN / 32);
-    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(256);
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kWaves * 64);
     if (out_mode == GEMM_OUT_I32)
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32>), grid, block, 0, s, a);
     else
