@@ -64,9 +64,10 @@ const char* convrot_version(void);
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
 /* Bytes of workspace convrot_linear needs: the activation-code image
- * (round_up(M, 32) * round_up(K, 128) bytes, INT8 codes) followed, at the
- * next 256-byte boundary, by the activation scales sx (round_up(M, 32)
- * floats).  Returns CONVROT_OK or CONVROT_EINVAL. */
+ * (round_up(M, 32) * round_up(K, 128) / 2 bytes, INT4 codes in the same
+ * layout as the weight image) followed, at the next 256-byte boundary, by the
+ * activation scales sx (round_up(M, 32) floats).  Returns CONVROT_OK or
+ * CONVROT_EINVAL. */
 int convrot_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
 
 /* ---- argument checks (host only, no HIP call) ------------------------- */

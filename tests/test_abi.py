@@ -50,10 +50,10 @@ def test_weight_image_bytes(N, K, g, want):
 
 
 def test_workspace_bytes():
-    # activation image (M up to 32 rows, K up to 128) + 256-aligned scales
-    assert B.convrot_workspace_bytes(1, 3072, 256) == 32 * 3072 + 32 * 4
-    assert B.convrot_workspace_bytes(1536, 3072, 256) == 1536 * 3072 + 1536 * 4
-    assert B.convrot_workspace_bytes(5, 192, 64) == 32 * 256 + 32 * 4
+    # packed INT4 activation image (M up to 32 rows, K up to 128) + 256-aligned scales
+    assert B.convrot_workspace_bytes(1, 3072, 256) == 32 * 3072 // 2 + 32 * 4
+    assert B.convrot_workspace_bytes(1536, 3072, 256) == 1536 * 3072 // 2 + 1536 * 4
+    assert B.convrot_workspace_bytes(5, 192, 64) == 32 * 256 // 2 + 32 * 4
 
 
 @pytest.mark.parametrize("N,K,g", [(16, 100, 64), (16, 512, 128), (16, 0, 64), (-1, 256, 256), (16, 32768, 256)])

@@ -60,7 +60,7 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.out = (uint8_t*)ws;
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
     a.rotated = nullptr;
-    launch_prep(g, OUT_ACT_IMAGE, a, s);
+    launch_prep(g, OUT_IMAGE, a, s);
     return launched();
 }
 
@@ -100,7 +100,7 @@ int convrot_prepare_weight(const void* W, int64_t N, int64_t K, int g, void* ima
     a.K_pad = round_up(K, kTileK);
     a.out = (uint8_t*)image;
     a.scales = sw;
-    launch_prep(g, OUT_WGT_IMAGE, a, as_stream(stream));
+    launch_prep(g, OUT_IMAGE, a, as_stream(stream));
     return launched();
 }
 

@@ -21,16 +21,12 @@ int check_shape(int64_t rows, int64_t K, int g)
     return CONVROT_OK;
 }
 
-size_t act_image_bytes(int64_t M, int64_t K) { return (size_t)round_up(M, kTileRows) * (size_t)round_up(K, kTileK); }
-
-size_t workspace_sx_offset(int64_t M, int64_t K) { return (size_t)round_up((int64_t)act_image_bytes(M, K), 256); }
+size_t workspace_sx_offset(int64_t M, int64_t K) { return (size_t)round_up((int64_t)image_bytes(M, K), 256); }
 
 size_t workspace_bytes(int64_t M, int64_t K)
 {
     return workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows);
 }
-
-size_t weight_image_bytes(int64_t N, int64_t K) { return (size_t)round_up(N, kTileRows) * (size_t)round_up(K, kTileK) / 2; }
 
 }  // namespace convrot
 
@@ -55,7 +51,7 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
     if (!bytes) return CONVROT_EINVAL;
     int rc = check_shape(N, K, g);
     if (rc) return rc;
-    *bytes = weight_image_bytes(N, K);
+    *bytes = image_bytes(N, K);
     return CONVROT_OK;
 }
 
@@ -150,13 +146,13 @@ int convrot_host_nk_to_image(const uint8_t* nk, int64_t N, int64_t K, uint8_t* i
 {
     if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
     const int64_t K_pad = round_up(K, kTileK);
-    memset(image, 0, weight_image_bytes(N, K));
+    memset(image, 0, image_bytes(N, K));
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; k += 8) {
             uint32_t word = 0;
             for (int b = 0; b < 4; ++b)
                 word |= (uint32_t)(nk_nib(nk, K, n, k + b) | (nk_nib(nk, K, n, k + 4 + b) << 4)) << (8 * b);
-            memcpy(image + wgt_word_offset(n, k, K_pad), &word, 4);
+            memcpy(image + image_word_offset(n, k, K_pad), &word, 4);
         }
     return CONVROT_OK;
 }
@@ -169,7 +165,7 @@ int convrot_host_image_to_nk(const uint8_t* image, int64_t N, int64_t K, uint8_t
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; k += 8) {
             uint32_t word;
-            memcpy(&word, image + wgt_word_offset(n, k, K_pad), 4);
+            memcpy(&word, image + image_word_offset(n, k, K_pad), 4);
             uint8_t* p = nk + n * (K / 2) + k / 2;
             for (int b = 0; b < 4; ++b) {
                 uint8_t byte = (uint8_t)(word >> (8 * b));
@@ -188,7 +184,15 @@ int convrot_host_act_image_to_codes(const uint8_t* image, int64_t M, int64_t K, 
     if (!image || !codes || M < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
     const int64_t K_pad = round_up(K, kTileK);
     for (int64_t m = 0; m < M; ++m)
-        for (int64_t k = 0; k < K; k += 16) memcpy(codes + m * K + k, image + act_chunk_offset(m, k, K_pad), 16);
+        for (int64_t k = 0; k < K; k += 8) {
+            uint32_t word;
+            memcpy(&word, image + image_word_offset(m, k, K_pad), 4);
+            for (int b = 0; b < 4; ++b) {
+                const uint8_t byte = (uint8_t)(word >> (8 * b));
+                codes[m * K + k + b] = sext4(byte & 0x0F);
+                codes[m * K + k + 4 + b] = sext4(byte >> 4);
+            }
+        }
     return CONVROT_OK;
 }
 

@@ -11,9 +11,7 @@ constexpr int64_t kMaxRows = 16777216;     // 2^24 rows / columns
 
 bool aligned(const void* p, size_t a);
 int check_shape(int64_t rows, int64_t K, int g);
-size_t act_image_bytes(int64_t M, int64_t K);
 size_t workspace_sx_offset(int64_t M, int64_t K);
 size_t workspace_bytes(int64_t M, int64_t K);
-size_t weight_image_bytes(int64_t N, int64_t K);
 
 }  // namespace convrot

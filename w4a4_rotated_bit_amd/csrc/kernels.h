@@ -5,14 +5,14 @@
 
 namespace convrot {
 
-enum PrepOut { OUT_ACT_IMAGE = 0, OUT_WGT_IMAGE = 1, OUT_ROWMAJOR = 2, OUT_NK = 3 };
+enum PrepOut { OUT_IMAGE = 0, OUT_ROWMAJOR = 2, OUT_NK = 3 };
 enum GemmOut { GEMM_OUT_BF16 = 0, GEMM_OUT_I32 = 1 };
 
 struct PrepArgs {
     const uint16_t* X;   // bf16 [rows][K]
     int64_t rows;        // rows holding data
-    int64_t rows_pad;    // rows written (image modes: rows rounded up to 32)
-    int64_t K, K_pad;    // K_pad = K rounded up to 128 (image modes)
+    int64_t rows_pad;    // rows written (image mode: rows rounded up to 32)
+    int64_t K, K_pad;    // K_pad = K rounded up to 128 (image mode)
     uint8_t* out;        // codes in the layout of the mode
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
@@ -21,8 +21,8 @@ struct PrepArgs {
 };
 
 struct GemmArgs {
-    const uint8_t* act;  // activation image
-    const uint8_t* wgt;  // weight image
+    const uint8_t* act;  // operand image of the activation codes
+    const uint8_t* wgt;  // operand image of the weight codes
     const float* sx;     // [M]
     const float* sw;     // [N]
     const uint16_t* bias;  // bf16 [N] or nullptr

@@ -1,12 +1,15 @@
 // kernels.hip -- gfx950 (CDNA4) kernels of the ConvRot W4A4 linear.
 //
-//   prep_kernel   rotation (grouped Sylvester Hadamard, fast Walsh-Hadamard
-//                 butterflies in fp32), row absmax, symmetric INT4
-//                 quantization; writes codes in one of four layouts.
-//   gemm_kernel   INT8 x INT4 GEMM on the INT8 matrix cores
-//                 (v_mfma_i32_32x32x32_i8) with int32 accumulation and the
-//                 scale + bias epilogue to bf16 (or raw int32 for parity).
-//   repack_nk_kernel / act_relayout_kernel: lossless layout moves.
+//   prep_kernel   rotation (grouped Sylvester Hadamard as fast Walsh-Hadamard
+//                 butterflies in binary64, rounded once to binary32), row
+//                 absmax, symmetric INT4 quantization; writes the codes as the
+//                 operand image (activations and weights alike) or in plain
+//                 layouts for parity checks.
+//   gemm_kernel   INT4 x INT4 products on the INT8 matrix cores
+//                 (v_mfma_i32_32x32x32_i8, codes widened to INT8 x 16 in
+//                 registers) with int32 accumulation and the scale + bias
+//                 epilogue to bf16 (or raw int32 for parity).
+//   relayout kernels: lossless layout moves into the operand image.
 //
 // Method: convrot-mlx README, "What is included" (normalized Hadamard
 // rotation over groups of 64 or 256, symmetric rowwise absmax INT4 in
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     if (!row_in) return;
     if (row_valid && slice == 0) a.scales[row] = s;
 
-    const bool write_slice = (MODE == OUT_ACT_IMAGE || MODE == OUT_WGT_IMAGE) ? (slice < a.slices_pad) : has_data;
+    const bool write_slice = (MODE == OUT_IMAGE) ? (slice < a.slices_pad) : has_data;
     if (!write_slice) return;
 
     int8_t qa[8][8];
@@ -240,16 +243,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     for (int j = 0; j < 8; ++j) {
         const int64_t k = slice_k<G>(slice, j);
         const int8_t* q = qa[j];
-        if constexpr (MODE == OUT_ACT_IMAGE) {
-            uint2 w;
-            w.x = pack4_i8(q);
-            w.y = pack4_i8(q + 4);
-            *(uint2*)(a.out + act_chunk_offset(row, k & ~(int64_t)15, a.K_pad) + (k & 8)) = w;
-        } else if constexpr (MODE == OUT_WGT_IMAGE) {
+        if constexpr (MODE == OUT_IMAGE) {
             uint32_t w = 0;
 #pragma unroll
             for (int b = 0; b < 4; ++b) w |= (nib(q[b]) | (nib(q[b + 4]) << 4)) << (8 * b);
-            *(uint32_t*)(a.out + wgt_word_offset(row, k, a.K_pad)) = w;
+            *(uint32_t*)(a.out + image_word_offset(row, k, a.K_pad)) = w;
         } else if constexpr (MODE == OUT_NK) {
             uint32_t w = 0;
 #pragma unroll
@@ -273,71 +271,72 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 // gemm_kernel
 //
 // Block tile 256 (M) x 256 (N); K advances 128 at a time through a ring of
-// three LDS stages, each holding 8 activation units (4 KB each) and 8 weight
-// units (2 KB each) = 48 KB.  The images are stored in exactly the LDS order,
-// so every global -> LDS copy is a straight 1 KB run per wave instruction
-// (global_load_lds_dwordx4, 16 bytes per lane, no registers involved); the
-// copy of stage k+2 is in flight while stage k feeds the matrix cores.  The
-// three stages are three distinct arrays and the main loop is unrolled by
-// three, so every LDS read names a stage that no copy in flight targets.
+// four LDS stages, each holding 8 activation units and 8 weight units of the
+// operand image (2 KB each) = 32 KB.  The image is stored in exactly the LDS
+// order, so every global -> LDS copy is a straight 1 KB run per wave
+// instruction (global_load_lds_dwordx4, 16 bytes per lane, no registers
+// involved); copies run three stages ahead of the MFMAs.
 // Eight waves, two per SIMD, each own a 128 (M) x 64 (N) output tile: 4 x 2
 // MFMA 32x32x32 tiles computed as W . X^T, so that each lane ends up holding
-// four consecutive output columns of one row (8-byte stores).  Weight nibbles
-// are widened to INT8 x 16 in registers right after the LDS read; the int32
-// sums are divided by 16 (exact) in the epilogue.
+// four consecutive output columns of one row.  Both operands are widened from
+// INT4 to INT8 x 16 in registers right after the LDS read; the int32 sums are
+// therefore 256 times the dot products and are divided by 256 (exactly) in
+// the epilogue.  |dot| <= 49 K <= 802816, so 256 |dot| < 2^31.
 // ---------------------------------------------------------------------------
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kWaves = 8;
-constexpr int kStageA = 8 * kActUnitBytes;   // 32 KB
-constexpr int kStageB = 8 * kWgtUnitBytes;   // 16 KB
-constexpr int kStage = kStageA + kStageB;    // 48 KB
+constexpr int kStageA = 8 * kUnitBytes;      // 16 KB
+constexpr int kStage = 2 * kStageA;          // 32 KB: activation units, then weight units
+constexpr int kStages = 4;
+constexpr int kCopies = 4;                   // copies per wave per stage: 2 x 1 KB activation + 2 x 1 KB weight
 
 // Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
 // M0 + 16 l.  Written as inline asm so that the compiler neither tracks the
 // copy (and waits for it before unrelated LDS reads) nor needs registers for
 // it: nothing is returned, the address VGPRs are consumed at issue, and the
-// LDS side is ordered by the explicit vmcnt waits below.
-__device__ inline void lds_copy16(const uint8_t* g, uint8_t* l)
+// LDS side is ordered by the explicit vmcnt waits of wait_copies_and_barrier.
+__device__ inline void lds_copy16(const uint8_t* g, uint32_t lds_addr)
 {
-    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(lds_addr)
                  : "memory", "m0");
 }
 
-// Wait until at most one stage of copies (6 per wave: 4 x 1 KB activation +
-// 2 x 1 KB weight) is in flight, then
-// synchronise the workgroup.  No fence: the only memory traffic to order is
-// LDS (all reads of the released stage were consumed before this point) and
-// the copies (ordered by vmcnt).
-__device__ inline void wait_stage_and_barrier()
+// Wait until at most `stages_in_flight` stages of copies (kCopies each) are
+// outstanding, then synchronise the workgroup.  No fence: the only memory
+// traffic to order is LDS (every read of the released stage has returned into
+// registers) and the copies (ordered by vmcnt).
+__device__ inline void wait_copies_and_barrier(int stages_in_flight)
 {
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-}
-__device__ inline void wait_all_and_barrier()
-{
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    switch (stages_in_flight) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory"); break;
+    }
 }
 
-// Wave w copies activation unit w (4 KB) and weight unit w (2 KB) of stage kb.
-// Units past the end of the matrix are re-read from the last valid unit (their
-// products land in rows/columns that are never stored), which keeps the
-// number of copies in flight per wave constant.
-__device__ inline void issue_stage(const GemmArgs& a, uint8_t* stage, int mt0, int nt0, int kb, int wave, int lane)
+// Wave w copies activation unit w and weight unit w of stage kb into the
+// stage buffer at LDS address `stage` (wave-uniform).  Units past the end of
+// the matrix are re-read from the last valid unit (their products land in
+// rows/columns that are never stored), which keeps the number of copies in
+// flight per wave constant.
+__device__ inline void issue_stage(const GemmArgs& a, uint32_t stage, int mt0, int nt0, int kb, int wave, int lane)
 {
     const int mt = min(mt0 + wave, a.MT - 1), nt = min(nt0 + wave, a.NT - 1);
-    const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kActUnitBytes + lane * 16;
-    const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kWgtUnitBytes + lane * 16;
-    uint8_t* da = stage + wave * kActUnitBytes;
-    uint8_t* db = stage + kStageA + wave * kWgtUnitBytes;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) lds_copy16(sa + p * 1024, da + p * 1024);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) lds_copy16(sb + p * 1024, db + p * 1024);
+    const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kUnitBytes + lane * 16;
+    const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kUnitBytes + lane * 16;
+    const uint32_t da = stage + wave * kUnitBytes;
+    const uint32_t db = stage + kStageA + wave * kUnitBytes;
+    lds_copy16(sa, da);
+    lds_copy16(sa + 1024, da + 1024);
+    lds_copy16(sb, db);
+    lds_copy16(sb + 1024, db + 1024);
 }
 
+// INT4 codes of one 8-byte group -> 16 INT8 values x 16 in natural order
 __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
 {
     v4i r;
@@ -348,48 +347,72 @@ __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
     return r;
 }
 
-// One 128-K stage of MFMAs out of LDS for a 128 (M) x 64 (N) wave tile;
-// acc[j][i] accumulates D = W_j . X_i^T (rows n, columns m).
-__device__ inline void compute_stage(const uint8_t* stage, int wm, int wn, int r32, int h, v16i (&acc)[2][4])
+// Per-lane LDS offsets of a 128 (M) x 64 (N) wave tile: this lane's row of
+// activation unit wm*4 and of weight unit wn*2 within a stage.
+struct Frag {
+    int sa, sb, swz, h;
+};
+
+// Quads of one pair of k-steps: 4 activation quads and 2 weight quads, each
+// 16 bytes = 2 k-steps x 16 codes of this lane's row.
+__device__ inline void load_pair(const Frag& f, const uint8_t* stage, int pr, uint4 (&aq)[4], uint4 (&bq)[2])
 {
-    const uint8_t* sa = stage + (wm * 4) * kActUnitBytes + r32 * 128;
-    const uint8_t* sb = stage + kStageA + (wn * 2) * kWgtUnitBytes + r32 * 64;
-    const int swz_a = act_swizzle(r32), swz_b = wgt_swizzle(r32);
+    const int off = ((2 * pr + f.h) ^ f.swz) * 16;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-        uint4 bq[2];
+    for (int i = 0; i < 4; ++i) aq[i] = *(const uint4*)(stage + f.sa + i * kUnitBytes + off);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bq[j] = *(const uint4*)(sb + j * kWgtUnitBytes + (((2 * pr + h) ^ swz_b) * 16));
+    for (int j = 0; j < 2; ++j) bq[j] = *(const uint4*)(stage + f.sb + j * kUnitBytes + off);
+}
+
+// Widened operands of one k-step: 4 activation and 2 weight fragments of 16
+// INT8 values x 16 each.
+struct Wide {
+    v4i a[4], b[2];
+};
+
+// k-step kk (0 or 1) of a pair of quads -> widened fragments
+__device__ inline void widen(const uint4 (&aq)[4], const uint4 (&bq)[2], int kk, Wide& w)
+{
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int ks = 2 * pr + kk;
-            v4i af[4];
+    for (int i = 0; i < 4; ++i) w.a[i] = kk == 0 ? widen_lo_hi(aq[i].x, aq[i].y) : widen_lo_hi(aq[i].z, aq[i].w);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *(const v4i*)(sa + i * kActUnitBytes + (((2 * ks + h) ^ swz_a) * 16));
-            v4i bf[2];
+    for (int j = 0; j < 2; ++j) w.b[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
+}
+
+// acc[j][i] += W_j . X_i^T for one k-step
+__device__ inline void mfmas(const Wide& w, v16i (&acc)[2][4])
+{
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w.b[j], w.a[i], acc[j][i], 0, 0, 0);
+}
+
+// Instruction-mix hints for one k-step phase (sched_group_barrier masks:
+// 0x008 MFMA, 0x100 LDS read, 0x002 VALU): each MFMA is followed by a few of
+// the widening instructions of the next k-step and, where there are any, one
+// LDS read, so the matrix core, the vector ALU and the LDS work side by side
+// instead of in bursts.
+__device__ inline void interleave_mfma_valu(int lds_reads)
+{
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[j][i], 0, 0, 0);
-        }
+    for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m < lds_reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
 }
 
 template <int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t s0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t s1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t s2[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves of 128 x 64
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps copy addresses scalar
+    const int wm = wave & 1, wn = wave >> 1;                     // 2 x 4 waves of 128 x 64
 
     // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous range of tiles (row tiles fastest) so tiles sharing weight
@@ -412,72 +435,68 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
 
     const int r32 = lane & 31, h = lane >> 5;
     const int KB = a.KB;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    Frag f;
+    f.sa = (wm * 4) * kUnitBytes + r32 * 64;
+    f.sb = kStageA + (wn * 2) * kUnitBytes + r32 * 64;
+    f.swz = row_swizzle(r32);
+    f.h = h;
 
-    issue_stage(a, s0, mt0, nt0, 0, wave, lane);
-    if (KB > 1) {
-        issue_stage(a, s1, mt0, nt0, 1, wave, lane);
-        wait_stage_and_barrier();
-    } else {
-        wait_all_and_barrier();
+    // prologue: the first kStages stages in flight; wait for stage 0
+    const int first = KB < kStages ? KB : kStages;
+    for (int s = 0; s < first; ++s) issue_stage(a, lds0 + s * kStage, mt0, nt0, s, wave, lane);
+    wait_copies_and_barrier(first - 1);
+    uint4 aq[2][4], bq[2][2];
+    Wide w[2];
+    load_pair(f, smem, 0, aq[0], bq[0]);
+    widen(aq[0], bq[0], 0, w[0]);
+
+    // Per stage: k-step 0 MFMAs with the reads of pair 1 and the widening of
+    // k-step 1; k-step 1 MFMAs with the widening of k-step 2; k-step 2 MFMAs
+    // with the widening of k-step 3; the stage barrier, the copy of stage
+    // kb + kStages into the released buffer and the reads of the next stage's
+    // pair 0; k-step 3 MFMAs with the widening of the next stage's k-step 0.
+    // sched_barrier(0) separates the phases so that no MFMA is hoisted above
+    // the stage barrier and no LDS read sinks below its phase.
+    for (int kb = 0; kb < KB; ++kb) {
+        const int slot = kb % kStages;
+        const uint8_t* cur = smem + slot * kStage;
+        load_pair(f, cur, 1, aq[1], bq[1]);
+        mfmas(w[0], acc);
+        widen(aq[0], bq[0], 1, w[1]);
+        interleave_mfma_valu(6);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(w[1], acc);
+        widen(aq[1], bq[1], 0, w[0]);
+        interleave_mfma_valu(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(w[0], acc);
+        widen(aq[1], bq[1], 1, w[1]);
+        interleave_mfma_valu(0);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kb + 1 must have landed; stages kb + 2 .. kb + kStages - 1 may be in flight
+        int in_flight = KB - kb - 2;
+        in_flight = in_flight < 0 ? 0 : (in_flight > kStages - 2 ? kStages - 2 : in_flight);
+        wait_copies_and_barrier(in_flight);
+        if (kb + kStages < KB) issue_stage(a, lds0 + slot * kStage, mt0, nt0, kb + kStages, wave, lane);
+        const bool more = kb + 1 < KB;
+        if (more) load_pair(f, smem + ((kb + 1) % kStages) * kStage, 0, aq[0], bq[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(w[1], acc);
+        if (more) widen(aq[0], bq[0], 0, w[0]);
+        interleave_mfma_valu(0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    int kb = 0;
-    for (; kb + 3 <= KB; kb += 3) {
-        // stage kb in s0, kb+1 in s1 (possibly in flight); kb+2 -> s2
-        if (kb + 2 < KB) issue_stage(a, s2, mt0, nt0, kb + 2, wave, lane);
-        compute_stage(s0, wm, wn, r32, h, acc);
-        if (kb + 2 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
-
-        if (kb + 3 < KB) issue_stage(a, s0, mt0, nt0, kb + 3, wave, lane);
-        compute_stage(s1, wm, wn, r32, h, acc);
-        if (kb + 3 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
-
-        if (kb + 4 < KB) issue_stage(a, s1, mt0, nt0, kb + 4, wave, lane);
-        compute_stage(s2, wm, wn, r32, h, acc);
-        if (kb + 4 < KB) wait_stage_and_barrier(); else wait_all_and_barrier();
-    }
-    // 0, 1 or 2 stages left: stage kb in s0, kb+1 in s1 (both already issued)
-    if (kb < KB) {
-        compute_stage(s0, wm, wn, r32, h, acc);
-        if (kb + 1 < KB) {
-            wait_all_and_barrier();
-            compute_stage(s1, wm, wn, r32, h, acc);
-        }
-    }
-
-    // epilogue: D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
-    // register (row / 8) * 4 + row % 4; here rows are output columns n and
-    // columns are output rows m, so lane l holds row m = l % 32 and, per group
-    // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
     const int64_t m_base = (int64_t)tm * kBM + wm * 128;
     const int64_t n_base = (int64_t)tn * kBN + wn * 64;
-    const bool vec_ok = (a.N % 4) == 0;
-
-    // The block's 256 column scales and biases and 256 row scales go through
-    // LDS (free again once every wave has finished its last stage): one
-    // cooperative load instead of per-lane scattered loads.
-    float* p_sw = (float*)s0;
-    float* p_b = p_sw + kBN;
-    float* p_sx = p_b + kBN;
-    if constexpr (OUT == GEMM_OUT_BF16) {
-        __syncthreads();
-        if (tid < kBN) {
-            const int64_t n = (int64_t)tn * kBN + tid;
-            const int64_t nc = n < a.N ? n : a.N - 1;
-            p_sw[tid] = a.sw[nc];
-            p_b[tid] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
-        } else if (tid < kBN + kBM) {
-            const int64_t m = (int64_t)tm * kBM + (tid - kBN);
-            p_sx[tid - kBN] = a.sx[m < a.M ? m : a.M - 1];
-        }
-        __syncthreads();
-    }
 
     // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
     // register (row / 8) * 4 + row % 4; here rows are output columns n and
     // columns are output rows m, so lane l holds row m = l % 32 and, per group
     // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
     if constexpr (OUT == GEMM_OUT_I32) {
+        const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = m_base + 32 * i + r32;
@@ -490,7 +509,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
                     if (n0 >= a.N) continue;
                     int32_t v[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * t + u] >> 4;  // weights entered as 16 * code
+                    for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
                     int32_t* dst = (int32_t*)a.out + m * a.N + n0;
                     if (vec_ok) {
                         *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
@@ -500,13 +519,31 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
                 }
         }
     } else {
-        // bf16 output through a per-wave LDS tile of 32 rows x 64 columns
-        // (row pitch 144 bytes: the 8-byte writes of 16 consecutive lanes hit
-        // distinct banks), one 32-row MFMA tile row at a time; then every lane
-        // stores 16 bytes and 8 lanes cover one 128-byte row segment.
+        // The block's 256 column scales and biases and 256 row scales go
+        // through LDS (free again: every copy has landed and every wave has
+        // passed the last stage barrier) -- one cooperative load instead of
+        // per-lane scattered loads.  Then the bf16 output goes through a
+        // per-wave LDS tile of 32 rows x 64 columns (row pitch 144 bytes: the
+        // 8-byte writes of 16 consecutive lanes hit distinct banks), one MFMA
+        // tile row at a time, and is stored as 16-byte row segments.
+        float* p_sw = (float*)smem;
+        float* p_b = p_sw + kBN;
+        float* p_sx = p_b + kBN;
         constexpr int kPitch = 144;
-        static_assert(kWaves * 32 * kPitch <= kStage, "output staging must fit one stage buffer");
-        uint8_t* tile = s1 + wave * (32 * kPitch);
+        constexpr int kParamBytes = 4096;
+        static_assert(kParamBytes + kWaves * 32 * kPitch <= kStages * kStage, "epilogue staging must fit in LDS");
+        __syncthreads();
+        if (tid < kBN) {
+            const int64_t n = (int64_t)tn * kBN + tid;
+            const int64_t nc = n < a.N ? n : a.N - 1;
+            p_sw[tid] = a.sw[nc];
+            p_b[tid] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
+        } else if (tid < kBN + kBM) {
+            const int64_t m = (int64_t)tm * kBM + (tid - kBN);
+            p_sx[tid - kBN] = a.sx[m < a.M ? m : a.M - 1];
+        }
+        __syncthreads();
+        uint8_t* tile = smem + kParamBytes + wave * (32 * kPitch);
         const bool vec8 = (a.N % 8) == 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -523,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
                     uint16_t y[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const int32_t v = acc[j][i][4 * t + u] >> 4;  // weights entered as 16 * code
+                        const int32_t v = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
                         y[u] = f32_to_bf16_rne(__builtin_fmaf((float)v * sxm, sc[u], bb[u]));
                     }
                     uint2 w;
@@ -556,20 +593,28 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
 // layout kernels
 // ---------------------------------------------------------------------------
 
-// int8 codes [M][K] -> activation image (zero padding); one thread per 16 codes.
+// int8 codes [M][K] -> operand image (zero padding); one thread per 8 codes.
 __global__ void act_relayout_kernel(const int8_t* codes, int64_t M, int64_t K, int64_t M_pad, int64_t K_pad,
                                     uint8_t* image)
 {
-    const int64_t chunks_per_row = K_pad / 16;
+    const int64_t words_per_row = K_pad / 8;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= M_pad * chunks_per_row) return;
-    const int64_t m = t / chunks_per_row, k = (t % chunks_per_row) * 16;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (m < M && k < K) w = *(const uint4*)(codes + m * K + k);
-    *(uint4*)(image + act_chunk_offset(m, k, K_pad)) = w;
+    if (t >= M_pad * words_per_row) return;
+    const int64_t m = t / words_per_row, k = (t % words_per_row) * 8;
+    uint32_t out = 0;
+    if (m < M && k < K) {
+        const uint2 in = *(const uint2*)(codes + m * K + k);  // codes k..k+7, one per byte
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t c_lo = (in.x >> (8 * b)) & 0xFu;  // code k + b
+            const uint32_t c_hi = (in.y >> (8 * b)) & 0xFu;  // code k + 4 + b
+            out |= (c_lo | (c_hi << 4)) << (8 * b);
+        }
+    }
+    *(uint32_t*)(image + image_word_offset(m, k, K_pad)) = out;
 }
 
-// N x packed-K [N][K/2] -> weight image (zero padding); one thread per 8 codes.
+// N x packed-K [N][K/2] -> operand image (zero padding); one thread per 8 codes.
 __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_t N_pad, int64_t K_pad,
                                  uint8_t* image)
 {
@@ -587,7 +632,7 @@ __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_
             out |= (c_lo | (c_hi << 4)) << (8 * b);
         }
     }
-    *(uint32_t*)(image + wgt_word_offset(n, k, K_pad)) = out;
+    *(uint32_t*)(image + image_word_offset(n, k, K_pad)) = out;
 }
 
 // ---------------------------------------------------------------------------
@@ -630,8 +675,7 @@ void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
         grid = dim3((unsigned)a.rows_pad);
     }
     switch (mode) {
-        case OUT_ACT_IMAGE: launch_prep_mode<OUT_ACT_IMAGE>(g, a, grid, block, s); break;
-        case OUT_WGT_IMAGE: launch_prep_mode<OUT_WGT_IMAGE>(g, a, grid, block, s); break;
+        case OUT_IMAGE: launch_prep_mode<OUT_IMAGE>(g, a, grid, block, s); break;
         case OUT_NK: launch_prep_mode<OUT_NK>(g, a, grid, block, s); break;
         default: launch_prep_mode<OUT_ROWMAJOR>(g, a, grid, block, s); break;
     }
@@ -651,7 +695,7 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, hipStream_t s)
 {
     const int64_t M_pad = round_up(M, kTileRows), K_pad = round_up(K, kTileK);
-    const int64_t n = M_pad * (K_pad / 16);
+    const int64_t n = M_pad * (K_pad / 8);
     hipLaunchKernelGGL(act_relayout_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, M, K, M_pad,
                        K_pad, image);
 }
