@@ -17,7 +17,6 @@ struct PrepArgs {
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
     int team;            // lanes per row (set by launch_prep)
-    int slices_pad;      // K_pad / 64 (set by launch_prep)
 };
 
 struct GemmArgs {

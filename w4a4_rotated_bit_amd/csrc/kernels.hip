@@ -41,54 +41,37 @@ __device__ inline uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-// Value of lane (lane ^ m) for m = 1, 2 within a quad (DPP quad_perm), for a
-// 64-bit value moved as two 32-bit halves.
-template <int M>
-__device__ inline double quad_xor(double v)
-{
-    constexpr int ctrl = (M == 1) ? 0xB1 /* [1,0,3,2] */ : 0x4E /* [2,3,0,1] */;
-    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), ctrl, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), ctrl, 0xF, 0xF, false);
-    return __hiloint2double(hi, lo);
-}
-
-// Codes = clamp(rint(fl32(r / s)), -7, 7) for the 8 x 8 values of a lane.
+// Codes = clamp(rint(fl32(r / s)), -7, 7) for the P values of a lane.
 // Fast path: y = r * rcp(s) is within 2 ulp of r / s (|y| < 8, so the error is
 // below 2^-20); whenever y is farther than 2^-18 from a half-integer, rint(y)
 // equals rint(fl32(r / s)) because no rounding boundary lies between them.
 // Elements near a half-integer (and rows whose s is not a normal number) take
 // the correctly rounded binary32 division, in a branch that is skipped unless
 // some lane of the wave needs it.
-__device__ inline void quantize_lane(const float (&r)[8][8], float s, bool zero_row, int8_t (&q)[8][8])
+template <int P>
+__device__ inline void quantize_run(const float (&r)[P], float s, bool zero_row, int8_t (&q)[P])
 {
     const bool exact_only = !(s >= 0x1p-126f);
     const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
-    float qf[8][8];
+    float qf[P];
     bool need = exact_only && !zero_row;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float y = r[j][e] * inv;
-            const float ry = rintf(y);
-            need |= fabsf(fabsf(y - ry) - 0.5f) < 0x1p-18f;
-            qf[j][e] = ry;
-        }
+    for (int e = 0; e < P; ++e) {
+        const float y = r[e] * inv;
+        const float ry = rintf(y);
+        need |= fabsf(fabsf(y - ry) - 0.5f) < 0x1p-18f;
+        qf[e] = ry;
+    }
     if (need && !zero_row) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = r[j][e] * inv;
-                if (exact_only || fabsf(fabsf(y - rintf(y)) - 0.5f) < 0x1p-18f)
-                    qf[j][e] = rintf(r[j][e] / s);  // IEEE binary32 division, round half to even
-            }
+        for (int e = 0; e < P; ++e) {
+            const float y = r[e] * inv;
+            if (exact_only || fabsf(fabsf(y - rintf(y)) - 0.5f) < 0x1p-18f)
+                qf[e] = rintf(r[e] / s);  // IEEE binary32 division, round half to even
+        }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            q[j][e] = zero_row ? (int8_t)0 : (int8_t)(int)fminf(fmaxf(qf[j][e], -7.0f), 7.0f);
+    for (int e = 0; e < P; ++e) q[e] = zero_row ? (int8_t)0 : (int8_t)(int)fminf(fmaxf(qf[e], -7.0f), 7.0f);
 }
 
 __device__ inline uint32_t nib(int8_t q) { return (uint32_t)(uint8_t)q & 0xFu; }
@@ -102,128 +85,136 @@ __device__ inline uint32_t pack4_i8(const int8_t* q)
 // ---------------------------------------------------------------------------
 // prep_kernel
 //
-// Work split: a row is cut into 64-element "slices"; each lane owns one
-// slice.  For g = 256 a group is 4 slices on 4 consecutive lanes (a quad):
-// lane q of the quad holds group elements 8q + 32j + e (j, e = 0..7), so the
-// butterflies over index bits 0-2 (e) and 5-7 (j) run in registers and the
-// two over bits 3-4 (q) are quad DPP exchanges.  For g = 64 a group is one
-// contiguous slice and all six butterfly stages run in registers.
-// A "team" of lanes covers one row: team <= 64 lanes share a wave with other
-// rows; team > 64 is a whole workgroup and reduces the row absmax via LDS.
-//
-// Precision: the butterflies run in binary64 (on gfx950 a double add issues
-// at the rate of an unpacked float add) and each rotated value is rounded
-// once to binary32.  A sum of g bf16 values whose magnitudes span fewer than
-// ~37 binary orders is exact in binary64, so the binary32 value is the
-// correctly rounded exact rotation and the codes do not depend on the
-// butterfly order.
+// The g-point Sylvester transform factors as H_g = H_P (x) H_P with P = 16
+// (g = 256) or P = 8 (g = 64): within a group, index u = P * hi + lo, and the
+// butterflies over the bits of lo and over the bits of hi commute.  So:
+//   phase 1: lane t owns the P consecutive elements t*P .. t*P + P - 1 of its
+//            row (lo varies) and runs log2 P butterfly stages in registers;
+//   transpose through LDS (within the wave: a group is P consecutive lanes);
+//   phase 2: lane owns the P elements lo + P * hi (hi varies) of one group and
+//            runs the other log2 P stages in registers.
+// The butterflies run in binary64 (a double add issues at the rate of an
+// unpacked float add on gfx950) and each value is rounded once to binary32; a
+// sum of g bf16 values whose magnitudes span fewer than ~37 binary orders is
+// exact in binary64, so the binary32 result is the correctly rounded exact
+// rotation whatever the butterfly order.  The rotated values go back through
+// LDS to phase-1 order, where the row absmax, the quantization and the packing
+// of 8 consecutive codes per 32-bit word happen.
+// A "team" of lanes covers one row (team = K_pad / P): teams of <= 64 lanes
+// share waves; larger teams are a whole workgroup and reduce the absmax via
+// LDS.
 // ---------------------------------------------------------------------------
 
 template <int G>
-__device__ inline int64_t slice_k(int s, int j)
-{
-    if constexpr (G == 256)
-        return (int64_t)(s >> 2) * 256 + 32 * j + 8 * (s & 3);
-    else
-        return (int64_t)s * 64 + 8 * j;
-}
+struct PrepShape {
+    static constexpr int P = (G == 256) ? 16 : 8;             // elements per lane per phase
+    static constexpr int kRunD = P + 2;                        // doubles per padded P-run in LDS
+    static constexpr int kRunF = P + 4;                        // floats per padded P-run in LDS
+    static constexpr int kWaveLdsBytes = 64 * kRunD * 8;       // LDS per wave
+};
 
 template <int G, int MODE>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
+__global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
 {
+    using S = PrepShape<G>;
+    constexpr int P = S::P;
+    extern __shared__ __attribute__((aligned(16))) uint8_t prep_lds[];
+
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     int64_t row;
-    int slice;
+    int t;  // lane within the row's team
     if (a.team <= 64) {
-        const int rows_per_block = blockDim.x / a.team;
-        row = (int64_t)blockIdx.x * rows_per_block + tid / a.team;
-        slice = tid % a.team;
+        row = (int64_t)blockIdx.x * (blockDim.x / a.team) + tid / a.team;
+        t = tid % a.team;
     } else {
         row = blockIdx.x;
-        slice = tid;
+        t = tid;
     }
-    const bool row_in = row < a.rows_pad;           // lane has a row to write
-    const bool row_valid = row < a.rows;            // row holds data
-    const int spr = (int)(a.K / 64);                // slices holding data
-    const bool has_data = row_valid && slice < spr;
+    const bool row_in = row < a.rows_pad;   // lane has a row to write
+    const bool row_valid = row < a.rows;    // row holds data
+    const int64_t k0 = (int64_t)t * P;      // first element of the phase-1 run
+    const bool has_data = row_valid && k0 < a.K;
 
-    double v[8][8];
+    // ---- phase 1: P consecutive elements, butterflies over the low bits ----
+    double v[P];
     {
-        uint4 w[8];
+        uint4 w[P / 8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            w[j] = make_uint4(0, 0, 0, 0);
-            if (has_data) w[j] = *(const uint4*)(a.X + row * a.K + slice_k<G>(slice, j));
+        for (int c = 0; c < P / 8; ++c) {
+            w[c] = make_uint4(0, 0, 0, 0);
+            if (has_data) w[c] = *(const uint4*)(a.X + row * a.K + k0 + 8 * c);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v[j][0] = bf16_lo(w[j].x); v[j][1] = bf16_hi(w[j].x);
-            v[j][2] = bf16_lo(w[j].y); v[j][3] = bf16_hi(w[j].y);
-            v[j][4] = bf16_lo(w[j].z); v[j][5] = bf16_hi(w[j].z);
-            v[j][6] = bf16_lo(w[j].w); v[j][7] = bf16_hi(w[j].w);
+        for (int c = 0; c < P / 8; ++c) {
+            v[8 * c + 0] = bf16_lo(w[c].x); v[8 * c + 1] = bf16_hi(w[c].x);
+            v[8 * c + 2] = bf16_lo(w[c].y); v[8 * c + 3] = bf16_hi(w[c].y);
+            v[8 * c + 4] = bf16_lo(w[c].z); v[8 * c + 5] = bf16_hi(w[c].z);
+            v[8 * c + 6] = bf16_lo(w[c].w); v[8 * c + 7] = bf16_hi(w[c].w);
         }
+    }
+#pragma unroll
+    for (int b = 1; b < P; b <<= 1)
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if (!(e & b)) {
+                const double x = v[e], y = v[e | b];
+                v[e] = x + y;
+                v[e | b] = x - y;
+            }
+
+    // ---- transpose through this wave's LDS region ----
+    // element u (wave-local) lives at double (u / P) * kRunD + u % P; the
+    // padding keeps both the 16-byte phase-1 writes and the 8-byte phase-2
+    // reads free of bank conflicts.
+    double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
+#pragma unroll
+    for (int e = 0; e < P; e += 2) *(double2*)(ld + lane * S::kRunD + e) = make_double2(v[e], v[e + 1]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    const int gbase = (lane / P) * P;    // first lane of this lane's group
+    const int lo = lane % P;             // phase-2: this lane's position in the low bits
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = ld[(gbase + i) * S::kRunD + lo];
+
+    // ---- phase 2: butterflies over the high bits ----
+#pragma unroll
+    for (int b = 1; b < P; b <<= 1)
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            if (!(i & b)) {
+                const double x = v[i], y = v[i | b];
+                v[i] = x + y;
+                v[i | b] = x - y;
+            }
+
+    // ---- round once to binary32, back to phase-1 order through LDS ----
+    constexpr double kNorm = (G == 256) ? 0.0625 : 0.125;  // 1/sqrt(g), exact
+    float* lf = (float*)ld;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // every lane's phase-2 reads are done before the region is rewritten
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < P; ++i) lf[(gbase + i) * S::kRunF + lo] = (float)(v[i] * kNorm);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    float r[P];
+#pragma unroll
+    for (int e = 0; e < P; e += 4) {
+        const float4 q = *(const float4*)(lf + lane * S::kRunF + e);
+        r[e] = q.x; r[e + 1] = q.y; r[e + 2] = q.z; r[e + 3] = q.w;
     }
 
-    // butterflies over e (index bits 0..2)
-#pragma unroll
-    for (int b = 1; b < 8; b <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!(e & b)) {
-                    double x = v[j][e], y = v[j][e | b];
-                    v[j][e] = x + y;
-                    v[j][e | b] = x - y;
-                }
-    // butterflies over j (index bits 5..7 for g = 256, 3..5 for g = 64)
-#pragma unroll
-    for (int b = 1; b < 8; b <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (!(j & b))
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    double x = v[j][e], y = v[j | b][e];
-                    v[j][e] = x + y;
-                    v[j | b][e] = x - y;
-                }
-    if constexpr (G == 256) {
-        // butterflies over q (index bits 3..4): lane pairs (l, l^1), (l, l^2)
-        const bool up1 = (tid & 1) != 0, up2 = (tid & 2) != 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                double p = quad_xor<1>(v[j][e]);
-                v[j][e] = up1 ? (p - v[j][e]) : (v[j][e] + p);
-            }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                double p = quad_xor<2>(v[j][e]);
-                v[j][e] = up2 ? (p - v[j][e]) : (v[j][e] + p);
-            }
-    }
-    constexpr double kNorm = (G == 256) ? 0.0625 : 0.125;  // 1/sqrt(g), exact
-    float r[8][8];
+    // ---- row absmax over the team ----
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            r[j][e] = (float)(v[j][e] * kNorm);  // the one rounding to binary32
-            amax = fmaxf(amax, fabsf(r[j][e]));
-        }
-
-    // row absmax over the team
+    for (int e = 0; e < P; ++e) amax = fmaxf(amax, fabsf(r[e]));
     if (a.team <= 64) {
         for (int o = 1; o < a.team; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     } else {
         __shared__ float red[16];
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        if (lane == 0) red[wave] = amax;
         __syncthreads();
         amax = red[0];
         for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
@@ -232,37 +223,42 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     const float s = zero_row ? 0.0f : amax / 7.0f;  // IEEE binary32 division
 
     if (!row_in) return;
-    if (row_valid && slice == 0) a.scales[row] = s;
+    if (row_valid && t == 0) a.scales[row] = s;
+    const bool write = (MODE == OUT_IMAGE) ? (k0 < a.K_pad) : has_data;
+    if (!write) return;
 
-    const bool write_slice = (MODE == OUT_IMAGE) ? (slice < a.slices_pad) : has_data;
-    if (!write_slice) return;
-
-    int8_t qa[8][8];
-    quantize_lane(r, s, zero_row, qa);
+    int8_t q[P];
+    quantize_run<P>(r, s, zero_row, q);
+    if constexpr (MODE == OUT_IMAGE) {
+        // P/8 words for k0, k0 + 8 (adjacent dwords of one 8-byte group when P = 16)
+        uint32_t w[P / 8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t k = slice_k<G>(slice, j);
-        const int8_t* q = qa[j];
-        if constexpr (MODE == OUT_IMAGE) {
+        for (int c = 0; c < P / 8; ++c) {
+            w[c] = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) w[c] |= (nib(q[8 * c + b]) | (nib(q[8 * c + b + 4]) << 4)) << (8 * b);
+        }
+        uint8_t* dst = a.out + image_word_offset(row, k0, a.K_pad);
+        if constexpr (P == 16)
+            *(uint2*)dst = make_uint2(w[0], w[1]);
+        else
+            *(uint32_t*)dst = w[0];
+    } else if constexpr (MODE == OUT_NK) {
+#pragma unroll
+        for (int c = 0; c < P / 8; ++c) {
             uint32_t w = 0;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) w |= (nib(q[b]) | (nib(q[b + 4]) << 4)) << (8 * b);
-            *(uint32_t*)(a.out + image_word_offset(row, k, a.K_pad)) = w;
-        } else if constexpr (MODE == OUT_NK) {
-            uint32_t w = 0;
+            for (int u = 0; u < 4; ++u) w |= (nib(q[8 * c + 2 * u]) | (nib(q[8 * c + 2 * u + 1]) << 4)) << (8 * u);
+            *(uint32_t*)(a.out + row * (a.K / 2) + (k0 + 8 * c) / 2) = w;
+        }
+    } else {  // OUT_ROWMAJOR
 #pragma unroll
-            for (int u = 0; u < 4; ++u) w |= (nib(q[2 * u]) | (nib(q[2 * u + 1]) << 4)) << (8 * u);
-            *(uint32_t*)(a.out + row * (a.K / 2) + k / 2) = w;
-        } else {  // OUT_ROWMAJOR
-            uint2 w;
-            w.x = pack4_i8(q);
-            w.y = pack4_i8(q + 4);
-            *(uint2*)(a.out + row * a.K + k) = w;
-            if (a.rotated) {
-                float4* rp = (float4*)(a.rotated + row * a.K + k);
-                rp[0] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
-                rp[1] = make_float4(r[j][4], r[j][5], r[j][6], r[j][7]);
-            }
+        for (int c = 0; c < P / 8; ++c)
+            *(uint2*)(a.out + row * a.K + k0 + 8 * c) = make_uint2(pack4_i8(q + 8 * c), pack4_i8(q + 8 * c + 4));
+        if (a.rotated) {
+#pragma unroll
+            for (int e = 0; e < P; e += 4)
+                *(float4*)(a.rotated + row * a.K + k0 + e) = make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
         }
     }
 }
@@ -590,6 +586,124 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// skinny_kernel: M <= 32 (one 32-row unit of activation codes)
+//
+// The product is a stream over the weight image: one workgroup per 32-column
+// strip, its four waves splitting K.  Every wave loads its weight units and
+// the matching activation units straight into registers (no reuse, so no LDS
+// staging), up to four 128-K units per batch with all loads of a batch in
+// flight at once, and issues one 32x32x32 MFMA per 32-wide k-step (W . X^T as
+// in gemm_kernel).  The four partial tiles are summed through LDS and the
+// epilogue writes the (<= 32) valid rows.
+// ---------------------------------------------------------------------------
+
+constexpr int kSkinnyWaves = 4;
+
+// 16-byte load that is not kept in the caches (the weight stream is read once)
+__device__ inline uint4 load_stream16(const uint8_t* p)
+{
+    const v4i v = __builtin_nontemporal_load((const v4i*)p);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+constexpr int kSkinnyBatch = 3;  // 128-K units per load batch
+
+template <int OUT>
+__global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) int32_t red[kSkinnyWaves - 1][16][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int nt = blockIdx.x;
+    const int KB = a.KB;
+    const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int kb0 = wave * per, kb1 = min(KB, kb0 + per);
+    const int swz = row_swizzle(r32);
+    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + r32 * 64;
+    const uint8_t* abase = a.act + r32 * 64;  // activation row tile 0
+    const int off0 = ((0 + h) ^ swz) * 16, off1 = ((2 + h) ^ swz) * 16;
+
+    v16i acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0;
+
+    for (int kb = kb0; kb < kb1; kb += kSkinnyBatch) {
+        uint4 wq[kSkinnyBatch][2], aq[kSkinnyBatch][2];
+#pragma unroll
+        for (int u = 0; u < kSkinnyBatch; ++u) {
+            if (kb + u < kb1) {
+                const uint8_t* wu = wbase + (size_t)(kb + u) * kUnitBytes;
+                const uint8_t* au = abase + (size_t)(kb + u) * kUnitBytes;
+                wq[u][0] = load_stream16(wu + off0);
+                wq[u][1] = load_stream16(wu + off1);
+                aq[u][0] = *(const uint4*)(au + off0);
+                aq[u][1] = *(const uint4*)(au + off1);
+            } else {
+                wq[u][0] = wq[u][1] = aq[u][0] = aq[u][1] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSkinnyBatch; ++u)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(widen_lo_hi(wq[u][p].x, wq[u][p].y),
+                                                           widen_lo_hi(aq[u][p].x, aq[u][p].y), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(widen_lo_hi(wq[u][p].z, wq[u][p].w),
+                                                           widen_lo_hi(aq[u][p].z, aq[u][p].w), acc, 0, 0, 0);
+            }
+    }
+
+    // sum the partial tiles of the waves (exact integer sums)
+    if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave - 1][r][lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += red[w][r][lane];
+
+    // lane holds output row m = r32 and, per group of four registers t, the
+    // four consecutive columns n = 32 nt + 8 t + 4 h + (0..3)
+    const int64_t m = r32;
+    if (m >= a.M) return;
+    const float sxm = (OUT == GEMM_OUT_BF16) ? a.sx[m] : 0.0f;
+    const bool vec_ok = (a.N % 4) == 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t n0 = (int64_t)nt * 32 + 8 * t + 4 * h;
+        if (n0 >= a.N) continue;
+        int32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[4 * t + u] >> 8;  // both operands entered x 16
+        if constexpr (OUT == GEMM_OUT_I32) {
+            int32_t* dst = (int32_t*)a.out + m * a.N + n0;
+            if (vec_ok) {
+                *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
+            } else {
+                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
+            }
+        } else {
+            uint16_t y[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t n = n0 + u < a.N ? n0 + u : a.N - 1;
+                const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
+                y[u] = f32_to_bf16_rne(__builtin_fmaf((float)v[u] * sxm, a.sw[n], bn));
+            }
+            uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
+            if (vec_ok) {
+                *(uint2*)dst = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+            } else {
+                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = y[u];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // layout kernels
 // ---------------------------------------------------------------------------
 
@@ -640,49 +754,61 @@ __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_
 // ---------------------------------------------------------------------------
 
 template <int G, int MODE>
-static void launch_prep_g(const PrepArgs& a, dim3 grid, dim3 block, hipStream_t s)
+static void launch_prep_g(PrepArgs a, hipStream_t s)
 {
-    hipLaunchKernelGGL((prep_kernel<G, MODE>), grid, block, 0, s, a);
-}
-
-template <int MODE>
-static void launch_prep_mode(int g, const PrepArgs& a, dim3 grid, dim3 block, hipStream_t s)
-{
-    if (g == 256)
-        launch_prep_g<256, MODE>(a, grid, block, s);
-    else
-        launch_prep_g<64, MODE>(a, grid, block, s);
-}
-
-void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
-{
-    const int slices_pad = (int)(a.K_pad / 64);
+    constexpr int P = PrepShape<G>::P;
+    const int lanes = (int)(a.K_pad / P);  // lanes per row
     int team = 1;
-    if (slices_pad <= 64) {
-        while (team < slices_pad) team <<= 1;
-    } else {
-        team = (slices_pad + 63) / 64 * 64;
-    }
-    a.team = team;
-    a.slices_pad = slices_pad;
     dim3 block, grid;
-    if (team <= 64) {
+    if (lanes <= 64) {
+        while (team < lanes) team <<= 1;
         block = dim3(256);
         const int64_t rows_per_block = 256 / team;
         grid = dim3((unsigned)((a.rows_pad + rows_per_block - 1) / rows_per_block));
     } else {
+        team = (lanes + 63) / 64 * 64;
         block = dim3(team);
         grid = dim3((unsigned)a.rows_pad);
     }
+    a.team = team;
+    const size_t lds = (size_t)(block.x / 64) * PrepShape<G>::kWaveLdsBytes;
+    static bool attr_set = false;  // benign race: every caller sets the same value
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)&prep_kernel<G, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  16 * PrepShape<G>::kWaveLdsBytes);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((prep_kernel<G, MODE>), grid, block, lds, s, a);
+}
+
+template <int MODE>
+static void launch_prep_mode(int g, const PrepArgs& a, hipStream_t s)
+{
+    if (g == 256)
+        launch_prep_g<256, MODE>(a, s);
+    else
+        launch_prep_g<64, MODE>(a, s);
+}
+
+void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
+{
     switch (mode) {
-        case OUT_IMAGE: launch_prep_mode<OUT_IMAGE>(g, a, grid, block, s); break;
-        case OUT_NK: launch_prep_mode<OUT_NK>(g, a, grid, block, s); break;
-        default: launch_prep_mode<OUT_ROWMAJOR>(g, a, grid, block, s); break;
+        case OUT_IMAGE: launch_prep_mode<OUT_IMAGE>(g, a, s); break;
+        case OUT_NK: launch_prep_mode<OUT_NK>(g, a, s); break;
+        default: launch_prep_mode<OUT_ROWMAJOR>(g, a, s); break;
     }
 }
 
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
 {
+    if (a.M <= 32) {
+        dim3 grid((unsigned)a.NT), block(kSkinnyWaves * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16>), grid, block, 0, s, a);
+        return;
+    }
     a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
     a.tiles_n = (a.NT + kBN / 32 - 1) / (kBN / 32);
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kWaves * 64);
