@@ -20,6 +20,10 @@
 #include "kernels.h"
 #include "layout.h"
 
+#ifndef CONVROT_GEMM_WAVES
+#define CONVROT_GEMM_WAVES 8
+#endif
+
 namespace convrot {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -33,12 +37,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// binary32 -> bf16 bits, round to nearest even (finite values)
-__device__ inline uint16_t f32_to_bf16_rne(float f)
+// Two binary32 -> two bf16 (round to nearest even) packed low | high << 16:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Codes = clamp(rint(fl32(r / s)), -7, 7) for the P values of a lane.
@@ -281,11 +287,9 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
 // ---------------------------------------------------------------------------
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kWaves = 8;
 constexpr int kStageA = 8 * kUnitBytes;      // 16 KB
 constexpr int kStage = 2 * kStageA;          // 32 KB: activation units, then weight units
 constexpr int kStages = 4;
-constexpr int kCopies = 4;                   // copies per wave per stage: 2 x 1 KB activation + 2 x 1 KB weight
 
 // Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
 // M0 + 16 l.  Written as inline asm so that the compiler neither tracks the
@@ -300,36 +304,56 @@ __device__ inline void lds_copy16(const uint8_t* g, uint32_t lds_addr)
                  : "memory", "m0");
 }
 
-// Wait until at most `stages_in_flight` stages of copies (kCopies each) are
-// outstanding, then synchronise the workgroup.  No fence: the only memory
-// traffic to order is LDS (every read of the released stage has returned into
-// registers) and the copies (ordered by vmcnt).
+// Wait until at most `stages_in_flight` stages of copies (COPIES each per
+// wave) are outstanding, then synchronise the workgroup.  No fence: the only
+// memory traffic to order is LDS (every read of a released stage has returned
+// into registers) and the copies (ordered by vmcnt).
+template <int COPIES>
 __device__ inline void wait_copies_and_barrier(int stages_in_flight)
 {
-    switch (stages_in_flight) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory"); break;
+    static_assert(COPIES == 4 || COPIES == 8, "copies per wave per stage");
+    if (stages_in_flight <= 0) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (stages_in_flight == 1) {
+        if constexpr (COPIES == 4)
+            asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else if (stages_in_flight == 2) {
+        if constexpr (COPIES == 4)
+            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    } else {
+        if constexpr (COPIES == 4)
+            asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
     }
 }
 
-// Wave w copies activation unit w and weight unit w of stage kb into the
-// stage buffer at LDS address `stage` (wave-uniform).  Units past the end of
-// the matrix are re-read from the last valid unit (their products land in
-// rows/columns that are never stored), which keeps the number of copies in
-// flight per wave constant.
+// A stage holds 8 activation and 8 weight units; with NW waves each wave
+// copies 8 / NW of each (two 1 KB runs per unit).  Units past the end of the
+// matrix are re-read from the last valid unit (their products land in rows /
+// columns that are never stored), which keeps the number of copies in flight
+// per wave constant.
+template <int NW>
 __device__ inline void issue_stage(const GemmArgs& a, uint32_t stage, int mt0, int nt0, int kb, int wave, int lane)
 {
-    const int mt = min(mt0 + wave, a.MT - 1), nt = min(nt0 + wave, a.NT - 1);
-    const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kUnitBytes + lane * 16;
-    const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kUnitBytes + lane * 16;
-    const uint32_t da = stage + wave * kUnitBytes;
-    const uint32_t db = stage + kStageA + wave * kUnitBytes;
-    lds_copy16(sa, da);
-    lds_copy16(sa + 1024, da + 1024);
-    lds_copy16(sb, db);
-    lds_copy16(sb + 1024, db + 1024);
+    constexpr int U = 8 / NW;  // units of each operand per wave
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int unit = wave * U + u;
+        const int mt = min(mt0 + unit, a.MT - 1), nt = min(nt0 + unit, a.NT - 1);
+        const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kUnitBytes + lane * 16;
+        const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kUnitBytes + lane * 16;
+        const uint32_t da = stage + unit * kUnitBytes;
+        const uint32_t db = stage + kStageA + unit * kUnitBytes;
+        lds_copy16(sa, da);
+        lds_copy16(sa + 1024, da + 1024);
+        lds_copy16(sb, db);
+        lds_copy16(sb + 1024, db + 1024);
+    }
 }
 
 // INT4 codes of one 8-byte group -> 16 INT8 values x 16 in natural order
@@ -343,72 +367,92 @@ __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
     return r;
 }
 
-// Per-lane LDS offsets of a 128 (M) x 64 (N) wave tile: this lane's row of
-// activation unit wm*4 and of weight unit wn*2 within a stage.
+// Per-lane LDS offsets of a 128 (M) x 32*BJ (N) wave tile: this lane's row of
+// activation unit wm*4 and of weight unit wn*BJ within a stage.
 struct Frag {
     int sa, sb, swz, h;
 };
 
-// Quads of one pair of k-steps: 4 activation quads and 2 weight quads, each
+// Quads of one pair of k-steps: 4 activation quads and BJ weight quads, each
 // 16 bytes = 2 k-steps x 16 codes of this lane's row.
-__device__ inline void load_pair(const Frag& f, const uint8_t* stage, int pr, uint4 (&aq)[4], uint4 (&bq)[2])
+template <int BJ>
+__device__ inline void load_pair(const Frag& f, const uint8_t* stage, int pr, uint4 (&aq)[4], uint4 (&bq)[BJ])
 {
     const int off = ((2 * pr + f.h) ^ f.swz) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) aq[i] = *(const uint4*)(stage + f.sa + i * kUnitBytes + off);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bq[j] = *(const uint4*)(stage + f.sb + j * kUnitBytes + off);
+    for (int j = 0; j < BJ; ++j) bq[j] = *(const uint4*)(stage + f.sb + j * kUnitBytes + off);
 }
 
-// Widened operands of one k-step: 4 activation and 2 weight fragments of 16
+// Widened operands of one k-step: 4 activation and BJ weight fragments of 16
 // INT8 values x 16 each.
+template <int BJ>
 struct Wide {
-    v4i a[4], b[2];
+    v4i a[4], b[BJ];
 };
 
 // k-step kk (0 or 1) of a pair of quads -> widened fragments
-__device__ inline void widen(const uint4 (&aq)[4], const uint4 (&bq)[2], int kk, Wide& w)
+template <int BJ>
+__device__ inline void widen(const uint4 (&aq)[4], const uint4 (&bq)[BJ], int kk, Wide<BJ>& w)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w.a[i] = kk == 0 ? widen_lo_hi(aq[i].x, aq[i].y) : widen_lo_hi(aq[i].z, aq[i].w);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) w.b[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
+    for (int j = 0; j < BJ; ++j) w.b[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
 }
 
 // acc[j][i] += W_j . X_i^T for one k-step
-__device__ inline void mfmas(const Wide& w, v16i (&acc)[2][4])
+template <int BJ>
+__device__ inline void mfmas(const Wide<BJ>& w, v16i (&acc)[BJ][4])
 {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w.b[j], w.a[i], acc[j][i], 0, 0, 0);
 }
 
-// Instruction-mix hints for one k-step phase (sched_group_barrier masks:
-// 0x008 MFMA, 0x100 LDS read, 0x002 VALU): each MFMA is followed by a few of
-// the widening instructions of the next k-step and, where there are any, one
-// LDS read, so the matrix core, the vector ALU and the LDS work side by side
-// instead of in bursts.
+// Instruction-mix hints for one k-step phase of NM MFMAs (sched_group_barrier
+// masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU): each MFMA is followed by a
+// few of the widening instructions of the next k-step and, where there are
+// any, one LDS read, so the matrix core, the vector ALU and the LDS work side
+// by side instead of in bursts.
+template <int NM>
 __device__ inline void interleave_mfma_valu(int lds_reads)
 {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < NM; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (m < lds_reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 40 / NM + 1, 0);
     }
 }
 
-template <int OUT>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
+// ---------------------------------------------------------------------------
+// gemm_kernel<OUT, NW>: NW waves (4 or 8) in a 2 x (NW/2) arrangement, each
+// owning a 128 (M) x 32*BJ (N) output tile, BJ = 16 / NW: 4 x BJ MFMA
+// 32x32x32 tiles computed as W . X^T, so that each lane ends up holding four
+// consecutive output columns of one row.  With NW = 8 two waves share a SIMD;
+// with NW = 4 each wave has a SIMD to itself and reads fewer LDS bytes per
+// MFMA.  Both operands are widened from INT4 to INT8 x 16 in registers right
+// after the LDS read; the int32 sums are therefore 256 times the dot products
+// and are divided by 256 (exactly) in the epilogue.  |dot| <= 49 K <= 802816,
+// so 256 |dot| < 2^31.
+// ---------------------------------------------------------------------------
+
+template <int OUT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
 {
+    constexpr int BJ = 16 / NW;            // weight fragments per wave
+    constexpr int COPIES = 32 / NW;        // copies per wave per stage
+    constexpr int WN = 32 * BJ;            // wave tile width in N
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps copy addresses scalar
-    const int wm = wave & 1, wn = wave >> 1;                     // 2 x 4 waves of 128 x 64
+    const int wm = wave & 1, wn = wave >> 1;
 
     // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous range of tiles (row tiles fastest) so tiles sharing weight
@@ -421,9 +465,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
     const int tm = vid % a.tiles_m, tn = vid / a.tiles_m;
     const int mt0 = tm * (kBM / 32), nt0 = tn * (kBN / 32);
 
-    v16i acc[2][4];
+    v16i acc[BJ][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -434,58 +478,64 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     Frag f;
     f.sa = (wm * 4) * kUnitBytes + r32 * 64;
-    f.sb = kStageA + (wn * 2) * kUnitBytes + r32 * 64;
+    f.sb = kStageA + (wn * BJ) * kUnitBytes + r32 * 64;
     f.swz = row_swizzle(r32);
     f.h = h;
 
     // prologue: the first kStages stages in flight; wait for stage 0
     const int first = KB < kStages ? KB : kStages;
-    for (int s = 0; s < first; ++s) issue_stage(a, lds0 + s * kStage, mt0, nt0, s, wave, lane);
-    wait_copies_and_barrier(first - 1);
-    uint4 aq[2][4], bq[2][2];
-    Wide w[2];
-    load_pair(f, smem, 0, aq[0], bq[0]);
-    widen(aq[0], bq[0], 0, w[0]);
+    for (int s = 0; s < first; ++s) issue_stage<NW>(a, lds0 + s * kStage, mt0, nt0, s, wave, lane);
+    wait_copies_and_barrier<COPIES>(first - 1);
+    uint4 aq[2][4], bq[2][BJ];
+    Wide<BJ> w[2];
+    load_pair<BJ>(f, smem, 0, aq[0], bq[0]);
+    widen<BJ>(aq[0], bq[0], 0, w[0]);
 
-    // Per stage: k-step 0 MFMAs with the reads of pair 1 and the widening of
-    // k-step 1; k-step 1 MFMAs with the widening of k-step 2; k-step 2 MFMAs
-    // with the widening of k-step 3; the stage barrier, the copy of stage
-    // kb + kStages into the released buffer and the reads of the next stage's
-    // pair 0; k-step 3 MFMAs with the widening of the next stage's k-step 0.
-    // sched_barrier(0) separates the phases so that no MFMA is hoisted above
-    // the stage barrier and no LDS read sinks below its phase.
+    // Per stage kb (buffer kb % kStages):
+    //   k-step 0 MFMAs | reads of pair 1 of this stage, widening of k-step 1
+    //   k-step 1 MFMAs | widening of k-step 2 (pair 1)
+    //   barrier: stage kb + 1 has landed everywhere, and every wave has
+    //            consumed this stage's buffer, which takes the copy of stage
+    //            kb + kStages (so copies run three stages ahead)
+    //   k-step 2 MFMAs | reads of pair 0 of stage kb + 1, widening of k-step 3
+    //   k-step 3 MFMAs | widening of k-step 0 of stage kb + 1
+    // LDS reads thus come in two even halves per stage and the barrier sits
+    // between MFMA phases.  sched_barrier(0) keeps the phases in this order
+    // (nothing hoisted above the barrier, no read sunk below its phase).
+    constexpr int NM = 4 * BJ;            // MFMAs per k-step
+    constexpr int NR = 4 + BJ;            // LDS reads per pair
     for (int kb = 0; kb < KB; ++kb) {
         const int slot = kb % kStages;
         const uint8_t* cur = smem + slot * kStage;
-        load_pair(f, cur, 1, aq[1], bq[1]);
-        mfmas(w[0], acc);
-        widen(aq[0], bq[0], 1, w[1]);
-        interleave_mfma_valu(6);
+        const bool more = kb + 1 < KB;
+        load_pair<BJ>(f, cur, 1, aq[1], bq[1]);
+        mfmas<BJ>(w[0], acc);
+        widen<BJ>(aq[0], bq[0], 1, w[1]);
+        interleave_mfma_valu<NM>(NR);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(w[1], acc);
-        widen(aq[1], bq[1], 0, w[0]);
-        interleave_mfma_valu(0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(w[0], acc);
-        widen(aq[1], bq[1], 1, w[1]);
-        interleave_mfma_valu(0);
+        mfmas<BJ>(w[1], acc);
+        widen<BJ>(aq[1], bq[1], 0, w[0]);
+        interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
         // stage kb + 1 must have landed; stages kb + 2 .. kb + kStages - 1 may be in flight
         int in_flight = KB - kb - 2;
         in_flight = in_flight < 0 ? 0 : (in_flight > kStages - 2 ? kStages - 2 : in_flight);
-        wait_copies_and_barrier(in_flight);
-        if (kb + kStages < KB) issue_stage(a, lds0 + slot * kStage, mt0, nt0, kb + kStages, wave, lane);
-        const bool more = kb + 1 < KB;
-        if (more) load_pair(f, smem + ((kb + 1) % kStages) * kStage, 0, aq[0], bq[0]);
+        wait_copies_and_barrier<COPIES>(in_flight);
+        if (kb + kStages < KB) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb + kStages, wave, lane);
+        if (more) load_pair<BJ>(f, smem + ((kb + 1) % kStages) * kStage, 0, aq[0], bq[0]);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(w[1], acc);
-        if (more) widen(aq[0], bq[0], 0, w[0]);
-        interleave_mfma_valu(0);
+        mfmas<BJ>(w[0], acc);
+        widen<BJ>(aq[1], bq[1], 1, w[1]);
+        interleave_mfma_valu<NM>(more ? NR : 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<BJ>(w[1], acc);
+        if (more) widen<BJ>(aq[0], bq[0], 0, w[0]);
+        interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
     }
 
     const int64_t m_base = (int64_t)tm * kBM + wm * 128;
-    const int64_t n_base = (int64_t)tn * kBN + wn * 64;
+    const int64_t n_base = (int64_t)tn * kBN + wn * WN;
 
     // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
     // register (row / 8) * 4 + row % 4; here rows are output columns n and
@@ -498,7 +548,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
             const int64_t m = m_base + 32 * i + r32;
             if (m >= a.M) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < BJ; ++j)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int64_t n0 = n_base + 32 * j + 8 * t + 4 * h;
@@ -519,24 +569,27 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
         // through LDS (free again: every copy has landed and every wave has
         // passed the last stage barrier) -- one cooperative load instead of
         // per-lane scattered loads.  Then the bf16 output goes through a
-        // per-wave LDS tile of 32 rows x 64 columns (row pitch 144 bytes: the
-        // 8-byte writes of 16 consecutive lanes hit distinct banks), one MFMA
-        // tile row at a time, and is stored as 16-byte row segments.
+        // per-wave LDS tile of 32 rows x WN columns (row pitch 2*WN + 16 bytes:
+        // the 8-byte writes of 16 consecutive lanes hit distinct banks), one
+        // MFMA tile row at a time, and is stored as 16-byte row segments.
         float* p_sw = (float*)smem;
         float* p_b = p_sw + kBN;
         float* p_sx = p_b + kBN;
-        constexpr int kPitch = 144;
+        constexpr int kPitch = 2 * WN + 16;
         constexpr int kParamBytes = 4096;
-        static_assert(kParamBytes + kWaves * 32 * kPitch <= kStages * kStage, "epilogue staging must fit in LDS");
+        constexpr int kChunks = WN / 8;       // 16-byte chunks per tile row
+        static_assert(kParamBytes + NW * 32 * kPitch <= kStages * kStage, "epilogue staging must fit in LDS");
         __syncthreads();
-        if (tid < kBN) {
-            const int64_t n = (int64_t)tn * kBN + tid;
-            const int64_t nc = n < a.N ? n : a.N - 1;
-            p_sw[tid] = a.sw[nc];
-            p_b[tid] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
-        } else if (tid < kBN + kBM) {
-            const int64_t m = (int64_t)tm * kBM + (tid - kBN);
-            p_sx[tid - kBN] = a.sx[m < a.M ? m : a.M - 1];
+        for (int e = tid; e < kBN + kBM; e += NW * 64) {
+            if (e < kBN) {
+                const int64_t n = (int64_t)tn * kBN + e;
+                const int64_t nc = n < a.N ? n : a.N - 1;
+                p_sw[e] = a.sw[nc];
+                p_b[e] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
+            } else {
+                const int64_t m = (int64_t)tm * kBM + (e - kBN);
+                p_sx[e - kBN] = a.sx[m < a.M ? m : a.M - 1];
+            }
         }
         __syncthreads();
         uint8_t* tile = smem + kParamBytes + wave * (32 * kPitch);
@@ -545,30 +598,27 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a)
         for (int i = 0; i < 4; ++i) {
             const float sxm = p_sx[wm * 128 + 32 * i + r32];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < BJ; ++j)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
-                    const float4 sw4 = *(const float4*)(p_sw + wn * 64 + nl);
-                    const float4 b4 = *(const float4*)(p_b + wn * 64 + nl);
+                    const float4 sw4 = *(const float4*)(p_sw + wn * WN + nl);
+                    const float4 b4 = *(const float4*)(p_b + wn * WN + nl);
                     const float sc[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
                     const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-                    uint16_t y[4];
+                    float y[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int32_t v = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
-                        y[u] = f32_to_bf16_rne(__builtin_fmaf((float)v * sxm, sc[u], bb[u]));
+                        y[u] = __builtin_fmaf((float)v * sxm, sc[u], bb[u]);
                     }
-                    uint2 w;
-                    w.x = (uint32_t)y[0] | ((uint32_t)y[1] << 16);
-                    w.y = (uint32_t)y[2] | ((uint32_t)y[3] << 16);
-                    *(uint2*)(tile + r32 * kPitch + nl * 2) = w;
+                    *(uint2*)(tile + r32 * kPitch + nl * 2) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
                 }
-            // read back row segments: lane l takes 16-byte chunk (l & 7) of rows (l >> 3) + 8 s
+            // read back row segments: lane l takes 16-byte chunk (l % kChunks) of rows (l / kChunks) + (64 / kChunks) s
 #pragma unroll
-            for (int sr = 0; sr < 4; ++sr) {
-                const int rho = (lane >> 3) + 8 * sr;
-                const int c = lane & 7;
+            for (int sr = 0; sr < 32 * kChunks / 64; ++sr) {
+                const int rho = lane / kChunks + (64 / kChunks) * sr;
+                const int c = lane % kChunks;
                 const uint4 w = *(const uint4*)(tile + rho * kPitch + c * 16);
                 const int64_t m = m_base + 32 * i + rho;
                 const int64_t n = n_base + 8 * c;
@@ -686,18 +736,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a)
                 for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
             }
         } else {
-            uint16_t y[4];
+            float y[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t n = n0 + u < a.N ? n0 + u : a.N - 1;
                 const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-                y[u] = f32_to_bf16_rne(__builtin_fmaf((float)v[u] * sxm, a.sw[n], bn));
+                y[u] = __builtin_fmaf((float)v[u] * sxm, a.sw[n], bn);
             }
+            const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
             uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
             if (vec_ok) {
-                *(uint2*)dst = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+                *(uint2*)dst = make_uint2(p01, p23);
             } else {
-                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = y[u];
+                const uint16_t yb[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = yb[u];
             }
         }
     }
@@ -811,11 +863,12 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     }
     a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
     a.tiles_n = (a.NT + kBN / 32 - 1) / (kBN / 32);
-    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kWaves * 64);
+    constexpr int NW = CONVROT_GEMM_WAVES;
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(NW * 64);
     if (out_mode == GEMM_OUT_I32)
-        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, NW>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, NW>), grid, block, 0, s, a);
 }
 
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, hipStream_t s)
