@@ -10,10 +10,13 @@ through enough independent buffer sets (>= 512 MiB in total) that the 256 MiB
 Infinity Cache cannot serve the weights from a previous step.
 
 Prints one JSON line on stdout.  ``value`` is effective TOPS = 2*M*N*K per
-step time.  ``roofline`` rates the GEMM kernel (the dominant one) from its
-average launch duration, measured with HIP events on the launch stream,
-against the dense INT8 matrix-core peak.  ``cpu_baseline`` is the CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+step time (the K timed steps run as one HIP graph).  ``roofline`` rates the
+GEMM kernel (the dominant one) from its average launch duration -- a pair of
+HIP events on the launch stream around each launch -- against the dense
+INT8 matrix-core peak (or, for weight-streaming shapes, the HBM peak);
+``traffic`` comes from the committed rocprofv3 byte counters when they match
+the current kernel source.  ``cpu_baseline`` is the CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -65,8 +68,10 @@ def read_traffic(workload: str, gemm_ops_unit_launches: int):
 
 
 def cpu_baseline(inp, target_s: float):
-    """The oracle's linear on a bounded sample of rows (weight prepared by the
-    oracle beforehand, untimed, like the GPU's offline weight step)."""
+    """The oracle's linear on a bounded sample of the workload: as many rows of
+    X as fit in about target_s seconds (the whole X, repeated, when one pass is
+    shorter).  The weight is prepared by the oracle beforehand, untimed, like
+    the GPU's offline weight step."""
     import oracle
     wl = inp["workload"]
     threads = oracle.default_threads()
@@ -78,14 +83,17 @@ def cpu_baseline(inp, target_s: float):
     oracle.linear(inp["x"][:probe], qw, sw, inp["bias"], wl.g, threads=threads)
     dt = time.perf_counter() - t0
     rows = int(max(probe, min(wl.M, probe * target_s / max(dt, 1e-6))))
+    reps = 1
+    if rows == wl.M:
+        reps = int(max(1, min(20, target_s / max(dt * wl.M / probe, 1e-6))))
     t0 = time.perf_counter()
-    oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], wl.g, threads=threads)
+    for _ in range(reps):
+        oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], wl.g, threads=threads)
     dt = time.perf_counter() - t0
-    tops = 2.0 * rows * wl.N * wl.K / dt / 1e12
+    tops = 2.0 * rows * reps * wl.N * wl.K / dt / 1e12
     return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows of X against the full {wl.N}x{wl.K} weight "
-                      f"(complete linear: rotation, quantization, int64 dot products, epilogue), "
-                      f"{dt:.2f} s"}
+            "sample": f"{rows} of {wl.M} rows of X x {reps} pass(es) against the full {wl.N}x{wl.K} weight "
+                      f"(complete linear: rotation, quantization, int64 dot products, epilogue), {dt:.2f} s"}
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -192,32 +200,56 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # GEMM kernel alone: per-launch HIP events on the launch stream, same cold rotation
-    n_gemm = max(10, min(args.steps, 200))
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_gemm)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_gemm)]
-    for i in range(n_gemm):
-        s = sets[i % n_sets]
-        binding.convrot_prepare_activations(s["X"], g, s["ws"])
-        starts[i].record()
-        binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
-        ends[i].record()
-    torch.cuda.synchronize()
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
-    # activation preparation alone, the same way
-    for i in range(n_gemm):
-        s = sets[i % n_sets]
-        starts[i].record()
-        binding.convrot_prepare_activations(s["X"], g, s["ws"])
-        ends[i].record()
-    torch.cuda.synchronize()
-    prep_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    # Launch durations of the two kernels, timed with a pair of HIP events
+    # around every launch on the launch stream, in the same prep -> GEMM order
+    # and over the same buffer rotation as the timed steps.  A bounded spin
+    # kernel holds the stream while the host enqueues, so that no event
+    # measures the host's launch latency.
+    def launch_avg_ms(n):
+        pairs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        hold = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold.record()
+        torch.cuda._sleep(int(2.0e5 * n))  # ~80 us per launch pair at 2.4 GHz
+        t0 = time.perf_counter()
+        for i in range(n):
+            s = sets[i % n_sets]
+            e = pairs[i]
+            e[0].record()
+            binding.convrot_prepare_activations(s["X"], g, s["ws"])
+            e[1].record()
+            binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
+            e[2].record()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        held_ms = hold.elapsed_time(pairs[0][0])
+        if held_ms < host_ms:
+            log(f"warning: stream held {held_ms:.2f} ms < host enqueue {host_ms:.2f} ms; "
+                "launch durations may include host latency")
+        prep = float(np.mean([e[0].elapsed_time(e[1]) for e in pairs]))
+        gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in pairs]))
+        return prep, gemm
+
+    n_k = max(20, min(args.steps, 200))
+    prep_ms, gemm_ms = launch_avg_ms(n_k)
 
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
-    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     gbs = wl.bytes_alg / (ms_per_step * 1e-3) / 1e9
     traffic = read_traffic(wl.name, 1)
+    # Roofline of the GEMM kernel: the matrix-core peak for compute-bound
+    # shapes; for weight-streaming shapes (arithmetic intensity below the ridge
+    # point) the HBM peak, with the kernel's algorithmic bytes: packed weight
+    # and activation codes, weight/activation scales, bias and Y.
+    gemm_bytes = N * K // 2 + M * K // 2 + 4 * M + 4 * N + 2 * N + 2 * M * N
+    if ops / wl.bytes_alg >= PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        ach = ops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
+    else:
+        ach = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,8 +276,7 @@ def main():
         "int8_frac": round(value / PEAK_INT8_TOPS, 4),
         "kernel_us": {"prep": round(prep_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)},
         "weight_prep_ms": round(weight_prep_ms, 4),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
