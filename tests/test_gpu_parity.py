@@ -109,7 +109,7 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
 # --------------------------------------------------------------------------
 
 GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
-               (513, 257, 256), (17, 33, 12288)]
+               (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)

@@ -638,16 +638,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
 // ---------------------------------------------------------------------------
 // skinny_kernel: M <= 32 (one 32-row unit of activation codes)
 //
-// The product is a stream over the weight image: one workgroup per 32-column
-// strip, its four waves splitting K.  Every wave loads its weight units and
-// the matching activation units straight into registers (no reuse, so no LDS
-// staging), up to four 128-K units per batch with all loads of a batch in
-// flight at once, and issues one 32x32x32 MFMA per 32-wide k-step (W . X^T as
-// in gemm_kernel).  The four partial tiles are summed through LDS and the
-// epilogue writes the (<= 32) valid rows.
+// The product is a stream over the weight image.  One workgroup per
+// 16-column strip (half of a 32-row weight unit: 1 KB per 128-K unit), its
+// four waves splitting K; each strip is computed with the 16x16x64 INT8 MFMA
+// as W . X^T for MH 16-row halves of the activation unit.  Every lane loads
+// one 16-byte chunk (32 codes) of its weight row and of its activation row(s)
+// per unit straight into registers -- no reuse, so no LDS staging -- with up
+// to kSkinnyBatch units of loads in flight per wave (at K <= 3072 the whole
+// strip, so the full weight image is requested as soon as the grid is
+// resident).  With 16-column strips a 12288-column weight is 768 equal
+// workgroups, three per CU.  The chunk of lane quad q feeds k-slots q of two
+// MFMAs (its first and second 16 codes); both operands use the same
+// assignment, so the sum over k is the dot product.  The four partial tiles
+// are summed through LDS and the epilogue writes the valid rows.
 // ---------------------------------------------------------------------------
 
 constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyBatch = 6;  // 128-K units per load batch
 
 // 16-byte load that is not kept in the caches (the weight stream is read once)
 __device__ inline uint4 load_stream16(const uint8_t* p)
@@ -655,93 +662,102 @@ __device__ inline uint4 load_stream16(const uint8_t* p)
     const v4i v = __builtin_nontemporal_load((const v4i*)p);
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
-constexpr int kSkinnyBatch = 3;  // 128-K units per load batch
 
-template <int OUT>
-__global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a)
+template <int OUT, int MH>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) int32_t red[kSkinnyWaves - 1][16][64];
+    __shared__ __attribute__((aligned(16))) int32_t red[kSkinnyWaves - 1][MH][4][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int r32 = lane & 31, h = lane >> 5;
-    const int nt = blockIdx.x;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int strip = blockIdx.x;                   // output columns 16 strip .. 16 strip + 15
+    const int nt = strip >> 1, half = strip & 1;    // weight unit row tile and its half
     const int KB = a.KB;
     const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;
     const int kb0 = wave * per, kb1 = min(KB, kb0 + per);
-    const int swz = row_swizzle(r32);
-    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + r32 * 64;
-    const uint8_t* abase = a.act + r32 * 64;  // activation row tile 0
-    const int off0 = ((0 + h) ^ swz) * 16, off1 = ((2 + h) ^ swz) * 16;
-
-    v16i acc;
+    const int wrow = 16 * half + r16;
+    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + wrow * 64 + ((q ^ row_swizzle(wrow)) * 16);
+    const uint8_t* abase[MH];
+    bool act_row[MH];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0;
+    for (int mh = 0; mh < MH; ++mh) {
+        const int arow = 16 * mh + r16;
+        abase[mh] = a.act + arow * 64 + ((q ^ row_swizzle(arow)) * 16);
+        act_row[mh] = arow < a.M;  // rows past M are zero in the image: not loaded
+    }
+
+    v4i acc[MH];
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh) acc[mh] = v4i{0, 0, 0, 0};
 
     for (int kb = kb0; kb < kb1; kb += kSkinnyBatch) {
-        uint4 wq[kSkinnyBatch][2], aq[kSkinnyBatch][2];
+        uint4 wq[kSkinnyBatch], aq[kSkinnyBatch][MH];
 #pragma unroll
         for (int u = 0; u < kSkinnyBatch; ++u) {
-            if (kb + u < kb1) {
-                const uint8_t* wu = wbase + (size_t)(kb + u) * kUnitBytes;
-                const uint8_t* au = abase + (size_t)(kb + u) * kUnitBytes;
-                wq[u][0] = load_stream16(wu + off0);
-                wq[u][1] = load_stream16(wu + off1);
-                aq[u][0] = *(const uint4*)(au + off0);
-                aq[u][1] = *(const uint4*)(au + off1);
-            } else {
-                wq[u][0] = wq[u][1] = aq[u][0] = aq[u][1] = make_uint4(0, 0, 0, 0);
-            }
+            const bool in = kb + u < kb1;
+            wq[u] = in ? load_stream16(wbase + (size_t)(kb + u) * kUnitBytes) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int mh = 0; mh < MH; ++mh)
+                aq[u][mh] = (in && act_row[mh]) ? *(const uint4*)(abase[mh] + (size_t)(kb + u) * kUnitBytes)
+                                                : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < kSkinnyBatch; ++u)
+        for (int u = 0; u < kSkinnyBatch; ++u) {
+            if (kb + u >= kb1) break;
+            const v4i w0 = widen_lo_hi(wq[u].x, wq[u].y), w1 = widen_lo_hi(wq[u].z, wq[u].w);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(widen_lo_hi(wq[u][p].x, wq[u][p].y),
-                                                           widen_lo_hi(aq[u][p].x, aq[u][p].y), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(widen_lo_hi(wq[u][p].z, wq[u][p].w),
-                                                           widen_lo_hi(aq[u][p].z, aq[u][p].w), acc, 0, 0, 0);
+            for (int mh = 0; mh < MH; ++mh) {
+                acc[mh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, widen_lo_hi(aq[u][mh].x, aq[u][mh].y), acc[mh],
+                                                                0, 0, 0);
+                acc[mh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, widen_lo_hi(aq[u][mh].z, aq[u][mh].w), acc[mh],
+                                                                0, 0, 0);
             }
+        }
     }
 
     // sum the partial tiles of the waves (exact integer sums)
     if (wave > 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave - 1][r][lane] = acc[r];
+        for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wave - 1][mh][j][lane] = acc[mh][j];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += red[w][r][lane];
+        for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mh][j] += red[w][mh][j][lane];
 
-    // lane holds output row m = r32 and, per group of four registers t, the
-    // four consecutive columns n = 32 nt + 8 t + 4 h + (0..3)
-    const int64_t m = r32;
-    if (m >= a.M) return;
-    const float sxm = (OUT == GEMM_OUT_BF16) ? a.sx[m] : 0.0f;
+    // lane holds, per half mh, output row m = 16 mh + r16 and the four
+    // consecutive columns n = 16 strip + 4 q + (0..3)
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    if (n0 >= a.N) return;
     const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t n0 = (int64_t)nt * 32 + 8 * t + 4 * h;
-        if (n0 >= a.N) continue;
+    for (int mh = 0; mh < MH; ++mh) {
+        const int64_t m = 16 * mh + r16;
+        if (m >= a.M) continue;
         int32_t v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[4 * t + u] >> 8;  // both operands entered x 16
+        for (int j = 0; j < 4; ++j) v[j] = acc[mh][j] >> 8;  // both operands entered x 16
         if constexpr (OUT == GEMM_OUT_I32) {
             int32_t* dst = (int32_t*)a.out + m * a.N + n0;
             if (vec_ok) {
                 *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
             } else {
-                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
+                for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = v[j];
             }
         } else {
+            const float sxm = a.sx[m];
             float y[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t n = n0 + u < a.N ? n0 + u : a.N - 1;
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
                 const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-                y[u] = __builtin_fmaf((float)v[u] * sxm, a.sw[n], bn);
+                y[j] = __builtin_fmaf((float)v[j] * sxm, a.sw[n], bn);
             }
             const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
             uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
@@ -749,7 +765,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a)
                 *(uint2*)dst = make_uint2(p01, p23);
             } else {
                 const uint16_t yb[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
-                for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = yb[u];
+                for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = yb[j];
             }
         }
     }
@@ -854,11 +870,19 @@ void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
 {
     if (a.M <= 32) {
-        dim3 grid((unsigned)a.NT), block(kSkinnyWaves * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16>), grid, block, 0, s, a);
+        dim3 grid((unsigned)((a.N + 15) / 16)), block(kSkinnyWaves * 64);
+        const bool one = a.M <= 16;
+        if (out_mode == GEMM_OUT_I32) {
+            if (one)
+                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32, 2>), grid, block, 0, s, a);
+        } else {
+            if (one)
+                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16, 2>), grid, block, 0, s, a);
+        }
         return;
     }
     a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
