@@ -17,6 +17,8 @@
 // QuaRot Stage 1c", section 1 (R = I_G (x) H, X.R = [X_1 H, ..., X_G H]).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "layout.h"
 
@@ -47,37 +49,89 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Codes = clamp(rint(fl32(r / s)), -7, 7) for the P values of a lane.
+// Codes = clamp(rint(fl32(r / s)), -7, 7) for the P values of a lane, each
+// returned as the bit pattern of the binary32 value 1.5 * 2^23 + code, whose
+// low byte is the code in two's complement (adding 1.5 * 2^23 to |y| < 2^22
+// rounds y to an integer, ties to even, held in the low mantissa bits).
 // Fast path: y = r * rcp(s) is within 2 ulp of r / s (|y| < 8, so the error is
 // below 2^-20); whenever y is farther than 2^-18 from a half-integer, rint(y)
 // equals rint(fl32(r / s)) because no rounding boundary lies between them.
-// Elements near a half-integer (and rows whose s is not a normal number) take
-// the correctly rounded binary32 division, in a branch that is skipped unless
-// some lane of the wave needs it.
+// The residual y - rint(y) is exact, so the test is exact.  Elements near a
+// half-integer (and rows whose s is not a normal number) take the correctly
+// rounded binary32 division, in a branch that is skipped unless some lane of
+// the wave needs it.  With a normal s, |r| <= 7 s (1 + 2^-23) keeps every
+// code in [-7, 7]; the clamp matters only on the division path, where a
+// subnormal s can be far from absmax / 7.
 template <int P>
-__device__ inline void quantize_run(const float (&r)[P], float s, bool zero_row, int8_t (&q)[P])
+__device__ inline void quantize_bits(const float (&r)[P], float s, bool zero_row, uint32_t (&f)[P])
 {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
     const bool exact_only = !(s >= 0x1p-126f);
     const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
-    float qf[P];
     bool need = exact_only && !zero_row;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
         const float y = r[e] * inv;
-        const float ry = rintf(y);
-        need |= fabsf(fabsf(y - ry) - 0.5f) < 0x1p-18f;
-        qf[e] = ry;
+        const float fy = y + kMagic;
+        need |= fabsf(y - (fy - kMagic)) > 0.5f - 0x1p-18f;
+        f[e] = __float_as_uint(fy);
     }
     if (need && !zero_row) {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
             const float y = r[e] * inv;
-            if (exact_only || fabsf(fabsf(y - rintf(y)) - 0.5f) < 0x1p-18f)
-                qf[e] = rintf(r[e] / s);  // IEEE binary32 division, round half to even
+            const float fy = y + kMagic;
+            if (exact_only || fabsf(y - (fy - kMagic)) > 0.5f - 0x1p-18f)
+                f[e] = __float_as_uint(fminf(fmaxf(r[e] / s, -7.0f), 7.0f) + kMagic);  // IEEE division
         }
     }
+    if (zero_row) {
 #pragma unroll
-    for (int e = 0; e < P; ++e) q[e] = zero_row ? (int8_t)0 : (int8_t)(int)fminf(fmaxf(qf[e], -7.0f), 7.0f);
+        for (int e = 0; e < P; ++e) f[e] = __float_as_uint(kMagic);
+    }
+}
+
+// Low bytes of four words, as bytes 0..3 of one word (v_perm_b32 selects bytes
+// of the pair {hi, lo}: selectors 0-3 pick bytes of lo, 4-7 of hi, 12 gives 0).
+__device__ inline uint32_t low_bytes4(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3)
+{
+    return __builtin_amdgcn_perm(f1, f0, 0x0C0C0400u) | __builtin_amdgcn_perm(f3, f2, 0x04000C0Cu);
+}
+
+// One image word from the quantized bit patterns of codes k .. k+7: byte b
+// holds code k+b in its low nibble and code k+4+b in its high nibble.
+__device__ inline uint32_t image_word(const uint32_t* f)
+{
+    const uint32_t lo = low_bytes4(f[0], f[1], f[2], f[3]);
+    const uint32_t hi = low_bytes4(f[4], f[5], f[6], f[7]);
+    return (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u);
+}
+
+// Max over a wave-row of DPP lanes.
+template <int CTRL>
+__device__ inline uint32_t max_dpp(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+// Max over the lanes of a team (8, 16 or 32 aligned lanes, or the whole wave
+// when team >= 64) of the bit patterns of non-negative floats, which order as
+// unsigned integers.
+__device__ inline uint32_t team_max(uint32_t v, int team)
+{
+    v = max_dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v = max_dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v = max_dpp<0x141>(v);  // row_half_mirror: lanes i and 7 - i of each 8
+    if (team >= 16) v = max_dpp<0x140>(v);  // row_mirror: lanes i and 15 - i of each 16
+    if (team == 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+    if (team >= 64) {
+        const uint32_t a0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+        const uint32_t a1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+        const uint32_t a2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+        const uint32_t a3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+        v = max(max(a0, a1), max(a2, a3));
+    }
+    return v;
 }
 
 __device__ inline uint32_t nib(int8_t q) { return (uint32_t)(uint8_t)q & 0xFu; }
@@ -116,48 +170,54 @@ struct PrepShape {
     static constexpr int P = (G == 256) ? 16 : 8;             // elements per lane per phase
     static constexpr int kRunD = P + 2;                        // doubles per padded P-run in LDS
     static constexpr int kRunF = P + 4;                        // floats per padded P-run in LDS
-    static constexpr int kWaveLdsBytes = 64 * kRunD * 8;       // LDS per wave
+    static constexpr int kWaveLdsBytes =                       // LDS per wave
+        (32 * kRunD * 8 > 64 * kRunF * 4) ? 32 * kRunD * 8 : 64 * kRunF * 4;
 };
 
+// Loads of the P bf16 values of a lane's phase-1 run.  The loads are always
+// issued (from row 0, element 0 when the lane has no data -- a valid address,
+// since rows >= 1 and K >= 64 whenever the kernel runs) and then replaced by
+// zeros, so the number of loads in flight is the same on every path and the
+// wait for a prefetched row does not have to drain the newer loads.
+template <int P>
+__device__ inline void load_run(const uint16_t* X, int64_t row, int64_t K, int64_t k0, bool has_data,
+                                uint4 (&w)[P / 8])
+{
+    const uint16_t* src = X + (has_data ? row * K + k0 : 0);
+#pragma unroll
+    for (int c = 0; c < P / 8; ++c) w[c] = *(const uint4*)(src + 8 * c);
+}
+
+template <int P>
+__device__ inline void zero_unless(bool has_data, uint4 (&w)[P / 8])
+{
+#pragma unroll
+    for (int c = 0; c < P / 8; ++c)
+        if (!has_data) w[c] = make_uint4(0, 0, 0, 0);
+}
+
+// One row of the prep kernel: rotation, absmax, quantization and the write
+// of the codes in the layout of MODE.  w holds the lane's P bf16 values.
 template <int G, int MODE>
-__global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
+__device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape<G>::P / 8], int64_t row, int t,
+                                         int64_t k0, int lane, int wave, double* ld, uint32_t (*red)[16], int parity)
 {
     using S = PrepShape<G>;
     constexpr int P = S::P;
-    extern __shared__ __attribute__((aligned(16))) uint8_t prep_lds[];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    int64_t row;
-    int t;  // lane within the row's team
-    if (a.team <= 64) {
-        row = (int64_t)blockIdx.x * (blockDim.x / a.team) + tid / a.team;
-        t = tid % a.team;
-    } else {
-        row = blockIdx.x;
-        t = tid;
-    }
-    const bool row_in = row < a.rows_pad;   // lane has a row to write
-    const bool row_valid = row < a.rows;    // row holds data
-    const int64_t k0 = (int64_t)t * P;      // first element of the phase-1 run
+    const int gbase = (lane / P) * P;  // first lane of this lane's group
+    const int lo = lane % P;           // phase-2: this lane's position in the low bits
+    float* lf = (float*)ld;
+    const bool row_valid = row < a.rows;  // row holds data
     const bool has_data = row_valid && k0 < a.K;
-
     // ---- phase 1: P consecutive elements, butterflies over the low bits ----
+    zero_unless<P>(has_data, w);
     double v[P];
-    {
-        uint4 w[P / 8];
 #pragma unroll
-        for (int c = 0; c < P / 8; ++c) {
-            w[c] = make_uint4(0, 0, 0, 0);
-            if (has_data) w[c] = *(const uint4*)(a.X + row * a.K + k0 + 8 * c);
-        }
-#pragma unroll
-        for (int c = 0; c < P / 8; ++c) {
-            v[8 * c + 0] = bf16_lo(w[c].x); v[8 * c + 1] = bf16_hi(w[c].x);
-            v[8 * c + 2] = bf16_lo(w[c].y); v[8 * c + 3] = bf16_hi(w[c].y);
-            v[8 * c + 4] = bf16_lo(w[c].z); v[8 * c + 5] = bf16_hi(w[c].z);
-            v[8 * c + 6] = bf16_lo(w[c].w); v[8 * c + 7] = bf16_hi(w[c].w);
-        }
+    for (int c = 0; c < P / 8; ++c) {
+        v[8 * c + 0] = bf16_lo(w[c].x); v[8 * c + 1] = bf16_hi(w[c].x);
+        v[8 * c + 2] = bf16_lo(w[c].y); v[8 * c + 3] = bf16_hi(w[c].y);
+        v[8 * c + 4] = bf16_lo(w[c].z); v[8 * c + 5] = bf16_hi(w[c].z);
+        v[8 * c + 6] = bf16_lo(w[c].w); v[8 * c + 7] = bf16_hi(w[c].w);
     }
 #pragma unroll
     for (int b = 1; b < P; b <<= 1)
@@ -169,19 +229,31 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
                 v[e | b] = x - y;
             }
 
-    // ---- transpose through this wave's LDS region ----
-    // element u (wave-local) lives at double (u / P) * kRunD + u % P; the
-    // padding keeps both the 16-byte phase-1 writes and the 8-byte phase-2
-    // reads free of bank conflicts.
-    double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
+    // ---- transpose through this wave's LDS region, half a group at a time ----
+    // Pass hh: the lanes holding runs hh*P/2 .. hh*P/2 + P/2 - 1 of each
+    // group write their P values to slot (group, run - hh*P/2); then every
+    // lane reads element lo of those P/2 runs.  Half the region of a
+    // whole-wave transpose; the padding keeps the 16-byte writes and the
+    // 8-byte reads free of bank conflicts.
+    double u[P];
+    {
+        const int slot_base = (lane / P) * (P / 2);
 #pragma unroll
-    for (int e = 0; e < P; e += 2) *(double2*)(ld + lane * S::kRunD + e) = make_double2(v[e], v[e + 1]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-    const int gbase = (lane / P) * P;    // first lane of this lane's group
-    const int lo = lane % P;             // phase-2: this lane's position in the low bits
+        for (int hh = 0; hh < 2; ++hh) {
+            if (lo / (P / 2) == hh) {
+                double* dst = ld + (slot_base + lo % (P / 2)) * S::kRunD;
 #pragma unroll
-    for (int i = 0; i < P; ++i) v[i] = ld[(gbase + i) * S::kRunD + lo];
+                for (int e = 0; e < P; e += 2) *(double2*)(dst + e) = make_double2(v[e], v[e + 1]);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+            for (int i = 0; i < P / 2; ++i) u[hh * (P / 2) + i] = ld[(slot_base + i) * S::kRunD + lo];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // every lane's reads are done before the region is rewritten
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
 
     // ---- phase 2: butterflies over the high bits ----
 #pragma unroll
@@ -189,19 +261,15 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
 #pragma unroll
         for (int i = 0; i < P; ++i)
             if (!(i & b)) {
-                const double x = v[i], y = v[i | b];
-                v[i] = x + y;
-                v[i | b] = x - y;
+                const double x = u[i], y = u[i | b];
+                u[i] = x + y;
+                u[i | b] = x - y;
             }
 
     // ---- round once to binary32, back to phase-1 order through LDS ----
     constexpr double kNorm = (G == 256) ? 0.0625 : 0.125;  // 1/sqrt(g), exact
-    float* lf = (float*)ld;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // every lane's phase-2 reads are done before the region is rewritten
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < P; ++i) lf[(gbase + i) * S::kRunF + lo] = (float)(v[i] * kNorm);
+    for (int i = 0; i < P; ++i) lf[(gbase + i) * S::kRunF + lo] = (float)(u[i] * kNorm);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     float r[P];
@@ -210,62 +278,113 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
         const float4 q = *(const float4*)(lf + lane * S::kRunF + e);
         r[e] = q.x; r[e + 1] = q.y; r[e + 2] = q.z; r[e + 3] = q.w;
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next row rewrites the region
+    __builtin_amdgcn_wave_barrier();
 
     // ---- row absmax over the team ----
-    float amax = 0.0f;
+    float lane_max = 0.0f;
 #pragma unroll
-    for (int e = 0; e < P; ++e) amax = fmaxf(amax, fabsf(r[e]));
-    if (a.team <= 64) {
-        for (int o = 1; o < a.team; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    } else {
-        __shared__ float red[16];
-        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-        if (lane == 0) red[wave] = amax;
+    for (int e = 0; e < P; ++e) lane_max = fmaxf(lane_max, fabsf(r[e]));
+    uint32_t amax_bits = team_max(__float_as_uint(lane_max), a.team);
+    if (a.team > 64) {
+        // red[parity] is rewritten two rows later, after every wave has
+        // passed the next row's barrier (and so has read it)
+        if (lane == 0) red[parity][wave] = amax_bits;
         __syncthreads();
-        amax = red[0];
-        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
+        amax_bits = red[parity][0];
+        for (int wv = 1; wv < (int)(blockDim.x >> 6); ++wv) amax_bits = max(amax_bits, red[parity][wv]);
     }
+    const float amax = __uint_as_float(amax_bits);
     const bool zero_row = !(amax > 0.0f);
     const float s = zero_row ? 0.0f : amax / 7.0f;  // IEEE binary32 division
 
-    if (!row_in) return;
     if (row_valid && t == 0) a.scales[row] = s;
-    const bool write = (MODE == OUT_IMAGE) ? (k0 < a.K_pad) : has_data;
-    if (!write) return;
+    const bool write = (MODE == OUT_IMAGE) ? (k0 < a.K_pad && row < a.rows_pad) : has_data;
+    if (write) {
+        uint32_t f[P];
+        quantize_bits<P>(r, s, zero_row, f);
+        if constexpr (MODE == OUT_IMAGE) {
+            // P/8 words for k0, k0 + 8 (adjacent dwords of one 8-byte group when P = 16)
+            uint8_t* dst = a.out + image_word_offset(row, k0, a.K_pad);
+            if constexpr (P == 16)
+                *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
+            else
+                *(uint32_t*)dst = image_word(f);
+        } else {
+            int8_t q[P];
+#pragma unroll
+            for (int e = 0; e < P; ++e) q[e] = (int8_t)(f[e] & 0xFFu);
+            if constexpr (MODE == OUT_NK) {
+#pragma unroll
+                for (int c = 0; c < P / 8; ++c) {
+                    uint32_t wd = 0;
+#pragma unroll
+                    for (int u2 = 0; u2 < 4; ++u2)
+                        wd |= (nib(q[8 * c + 2 * u2]) | (nib(q[8 * c + 2 * u2 + 1]) << 4)) << (8 * u2);
+                    *(uint32_t*)(a.out + row * (a.K / 2) + (k0 + 8 * c) / 2) = wd;
+                }
+            } else {  // OUT_ROWMAJOR
+#pragma unroll
+                for (int c = 0; c < P / 8; ++c)
+                    *(uint2*)(a.out + row * a.K + k0 + 8 * c) = make_uint2(pack4_i8(q + 8 * c), pack4_i8(q + 8 * c + 4));
+                if (a.rotated) {
+#pragma unroll
+                    for (int e = 0; e < P; e += 4)
+                        *(float4*)(a.rotated + row * a.K + k0 + e) = make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
+                }
+            }
+        }
+    }
+}
 
-    int8_t q[P];
-    quantize_run<P>(r, s, zero_row, q);
-    if constexpr (MODE == OUT_IMAGE) {
-        // P/8 words for k0, k0 + 8 (adjacent dwords of one 8-byte group when P = 16)
-        uint32_t w[P / 8];
-#pragma unroll
-        for (int c = 0; c < P / 8; ++c) {
-            w[c] = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) w[c] |= (nib(q[8 * c + b]) | (nib(q[8 * c + b + 4]) << 4)) << (8 * b);
-        }
-        uint8_t* dst = a.out + image_word_offset(row, k0, a.K_pad);
-        if constexpr (P == 16)
-            *(uint2*)dst = make_uint2(w[0], w[1]);
-        else
-            *(uint32_t*)dst = w[0];
-    } else if constexpr (MODE == OUT_NK) {
-#pragma unroll
-        for (int c = 0; c < P / 8; ++c) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) w |= (nib(q[8 * c + 2 * u]) | (nib(q[8 * c + 2 * u + 1]) << 4)) << (8 * u);
-            *(uint32_t*)(a.out + row * (a.K / 2) + (k0 + 8 * c) / 2) = w;
-        }
-    } else {  // OUT_ROWMAJOR
-#pragma unroll
-        for (int c = 0; c < P / 8; ++c)
-            *(uint2*)(a.out + row * a.K + k0 + 8 * c) = make_uint2(pack4_i8(q + 8 * c), pack4_i8(q + 8 * c + 4));
-        if (a.rotated) {
-#pragma unroll
-            for (int e = 0; e < P; e += 4)
-                *(float4*)(a.rotated + row * a.K + k0 + e) = make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
-        }
+template <int G, int MODE>
+__global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
+{
+    using S = PrepShape<G>;
+    constexpr int P = S::P;
+    extern __shared__ __attribute__((aligned(16))) uint8_t prep_lds[];
+    __shared__ uint32_t red[2][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // Rows are walked with a stride of one grid's worth of rows; the loads of
+    // a lane's next row are issued before the current row is processed, into
+    // the other of two register buffers (no copy between them, so the wait
+    // for one row never drains the next row's loads).
+    // The trip count is the same for every lane of the workgroup (rows past
+    // the end are processed as empty rows and not written), so the loop is
+    // uniform control flow.
+    int64_t row, row_step, first;
+    int t;  // lane within the row's team
+    if (a.team <= 64) {
+        const int per_block = blockDim.x / a.team;
+        first = (int64_t)blockIdx.x * per_block;
+        row = first + tid / a.team;
+        row_step = (int64_t)gridDim.x * per_block;
+        t = tid % a.team;
+    } else {
+        first = row = blockIdx.x;
+        row_step = gridDim.x;
+        t = tid;
+    }
+    const int64_t n_it = first < a.rows_pad ? (a.rows_pad - first + row_step - 1) / row_step : 0;
+    const int64_t k0 = (int64_t)t * P;  // first element of the phase-1 run
+    double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
+    const bool lane_k = k0 < a.K;
+
+    uint4 wa[P / 8], wb[P / 8];
+    load_run<P>(a.X, row, a.K, k0, row < a.rows && lane_k, wa);
+    for (int64_t it = 0; it < n_it; it += 2) {
+        int64_t nx = row + row_step;
+        load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wb);
+        prep_row<G, MODE>(a, wa, row, t, k0, lane, wave, ld, red, 0);
+        row = nx;
+        if (it + 1 >= n_it) break;
+        nx = row + row_step;
+        load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wa);
+        prep_row<G, MODE>(a, wb, row, t, k0, lane, wave, ld, red, 1);
+        row = nx;
     }
 }
 
@@ -821,32 +940,61 @@ __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_
 // host-side launchers
 // ---------------------------------------------------------------------------
 
+// Compute units of the current device (cached per device).
+static int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int G, int MODE>
 static void launch_prep_g(PrepArgs a, hipStream_t s)
 {
     constexpr int P = PrepShape<G>::P;
     const int lanes = (int)(a.K_pad / P);  // lanes per row
     int team = 1;
-    dim3 block, grid;
+    int block;
+    int64_t row_slots;  // rows one workgroup holds at a time
     if (lanes <= 64) {
         while (team < lanes) team <<= 1;
-        block = dim3(256);
-        const int64_t rows_per_block = 256 / team;
-        grid = dim3((unsigned)((a.rows_pad + rows_per_block - 1) / rows_per_block));
+        block = 256;
+        row_slots = 256 / team;
     } else {
         team = (lanes + 63) / 64 * 64;
-        block = dim3(team);
-        grid = dim3((unsigned)a.rows_pad);
+        block = team;
+        row_slots = 1;
     }
     a.team = team;
-    const size_t lds = (size_t)(block.x / 64) * PrepShape<G>::kWaveLdsBytes;
+    const size_t lds = (size_t)(block / 64) * PrepShape<G>::kWaveLdsBytes;
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)&prep_kernel<G, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   16 * PrepShape<G>::kWaveLdsBytes);
         attr_set = true;
     }
-    hipLaunchKernelGGL((prep_kernel<G, MODE>), grid, block, lds, s, a);
+    // One resident grid's worth of workgroups at most; each walks its rows
+    // with a stride of the grid.
+    static std::atomic<int> per_cu_cache[17];  // by waves per workgroup
+    const int waves = block / 64;
+    int per_cu = per_cu_cache[waves].load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)&prep_kernel<G, MODE>, block, lds) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        per_cu_cache[waves].store(per_cu, std::memory_order_relaxed);
+    }
+    const int64_t need = (a.rows_pad + row_slots - 1) / row_slots;
+    const int64_t resident = (int64_t)device_cus() * per_cu;
+    const unsigned grid = (unsigned)(need < resident ? need : resident);
+    hipLaunchKernelGGL((prep_kernel<G, MODE>), dim3(grid), dim3(block), lds, s, a);
 }
 
 template <int MODE>
