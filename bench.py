@@ -158,7 +158,7 @@ def main():
     torch.cuda.synchronize()
     weight_prep_ms = ev0.elapsed_time(ev1) / 3
 
-    ws_bytes = binding.convrot_workspace_bytes(M, K, g)
+    ws_bytes = binding.convrot_workspace_bytes(M, K, N, g)
     set_bytes = X0.numel() * 2 + image0.numel() + sw0.numel() * 4 + B0.numel() * 2 + M * N * 2 + ws_bytes
     n_sets = int(min(64, max(1, -(-args.cold_bytes // set_bytes))))
     sets = []

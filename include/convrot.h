@@ -63,12 +63,20 @@ const char* convrot_version(void);
  * 64 or 256 and K % g == 0.  Returns CONVROT_OK or CONVROT_EINVAL. */
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
-/* Bytes of workspace convrot_linear needs: the activation-code image
- * (round_up(M, 32) * round_up(K, 128) / 2 bytes, INT4 codes in the same
- * layout as the weight image) followed, at the next 256-byte boundary, by the
- * activation scales sx (round_up(M, 32) floats).  Returns CONVROT_OK or
- * CONVROT_EINVAL. */
-int convrot_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
+/* Bytes of workspace convrot_linear needs for an M x K input and N outputs.
+ * Layout, each part starting at a 256-byte boundary:
+ *   1. the activation-code image: round_up(M, 32) * round_up(K, 128) / 2
+ *      bytes, INT4 codes in the same layout as the weight image;
+ *   2. the activation scales sx: round_up(M, 32) floats;
+ *   3. 512 uint32 counters of the split-K GEMM (cleared by
+ *      convrot_prepare_activations, left cleared by every GEMM);
+ *   4. split-K partial tiles: when M > 32 and the 256 x 256 output tiles are
+ *      too few to occupy the GPU, each tile's K range is shared by S
+ *      workgroups and S - 1 int32 partial tiles of 256 KB per output tile
+ *      live here (0 bytes otherwise).
+ * Parts 1-3 depend on M and K only; convrot_prepare_activations needs only
+ * them.  Returns CONVROT_OK or CONVROT_EINVAL. */
+int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes_host);
 
 /* ---- argument checks (host only, no HIP call) ------------------------- */
 
@@ -121,9 +129,9 @@ int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t
  *   sw_dev     float [N].
  *   bias_dev   bf16 [N], or NULL for no bias.
  *   Y_dev      bf16 [M][N], written.
- *   workspace_dev / ws_bytes: at least convrot_workspace_bytes(M, K, g); its
- *              contents on entry are ignored and on exit hold the activation
- *              codes and scales of X.
+ *   workspace_dev / ws_bytes: at least convrot_workspace_bytes(M, K, N, g);
+ *              its contents on entry are ignored and on exit hold the
+ *              activation codes and scales of X.
  */
 int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_dev, const float* sw_dev,
                    const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
@@ -134,7 +142,9 @@ int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_de
  * and scales of X into the workspace (rotation, row absmax, quantization);
  * convrot_gemm consumes that workspace: integer products against the weight
  * image, then the scale + bias epilogue into Y.  Same arguments and rules as
- * convrot_linear. */
+ * convrot_linear, except that convrot_prepare_activations needs only the
+ * first three parts of the workspace (it does not know N).  convrot_gemm
+ * leaves the workspace valid for another convrot_gemm. */
 int convrot_prepare_activations(const void* X_dev, int64_t M, int64_t K, int g, void* workspace_dev,
                                 size_t ws_bytes, void* stream);
 int convrot_gemm(const void* workspace_dev, size_t ws_bytes, int64_t M, int64_t K, const void* image_dev,
@@ -151,7 +161,7 @@ int convrot_prepare_rows(const void* X_dev, int64_t rows, int64_t K, int g, int8
 
 /* The integer product alone: acc_dev int32 [M][N] = qx . codes(image)^T for
  * activation codes qx_dev int8 [M][K] (values in [-7, 7]).  The codes are first
- * re-laid-out into the workspace (convrot_workspace_bytes(M, K, 64) bytes),
+ * re-laid-out into the workspace (convrot_workspace_bytes(M, K, N, 64) bytes),
  * then the GEMM kernel of convrot_linear runs with its epilogue replaced by
  * an int32 store. */
 int convrot_gemm_i32(const int8_t* qx_dev, int64_t M, int64_t K, const void* image_dev, int64_t N,

@@ -50,10 +50,18 @@ def test_weight_image_bytes(N, K, g, want):
 
 
 def test_workspace_bytes():
-    # packed INT4 activation image (M up to 32 rows, K up to 128) + 256-aligned scales
-    assert B.convrot_workspace_bytes(1, 3072, 256) == 32 * 3072 // 2 + 32 * 4
-    assert B.convrot_workspace_bytes(1536, 3072, 256) == 1536 * 3072 // 2 + 1536 * 4
-    assert B.convrot_workspace_bytes(5, 192, 64) == 32 * 256 // 2 + 32 * 4
+    # image (M up to 32 rows, K up to 128, INT4) | sx | 512 counters | split-K partials,
+    # each part 256-byte aligned (values worked out by hand from that layout)
+    # M <= 32: weight streaming, never split
+    assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 49152 + 256 + 2048
+    # 1536 x 3072 -> 9216: 216 tiles of 256 x 256 fill the GPU, no split
+    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 2359296 + 6144 + 2048
+    # 1536 x 12288 -> 3072: 72 tiles, K split 3 ways -> 2 partial tiles of 256 KB each
+    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 9437184 + 6144 + 2048 + 72 * 2 * 262144
+    # 5 x 192 -> N: M <= 32
+    assert B.convrot_workspace_bytes(5, 192, 100, 64) == 32 * 256 // 2 + 256 + 2048
+    # N = 0: nothing to split
+    assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 9437184 + 6144 + 2048
 
 
 @pytest.mark.parametrize("N,K,g", [(16, 100, 64), (16, 512, 128), (16, 0, 64), (-1, 256, 256), (16, 32768, 256)])
@@ -65,7 +73,7 @@ def test_size_queries_reject_bad_shapes(N, K, g):
 
 def _validate_linear(**over):
     args = dict(X=4096, M=64, K=1024, image=8192, sw=16384, bias=0, N=1024, g=256, Y=32768, ws=65536,
-                ws_bytes=B.convrot_workspace_bytes(64, 1024, 256))
+                ws_bytes=B.convrot_workspace_bytes(64, 1024, 1024, 256))
     args.update(over)
     return B.convrot_validate_linear(args["X"], args["M"], args["K"], args["image"], args["sw"], args["bias"],
                                      args["N"], args["g"], args["Y"], args["ws"], args["ws_bytes"])

@@ -109,7 +109,8 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
 # --------------------------------------------------------------------------
 
 GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
-               (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072)]
+               (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072),
+               (256, 512, 8192), (100, 300, 6144)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -133,6 +134,34 @@ def test_gemm_i32_integer_edges(gpu):
     assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (64, 1024, 8192), (300, 700, 4096)])
+def test_split_k_workspace_reuse(gpu, M, N, K):
+    """Shapes whose tiles are split along K: a workspace full of garbage is
+    cleared by the activation step, and repeated GEMMs on one workspace (the
+    split-K counters are returned to zero by each launch) -- also with a
+    different N in between -- give identical, oracle-exact results."""
+    import torch
+    # the workspace holds split-K partial tiles only when the GEMM splits K
+    assert gpu.convrot_workspace_bytes(M, K, N, 256) > gpu.convrot_workspace_bytes(M, K, 0, 256)
+    x = synth.random_bf16((M, K), seed=M + K, outliers=4)
+    w = synth.random_bf16((N, K), seed=N + K + 1, std=0.02)
+    b = synth.random_bf16((N,), seed=N, std=0.01)
+    oq_w, osw = oracle.prepare_weight(w, 256)
+    y_or = oracle.linear(x, oq_w, osw, b, 256)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), 256)
+    ws = gpu.new_workspace(M, K, N, 256)
+    ws.fill_(0xFF)
+    gpu.convrot_prepare_activations(_dev(x), 256, ws)
+    outs = [gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N) for _ in range(3)]
+    # a narrower GEMM on the same workspace, then the original again
+    Nn = N // 2
+    gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), Nn)
+    outs.append(gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N))
+    torch.cuda.synchronize()
+    for Y in outs:
+        assert np.array_equal(_host_bits(Y), y_or)
+
+
 # --------------------------------------------------------------------------
 # the whole linear
 # --------------------------------------------------------------------------
@@ -142,7 +171,7 @@ def _linear_parity(gpu, x, w, bias, g):
     oq_w, osw = oracle.prepare_weight(w, g)
     y_or, parts = oracle.linear(x, oq_w, osw, bias, g, want_parts=True)
     image, sw = gpu.convrot_prepare_weight(_dev(w), g)
-    ws = gpu.new_workspace(x.shape[0], K, g)
+    ws = gpu.new_workspace(x.shape[0], K, N, g)
     Y = gpu.convrot_linear(_dev(x), image, sw, None if bias is None else _dev(bias), N, g, workspace=ws)
     gy = _host_bits(Y)
     # codes of X (from the workspace) and of W (from the image)
@@ -222,7 +251,7 @@ def test_linear_full_size_sampled(gpu, name):
     M, N, K, g = wl.M, wl.N, wl.K, wl.g
     W = _dev(inp["w"])
     image, sw = gpu.convrot_prepare_weight(W, g)
-    ws = gpu.new_workspace(M, K, g)
+    ws = gpu.new_workspace(M, K, N, g)
     Y = gpu.convrot_linear(_dev(inp["x"]), image, sw, _dev(inp["bias"]), N, g, workspace=ws)
     Y2 = gpu.convrot_linear(_dev(inp["x"]), image, sw, _dev(inp["bias"]), N, g)
     torch.cuda.synchronize()

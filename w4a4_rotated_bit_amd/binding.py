@@ -45,7 +45,7 @@ _SIGNATURES = {
     "convrot_status_string": ([_I], ctypes.c_char_p),
     "convrot_version": ([], ctypes.c_char_p),
     "convrot_weight_image_bytes": ([_I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
-    "convrot_workspace_bytes": ([_I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
+    "convrot_workspace_bytes": ([_I64, _I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_validate_weight": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_validate_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_prepare_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
@@ -126,9 +126,9 @@ def convrot_weight_image_bytes(N: int, K: int, g: int) -> int:
     return out.value
 
 
-def convrot_workspace_bytes(M: int, K: int, g: int) -> int:
+def convrot_workspace_bytes(M: int, K: int, N: int, g: int) -> int:
     out = _SZ(0)
-    _call("convrot_workspace_bytes", M, K, g, ctypes.byref(out))
+    _call("convrot_workspace_bytes", M, K, N, g, ctypes.byref(out))
     return out.value
 
 
@@ -181,9 +181,9 @@ def convrot_repack_nk_to_image(nk, N: int, K: int, stream=None):
     return image
 
 
-def new_workspace(M: int, K: int, g: int, device="cuda"):
+def new_workspace(M: int, K: int, N: int, g: int, device="cuda"):
     import torch
-    return torch.empty(convrot_workspace_bytes(M, K, g), dtype=torch.uint8, device=device)
+    return torch.empty(convrot_workspace_bytes(M, K, N, g), dtype=torch.uint8, device=device)
 
 
 def convrot_linear(X, image, sw, bias, N: int, g: int, Y=None, workspace=None, stream=None):
@@ -193,7 +193,7 @@ def convrot_linear(X, image, sw, bias, N: int, g: int, Y=None, workspace=None, s
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     if workspace is None:
-        workspace = new_workspace(M, K, g, X.device)
+        workspace = new_workspace(M, K, N, g, X.device)
     bias_p = None if bias is None else _dev(bias, torch.bfloat16, "bias")
     _call("convrot_linear", _dev(X, torch.bfloat16, "X"), M, K, _dev(image, torch.uint8, "image"),
           _dev(sw, torch.float32, "sw"), bias_p, N, g, _dev(Y, torch.bfloat16, "Y"),
@@ -238,7 +238,7 @@ def convrot_gemm_i32(qx, image, N: int, workspace=None, stream=None):
     import torch
     M, K = qx.shape
     if workspace is None:
-        workspace = new_workspace(M, K, 64, qx.device)
+        workspace = new_workspace(M, K, N, 64, qx.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=qx.device)
     _call("convrot_gemm_i32", _dev(qx, torch.int8, "qx"), M, K, _dev(image, torch.uint8, "image"), N,
           _dev(acc, torch.int32, "acc"), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),

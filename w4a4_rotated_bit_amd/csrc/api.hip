@@ -60,6 +60,8 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.out = (uint8_t*)ws;
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
     a.rotated = nullptr;
+    a.zero = (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K));
+    a.zero_count = 2 * kSplitCounters;
     launch_prep(g, OUT_IMAGE, a, s);
     return launched();
 }
@@ -79,6 +81,9 @@ int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void*
     a.MT = (int)(round_up(M, kTileRows) / kTileRows);
     a.NT = (int)(round_up(N, kTileRows) / kTileRows);
     a.KB = (int)(round_up(K, kTileK) / kTileK);
+    a.splits = gemm_splits(M, N, K);
+    a.counters = (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K));
+    a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K));
     launch_gemm(out_mode, a, s);
     return launched();
 }
@@ -139,7 +144,7 @@ int convrot_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     int rc = validate_rows_out(X, M, K, g);
     if (rc || M == 0) return rc;
     if (!ws || !aligned(ws, 16)) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, K)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_partial_offset(M, K)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     return enqueue_prepare_activations(X, M, K, g, ws, as_stream(stream));
 }
@@ -194,10 +199,11 @@ int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, 
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!qx || !image || !acc || !ws) return CONVROT_EINVAL;
     if (!aligned(qx, 16) || !aligned(image, 16) || !aligned(acc, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, K)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    launch_act_relayout(qx, M, K, (uint8_t*)ws, s);
+    launch_act_relayout(qx, M, K, (uint8_t*)ws, (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K)),
+                        2 * kSplitCounters, s);
     if ((rc = launched())) return rc;
     return enqueue_gemm(GEMM_OUT_I32, ws, M, K, image, nullptr, nullptr, N, acc, s);
 }

@@ -23,9 +23,19 @@ int check_shape(int64_t rows, int64_t K, int g)
 
 size_t workspace_sx_offset(int64_t M, int64_t K) { return (size_t)round_up((int64_t)image_bytes(M, K), 256); }
 
-size_t workspace_bytes(int64_t M, int64_t K)
+size_t workspace_counter_offset(int64_t M, int64_t K)
 {
-    return workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows);
+    return (size_t)round_up((int64_t)(workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows)), 256);
+}
+
+size_t workspace_partial_offset(int64_t M, int64_t K)
+{
+    return workspace_counter_offset(M, K) + 2 * kSplitCounters * sizeof(uint32_t);
+}
+
+size_t workspace_bytes(int64_t M, int64_t K, int64_t N)
+{
+    return workspace_partial_offset(M, K) + gemm_partial_bytes(M, N, K);
 }
 
 }  // namespace convrot
@@ -55,12 +65,13 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
     return CONVROT_OK;
 }
 
-int convrot_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes)
+int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes)
 {
     if (!bytes) return CONVROT_EINVAL;
     int rc = check_shape(M, K, g);
     if (rc) return rc;
-    *bytes = workspace_bytes(M, K);
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    *bytes = workspace_bytes(M, K, N);
     return CONVROT_OK;
 }
 
@@ -84,7 +95,7 @@ int convrot_validate_linear(const void* X, int64_t M, int64_t K, const void* ima
     if (!X || !image || !sw || !Y || !ws) return CONVROT_EINVAL;
     if (!aligned(X, 16) || !aligned(image, 16) || !aligned(Y, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
     if (!aligned(sw, 4) || (bias && !aligned(bias, 2))) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, K)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
     return CONVROT_OK;
 }
 

@@ -11,7 +11,11 @@ constexpr int64_t kMaxRows = 16777216;     // 2^24 rows / columns
 
 bool aligned(const void* p, size_t a);
 int check_shape(int64_t rows, int64_t K, int g);
+// Workspace: activation image | sx (256-aligned) | split-K counters
+// (2 * kSplitCounters uint32, 256-aligned) | split-K partial tiles (256-aligned).
 size_t workspace_sx_offset(int64_t M, int64_t K);
-size_t workspace_bytes(int64_t M, int64_t K);
+size_t workspace_counter_offset(int64_t M, int64_t K);
+size_t workspace_partial_offset(int64_t M, int64_t K);
+size_t workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 }  // namespace convrot

@@ -16,6 +16,8 @@ struct PrepArgs {
     uint8_t* out;        // codes in the layout of the mode
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
+    uint32_t* zero;      // words cleared by workgroup 0 (split-K counters) or nullptr
+    int zero_count;
     int team;            // lanes per row (set by launch_prep)
 };
 
@@ -29,11 +31,15 @@ struct GemmArgs {
     int64_t M, N;
     int MT, NT, KB;      // 32-row tiles, 32-column tiles, 128-K blocks
     int tiles_m, tiles_n;  // set by launch_gemm
+    int splits;          // K splits per 256 x 256 tile (gemm_splits)
+    uint32_t* counters;  // 2 * kSplitCounters zeroed words (tickets, then finished writers)
+    int32_t* partial;    // (splits - 1) partial tiles per tile
 };
 
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
-void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, hipStream_t s);
+void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
+                         hipStream_t s);
 void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s);
 
 }  // namespace convrot

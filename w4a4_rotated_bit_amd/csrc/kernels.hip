@@ -348,6 +348,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    if (a.zero && blockIdx.x == 0)  // split-K counters of the GEMM that consumes this workspace
+        for (int i = tid; i < a.zero_count; i += blockDim.x) a.zero[i] = 0;
     // Rows are walked with a stride of one grid's worth of rows; the loads of
     // a lane's next row are issued before the current row is processed, into
     // the other of two register buffers (no copy between them, so the wait
@@ -549,6 +551,102 @@ __device__ inline void interleave_mfma_valu(int lds_reads)
 }
 
 // ---------------------------------------------------------------------------
+// Split-K exchange.  Every workgroup of a split tile takes a ticket from the
+// tile's counter.  The first S - 1 ticket holders store their int32 partial
+// tile (one 256 KB slot per ticket: 8-byte word u of thread t at
+// (u * threads + t) * 8, so each store instruction covers 512 contiguous bytes)
+// with device-coherent stores, wait until the stores
+// have completed, and count themselves finished.  The last ticket holder waits
+// until S - 1 writers have finished -- each of them already holds a ticket, so
+// it is running and finishes without waiting on anyone -- then pulls each
+// slot into LDS half by half with device-coherent global -> LDS copies (all in
+// flight at once), adds it to its own tile (exact integer sums, any order) and
+// goes on to the epilogue; it also returns both counters to zero for the next
+// launch.  Device-coherent (agent-scope, sc1) accesses go to the level of the
+// memory system that every compute unit sees, so no cache-wide write-back or
+// invalidation is needed.  Returns true for the workgroup that finishes the
+// tile.
+// ---------------------------------------------------------------------------
+
+// lds_copy16 with a device-coherent global read
+__device__ inline void lds_copy16_coherent(const uint8_t* g, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+template <int BJ, int NW>
+__device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, int wave, int lane, uint32_t lds0,
+                                        const uint8_t* smem, v16i (&acc)[BJ][4])
+{
+    constexpr int kThreads = NW * 64;
+    constexpr int kWords = BJ * 4 * 8;                 // 8-byte words per thread
+    constexpr int kSlotBytes = kThreads * kWords * 8;  // 256 KB
+    constexpr int kHalf = kSlotBytes / 2;              // fits the 128 KB stage ring
+    static_assert(kHalf <= kStages * kStage, "half a partial tile must fit in LDS");
+    __shared__ int ticket_sh;
+    uint32_t* tickets = a.counters + tile;
+    uint32_t* finished = a.counters + kSplitCounters + tile;
+    if (tid == 0) ticket_sh = (int)__hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // also: every wave is done with the stage ring
+    const int ticket = ticket_sh;
+    const int S = a.splits;
+    uint8_t* slots = (uint8_t*)a.partial + (size_t)tile * (S - 1) * kSlotBytes;
+    if (ticket < S - 1) {
+        uint64_t* dst = (uint64_t*)(slots + (size_t)ticket * kSlotBytes);
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int u = (j * 4 + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
+                    const uint64_t v = (uint64_t)(uint32_t)acc[j][i][2 * q] | ((uint64_t)(uint32_t)acc[j][i][2 * q + 1] << 32);
+                    __hip_atomic_store(dst + (size_t)u * kThreads + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        __builtin_amdgcn_s_waitcnt(0);  // every store of this wave has completed
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    if (tid == 0) {
+        // bounded: the writers are running and never wait
+        for (int spin = 0; spin < (1 << 26); ++spin) {
+            if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(S - 1)) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    constexpr int kChunksPerWave = kHalf / 1024 / NW;  // 1 KB per copy instruction
+    for (int sl = 0; sl < S - 1; ++sl) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint8_t* src = slots + (size_t)sl * kSlotBytes + half * kHalf;
+#pragma unroll
+            for (int c = 0; c < kChunksPerWave; ++c) {
+                const int chunk = wave * kChunksPerWave + c;
+                lds_copy16_coherent(src + chunk * 1024 + lane * 16, lds0 + chunk * 1024);
+            }
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int u2 = 0; u2 < kWords / 2; ++u2) {
+                const int u = half * (kWords / 2) + u2;
+                const int j = u / 32, i = (u / 8) % 4, q = u % 8;
+                const uint2 w = *(const uint2*)(smem + ((size_t)u2 * kThreads + tid) * 8);
+                acc[j][i][2 * q] += (int32_t)w.x;
+                acc[j][i][2 * q + 1] += (int32_t)w.y;
+            }
+            __syncthreads();  // every read of this half is done before the next copy
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // gemm_kernel<OUT, NW>: NW waves (4 or 8) in a 2 x (NW/2) arrangement, each
 // owning a 128 (M) x 32*BJ (N) output tile, BJ = 16 / NW: 4 x BJ MFMA
 // 32x32x32 tiles computed as W . X^T, so that each lane ends up holding four
@@ -573,16 +671,22 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps copy addresses scalar
     const int wm = wave & 1, wn = wave >> 1;
 
-    // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a
-    // contiguous range of tiles (row tiles fastest) so tiles sharing weight
-    // columns share that XCD's L2.
-    const int total = a.tiles_m * a.tiles_n;
+    // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
+    // contiguous range of (split, tile) items -- splits slowest, row tiles
+    // fastest -- so workgroups sharing weight columns and a K range share
+    // that XCD's L2.
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int total = tiles * a.splits;
     const int wg = blockIdx.x;
     const int qx = total / 8, rx = total % 8;
     const int xcd = wg % 8, idx = wg / 8;
     const int vid = xcd * qx + (xcd < rx ? xcd : rx) + idx;
-    const int tm = vid % a.tiles_m, tn = vid / a.tiles_m;
+    const int split = vid / tiles, tile = vid % tiles;
+    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int mt0 = tm * (kBM / 32), nt0 = tn * (kBN / 32);
+    // this workgroup's K blocks: [kb0, kb0 + KC)
+    const int kb0 = (int)((int64_t)split * a.KB / a.splits);
+    const int KC = (int)((int64_t)(split + 1) * a.KB / a.splits) - kb0;
 
     v16i acc[BJ][4];
 #pragma unroll
@@ -593,7 +697,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
     const int r32 = lane & 31, h = lane >> 5;
-    const int KB = a.KB;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     Frag f;
     f.sa = (wm * 4) * kUnitBytes + r32 * 64;
@@ -602,8 +705,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     f.h = h;
 
     // prologue: the first kStages stages in flight; wait for stage 0
-    const int first = KB < kStages ? KB : kStages;
-    for (int s = 0; s < first; ++s) issue_stage<NW>(a, lds0 + s * kStage, mt0, nt0, s, wave, lane);
+    const int first = KC < kStages ? KC : kStages;
+    for (int s = 0; s < first; ++s) issue_stage<NW>(a, lds0 + s * kStage, mt0, nt0, kb0 + s, wave, lane);
     wait_copies_and_barrier<COPIES>(first - 1);
     uint4 aq[2][4], bq[2][BJ];
     Wide<BJ> w[2];
@@ -623,10 +726,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     // (nothing hoisted above the barrier, no read sunk below its phase).
     constexpr int NM = 4 * BJ;            // MFMAs per k-step
     constexpr int NR = 4 + BJ;            // LDS reads per pair
-    for (int kb = 0; kb < KB; ++kb) {
-        const int slot = kb % kStages;
+    for (int kr = 0; kr < KC; ++kr) {
+        const int slot = kr % kStages;
         const uint8_t* cur = smem + slot * kStage;
-        const bool more = kb + 1 < KB;
+        const bool more = kr + 1 < KC;
         load_pair<BJ>(f, cur, 1, aq[1], bq[1]);
         mfmas<BJ>(w[0], acc);
         widen<BJ>(aq[0], bq[0], 1, w[1]);
@@ -637,11 +740,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
         interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
         // stage kb + 1 must have landed; stages kb + 2 .. kb + kStages - 1 may be in flight
-        int in_flight = KB - kb - 2;
+        int in_flight = KC - kr - 2;
         in_flight = in_flight < 0 ? 0 : (in_flight > kStages - 2 ? kStages - 2 : in_flight);
         wait_copies_and_barrier<COPIES>(in_flight);
-        if (kb + kStages < KB) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb + kStages, wave, lane);
-        if (more) load_pair<BJ>(f, smem + ((kb + 1) % kStages) * kStage, 0, aq[0], bq[0]);
+        if (kr + kStages < KC) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb0 + kr + kStages, wave, lane);
+        if (more) load_pair<BJ>(f, smem + ((kr + 1) % kStages) * kStage, 0, aq[0], bq[0]);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<BJ>(w[0], acc);
         widen<BJ>(aq[1], bq[1], 1, w[1]);
@@ -652,6 +755,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
         interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
     }
+
+    if (a.splits > 1 && !split_k_exchange<BJ, NW>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
 
     const int64_t m_base = (int64_t)tm * kBM + wm * 128;
     const int64_t n_base = (int64_t)tn * kBN + wn * WN;
@@ -896,10 +1001,11 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 
 // int8 codes [M][K] -> operand image (zero padding); one thread per 8 codes.
 __global__ void act_relayout_kernel(const int8_t* codes, int64_t M, int64_t K, int64_t M_pad, int64_t K_pad,
-                                    uint8_t* image)
+                                    uint8_t* image, uint32_t* zero, int zero_count)
 {
     const int64_t words_per_row = K_pad / 8;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < zero_count) zero[t] = 0;  // split-K counters of the GEMM that consumes this workspace
     if (t >= M_pad * words_per_row) return;
     const int64_t m = t / words_per_row, k = (t % words_per_row) * 8;
     uint32_t out = 0;
@@ -1035,20 +1141,23 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     }
     a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
     a.tiles_n = (a.NT + kBN / 32 - 1) / (kBN / 32);
+    if (a.splits < 1) a.splits = 1;
     constexpr int NW = CONVROT_GEMM_WAVES;
-    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(NW * 64);
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits)), block(NW * 64);
     if (out_mode == GEMM_OUT_I32)
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, NW>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, NW>), grid, block, 0, s, a);
 }
 
-void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, hipStream_t s)
+void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
+                         hipStream_t s)
 {
     const int64_t M_pad = round_up(M, kTileRows), K_pad = round_up(K, kTileK);
-    const int64_t n = M_pad * (K_pad / 8);
+    int64_t n = M_pad * (K_pad / 8);
+    if (n < zero_count) n = zero_count;
     hipLaunchKernelGGL(act_relayout_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, M, K, M_pad,
-                       K_pad, image);
+                       K_pad, image, zero, zero_count);
 }
 
 void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s)

@@ -70,4 +70,34 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
            (size_t)((ks % 2) * 8 + d * 4);
 }
 
+// ---- GEMM work split ------------------------------------------------------
+// The GEMM covers the output with 256 x 256 tiles.  When there are too few
+// tiles to fill the chip, each tile's K range is split over S workgroups
+// (the integer partial sums are exact in any order): S is the largest value
+// <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks per split
+// (enough main-loop work to pay for the exchange of partial tiles).
+// M <= 32 goes to the weight-streaming kernel and is never split.
+constexpr int kGemmTile = 256;
+constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
+constexpr int kSplitCounters = 256;    // counter slots (tiles of a split launch <= 128)
+
+CONVROT_HD inline int gemm_splits(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 32 || M <= 0 || N <= 0) return 1;
+    const int64_t tiles = ((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+    const int64_t KB = (K + kTileK - 1) / kTileK;
+    int S = 1;
+    while (S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
+    return S;
+}
+
+// Bytes of split-K partial tiles: (S - 1) int32 tiles of 256 x 256 per tile.
+CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int S = gemm_splits(M, N, K);
+    if (S <= 1) return 0;
+    const int64_t tiles = ((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+    return (size_t)tiles * (size_t)(S - 1) * (size_t)kGemmTile * kGemmTile * 4;
+}
+
 }  // namespace convrot
