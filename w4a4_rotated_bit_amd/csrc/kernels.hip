@@ -849,7 +849,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
                 if (m >= a.M || n >= a.N) continue;
                 uint16_t* dst = (uint16_t*)a.out + m * a.N + n;
                 if (vec8 && n + 8 <= a.N) {
-                    *(uint4*)dst = w;
+                    // streaming store: Y is not read back by this kernel, and
+                    // keeping it out of the caches shortens the final drain
+                    __builtin_nontemporal_store(v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w}, (v4i*)dst);
                 } else {
                     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
                     for (int u = 0; u < 8 && n + u < a.N; ++u) dst[u] = (uint16_t)(ww[u >> 1] >> (16 * (u & 1)));
