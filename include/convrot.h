@@ -65,17 +65,20 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
 /* Bytes of workspace convrot_linear needs for an M x K input and N outputs.
  * Layout, each part starting at a 256-byte boundary:
- *   1. the activation-code image: round_up(M, 32) * round_up(K, 128) / 2
- *      bytes, INT4 codes in the same layout as the weight image;
- *   2. the activation scales sx: round_up(M, 32) floats;
- *   3. 512 uint32 counters of the split-K GEMM (cleared by
- *      convrot_prepare_activations, left cleared by every GEMM);
+ *   1. offset 0: 512 uint32 counters of the split-K GEMM (cleared by
+ *      convrot_prepare_activations, left cleared by every GEMM; at the same
+ *      offset for every shape);
+ *   2. offset CONVROT_WORKSPACE_IMAGE_OFFSET: the activation-code image,
+ *      round_up(M, 32) * round_up(K, 128) / 2 bytes, INT4 codes in the same
+ *      layout as the weight image;
+ *   3. the activation scales sx: round_up(M, 32) floats;
  *   4. split-K partial tiles: when M > 32 and the 256 x 256 output tiles are
  *      too few to occupy the GPU, each tile's K range is shared by S
  *      workgroups and S - 1 int32 partial tiles of 256 KB per output tile
  *      live here (0 bytes otherwise).
  * Parts 1-3 depend on M and K only; convrot_prepare_activations needs only
  * them.  Returns CONVROT_OK or CONVROT_EINVAL. */
+#define CONVROT_WORKSPACE_IMAGE_OFFSET 2048
 int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes_host);
 
 /* ---- argument checks (host only, no HIP call) ------------------------- */
@@ -180,7 +183,8 @@ int convrot_host_kn_to_nk(const uint8_t* kn_host, int64_t N, int64_t K, uint8_t*
  * image_to_nk ignores the padding. */
 int convrot_host_nk_to_image(const uint8_t* nk_host, int64_t N, int64_t K, uint8_t* image_host);
 int convrot_host_image_to_nk(const uint8_t* image_host, int64_t N, int64_t K, uint8_t* nk_host);
-/* Activation-code image (workspace head) -> int8 codes [M][K]. */
+/* Activation-code image (workspace + CONVROT_WORKSPACE_IMAGE_OFFSET) -> int8
+ * codes [M][K]. */
 int convrot_host_act_image_to_codes(const uint8_t* image_host, int64_t M, int64_t K, int8_t* codes_host);
 
 #ifdef __cplusplus

@@ -33,6 +33,11 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(B._SIGNATURES), set(names) ^ set(B._SIGNATURES)
 
 
+def test_workspace_image_offset_matches_header():
+    m = re.search(r"#define\s+CONVROT_WORKSPACE_IMAGE_OFFSET\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == B.WORKSPACE_IMAGE_OFFSET
+
+
 def test_version_and_status_strings():
     assert B.convrot_version().startswith("convrot-gfx950")
     for code in (0, 1, 2, 3, 4):

@@ -110,7 +110,7 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
 
 GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
                (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072),
-               (256, 512, 8192), (100, 300, 6144)]
+               (256, 512, 8192), (100, 300, 6144), (20, 9000, 1024), (7, 17000, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -176,7 +176,7 @@ def _linear_parity(gpu, x, w, bias, g):
     gy = _host_bits(Y)
     # codes of X (from the workspace) and of W (from the image)
     M = x.shape[0]
-    qx = gpu.convrot_host_act_image_to_codes(ws.cpu().numpy(), M, K)
+    qx = gpu.workspace_act_codes(ws, M, K)
     orx = oracle.rotate_rows(x, g)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
     qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
@@ -266,7 +266,7 @@ def test_linear_full_size_sampled(gpu, name):
     # scales and codes
     assert np.array_equal(sw.cpu().numpy()[cols], osw)
     wsh = ws.cpu().numpy()
-    gq_x = gpu.convrot_host_act_image_to_codes(wsh, M, K)[rows]
+    gq_x = gpu.workspace_act_codes(wsh, M, K)[rows]
     n_x = compare_codes(gq_x, oq_x, orx, osx, "activation codes")
     qw_all = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     assert qw_all.min() >= -7 and qw_all.max() <= 7

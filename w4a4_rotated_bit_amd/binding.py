@@ -302,6 +302,17 @@ def convrot_host_image_to_nk(image, N: int, K: int) -> np.ndarray:
     return out
 
 
+# Offset of the activation-code image inside a workspace
+# (CONVROT_WORKSPACE_IMAGE_OFFSET in include/convrot.h).
+WORKSPACE_IMAGE_OFFSET = 2048
+
+
+def workspace_act_codes(workspace, M: int, K: int) -> np.ndarray:
+    """Activation codes int8 [M, K] decoded from a workspace (tensor or array)."""
+    ws = workspace.cpu().numpy() if hasattr(workspace, "cpu") else np.asarray(workspace)
+    return convrot_host_act_image_to_codes(ws[WORKSPACE_IMAGE_OFFSET:], M, K)
+
+
 def convrot_host_act_image_to_codes(image, M: int, K: int) -> np.ndarray:
     p = _np(image, np.uint8)
     out = np.empty((M, K), np.int8)

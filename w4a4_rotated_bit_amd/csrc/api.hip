@@ -57,10 +57,10 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.rows_pad = round_up(M, kTileRows);
     a.K = K;
     a.K_pad = round_up(K, kTileK);
-    a.out = (uint8_t*)ws;
+    a.out = (uint8_t*)ws + workspace_image_offset();
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
     a.rotated = nullptr;
-    a.zero = (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K));
+    a.zero = (uint32_t*)ws;
     a.zero_count = 2 * kSplitCounters;
     launch_prep(g, OUT_IMAGE, a, s);
     return launched();
@@ -70,7 +70,7 @@ int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void*
                  const void* bias, int64_t N, void* Y, hipStream_t s)
 {
     GemmArgs a{};
-    a.act = (const uint8_t*)ws;
+    a.act = (const uint8_t*)ws + workspace_image_offset();
     a.wgt = (const uint8_t*)image;
     a.sx = (const float*)((const uint8_t*)ws + workspace_sx_offset(M, K));
     a.sw = sw;
@@ -82,7 +82,7 @@ int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void*
     a.NT = (int)(round_up(N, kTileRows) / kTileRows);
     a.KB = (int)(round_up(K, kTileK) / kTileK);
     a.splits = gemm_splits(M, N, K);
-    a.counters = (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K));
+    a.counters = (uint32_t*)ws;
     a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K));
     launch_gemm(out_mode, a, s);
     return launched();
@@ -202,7 +202,7 @@ int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, 
     if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    launch_act_relayout(qx, M, K, (uint8_t*)ws, (uint32_t*)((uint8_t*)ws + workspace_counter_offset(M, K)),
+    launch_act_relayout(qx, M, K, (uint8_t*)ws + workspace_image_offset(), (uint32_t*)ws,
                         2 * kSplitCounters, s);
     if ((rc = launched())) return rc;
     return enqueue_gemm(GEMM_OUT_I32, ws, M, K, image, nullptr, nullptr, N, acc, s);

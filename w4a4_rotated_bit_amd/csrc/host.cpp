@@ -21,16 +21,20 @@ int check_shape(int64_t rows, int64_t K, int g)
     return CONVROT_OK;
 }
 
-size_t workspace_sx_offset(int64_t M, int64_t K) { return (size_t)round_up((int64_t)image_bytes(M, K), 256); }
+// Workspace layout (each part 256-byte aligned): the split-K counters at
+// offset 0 -- the same place for every shape, so a workspace reused across
+// shapes keeps them cleared -- then the activation image, sx, and the split-K
+// partial tiles.
+size_t workspace_image_offset() { return CONVROT_WORKSPACE_IMAGE_OFFSET; }
 
-size_t workspace_counter_offset(int64_t M, int64_t K)
+size_t workspace_sx_offset(int64_t M, int64_t K)
 {
-    return (size_t)round_up((int64_t)(workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows)), 256);
+    return (size_t)round_up((int64_t)(workspace_image_offset() + image_bytes(M, K)), 256);
 }
 
 size_t workspace_partial_offset(int64_t M, int64_t K)
 {
-    return workspace_counter_offset(M, K) + 2 * kSplitCounters * sizeof(uint32_t);
+    return (size_t)round_up((int64_t)(workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows)), 256);
 }
 
 size_t workspace_bytes(int64_t M, int64_t K, int64_t N)
