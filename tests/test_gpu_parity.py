@@ -194,7 +194,10 @@ def test_linear_small_workloads_full(gpu, name):
 
 
 @pytest.mark.parametrize("M,N,K,g", [(1, 96, 256, 256), (37, 70, 512, 256), (300, 520, 1280, 256),
-                                     (33, 64, 192, 64), (257, 300, 2048, 64), (2, 2, 64, 64)])
+                                     (33, 64, 192, 64), (257, 300, 2048, 64), (2, 2, 64, 64),
+                                     # M <= 4: the single-kernel path (1..3 strips per workgroup, 1..4 waves per row)
+                                     (1, 100, 1024, 256), (3, 5000, 4096, 256), (4, 33, 512, 64),
+                                     (2, 17000, 2048, 64), (4, 48, 1280, 256), (1, 12288, 3072, 256)])
 def test_linear_ragged_shapes(gpu, M, N, K, g):
     x = synth.random_bf16((M, K), seed=M + N, outliers=3)
     w = synth.random_bf16((N, K), seed=N + K, std=0.02)

@@ -66,8 +66,8 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     return launched();
 }
 
-int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void* image, const float* sw,
-                 const void* bias, int64_t N, void* Y, hipStream_t s)
+GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
+                   int64_t N, void* Y)
 {
     GemmArgs a{};
     a.act = (const uint8_t*)ws + workspace_image_offset();
@@ -84,7 +84,13 @@ int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void*
     a.splits = gemm_splits(M, N, K);
     a.counters = (uint32_t*)ws;
     a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K));
-    launch_gemm(out_mode, a, s);
+    return a;
+}
+
+int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void* image, const float* sw,
+                 const void* bias, int64_t N, void* Y, hipStream_t s)
+{
+    launch_gemm(out_mode, gemm_args(ws, M, K, image, sw, bias, N, Y), s);
     return launched();
 }
 
@@ -166,6 +172,19 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
     if (rc || M == 0 || N == 0) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
+    if (small_m_fits(M, K, g)) {
+        // one kernel: each workgroup quantizes the few activation rows itself
+        GemmArgs ga = gemm_args(ws, M, K, image, sw, bias, N, Y);
+        PrepArgs pa{};
+        pa.X = (const uint16_t*)X;
+        pa.rows = M;
+        pa.K = K;
+        pa.K_pad = round_up(K, kTileK);
+        pa.out = (uint8_t*)ws + workspace_image_offset();
+        pa.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
+        launch_small_m(g, ga, pa, s);
+        return launched();
+    }
     if ((rc = enqueue_prepare_activations(X, M, K, g, ws, s))) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, ws, M, K, image, sw, bias, N, Y, s);
 }

@@ -5,7 +5,7 @@
 
 namespace convrot {
 
-enum PrepOut { OUT_IMAGE = 0, OUT_ROWMAJOR = 2, OUT_NK = 3 };
+enum PrepOut { OUT_IMAGE = 0, OUT_ROWMAJOR = 2, OUT_NK = 3, OUT_LDS = 4 };
 enum GemmOut { GEMM_OUT_BF16 = 0, GEMM_OUT_I32 = 1 };
 
 struct PrepArgs {
@@ -38,6 +38,10 @@ struct GemmArgs {
 
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
+// Whole linear in one launch for M <= 4 when 64 <= K / P <= 256 (P = 16 for
+// g = 256, 8 for g = 64); see kernels.hip.
+bool small_m_fits(int64_t M, int64_t K, int g);
+void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s);
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
                          hipStream_t s);
 void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s);

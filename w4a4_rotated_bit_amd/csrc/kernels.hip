@@ -17,6 +17,7 @@
 // QuaRot Stage 1c", section 1 (R = I_G (x) H, X.R = [X_1 H, ..., X_G H]).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "kernels.h"
@@ -198,9 +199,14 @@ __device__ inline void zero_unless(bool has_data, uint4 (&w)[P / 8])
 
 // One row of the prep kernel: rotation, absmax, quantization and the write
 // of the codes in the layout of MODE.  w holds the lane's P bf16 values.
-template <int G, int MODE>
+// A team of more than 64 lanes is waves team_w0 .. team_w0 + team_nw - 1 of
+// the workgroup.  OUT_LDS writes the image rows of a small row block into
+// shared memory: row r of 128-K unit kb at ((kb * LDS_ROWS + r) * 64) with
+// the image's in-row layout.
+template <int G, int MODE, int LDS_ROWS = 0>
 __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape<G>::P / 8], int64_t row, int t,
-                                         int64_t k0, int lane, int wave, double* ld, uint32_t (*red)[16], int parity)
+                                         int64_t k0, int lane, int wave, double* ld, uint32_t (*red)[16], int parity,
+                                         int team_w0, int team_nw)
 {
     using S = PrepShape<G>;
     constexpr int P = S::P;
@@ -292,21 +298,28 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
         // passed the next row's barrier (and so has read it)
         if (lane == 0) red[parity][wave] = amax_bits;
         __syncthreads();
-        amax_bits = red[parity][0];
-        for (int wv = 1; wv < (int)(blockDim.x >> 6); ++wv) amax_bits = max(amax_bits, red[parity][wv]);
+        amax_bits = red[parity][team_w0];
+        for (int wv = 1; wv < team_nw; ++wv) amax_bits = max(amax_bits, red[parity][team_w0 + wv]);
     }
     const float amax = __uint_as_float(amax_bits);
     const bool zero_row = !(amax > 0.0f);
     const float s = zero_row ? 0.0f : amax / 7.0f;  // IEEE binary32 division
 
     if (row_valid && t == 0) a.scales[row] = s;
-    const bool write = (MODE == OUT_IMAGE) ? (k0 < a.K_pad && row < a.rows_pad) : has_data;
+    const bool write = (MODE == OUT_IMAGE || MODE == OUT_LDS) ? (k0 < a.K_pad && row < a.rows_pad) : has_data;
     if (write) {
         uint32_t f[P];
         quantize_bits<P>(r, s, zero_row, f);
         if constexpr (MODE == OUT_IMAGE) {
             // P/8 words for k0, k0 + 8 (adjacent dwords of one 8-byte group when P = 16)
             uint8_t* dst = a.out + image_word_offset(row, k0, a.K_pad);
+            if constexpr (P == 16)
+                *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
+            else
+                *(uint32_t*)dst = image_word(f);
+        } else if constexpr (MODE == OUT_LDS) {
+            const size_t unit_off = image_word_offset(row, k0, a.K_pad) % kUnitBytes;  // in-unit offset of row, k0
+            uint8_t* dst = a.out + ((k0 / kTileK) * LDS_ROWS + row) * 64 + (unit_off % 64);
             if constexpr (P == 16)
                 *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
             else
@@ -380,12 +393,12 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
     for (int64_t it = 0; it < n_it; it += 2) {
         int64_t nx = row + row_step;
         load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wb);
-        prep_row<G, MODE>(a, wa, row, t, k0, lane, wave, ld, red, 0);
+        prep_row<G, MODE>(a, wa, row, t, k0, lane, wave, ld, red, 0, 0, blockDim.x >> 6);
         row = nx;
         if (it + 1 >= n_it) break;
         nx = row + row_step;
         load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wa);
-        prep_row<G, MODE>(a, wb, row, t, k0, lane, wave, ld, red, 1);
+        prep_row<G, MODE>(a, wb, row, t, k0, lane, wave, ld, red, 1, 0, blockDim.x >> 6);
         row = nx;
     }
 }
@@ -998,6 +1011,152 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// small_m_kernel: the whole linear in one launch for M <= kSmallRows, when a
+// row's prep team is whole waves (64 <= K / P <= 256).
+//
+// A workgroup owns SW 16-column strips, four waves per strip splitting K as
+// in skinny_kernel.  It first requests its whole weight range (every wave's
+// loads in flight), then -- while the weights stream in -- computes the
+// activation codes of all M rows itself, with the prep kernel's rotation and
+// quantization, into its own shared memory: a team of K / (64 P) waves per
+// row, several rows at once.  Every workgroup repeats this small prep (M rows
+// of at most 4096 values: a few microseconds of vector work over the whole
+// GPU, hidden under the memory-bound weight stream), which needs no exchange
+// between workgroups at all.  Then the MFMAs read the codes from shared
+// memory, and each strip's four partial tiles are reduced and stored as in
+// skinny_kernel.  Workgroup 0 also writes the codes and scales to the
+// workspace, as the two-kernel path leaves them there.
+// ---------------------------------------------------------------------------
+constexpr int kSmallRows = 4;      // M limit of the single-launch path
+constexpr int kSmallUnits = 8;     // 128-K units per wave: K <= 4096 over four waves
+
+template <int G, int SW>
+__global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArgs a, PrepArgs p)
+{
+    using PS = PrepShape<G>;
+    constexpr int P = PS::P;
+    constexpr int NWAVES = SW * kSkinnyWaves;
+    __shared__ __attribute__((aligned(16))) uint8_t plds[NWAVES * PS::kWaveLdsBytes];
+    __shared__ uint32_t pred[2][16];
+    __shared__ __attribute__((aligned(16))) uint8_t act[kSmallUnits * kSkinnyWaves * kSmallRows * 64];
+    __shared__ float sxl[kSmallRows];
+    __shared__ __attribute__((aligned(16))) int32_t red[SW][kSkinnyWaves - 1][4][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int sl = wave / kSkinnyWaves, kq = wave % kSkinnyWaves;  // strip within the workgroup, K quarter
+    const int r16 = lane & 15, q = lane >> 4;
+    const int strip = blockIdx.x * SW + sl;
+    const int nstrips = (int)((a.N + 15) / 16);
+    const int strip_c = min(strip, nstrips - 1);  // past the end: re-read the last strip, never stored
+    const int nt = strip_c >> 1, half = strip_c & 1;
+    const int KB = a.KB;
+    const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;  // <= kSmallUnits
+    const int kb0 = kq * per;
+    const int kn = max(0, min(KB, kb0 + per) - kb0);          // units of this wave
+    const int wrow = 16 * half + r16;
+    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + wrow * 64 + ((q ^ row_swizzle(wrow)) * 16);
+
+    // prep teams: K / (64 P) waves per activation row, `teams` rows at a time
+    const int team_nw = (int)(p.K_pad / P + 63) / 64;  // waves per row
+    const int teams = NWAVES / team_nw;
+    const int team = wave / team_nw;
+    const bool live = team < teams;  // waves past the last whole team only take part in the barriers
+    const int t = tid - team * team_nw * 64;           // lane within the team
+    const int64_t k0 = (int64_t)t * P;
+
+    // 1. the activation values of the first pass, then the wave's whole weight
+    //    range, all in flight (weight units past the wave's range re-read its
+    //    last unit and are not used, so every path issues the same number of
+    //    loads -- and the wait for the activation values, issued first, does
+    //    not wait for the weights)
+    uint4 xw[P / 8];
+    load_run<P>(p.X, live ? team : 0, p.K, k0, live && team < p.rows && k0 < p.K, xw);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads
+    uint4 wq[kSmallUnits];
+#pragma unroll
+    for (int u = 0; u < kSmallUnits; ++u) {
+        const int kb = min(kb0 + min(u, max(kn - 1, 0)), KB - 1);
+        wq[u] = load_stream16(wbase + (size_t)kb * kUnitBytes);
+    }
+
+    // 2. activation codes of the M rows into shared memory (the first pass is
+    //    outside the loop: a load inside the loop body would make the wait for
+    //    the first pass's values also wait for the weights)
+    {
+        double* ld = (double*)(plds + wave * PS::kWaveLdsBytes);
+        PrepArgs pl = p;
+        pl.out = act;     // codes and scales go to this workgroup's shared memory
+        pl.scales = sxl;
+        if (!live) pl.rows = pl.rows_pad = 0;  // nothing read or written
+        prep_row<G, OUT_LDS, kSmallRows>(pl, xw, live ? team : 0, t, k0, lane, wave, ld, pred, 0, team * team_nw,
+                                          team_nw);
+        const int passes = (kSmallRows + teams - 1) / teams;  // covers rows 0 .. kSmallRows - 1
+        for (int pass = 1; pass < passes; ++pass) {
+            const int64_t row = (int64_t)pass * teams + (live ? team : 0);
+            load_run<P>(p.X, row, p.K, k0, live && row < p.rows && k0 < p.K, xw);
+            prep_row<G, OUT_LDS, kSmallRows>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
+                                              team_nw);
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        // the workspace also receives the codes and scales (rows 0 .. M-1 of the
+        // image's first row tile; same in-row layout)
+        const int words = KB * (int)a.M * 4;  // 16-byte words
+        for (int i = tid; i < words; i += NWAVES * 64) {
+            const int kb = i / ((int)a.M * 4), r = (i / 4) % (int)a.M, c = i % 4;
+            *(uint4*)(p.out + (size_t)kb * kUnitBytes + r * 64 + c * 16) =
+                *(const uint4*)(act + (kb * kSmallRows + r) * 64 + c * 16);
+        }
+        if (tid < a.M) p.scales[tid] = sxl[tid];
+    }
+
+    // 3. products: weights from registers, activation codes from shared memory
+    const bool act_row = r16 < a.M;
+    v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kSmallUnits; ++u) {
+        if (u >= kn) break;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (act_row) x = *(const uint4*)(act + ((kb0 + u) * kSmallRows + r16) * 64 + ((q ^ row_swizzle(r16)) * 16));
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo_hi(wq[u].x, wq[u].y), widen_lo_hi(x.x, x.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo_hi(wq[u].z, wq[u].w), widen_lo_hi(x.z, x.w), acc, 0, 0, 0);
+    }
+
+    // 4. reduce each strip's partial tiles, store
+    if (kq > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[sl][kq - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (kq != 0) return;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += red[sl][w][j][lane];
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    const int64_t m = r16;
+    if (n0 >= a.N || m >= a.M) return;
+    const float sxm = sxl[m];
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
+        const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
+        y[j] = __builtin_fmaf((float)(acc[j] >> 8) * sxm, a.sw[n], bn);  // both operands entered x 16
+    }
+    const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
+    uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
+    if ((a.N % 4) == 0) {
+        *(uint2*)dst = make_uint2(p01, p23);
+    } else {
+        const uint16_t yb[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+        for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = yb[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // layout kernels
 // ---------------------------------------------------------------------------
 
@@ -1150,6 +1309,37 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, NW>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, NW>), grid, block, 0, s, a);
+}
+
+bool small_m_fits(int64_t M, int64_t K, int g)
+{
+    const int64_t lanes = round_up(K, kTileK) / (g == 256 ? 16 : 8);
+    return M >= 1 && M <= kSmallRows && lanes >= 64 && lanes <= 256;
+}
+
+template <int G>
+static void launch_small_m_g(int sw, const GemmArgs& a, const PrepArgs& p, dim3 grid, hipStream_t s)
+{
+    switch (sw) {
+        case 1: hipLaunchKernelGGL((small_m_kernel<G, 1>), grid, dim3(1 * kSkinnyWaves * 64), 0, s, a, p); break;
+        case 2: hipLaunchKernelGGL((small_m_kernel<G, 2>), grid, dim3(2 * kSkinnyWaves * 64), 0, s, a, p); break;
+        default: hipLaunchKernelGGL((small_m_kernel<G, 3>), grid, dim3(3 * kSkinnyWaves * 64), 0, s, a, p); break;
+    }
+}
+
+void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s)
+{
+    // strips per workgroup: about one workgroup per compute unit, at most 3
+    const int64_t strips = (a.N + 15) / 16;
+    const int cus = device_cus();
+    const int sw = (int)std::min<int64_t>(3, std::max<int64_t>(1, (strips + cus - 1) / cus));
+    p.team = (int)(p.K_pad / (g == 256 ? 16 : 8));  // lanes per row (whole waves: 64 .. 256)
+    p.rows_pad = kSmallRows;
+    const dim3 grid((unsigned)((strips + sw - 1) / sw));
+    if (g == 256)
+        launch_small_m_g<256>(sw, a, p, grid, s);
+    else
+        launch_small_m_g<64>(sw, a, p, grid, s);
 }
 
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
