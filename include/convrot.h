@@ -135,6 +135,10 @@ int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t
  *   workspace_dev / ws_bytes: at least convrot_workspace_bytes(M, K, N, g);
  *              its contents on entry are ignored and on exit hold the
  *              activation codes and scales of X.
+ * For M <= 4 with 1024 <= K <= 4096 (g = 256) or 512 <= K <= 2048 (g = 64)
+ * the whole linear is one kernel: every workgroup quantizes the few
+ * activation rows itself, in shared memory, while its weight loads are in
+ * flight; otherwise an activation kernel is followed by the GEMM.
  */
 int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_dev, const float* sw_dev,
                    const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
