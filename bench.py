@@ -11,8 +11,9 @@ Infinity Cache cannot serve the weights from a previous step.
 
 Prints one JSON line on stdout.  ``value`` is effective TOPS = 2*M*N*K per
 step time (the K timed steps run as one HIP graph).  ``roofline`` rates the
-GEMM kernel (the dominant one) from its average launch duration -- a pair of
-HIP events on the launch stream around each launch -- against the dense
+dominant kernel -- the GEMM, or the whole linear where it is a single kernel
+(M <= 4) -- from its average launch duration (a pair of HIP events on the
+launch stream around each launch) against the dense
 INT8 matrix-core peak (or, for weight-streaming shapes, the HBM peak);
 ``traffic`` comes from the committed rocprofv3 byte counters when they match
 the current kernel source.  ``cpu_baseline`` is the CPU oracle timed on a
@@ -205,7 +206,11 @@ def main():
     # and over the same buffer rotation as the timed steps.  A bounded spin
     # kernel holds the stream while the host enqueues, so that no event
     # measures the host's launch latency.
+    single = binding.convrot_linear_kernel_count(M, K, N, g) == 1
+
     def launch_avg_ms(n):
+        """Average launch durations: (prep, gemm) for the two-kernel path,
+        (None, whole linear) where the linear is a single kernel."""
         pairs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         hold = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -216,9 +221,13 @@ def main():
             s = sets[i % n_sets]
             e = pairs[i]
             e[0].record()
-            binding.convrot_prepare_activations(s["X"], g, s["ws"])
-            e[1].record()
-            binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
+            if single:
+                e[1].record()
+                binding.convrot_linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
+            else:
+                binding.convrot_prepare_activations(s["X"], g, s["ws"])
+                e[1].record()
+                binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
             e[2].record()
         host_ms = (time.perf_counter() - t0) * 1e3
         torch.cuda.synchronize()
@@ -226,7 +235,7 @@ def main():
         if held_ms < host_ms:
             log(f"warning: stream held {held_ms:.2f} ms < host enqueue {host_ms:.2f} ms; "
                 "launch durations may include host latency")
-        prep = float(np.mean([e[0].elapsed_time(e[1]) for e in pairs]))
+        prep = None if single else float(np.mean([e[0].elapsed_time(e[1]) for e in pairs]))
         gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in pairs]))
         return prep, gemm
 
@@ -241,7 +250,8 @@ def main():
     # shapes; for weight-streaming shapes (arithmetic intensity below the ridge
     # point) the HBM peak, with the kernel's algorithmic bytes: packed weight
     # and activation codes, weight/activation scales, bias and Y.
-    gemm_bytes = N * K // 2 + M * K // 2 + 4 * M + 4 * N + 2 * N + 2 * M * N
+    # (a single-kernel linear moves the whole path's algorithmic bytes)
+    gemm_bytes = wl.bytes_alg if single else N * K // 2 + M * K // 2 + 4 * M + 4 * N + 2 * N + 2 * M * N
     if ops / wl.bytes_alg >= PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         ach = ops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
@@ -274,7 +284,8 @@ def main():
         "gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "int8_frac": round(value / PEAK_INT8_TOPS, 4),
-        "kernel_us": {"prep": round(prep_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)},
+        "kernel_us": ({"linear": round(gemm_ms * 1e3, 2)} if single else
+                      {"prep": round(prep_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)}),
         "weight_prep_ms": round(weight_prep_ms, 4),
         "roofline": roof,
         "cpu_baseline": cpu,

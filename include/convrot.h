@@ -81,6 +81,12 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 #define CONVROT_WORKSPACE_IMAGE_OFFSET 2048
 int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes_host);
 
+/* *count = the number of kernels convrot_linear launches for this shape: 1
+ * (M <= 4 with 1024 <= K <= 4096 for g = 256 or 512 <= K <= 2048 for g = 64),
+ * 2 (activation kernel, then GEMM), or 0 (M or N is 0).  Returns CONVROT_OK
+ * or CONVROT_EINVAL. */
+int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* count_host);
+
 /* ---- argument checks (host only, no HIP call) ------------------------- */
 
 /* The checks convrot_prepare_weight performs.  Returns a status code. */

@@ -69,6 +69,15 @@ def test_workspace_bytes():
     assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 9437184 + 6144 + 2048
 
 
+@pytest.mark.parametrize("M,K,N,g,want", [(1, 3072, 12288, 256, 1), (4, 4096, 64, 256, 1), (5, 3072, 64, 256, 2),
+                                          (1, 768, 64, 256, 2), (1, 4352, 64, 256, 2), (4, 512, 64, 64, 1),
+                                          (4, 2176, 64, 64, 2), (1536, 3072, 9216, 256, 2), (0, 3072, 64, 256, 0),
+                                          (3, 3072, 0, 256, 0)])
+def test_linear_kernel_count(M, K, N, g, want):
+    # one kernel when M <= 4 and a row is 1..4 whole waves of the prep (K / 16 lanes for g = 256, K / 8 for g = 64)
+    assert B.convrot_linear_kernel_count(M, K, N, g) == want
+
+
 @pytest.mark.parametrize("N,K,g", [(16, 100, 64), (16, 512, 128), (16, 0, 64), (-1, 256, 256), (16, 32768, 256)])
 def test_size_queries_reject_bad_shapes(N, K, g):
     with pytest.raises(B.ConvRotError) as e:

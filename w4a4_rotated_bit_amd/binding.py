@@ -46,6 +46,7 @@ _SIGNATURES = {
     "convrot_version": ([], ctypes.c_char_p),
     "convrot_weight_image_bytes": ([_I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_workspace_bytes": ([_I64, _I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
+    "convrot_linear_kernel_count": ([_I64, _I64, _I64, _I, ctypes.POINTER(_I)], _I),
     "convrot_validate_weight": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_validate_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_prepare_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
@@ -129,6 +130,12 @@ def convrot_weight_image_bytes(N: int, K: int, g: int) -> int:
 def convrot_workspace_bytes(M: int, K: int, N: int, g: int) -> int:
     out = _SZ(0)
     _call("convrot_workspace_bytes", M, K, N, g, ctypes.byref(out))
+    return out.value
+
+
+def convrot_linear_kernel_count(M: int, K: int, N: int, g: int) -> int:
+    out = _I(0)
+    _call("convrot_linear_kernel_count", M, K, N, g, ctypes.byref(out))
     return out.value
 
 

@@ -172,7 +172,7 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
     if (rc || M == 0 || N == 0) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    if (small_m_fits(M, K, g)) {
+    if (single_kernel_linear(M, K, g)) {
         // one kernel: each workgroup quantizes the few activation rows itself
         GemmArgs ga = gemm_args(ws, M, K, image, sw, bias, N, Y);
         PrepArgs pa{};

@@ -79,6 +79,16 @@ int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* byte
     return CONVROT_OK;
 }
 
+int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* count)
+{
+    if (!count) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, g);
+    if (rc) return rc;
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    *count = (M == 0 || N == 0) ? 0 : single_kernel_linear(M, K, g) ? 1 : 2;
+    return CONVROT_OK;
+}
+
 int convrot_validate_weight(const void* W, int64_t N, int64_t K, int g, const void* image, const float* sw)
 {
     int rc = check_shape(N, K, g);

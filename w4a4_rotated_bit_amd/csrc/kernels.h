@@ -38,9 +38,8 @@ struct GemmArgs {
 
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
-// Whole linear in one launch for M <= 4 when 64 <= K / P <= 256 (P = 16 for
-// g = 256, 8 for g = 64); see kernels.hip.
-bool small_m_fits(int64_t M, int64_t K, int g);
+// Whole linear in one launch when single_kernel_linear(M, K, g) holds; see
+// kernels.hip.
 void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s);
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
                          hipStream_t s);

@@ -1027,7 +1027,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 // skinny_kernel.  Workgroup 0 also writes the codes and scales to the
 // workspace, as the two-kernel path leaves them there.
 // ---------------------------------------------------------------------------
-constexpr int kSmallRows = 4;      // M limit of the single-launch path
 constexpr int kSmallUnits = 8;     // 128-K units per wave: K <= 4096 over four waves
 
 template <int G, int SW>
@@ -1309,12 +1308,6 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, NW>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, NW>), grid, block, 0, s, a);
-}
-
-bool small_m_fits(int64_t M, int64_t K, int g)
-{
-    const int64_t lanes = round_up(K, kTileK) / (g == 256 ? 16 : 8);
-    return M >= 1 && M <= kSmallRows && lanes >= 64 && lanes <= 256;
 }
 
 template <int G>

@@ -100,4 +100,15 @@ CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
     return (size_t)tiles * (size_t)(S - 1) * (size_t)kGemmTile * kGemmTile * 4;
 }
 
+// ---- single-kernel linear ---------------------------------------------------
+// convrot_linear is one kernel (small_m_kernel) when M <= 4 and an activation
+// row is one to four whole waves of the prep (K / P lanes, P = 16 for g = 256,
+// 8 for g = 64); otherwise an activation kernel followed by the GEMM.
+constexpr int kSmallRows = 4;
+CONVROT_HD inline bool single_kernel_linear(int64_t M, int64_t K, int g)
+{
+    const int64_t lanes = round_up(K, kTileK) / (g == 256 ? 16 : 8);
+    return M >= 1 && M <= kSmallRows && lanes >= 64 && lanes <= 256;
+}
+
 }  // namespace convrot
