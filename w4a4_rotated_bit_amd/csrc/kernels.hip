@@ -466,6 +466,16 @@ __device__ inline void wait_copies_and_barrier(int stages_in_flight)
     }
 }
 
+// The same wait with the number of stages known at compile time, so that the
+// main loop body has no branches.
+template <int COPIES, int IN_FLIGHT>
+__device__ inline void wait_copies_and_barrier()
+{
+    static_assert(COPIES == 4 || COPIES == 8, "copies per wave per stage");
+    static_assert(IN_FLIGHT >= 0 && IN_FLIGHT * COPIES <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(IN_FLIGHT * COPIES) : "memory");
+}
+
 // A stage holds 8 activation and 8 weight units; with NW waves each wave
 // copies 8 / NW of each (two 1 KB runs per unit).  Units past the end of the
 // matrix are re-read from the last valid unit (their products land in rows /
@@ -671,6 +681,11 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
 // so 256 |dot| < 2^31.
 // ---------------------------------------------------------------------------
 
+template <int V>
+struct Const {
+    static constexpr int value = V;
+};
+
 template <int OUT, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
 {
@@ -739,10 +754,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     // (nothing hoisted above the barrier, no read sunk below its phase).
     constexpr int NM = 4 * BJ;            // MFMAs per k-step
     constexpr int NR = 4 + BJ;            // LDS reads per pair
-    for (int kr = 0; kr < KC; ++kr) {
+    // One stage.  ISSUE: copy stage kr + kStages into the buffer this stage
+    // frees; IN_FLIGHT: stages that may still be in flight at the barrier;
+    // MORE: a stage kr + 1 follows.  All three are compile-time constants, so
+    // each call is straight-line code and the phase hints above hold.
+    auto step = [&](int kr, auto issue_c, auto in_flight_c, auto more_c) __attribute__((always_inline)) {
+        constexpr bool ISSUE = decltype(issue_c)::value != 0;
+        constexpr int IN_FLIGHT = decltype(in_flight_c)::value;
+        constexpr bool MORE = decltype(more_c)::value != 0;
         const int slot = kr % kStages;
         const uint8_t* cur = smem + slot * kStage;
-        const bool more = kr + 1 < KC;
         load_pair<BJ>(f, cur, 1, aq[1], bq[1]);
         mfmas<BJ>(w[0], acc);
         widen<BJ>(aq[0], bq[0], 1, w[1]);
@@ -752,22 +773,28 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
         widen<BJ>(aq[1], bq[1], 0, w[0]);
         interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
-        // stage kb + 1 must have landed; stages kb + 2 .. kb + kStages - 1 may be in flight
-        int in_flight = KC - kr - 2;
-        in_flight = in_flight < 0 ? 0 : (in_flight > kStages - 2 ? kStages - 2 : in_flight);
-        wait_copies_and_barrier<COPIES>(in_flight);
-        if (kr + kStages < KC) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb0 + kr + kStages, wave, lane);
-        if (more) load_pair<BJ>(f, smem + ((kr + 1) % kStages) * kStage, 0, aq[0], bq[0]);
+        wait_copies_and_barrier<COPIES, IN_FLIGHT>();
+        if constexpr (ISSUE) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb0 + kr + kStages, wave, lane);
+        if constexpr (MORE) load_pair<BJ>(f, smem + ((kr + 1) % kStages) * kStage, 0, aq[0], bq[0]);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<BJ>(w[0], acc);
         widen<BJ>(aq[1], bq[1], 1, w[1]);
-        interleave_mfma_valu<NM>(more ? NR : 0);
+        interleave_mfma_valu<NM>(MORE ? NR : 0);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<BJ>(w[1], acc);
-        if (more) widen<BJ>(aq[0], bq[0], 0, w[0]);
+        if constexpr (MORE) widen<BJ>(aq[0], bq[0], 0, w[0]);
         interleave_mfma_valu<NM>(0);
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    // Steady state: stage kr + 1 must have landed, stages kr + 2 and kr + 3
+    // may be in flight, stage kr + 4 is issued.  Then the last four stages
+    // (fewer of them when KC < 4), which copy nothing and wait for less.
+    static_assert(kStages == 4, "the tail below is written for four stages");
+    for (int kr = 0; kr < KC - kStages; ++kr) step(kr, Const<1>{}, Const<2>{}, Const<1>{});
+    if (KC >= 4) step(KC - 4, Const<0>{}, Const<2>{}, Const<1>{});
+    if (KC >= 3) step(KC - 3, Const<0>{}, Const<1>{}, Const<1>{});
+    if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
+    step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
     if (a.splits > 1 && !split_k_exchange<BJ, NW>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
 
@@ -1071,6 +1098,20 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
     //    not wait for the weights)
     uint4 xw[P / 8];
     load_run<P>(p.X, live ? team : 0, p.K, k0, live && team < p.rows && k0 < p.K, xw);
+    // the epilogue's column scales and biases (clamped columns: every lane
+    // issues the same loads; only the first wave of each strip uses them)
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    // (no branch around a load here: the wait for a load issued inside a
+    // branch would also wait for every load before it)
+    const uint16_t* bsrc = a.bias ? a.bias : (const uint16_t*)a.sw;  // a valid address either way
+    const uint32_t bmask = a.bias ? 0xFFFFu : 0u;
+    float swv[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = min(n0 + j, a.N - 1);
+        swv[j] = a.sw[n];
+        bv[j] = __uint_as_float(((uint32_t)bsrc[n] & bmask) << 16);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads
     uint4 wq[kSmallUnits];
 #pragma unroll
@@ -1081,21 +1122,28 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
 
     // 2. activation codes of the M rows into shared memory (the first pass is
     //    outside the loop: a load inside the loop body would make the wait for
-    //    the first pass's values also wait for the weights)
+    //    the first pass's values also wait for the weights).  Only rows < M
+    //    are computed -- the products never read the others -- and a team
+    //    without a row still takes the team-absmax barrier of prep_row.
     {
         double* ld = (double*)(plds + wave * PS::kWaveLdsBytes);
         PrepArgs pl = p;
         pl.out = act;     // codes and scales go to this workgroup's shared memory
         pl.scales = sxl;
-        if (!live) pl.rows = pl.rows_pad = 0;  // nothing read or written
-        prep_row<G, OUT_LDS, kSmallRows>(pl, xw, live ? team : 0, t, k0, lane, wave, ld, pred, 0, team * team_nw,
-                                          team_nw);
-        const int passes = (kSmallRows + teams - 1) / teams;  // covers rows 0 .. kSmallRows - 1
+        const int passes = (int)((a.M + teams - 1) / teams);  // rows 0 .. M - 1
+        if (live && team < a.M)  // uniform over the team's waves
+            prep_row<G, OUT_LDS, kSmallRows>(pl, xw, team, t, k0, lane, wave, ld, pred, 0, team * team_nw, team_nw);
+        else if (p.team > 64)
+            __syncthreads();
         for (int pass = 1; pass < passes; ++pass) {
             const int64_t row = (int64_t)pass * teams + (live ? team : 0);
-            load_run<P>(p.X, row, p.K, k0, live && row < p.rows && k0 < p.K, xw);
-            prep_row<G, OUT_LDS, kSmallRows>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
-                                              team_nw);
+            const bool active = live && row < a.M;
+            load_run<P>(p.X, row, p.K, k0, active && k0 < p.K, xw);
+            if (active)
+                prep_row<G, OUT_LDS, kSmallRows>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
+                                                  team_nw);
+            else if (p.team > 64)
+                __syncthreads();
         }
     }
     __syncthreads();
@@ -1113,15 +1161,16 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
 
     // 3. products: weights from registers, activation codes from shared memory
     const bool act_row = r16 < a.M;
-    v4i acc = v4i{0, 0, 0, 0};
+    v4i acc = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};  // two chains of dependent MFMAs
 #pragma unroll
     for (int u = 0; u < kSmallUnits; ++u) {
         if (u >= kn) break;
         uint4 x = make_uint4(0, 0, 0, 0);
         if (act_row) x = *(const uint4*)(act + ((kb0 + u) * kSmallRows + r16) * 64 + ((q ^ row_swizzle(r16)) * 16));
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo_hi(wq[u].x, wq[u].y), widen_lo_hi(x.x, x.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo_hi(wq[u].z, wq[u].w), widen_lo_hi(x.z, x.w), acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo_hi(wq[u].z, wq[u].w), widen_lo_hi(x.z, x.w), acc1, 0, 0, 0);
     }
+    acc += acc1;
 
     // 4. reduce each strip's partial tiles, store
     if (kq > 0) {
@@ -1134,17 +1183,12 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
     for (int w = 0; w < kSkinnyWaves - 1; ++w)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] += red[sl][w][j][lane];
-    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
     const int64_t m = r16;
     if (n0 >= a.N || m >= a.M) return;
     const float sxm = sxl[m];
     float y[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
-        const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-        y[j] = __builtin_fmaf((float)(acc[j] >> 8) * sxm, a.sw[n], bn);  // both operands entered x 16
-    }
+    for (int j = 0; j < 4; ++j) y[j] = __builtin_fmaf((float)(acc[j] >> 8) * sxm, swv[j], bv[j]);  // operands x 16
     const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
     uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
     if ((a.N % 4) == 0) {
