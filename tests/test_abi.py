@@ -61,8 +61,15 @@ def test_workspace_bytes():
     assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 49152 + 256 + 2048
     # 1536 x 3072 -> 9216: 216 tiles of 256 x 256 fill the GPU, no split
     assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 2359296 + 6144 + 2048
-    # 1536 x 12288 -> 3072: 72 tiles, K split 3 ways -> 2 partial tiles of 256 KB each
-    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 9437184 + 6144 + 2048 + 72 * 2 * 262144
+    # 1536 x 12288 -> 3072: 128 tiles of 192 x 192, K split 2 ways -> 1 partial tile of
+    # 192 x 192 int32 per tile (fewer partial bytes than 72 tiles of 256 x 256 split 3 ways)
+    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 9437184 + 6144 + 2048 + 128 * 147456
+    # 1536 x 3072 -> 12288: 288 tiles of 256 x 256 would take two rounds; 256 tiles
+    # of 192 x 384 take one, unsplit
+    assert B.convrot_workspace_bytes(1536, 3072, 12288, 256) == 2359296 + 6144 + 2048
+    # 256 x 4096 -> 256: 2 x 2 tiles of 192 x 192; 32 K blocks split 2 ways (at least
+    # 16 K blocks per split) -> 1 partial tile each
+    assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 524288 + 1024 + 2048 + 4 * 147456
     # 5 x 192 -> N: M <= 32
     assert B.convrot_workspace_bytes(5, 192, 100, 64) == 32 * 256 // 2 + 256 + 2048
     # N = 0: nothing to split

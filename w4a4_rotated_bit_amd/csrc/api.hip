@@ -81,7 +81,11 @@ GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, cons
     a.MT = (int)(round_up(M, kTileRows) / kTileRows);
     a.NT = (int)(round_up(N, kTileRows) / kTileRows);
     a.KB = (int)(round_up(K, kTileK) / kTileK);
-    a.splits = gemm_splits(M, N, K);
+    const GemmPlan plan = gemm_plan(M, N, K);
+    a.shape = plan.shape;
+    a.tiles_m = plan.tiles_m;
+    a.tiles_n = plan.tiles_n;
+    a.splits = plan.splits;
     a.counters = (uint32_t*)ws;
     a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K));
     return a;

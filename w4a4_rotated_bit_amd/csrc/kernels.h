@@ -30,8 +30,9 @@ struct GemmArgs {
     void* out;           // bf16 or int32 [M][N]
     int64_t M, N;
     int MT, NT, KB;      // 32-row tiles, 32-column tiles, 128-K blocks
-    int tiles_m, tiles_n;  // set by launch_gemm
-    int splits;          // K splits per 256 x 256 tile (gemm_splits)
+    int shape;           // block tile shape, tiles and K splits (gemm_plan)
+    int tiles_m, tiles_n;
+    int splits;
     uint32_t* counters;  // 2 * kSplitCounters zeroed words (tickets, then finished writers)
     int32_t* partial;    // (splits - 1) partial tiles per tile
 };

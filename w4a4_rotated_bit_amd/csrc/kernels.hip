@@ -23,10 +23,6 @@
 #include "kernels.h"
 #include "layout.h"
 
-#ifndef CONVROT_GEMM_WAVES
-#define CONVROT_GEMM_WAVES 8
-#endif
-
 namespace convrot {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -352,7 +348,7 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
 }
 
 template <int G, int MODE>
-__global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void prep_kernel(PrepArgs a)
 {
     using S = PrepShape<G>;
     constexpr int P = S::P;
@@ -406,98 +402,138 @@ __global__ __launch_bounds__(1024) void prep_kernel(PrepArgs a)
 // ---------------------------------------------------------------------------
 // gemm_kernel
 //
-// Block tile 256 (M) x 256 (N); K advances 128 at a time through a ring of
-// four LDS stages, each holding 8 activation units and 8 weight units of the
-// operand image (2 KB each) = 32 KB.  The image is stored in exactly the LDS
-// order, so every global -> LDS copy is a straight 1 KB run per wave
-// instruction (global_load_lds_dwordx4, 16 bytes per lane, no registers
-// involved); copies run three stages ahead of the MFMAs.
-// Eight waves, two per SIMD, each own a 128 (M) x 64 (N) output tile: 4 x 2
-// MFMA 32x32x32 tiles computed as W . X^T, so that each lane ends up holding
-// four consecutive output columns of one row.  Both operands are widened from
-// INT4 to INT8 x 16 in registers right after the LDS read; the int32 sums are
-// therefore 256 times the dot products and are divided by 256 (exactly) in
-// the epilogue.  |dot| <= 49 K <= 802816, so 256 |dot| < 2^31.
+// Two block-tile shapes (GemmShape, chosen per problem by gemm_plan):
+//   shape 0: 256 (M) x 256 (N), eight waves (two per SIMD) in a 2 x 4 grid,
+//            each owning 128 x 64 = 4 x 2 MFMA tiles;
+//   shape 1: 192 (M) x 384 (N), eight waves in a 2 x 4 grid, each owning
+//            96 x 96 = 3 x 3 MFMA tiles -- the shape that covers
+//            1536 x 12288 in exactly 256 tiles;
+//   shape 2: 192 (M) x 192 (N), four waves (one per SIMD) in a 2 x 2 grid,
+//            each owning 96 x 96 -- 1536 x 3072 in 128 tiles, two K splits
+//            each, with half the partial-tile bytes of larger tiles.
+// K advances 128 at a time through a ring of four LDS stages, each holding
+// the tile's activation units and then its weight units of the operand image
+// (2 KB each).  The image is stored in exactly the LDS order, so every
+// global -> LDS copy is a straight 1 KB run per wave instruction
+// (global_load_lds_dwordx4, 16 bytes per lane, no registers involved); copies
+// run three stages ahead of the MFMAs.  The MFMA 32x32x32 tiles are computed
+// as W . X^T, so that each lane ends up holding four consecutive output
+// columns of one row.  Both operands are widened from INT4 to INT8 x 16 in
+// registers right after the LDS read; the int32 sums are therefore 256 times
+// the dot products and are divided by 256 (exactly) in the epilogue.
+// |dot| <= 49 K <= 802816, so 256 |dot| < 2^31.
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 256, kBN = 256;
-constexpr int kStageA = 8 * kUnitBytes;      // 16 KB
-constexpr int kStage = 2 * kStageA;          // 32 KB: activation units, then weight units
+template <int SHAPE>
+struct GemmShape;
+template <>
+struct GemmShape<0> {
+    static constexpr int NW = 8, NWM = 2, BI = 4, BJ = 2;
+};
+template <>
+struct GemmShape<1> {
+    static constexpr int NW = 8, NWM = 2, BI = 3, BJ = 3;
+};
+template <>
+struct GemmShape<2> {
+    static constexpr int NW = 4, NWM = 2, BI = 3, BJ = 3;
+};
+template <int SHAPE>
+struct GemmGeom : GemmShape<SHAPE> {
+    using S = GemmShape<SHAPE>;
+    static constexpr int NWN = S::NW / S::NWM;          // waves along N
+    static constexpr int BM = S::NWM * 32 * S::BI;      // block tile rows
+    static constexpr int BN = NWN * 32 * S::BJ;         // block tile columns
+    static constexpr int WN = 32 * S::BJ;               // wave tile columns
+    static constexpr int UA = BM / 32, UB = BN / 32;    // activation / weight units per stage
+    static constexpr int kStageA = UA * kUnitBytes;     // activation part of a stage
+    static constexpr int kStage = (UA + UB) * kUnitBytes;
+    static constexpr int COPIES = (2 * (UA + UB) + S::NW - 1) / S::NW;  // 1 KB copies per wave per stage
+    static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
+};
 constexpr int kStages = 4;
 
-// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
-// M0 + 16 l.  Written as inline asm so that the compiler neither tracks the
-// copy (and waits for it before unrelated LDS reads) nor needs registers for
-// it: nothing is returned, the address VGPRs are consumed at issue, and the
-// LDS side is ordered by the explicit vmcnt waits of wait_copies_and_barrier.
-__device__ inline void lds_copy16(const uint8_t* g, uint32_t lds_addr)
+// Global -> LDS copy of 16 bytes per lane from base + voff (voff per lane):
+// lane l's bytes land at LDS address M0 + 16 l.  Written as inline asm so
+// that the compiler neither tracks the copy (and waits for it before
+// unrelated LDS reads) nor needs registers for it: nothing is returned, the
+// address registers are consumed at issue, and the LDS side is ordered by the
+// explicit vmcnt waits of wait_copies_and_barrier.
+__device__ inline void lds_copy16(const uint8_t* base, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(g), "s"(lds_addr)
+                 : "v"(voff), "s"(base), "s"(lds_addr)
                  : "memory", "m0");
 }
 
-// Wait until at most `stages_in_flight` stages of copies (COPIES each per
-// wave) are outstanding, then synchronise the workgroup.  No fence: the only
-// memory traffic to order is LDS (every read of a released stage has returned
-// into registers) and the copies (ordered by vmcnt).
-template <int COPIES>
-__device__ inline void wait_copies_and_barrier(int stages_in_flight)
-{
-    static_assert(COPIES == 4 || COPIES == 8, "copies per wave per stage");
-    if (stages_in_flight <= 0) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    } else if (stages_in_flight == 1) {
-        if constexpr (COPIES == 4)
-            asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    } else if (stages_in_flight == 2) {
-        if constexpr (COPIES == 4)
-            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    } else {
-        if constexpr (COPIES == 4)
-            asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-    }
-}
-
-// The same wait with the number of stages known at compile time, so that the
-// main loop body has no branches.
+// Wait until at most IN_FLIGHT stages of copies (COPIES each per wave) are
+// outstanding, then synchronise the workgroup.  No fence: the only memory
+// traffic to order is LDS (every read of a released stage has returned into
+// registers) and the copies (ordered by vmcnt).  The count is a compile-time
+// constant, so that the main loop body has no branches.
 template <int COPIES, int IN_FLIGHT>
 __device__ inline void wait_copies_and_barrier()
 {
-    static_assert(COPIES == 4 || COPIES == 8, "copies per wave per stage");
     static_assert(IN_FLIGHT >= 0 && IN_FLIGHT * COPIES <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(IN_FLIGHT * COPIES) : "memory");
 }
 
-// A stage holds 8 activation and 8 weight units; with NW waves each wave
-// copies 8 / NW of each (two 1 KB runs per unit).  Units past the end of the
-// matrix are re-read from the last valid unit (their products land in rows /
-// columns that are never stored), which keeps the number of copies in flight
-// per wave constant.
-template <int NW>
-__device__ inline void issue_stage(const GemmArgs& a, uint32_t stage, int mt0, int nt0, int kb, int wave, int lane)
+// The same with a run-time count of 0 .. kStages - 1 stages (prologue).
+template <int COPIES>
+__device__ inline void wait_copies_and_barrier(int stages_in_flight)
 {
-    constexpr int U = 8 / NW;  // units of each operand per wave
+    if (stages_in_flight <= 0)
+        wait_copies_and_barrier<COPIES, 0>();
+    else if (stages_in_flight == 1)
+        wait_copies_and_barrier<COPIES, 1>();
+    else if (stages_in_flight == 2)
+        wait_copies_and_barrier<COPIES, 2>();
+    else
+        wait_copies_and_barrier<COPIES, 3>();
+}
+
+// A stage is UA activation and UB weight units, two 1 KB runs each: copy c
+// of 2 (UA + UB) is half c % 2 of unit c / 2, activation units first.  Wave w
+// issues copies (w * COPIES + i) mod 2 (UA + UB), i < COPIES; when the copies
+// do not divide evenly, the last wave's surplus copies repeat copies of the
+// first wave (the same bytes to the same place), so that every wave issues
+// the same number and waits for the same count.  The global addresses of a
+// wave's copies differ only by the stage's K block, so their bases are
+// computed once (uniform, in scalar registers).  Units past the end of the
+// matrix are re-read from the last valid unit (their products land in rows /
+// columns that are never stored).
+template <int SHAPE>
+struct StageCopies {
+    const uint8_t* src[GemmGeom<SHAPE>::COPIES];  // unit row tile, half; K block 0
+    uint32_t dst[GemmGeom<SHAPE>::COPIES];        // offset within a stage
+};
+
+template <int SHAPE>
+__device__ inline StageCopies<SHAPE> stage_copies(const GemmArgs& a, int mt0, int nt0, int wave)
+{
+    using G = GemmGeom<SHAPE>;
+    constexpr int TC = 2 * (G::UA + G::UB);
+    StageCopies<SHAPE> sc;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int unit = wave * U + u;
-        const int mt = min(mt0 + unit, a.MT - 1), nt = min(nt0 + unit, a.NT - 1);
-        const uint8_t* sa = a.act + ((size_t)mt * a.KB + kb) * kUnitBytes + lane * 16;
-        const uint8_t* sb = a.wgt + ((size_t)nt * a.KB + kb) * kUnitBytes + lane * 16;
-        const uint32_t da = stage + unit * kUnitBytes;
-        const uint32_t db = stage + kStageA + unit * kUnitBytes;
-        lds_copy16(sa, da);
-        lds_copy16(sa + 1024, da + 1024);
-        lds_copy16(sb, db);
-        lds_copy16(sb + 1024, db + 1024);
+    for (int i = 0; i < G::COPIES; ++i) {
+        const int c = (wave * G::COPIES + i) % TC;
+        const int unit = c >> 1, half = c & 1;
+        const bool is_a = unit < G::UA;
+        const int ua = is_a ? unit : unit - G::UA;
+        const int row_tile = is_a ? min(mt0 + ua, a.MT - 1) : min(nt0 + ua, a.NT - 1);
+        sc.src[i] = (is_a ? a.act : a.wgt) + (size_t)row_tile * a.KB * kUnitBytes + half * 1024;
+        sc.dst[i] = (is_a ? 0 : G::kStageA) + ua * kUnitBytes + half * 1024;
     }
+    return sc;
+}
+
+template <int SHAPE>
+__device__ inline void issue_stage(const StageCopies<SHAPE>& sc, uint32_t stage, int kb, int lane)
+{
+    const uint32_t voff = (uint32_t)kb * kUnitBytes + lane * 16;
+#pragma unroll
+    for (int i = 0; i < GemmGeom<SHAPE>::COPIES; ++i) lds_copy16(sc.src[i], voff, stage + sc.dst[i]);
 }
 
 // INT4 codes of one 8-byte group -> 16 INT8 values x 16 in natural order
@@ -511,82 +547,82 @@ __device__ inline v4i widen_lo_hi(uint32_t w0, uint32_t w1)
     return r;
 }
 
-// Per-lane LDS offsets of a 128 (M) x 32*BJ (N) wave tile: this lane's row of
-// activation unit wm*4 and of weight unit wn*BJ within a stage.
+// Per-lane LDS offsets of a 32*BI (M) x 32*BJ (N) wave tile: this lane's row
+// of activation unit wm*BI and of weight unit wn*BJ within a stage.
 struct Frag {
     int sa, sb, swz, h;
 };
 
-// Quads of one pair of k-steps: 4 activation quads and BJ weight quads, each
+// Quads of one pair of k-steps: BI activation quads and BJ weight quads, each
 // 16 bytes = 2 k-steps x 16 codes of this lane's row.
-template <int BJ>
-__device__ inline void load_pair(const Frag& f, const uint8_t* stage, int pr, uint4 (&aq)[4], uint4 (&bq)[BJ])
+template <int BI, int BJ>
+__device__ inline void load_pair(const Frag& f, const uint8_t* stage, int pr, uint4 (&aq)[BI], uint4 (&bq)[BJ])
 {
     const int off = ((2 * pr + f.h) ^ f.swz) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aq[i] = *(const uint4*)(stage + f.sa + i * kUnitBytes + off);
+    for (int i = 0; i < BI; ++i) aq[i] = *(const uint4*)(stage + f.sa + i * kUnitBytes + off);
 #pragma unroll
     for (int j = 0; j < BJ; ++j) bq[j] = *(const uint4*)(stage + f.sb + j * kUnitBytes + off);
 }
 
-// Widened operands of one k-step: 4 activation and BJ weight fragments of 16
+// Widened operands of one k-step: BI activation and BJ weight fragments of 16
 // INT8 values x 16 each.
-template <int BJ>
+template <int BI, int BJ>
 struct Wide {
-    v4i a[4], b[BJ];
+    v4i a[BI], b[BJ];
 };
 
 // k-step kk (0 or 1) of a pair of quads -> widened fragments
-template <int BJ>
-__device__ inline void widen(const uint4 (&aq)[4], const uint4 (&bq)[BJ], int kk, Wide<BJ>& w)
+template <int BI, int BJ>
+__device__ inline void widen(const uint4 (&aq)[BI], const uint4 (&bq)[BJ], int kk, Wide<BI, BJ>& w)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w.a[i] = kk == 0 ? widen_lo_hi(aq[i].x, aq[i].y) : widen_lo_hi(aq[i].z, aq[i].w);
+    for (int i = 0; i < BI; ++i) w.a[i] = kk == 0 ? widen_lo_hi(aq[i].x, aq[i].y) : widen_lo_hi(aq[i].z, aq[i].w);
 #pragma unroll
     for (int j = 0; j < BJ; ++j) w.b[j] = kk == 0 ? widen_lo_hi(bq[j].x, bq[j].y) : widen_lo_hi(bq[j].z, bq[j].w);
 }
 
 // acc[j][i] += W_j . X_i^T for one k-step
-template <int BJ>
-__device__ inline void mfmas(const Wide<BJ>& w, v16i (&acc)[BJ][4])
+template <int BI, int BJ>
+__device__ inline void mfmas(const Wide<BI, BJ>& w, v16i (&acc)[BJ][BI])
 {
 #pragma unroll
     for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < BI; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w.b[j], w.a[i], acc[j][i], 0, 0, 0);
 }
 
 // Instruction-mix hints for one k-step phase of NM MFMAs (sched_group_barrier
-// masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU): each MFMA is followed by a
-// few of the widening instructions of the next k-step and, where there are
-// any, one LDS read, so the matrix core, the vector ALU and the LDS work side
-// by side instead of in bursts.
-template <int NM>
+// masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU): each MFMA is followed by NV
+// of the widening instructions of the next k-step and, where there are any,
+// one LDS read, so the matrix core, the vector ALU and the LDS work side by
+// side instead of in bursts.
+template <int NM, int NV>
 __device__ inline void interleave_mfma_valu(int lds_reads)
 {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (m < lds_reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 40 / NM + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Split-K exchange.  Every workgroup of a split tile takes a ticket from the
 // tile's counter.  The first S - 1 ticket holders store their int32 partial
-// tile (one 256 KB slot per ticket: 8-byte word u of thread t at
-// (u * threads + t) * 8, so each store instruction covers 512 contiguous bytes)
-// with device-coherent stores, wait until the stores
-// have completed, and count themselves finished.  The last ticket holder waits
-// until S - 1 writers have finished -- each of them already holds a ticket, so
-// it is running and finishes without waiting on anyone -- then pulls each
-// slot into LDS half by half with device-coherent global -> LDS copies (all in
-// flight at once), adds it to its own tile (exact integer sums, any order) and
-// goes on to the epilogue; it also returns both counters to zero for the next
-// launch.  Device-coherent (agent-scope, sc1) accesses go to the level of the
-// memory system that every compute unit sees, so no cache-wide write-back or
+// tile (one slot per ticket: 8-byte word u of thread t at (u * threads + t) *
+// 8, so each store instruction covers 512 contiguous bytes) with
+// device-coherent stores, wait until the stores have completed, and count
+// themselves finished.  The last ticket holder waits until S - 1 writers have
+// finished -- each of them already holds a ticket, so it is running and
+// finishes without waiting on anyone -- then pulls each slot into LDS half by
+// half with device-coherent global -> LDS copies (all in flight at once), adds
+// it to its own tile (exact integer sums, any order) and goes on to the
+// epilogue; it also returns both counters to zero for the next launch.
+// Device-coherent (agent-scope, sc1) accesses go to the level of the memory
+// system that every compute unit sees, so no cache-wide write-back or
 // invalidation is needed.  Returns true for the workgroup that finishes the
 // tile.
 // ---------------------------------------------------------------------------
@@ -600,15 +636,19 @@ __device__ inline void lds_copy16_coherent(const uint8_t* g, uint32_t lds_addr)
                  : "memory", "m0");
 }
 
-template <int BJ, int NW>
+template <int SHAPE>
 __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, int wave, int lane, uint32_t lds0,
-                                        const uint8_t* smem, v16i (&acc)[BJ][4])
+                                        const uint8_t* smem,
+                                        v16i (&acc)[GemmShape<SHAPE>::BJ][GemmShape<SHAPE>::BI])
 {
-    constexpr int kThreads = NW * 64;
-    constexpr int kWords = BJ * 4 * 8;                 // 8-byte words per thread
-    constexpr int kSlotBytes = kThreads * kWords * 8;  // 256 KB
-    constexpr int kHalf = kSlotBytes / 2;              // fits the 128 KB stage ring
-    static_assert(kHalf <= kStages * kStage, "half a partial tile must fit in LDS");
+    using G = GemmGeom<SHAPE>;
+    constexpr int BI = G::BI, BJ = G::BJ;
+    constexpr int kThreads = G::NW * 64;
+    constexpr int kWords = BJ * BI * 8;                // 8-byte words per thread
+    constexpr int kSlotBytes = kThreads * kWords * 8;  // BM x BN int32
+    constexpr int kHalf = kSlotBytes / 2;              // fits the stage ring
+    static_assert(kHalf <= kStages * G::kStage, "half a partial tile must fit in LDS");
+    static_assert(kSlotBytes == G::BM * G::BN * 4, "slot = one int32 tile");
     __shared__ int ticket_sh;
     uint32_t* tickets = a.counters + tile;
     uint32_t* finished = a.counters + kSplitCounters + tile;
@@ -622,10 +662,10 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
 #pragma unroll
         for (int j = 0; j < BJ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < BI; ++i)
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const int u = (j * 4 + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
+                    const int u = (j * BI + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
                     const uint64_t v = (uint64_t)(uint32_t)acc[j][i][2 * q] | ((uint64_t)(uint32_t)acc[j][i][2 * q + 1] << 32);
                     __hip_atomic_store(dst + (size_t)u * kThreads + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -644,7 +684,8 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
         __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    constexpr int kChunksPerWave = kHalf / 1024 / NW;  // 1 KB per copy instruction
+    constexpr int kChunksPerWave = kHalf / 1024 / G::NW;  // 1 KB per copy instruction
+    static_assert(kChunksPerWave * 1024 * G::NW == kHalf, "copies divide evenly over the waves");
     for (int sl = 0; sl < S - 1; ++sl) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -658,7 +699,7 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
 #pragma unroll
             for (int u2 = 0; u2 < kWords / 2; ++u2) {
                 const int u = half * (kWords / 2) + u2;
-                const int j = u / 32, i = (u / 8) % 4, q = u % 8;
+                const int j = u / (BI * 8), i = (u / 8) % BI, q = u % 8;
                 const uint2 w = *(const uint2*)(smem + ((size_t)u2 * kThreads + tid) * 8);
                 acc[j][i][2 * q] += (int32_t)w.x;
                 acc[j][i][2 * q + 1] += (int32_t)w.y;
@@ -669,35 +710,26 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
     return true;
 }
 
-// ---------------------------------------------------------------------------
-// gemm_kernel<OUT, NW>: NW waves (4 or 8) in a 2 x (NW/2) arrangement, each
-// owning a 128 (M) x 32*BJ (N) output tile, BJ = 16 / NW: 4 x BJ MFMA
-// 32x32x32 tiles computed as W . X^T, so that each lane ends up holding four
-// consecutive output columns of one row.  With NW = 8 two waves share a SIMD;
-// with NW = 4 each wave has a SIMD to itself and reads fewer LDS bytes per
-// MFMA.  Both operands are widened from INT4 to INT8 x 16 in registers right
-// after the LDS read; the int32 sums are therefore 256 times the dot products
-// and are divided by 256 (exactly) in the epilogue.  |dot| <= 49 K <= 802816,
-// so 256 |dot| < 2^31.
-// ---------------------------------------------------------------------------
+// 8 when the epilogue staging row r has its 8-byte halves exchanged, else 0
+__device__ inline int half_swap(int r) { return (((r >> 3) ^ (r >> 4)) & 1) * 8; }
 
 template <int V>
 struct Const {
     static constexpr int value = V;
 };
 
-template <int OUT, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
+template <int OUT, int SHAPE>
+__global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(GemmArgs a)
 {
-    constexpr int BJ = 16 / NW;            // weight fragments per wave
-    constexpr int COPIES = 32 / NW;        // copies per wave per stage
-    constexpr int WN = 32 * BJ;            // wave tile width in N
+    using G = GemmGeom<SHAPE>;
+    constexpr int NW = G::NW, BI = G::BI, BJ = G::BJ, WN = G::WN;
+    constexpr int kStage = G::kStage;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps copy addresses scalar
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % G::NWM, wn = wave / G::NWM;
 
     // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous range of (split, tile) items -- splits slowest, row tiles
@@ -711,35 +743,36 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     const int vid = xcd * qx + (xcd < rx ? xcd : rx) + idx;
     const int split = vid / tiles, tile = vid % tiles;
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
-    const int mt0 = tm * (kBM / 32), nt0 = tn * (kBN / 32);
+    const int mt0 = tm * G::UA, nt0 = tn * G::UB;
     // this workgroup's K blocks: [kb0, kb0 + KC)
     const int kb0 = (int)((int64_t)split * a.KB / a.splits);
     const int KC = (int)((int64_t)(split + 1) * a.KB / a.splits) - kb0;
 
-    v16i acc[BJ][4];
+    v16i acc[BJ][BI];
 #pragma unroll
     for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < BI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
     const int r32 = lane & 31, h = lane >> 5;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     Frag f;
-    f.sa = (wm * 4) * kUnitBytes + r32 * 64;
-    f.sb = kStageA + (wn * BJ) * kUnitBytes + r32 * 64;
+    f.sa = (wm * BI) * kUnitBytes + r32 * 64;
+    f.sb = G::kStageA + (wn * BJ) * kUnitBytes + r32 * 64;
     f.swz = row_swizzle(r32);
     f.h = h;
 
     // prologue: the first kStages stages in flight; wait for stage 0
     const int first = KC < kStages ? KC : kStages;
-    for (int s = 0; s < first; ++s) issue_stage<NW>(a, lds0 + s * kStage, mt0, nt0, kb0 + s, wave, lane);
-    wait_copies_and_barrier<COPIES>(first - 1);
-    uint4 aq[2][4], bq[2][BJ];
-    Wide<BJ> w[2];
-    load_pair<BJ>(f, smem, 0, aq[0], bq[0]);
-    widen<BJ>(aq[0], bq[0], 0, w[0]);
+    const StageCopies<SHAPE> sc = stage_copies<SHAPE>(a, mt0, nt0, wave);
+    for (int s = 0; s < first; ++s) issue_stage<SHAPE>(sc, lds0 + s * kStage, kb0 + s, lane);
+    wait_copies_and_barrier<G::COPIES>(first - 1);
+    uint4 aq[2][BI], bq[2][BJ];
+    Wide<BI, BJ> w[2];
+    load_pair<BI, BJ>(f, smem, 0, aq[0], bq[0]);
+    widen<BI, BJ>(aq[0], bq[0], 0, w[0]);
 
     // Per stage kb (buffer kb % kStages):
     //   k-step 0 MFMAs | reads of pair 1 of this stage, widening of k-step 1
@@ -752,8 +785,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     // LDS reads thus come in two even halves per stage and the barrier sits
     // between MFMA phases.  sched_barrier(0) keeps the phases in this order
     // (nothing hoisted above the barrier, no read sunk below its phase).
-    constexpr int NM = 4 * BJ;            // MFMAs per k-step
-    constexpr int NR = 4 + BJ;            // LDS reads per pair
+    constexpr int NM = BI * BJ;                  // MFMAs per k-step
+    constexpr int NR = BI + BJ;                  // LDS reads per pair
+    constexpr int NV = 6 * (BI + BJ) / NM + 1;   // widening instructions per MFMA
     // One stage.  ISSUE: copy stage kr + kStages into the buffer this stage
     // frees; IN_FLIGHT: stages that may still be in flight at the barrier;
     // MORE: a stage kr + 1 follows.  All three are compile-time constants, so
@@ -764,26 +798,26 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
         constexpr bool MORE = decltype(more_c)::value != 0;
         const int slot = kr % kStages;
         const uint8_t* cur = smem + slot * kStage;
-        load_pair<BJ>(f, cur, 1, aq[1], bq[1]);
-        mfmas<BJ>(w[0], acc);
-        widen<BJ>(aq[0], bq[0], 1, w[1]);
-        interleave_mfma_valu<NM>(NR);
+        load_pair<BI, BJ>(f, cur, 1, aq[1], bq[1]);
+        mfmas<BI, BJ>(w[0], acc);
+        widen<BI, BJ>(aq[0], bq[0], 1, w[1]);
+        interleave_mfma_valu<NM, NV>(NR);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<BJ>(w[1], acc);
-        widen<BJ>(aq[1], bq[1], 0, w[0]);
-        interleave_mfma_valu<NM>(0);
+        mfmas<BI, BJ>(w[1], acc);
+        widen<BI, BJ>(aq[1], bq[1], 0, w[0]);
+        interleave_mfma_valu<NM, NV>(0);
         __builtin_amdgcn_sched_barrier(0);
-        wait_copies_and_barrier<COPIES, IN_FLIGHT>();
-        if constexpr (ISSUE) issue_stage<NW>(a, lds0 + slot * kStage, mt0, nt0, kb0 + kr + kStages, wave, lane);
-        if constexpr (MORE) load_pair<BJ>(f, smem + ((kr + 1) % kStages) * kStage, 0, aq[0], bq[0]);
+        wait_copies_and_barrier<G::COPIES, IN_FLIGHT>();
+        if constexpr (ISSUE) issue_stage<SHAPE>(sc, lds0 + slot * kStage, kb0 + kr + kStages, lane);
+        if constexpr (MORE) load_pair<BI, BJ>(f, smem + ((kr + 1) % kStages) * kStage, 0, aq[0], bq[0]);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<BJ>(w[0], acc);
-        widen<BJ>(aq[1], bq[1], 1, w[1]);
-        interleave_mfma_valu<NM>(MORE ? NR : 0);
+        mfmas<BI, BJ>(w[0], acc);
+        widen<BI, BJ>(aq[1], bq[1], 1, w[1]);
+        interleave_mfma_valu<NM, NV>(MORE ? NR : 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas<BJ>(w[1], acc);
-        if constexpr (MORE) widen<BJ>(aq[0], bq[0], 0, w[0]);
-        interleave_mfma_valu<NM>(0);
+        mfmas<BI, BJ>(w[1], acc);
+        if constexpr (MORE) widen<BI, BJ>(aq[0], bq[0], 0, w[0]);
+        interleave_mfma_valu<NM, NV>(0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // Steady state: stage kr + 1 must have landed, stages kr + 2 and kr + 3
@@ -796,10 +830,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if (a.splits > 1 && !split_k_exchange<BJ, NW>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if (a.splits > 1 && !split_k_exchange<SHAPE>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
 
-    const int64_t m_base = (int64_t)tm * kBM + wm * 128;
-    const int64_t n_base = (int64_t)tn * kBN + wn * WN;
+    const int64_t m_base = (int64_t)tm * G::BM + wm * (32 * BI);
+    const int64_t n_base = (int64_t)tn * G::BN + wn * WN;
 
     // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
     // register (row / 8) * 4 + row % 4; here rows are output columns n and
@@ -808,7 +842,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
     if constexpr (OUT == GEMM_OUT_I32) {
         const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < BI; ++i) {
             const int64_t m = m_base + 32 * i + r32;
             if (m >= a.M) continue;
 #pragma unroll
@@ -829,38 +863,45 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
                 }
         }
     } else {
-        // The block's 256 column scales and biases and 256 row scales go
+        // The block's BN column scales and biases and BM row scales go
         // through LDS (free again: every copy has landed and every wave has
         // passed the last stage barrier) -- one cooperative load instead of
         // per-lane scattered loads.  Then the bf16 output goes through a
-        // per-wave LDS tile of 32 rows x WN columns (row pitch 2*WN + 16 bytes:
-        // the 8-byte writes of 16 consecutive lanes hit distinct banks), one
-        // MFMA tile row at a time, and is stored as 16-byte row segments.
+        // per-wave LDS tile of 32 rows x WN columns, one MFMA tile row at a
+        // time, and is stored as 16-byte row segments.  Row pitch 2*WN + 16
+        // bytes (36 banks modulo 64) keeps rows 16-byte aligned; rows r and
+        // r + 16 would still meet on the same banks, so in rows with
+        // half_swap(r) the two 8-byte halves of every 16-byte chunk trade
+        // places: the 8-byte writes of 16 (32-bank LDS) or 32 (64-bank LDS)
+        // consecutive lanes then hit distinct banks.
         float* p_sw = (float*)smem;
-        float* p_b = p_sw + kBN;
-        float* p_sx = p_b + kBN;
+        float* p_b = p_sw + G::BN;
+        float* p_sx = p_b + G::BN;
         constexpr int kPitch = 2 * WN + 16;
         constexpr int kParamBytes = 4096;
-        constexpr int kChunks = WN / 8;       // 16-byte chunks per tile row
+        constexpr int kChunks = WN / 8;              // 16-byte chunks per tile row
+        constexpr int kReads = 32 * kChunks / 64;    // chunks per lane per tile row block
+        static_assert(kReads * 64 == 32 * kChunks, "row chunks divide evenly over the lanes");
+        static_assert((2 * G::BN + G::BM) * 4 <= kParamBytes, "scales and biases fit");
         static_assert(kParamBytes + NW * 32 * kPitch <= kStages * kStage, "epilogue staging must fit in LDS");
         __syncthreads();
-        for (int e = tid; e < kBN + kBM; e += NW * 64) {
-            if (e < kBN) {
-                const int64_t n = (int64_t)tn * kBN + e;
+        for (int e = tid; e < G::BN + G::BM; e += NW * 64) {
+            if (e < G::BN) {
+                const int64_t n = (int64_t)tn * G::BN + e;
                 const int64_t nc = n < a.N ? n : a.N - 1;
                 p_sw[e] = a.sw[nc];
                 p_b[e] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
             } else {
-                const int64_t m = (int64_t)tm * kBM + (e - kBN);
-                p_sx[e - kBN] = a.sx[m < a.M ? m : a.M - 1];
+                const int64_t m = (int64_t)tm * G::BM + (e - G::BN);
+                p_sx[e - G::BN] = a.sx[m < a.M ? m : a.M - 1];
             }
         }
         __syncthreads();
-        uint8_t* tile = smem + kParamBytes + wave * (32 * kPitch);
+        uint8_t* tile_lds = smem + kParamBytes + wave * (32 * kPitch);
         const bool vec8 = (a.N % 8) == 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float sxm = p_sx[wm * 128 + 32 * i + r32];
+        for (int i = 0; i < BI; ++i) {
+            const float sxm = p_sx[wm * (32 * BI) + 32 * i + r32];
 #pragma unroll
             for (int j = 0; j < BJ; ++j)
 #pragma unroll
@@ -876,14 +917,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs a)
                         const int32_t v = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
                         y[u] = __builtin_fmaf((float)v * sxm, sc[u], bb[u]);
                     }
-                    *(uint2*)(tile + r32 * kPitch + nl * 2) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+                    *(uint2*)(tile_lds + r32 * kPitch + ((nl * 2) ^ half_swap(r32))) =
+                        make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
                 }
-            // read back row segments: lane l takes 16-byte chunk (l % kChunks) of rows (l / kChunks) + (64 / kChunks) s
+            // read back row segments: lane l takes the 16-byte chunks l + 64 s
+            // of the tile row block (row rho = chunk / kChunks)
 #pragma unroll
-            for (int sr = 0; sr < 32 * kChunks / 64; ++sr) {
-                const int rho = lane / kChunks + (64 / kChunks) * sr;
-                const int c = lane % kChunks;
-                const uint4 w = *(const uint4*)(tile + rho * kPitch + c * 16);
+            for (int sr = 0; sr < kReads; ++sr) {
+                const int idx = lane + 64 * sr;
+                const int rho = idx / kChunks;
+                const int c = idx % kChunks;
+                uint4 w = *(const uint4*)(tile_lds + rho * kPitch + c * 16);
+                if (half_swap(rho)) w = make_uint4(w.z, w.w, w.x, w.y);
                 const int64_t m = m_base + 32 * i + rho;
                 const int64_t n = n_base + 8 * c;
                 if (m >= a.M || n >= a.N) continue;
@@ -1343,15 +1388,27 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
         }
         return;
     }
-    a.tiles_m = (a.MT + kBM / 32 - 1) / (kBM / 32);
-    a.tiles_n = (a.NT + kBN / 32 - 1) / (kBN / 32);
     if (a.splits < 1) a.splits = 1;
-    constexpr int NW = CONVROT_GEMM_WAVES;
-    dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits)), block(NW * 64);
-    if (out_mode == GEMM_OUT_I32)
-        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, NW>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, NW>), grid, block, 0, s, a);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
+    if (a.shape == 0) {
+        const dim3 block(GemmShape<0>::NW * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 0>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 0>), grid, block, 0, s, a);
+    } else if (a.shape == 1) {
+        const dim3 block(GemmShape<1>::NW * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
+    } else {
+        const dim3 block(GemmShape<2>::NW * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 2>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 2>), grid, block, 0, s, a);
+    }
 }
 
 template <int G>

@@ -70,34 +70,63 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
            (size_t)((ks % 2) * 8 + d * 4);
 }
 
-// ---- GEMM work split ------------------------------------------------------
-// The GEMM covers the output with 256 x 256 tiles.  When there are too few
-// tiles to fill the chip, each tile's K range is split over S workgroups
+// ---- GEMM plan -------------------------------------------------------------
+// The GEMM covers the output with one of three block tiles: shape 0 is
+// 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192.  When there are too
+// few tiles to fill the chip, each tile's K range is split over S workgroups
 // (the integer partial sums are exact in any order): S is the largest value
-// <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks per split
-// (enough main-loop work to pay for the exchange of partial tiles).
-// M <= 32 goes to the weight-streaming kernel and is never split.
-constexpr int kGemmTile = 256;
+// <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks per split.
+// Of the shapes the plan takes the one with the smallest estimated time:
+// rounds of workgroups x 128-K blocks per workgroup x tile area at about
+// 24 ns per 1024 outputs per block, one prologue + epilogue (about 4 us) per
+// round, and for a split the exchange of (S - 1) int32 partial tiles per tile
+// through memory (written and read back at about 4 TB/s, plus 3 us).
+// M <= 32 goes to the weight-streaming kernels and is never split.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
 constexpr int kSplitCounters = 256;    // counter slots (tiles of a split launch <= 128)
+constexpr int kGemmShapes = 3;
 
-CONVROT_HD inline int gemm_splits(int64_t M, int64_t N, int64_t K)
+CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 0 ? 256 : 192; }
+CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 256 : (shape == 1 ? 384 : 192); }
+
+struct GemmPlan {
+    int shape;             // block tile shape (0, 1 or 2)
+    int tiles_m, tiles_n;  // block tiles along M and N
+    int splits;            // workgroups per tile along K
+};
+
+CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 32 || M <= 0 || N <= 0) return 1;
-    const int64_t tiles = ((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+    GemmPlan best{0, 1, 1, 1};
+    if (M <= 32 || M <= 0 || N <= 0) return best;
     const int64_t KB = (K + kTileK - 1) / kTileK;
-    int S = 1;
-    while (S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
-    return S;
+    int64_t best_ns = -1;
+    for (int shape = 0; shape < kGemmShapes; ++shape) {
+        const int64_t bm = gemm_tile_m(shape), bn = gemm_tile_n(shape);
+        const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+        const int64_t tiles = tm * tn;
+        int S = 1;
+        while (S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
+        const int64_t rounds = (tiles * S + kSplitTargetWGs - 1) / kSplitTargetWGs;
+        int64_t ns = rounds * ((KB + S - 1) / S) * (bm * bn / 1024) * 24 + rounds * 4000;
+        if (S > 1) ns += tiles * (S - 1) * bm * bn * 8 / 4000 + 3000;
+        if (best_ns < 0 || ns < best_ns) {
+            best_ns = ns;
+            best = GemmPlan{shape, (int)tm, (int)tn, S};
+        }
+    }
+    return best;
 }
 
-// Bytes of split-K partial tiles: (S - 1) int32 tiles of 256 x 256 per tile.
+CONVROT_HD inline int gemm_splits(int64_t M, int64_t N, int64_t K) { return gemm_plan(M, N, K).splits; }
+
+// Bytes of split-K partial tiles: (S - 1) int32 block tiles per tile.
 CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
 {
-    const int S = gemm_splits(M, N, K);
-    if (S <= 1) return 0;
-    const int64_t tiles = ((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
-    return (size_t)tiles * (size_t)(S - 1) * (size_t)kGemmTile * kGemmTile * 4;
+    const GemmPlan p = gemm_plan(M, N, K);
+    if (p.splits <= 1) return 0;
+    return (size_t)p.tiles_m * p.tiles_n * (size_t)(p.splits - 1) * (size_t)gemm_tile_m(p.shape) *
+           gemm_tile_n(p.shape) * 4;
 }
 
 // ---- single-kernel linear ---------------------------------------------------
