@@ -410,7 +410,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
 //            1536 x 12288 in exactly 256 tiles;
 //   shape 2: 192 (M) x 192 (N), four waves (one per SIMD) in a 2 x 2 grid,
 //            each owning 96 x 96 -- 1536 x 3072 in 128 tiles, two K splits
-//            each, with half the partial-tile bytes of larger tiles.
+//            each, with half the partial-tile bytes of larger tiles;
+//   shape 3: 256 (M) x 192 (N), four waves in a 2 x 2 grid, each owning
+//            128 x 96 = 4 x 3 MFMA tiles -- 4096 x 3072 in exactly 256.
 // K advances 128 at a time through a ring of four LDS stages, each holding
 // the tile's activation units and then its weight units of the operand image
 // (2 KB each).  The image is stored in exactly the LDS order, so every
@@ -437,6 +439,10 @@ struct GemmShape<1> {
 template <>
 struct GemmShape<2> {
     static constexpr int NW = 4, NWM = 2, BI = 3, BJ = 3;
+};
+template <>
+struct GemmShape<3> {
+    static constexpr int NW = 4, NWM = 2, BI = 4, BJ = 3;
 };
 template <int SHAPE>
 struct GemmGeom : GemmShape<SHAPE> {
@@ -1402,12 +1408,18 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
-    } else {
+    } else if (a.shape == 2) {
         const dim3 block(GemmShape<2>::NW * 64);
         if (out_mode == GEMM_OUT_I32)
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 2>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 2>), grid, block, 0, s, a);
+    } else {
+        const dim3 block(GemmShape<3>::NW * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 3>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 3>), grid, block, 0, s, a);
     }
 }
 

@@ -71,8 +71,9 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
 }
 
 // ---- GEMM plan -------------------------------------------------------------
-// The GEMM covers the output with one of three block tiles: shape 0 is
-// 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192.  When there are too
+// The GEMM covers the output with one of four block tiles: shape 0 is
+// 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192, shape 3 is
+// 256 x 192.  When there are too
 // few tiles to fill the chip, each tile's K range is split over S workgroups
 // (the integer partial sums are exact in any order): S is the largest value
 // <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks per split.
@@ -84,13 +85,13 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
 // M <= 32 goes to the weight-streaming kernels and is never split.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
 constexpr int kSplitCounters = 256;    // counter slots (tiles of a split launch <= 128)
-constexpr int kGemmShapes = 3;
+constexpr int kGemmShapes = 4;
 
-CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 0 ? 256 : 192; }
+CONVROT_HD constexpr int gemm_tile_m(int shape) { return (shape == 0 || shape == 3) ? 256 : 192; }
 CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 256 : (shape == 1 ? 384 : 192); }
 
 struct GemmPlan {
-    int shape;             // block tile shape (0, 1 or 2)
+    int shape;             // block tile shape (0 .. 3)
     int tiles_m, tiles_n;  // block tiles along M and N
     int splits;            // workgroups per tile along K
 };
