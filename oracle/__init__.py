@@ -68,6 +68,8 @@ def _load():
         lib.oracle_f32_to_bf16_array.restype = None
         lib.oracle_sylvester.argtypes = [I, P]
         lib.oracle_sylvester.restype = I
+        lib.oracle_regular_hadamard.argtypes = [I, P]
+        lib.oracle_regular_hadamard.restype = I
         lib.oracle_rotate_rows.argtypes = [P, I64, I64, I, P, I]
         lib.oracle_rotate_rows.restype = I
         lib.oracle_quantize_rows.argtypes = [P, I64, I64, P, P, I]
@@ -124,6 +126,10 @@ def f32_to_bf16(values) -> np.ndarray:
 # the method's steps
 # --------------------------------------------------------------------------
 
+# Group-size flag (OR'd into g): rotate with the regular Hadamard matrix.
+REGULAR = 0x10000
+
+
 def sylvester(g: int) -> np.ndarray:
     """Integer Sylvester Hadamard matrix H_g (entries +-1), natural order."""
     H = np.empty((g, g), dtype=np.int8)
@@ -131,8 +137,16 @@ def sylvester(g: int) -> np.ndarray:
     return H
 
 
+def regular_hadamard(g: int) -> np.ndarray:
+    """Integer regular Hadamard matrix (J_4 - 2 I_4)^(x k) of order g = 4^k."""
+    H = np.empty((g, g), dtype=np.int8)
+    _check(_load().oracle_regular_hadamard(int(g), _ptr(H)), "regular_hadamard")
+    return H
+
+
 def rotate_rows(x_bf16, g: int, threads: int | None = None) -> np.ndarray:
-    """r = x (I_G (x) H_g) / sqrt(g), each group in binary64, rounded once to binary32."""
+    """r = x (I_G (x) H_g) / sqrt(g), each group in binary64, rounded once to
+    binary32; H is Sylvester, or regular when g carries REGULAR."""
     x = _c(x_bf16, np.uint16)
     rows, K = x.shape
     r = np.empty((rows, K), dtype=np.float32)

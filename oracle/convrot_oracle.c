@@ -17,7 +17,15 @@
  *        [comfy-quants issue "convrot is ... QuaRot Stage 1c", section 1
  *         "Both apply group-wise operator": R = I_G (x) H_{N0} and
  *         X.R = [X_1 H, ..., X_G H]]
- *      H is the Sylvester matrix (recursive doubling), natural order.
+ *      H is the Sylvester matrix (recursive doubling), natural order; or,
+ *      when the group-size argument carries ORACLE_REGULAR, the regular
+ *      Hadamard matrix (J_4 - 2 I_4) (x) ... (x) (J_4 - 2 I_4), k factors for
+ *      g = 4^k (every row sums to 2^k).
+ *        [convrot-mlx README, "What is included": normalized regular-Hadamard
+ *         rotation for group sizes 64 and 256]
+ *        [comfy-quants issue, section 2 "The equivalent Hadamard matrix": for
+ *         N0 = 4^k the regular and Sylvester matrices differ by signed
+ *         permutations of rows and columns]
  *   2. Quantize every rotated row symmetrically to signed 4-bit codes in
  *      [-7, 7] with one absmax/7 scale per row.
  *        [convrot-mlx README, "What is included": symmetric signed W4/A4
@@ -163,6 +171,37 @@ int oracle_sylvester(int g, int8_t* H)
 }
 
 /* ------------------------------------------------------------------------ */
+/* 1b. Regular Hadamard matrix of order 4^k by Kronecker powers of the       */
+/*     order-4 regular matrix B = J_4 - 2 I_4 (-1 on the diagonal, +1 off):  */
+/*       R_4 = B,  R_4n = B (x) R_n  (block (a, b) is B[a][b] * R_n).        */
+/* ------------------------------------------------------------------------ */
+
+/* Group-size flag: rotate with the regular matrix instead of Sylvester. */
+#define ORACLE_REGULAR 0x10000
+
+/* Returns 0 on success, -1 if g is not a power of four in [4, 4096]. */
+int oracle_regular_hadamard(int g, int8_t* H)
+{
+    if (g < 4 || g > 4096 || (g & (g - 1)) != 0) return -1;
+    int k = 0;
+    while ((1 << (2 * k)) < g) ++k;
+    if ((1 << (2 * k)) != g) return -1;
+    static const int8_t B[4][4] = {{-1, 1, 1, 1}, {1, -1, 1, 1}, {1, 1, -1, 1}, {1, 1, 1, -1}};
+    /* build R_n for n = 4, 16, ... in the top-left corner of H */
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) H[(int64_t)i * g + j] = B[i][j];
+    for (int n = 4; n < g; n *= 4) {
+        /* R_4n = B (x) R_n; fill blocks (a, b) != (0, 0) first, then block (0, 0) */
+        for (int a = 3; a >= 0; --a)
+            for (int b = 3; b >= 0; --b)
+                for (int i = 0; i < n; ++i)
+                    for (int j = 0; j < n; ++j)
+                        H[(int64_t)(a * n + i) * g + (b * n + j)] = (int8_t)(B[a][b] * H[(int64_t)i * g + j]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* 2. Grouped rotation r = x (I_G (x) H_g) / sqrt(g), row vector times matrix */
 /* ------------------------------------------------------------------------ */
 
@@ -191,14 +230,20 @@ static void rotate_one_row(void* p, int64_t m)
     }
 }
 
-/* X: bf16 bits [rows][K]; R: binary32 [rows][K].  Returns 0, or -1 on bad
- * arguments (g not 64/256-style power of two, K not a multiple of g). */
-int oracle_rotate_rows(const uint16_t* X, int64_t rows, int64_t K, int g, float* R, int nthreads)
+/* X: bf16 bits [rows][K]; R: binary32 [rows][K].  g_arg is the group size,
+ * optionally with ORACLE_REGULAR.  Returns 0, or -1 on bad arguments (g not a
+ * power of two -- of four for the regular matrix --, K not a multiple of g). */
+int oracle_rotate_rows(const uint16_t* X, int64_t rows, int64_t K, int g_arg, float* R, int nthreads)
 {
+    const int regular = (g_arg & ORACLE_REGULAR) != 0;
+    const int g = g_arg & ~ORACLE_REGULAR;
     if (g < 2 || (g & (g - 1)) != 0 || g > 4096 || K <= 0 || K % g != 0 || rows < 0) return -1;
     int8_t* H = (int8_t*)malloc((size_t)g * g);
     if (!H) return -2;
-    oracle_sylvester(g, H);
+    if ((regular ? oracle_regular_hadamard(g, H) : oracle_sylvester(g, H)) != 0) {
+        free(H);
+        return -1;
+    }
     struct rot_ctx c = {X, K, g, H, 1.0 / sqrt((double)g), R};
     parallel_rows(rotate_one_row, &c, rows, nthreads);
     free(H);

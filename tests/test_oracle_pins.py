@@ -3,10 +3,12 @@ itself -- a library routine, a closed form, an exact-arithmetic invariant, a
 hand-derived golden case or brute force -- so that a dropped term, a wrong
 sign or index, or a transposed operand in the oracle fails here.
 
-Sources: convrot-mlx README ("What is included": normalized Hadamard rotation
-for groups 64/256, rowwise absmax INT4 in [-7, 7], reversible N x packed-K and
-K x packed-N layouts); comfy-quants issue "convrot is ... QuaRot Stage 1c",
-section 1 (R = I_G (x) H, X.R = [X_1 H, ..., X_G H], Y = sum_i RHT(X_i)RHT(W_i)^T).
+Sources: convrot-mlx README ("What is included": normalized regular-Hadamard
+rotation for groups 64/256, rowwise absmax INT4 in [-7, 7], reversible
+N x packed-K and K x packed-N layouts); comfy-quants issue "convrot is ...
+QuaRot Stage 1c", section 1 (R = I_G (x) H, X.R = [X_1 H, ..., X_G H],
+Y = sum_i RHT(X_i)RHT(W_i)^T) and section 2 (for N0 = 4^k the regular and the
+Sylvester matrix differ by signed permutations of rows and columns).
 """
 import json
 import os
@@ -59,9 +61,94 @@ def test_sylvester_closed_form_and_orthogonality(g):
     assert np.array_equal(Hn @ Hn.T, np.eye(g))
 
 
+# the order-4 regular Hadamard matrix J_4 - 2 I_4 (every row sums to 2), written out
+_B4 = np.array([[-1, 1, 1, 1], [1, -1, 1, 1], [1, 1, -1, 1], [1, 1, 1, -1]], dtype=np.int64)
+
+
+def test_regular_base_matrix():
+    assert np.array_equal(oracle.regular_hadamard(4).astype(np.int64), _B4)
+
+
+@pytest.mark.parametrize("g", [16, 64, 256])
+def test_regular_matches_numpy_kron_and_closed_form(g):
+    R = oracle.regular_hadamard(g).astype(np.int64)
+    ref = _B4
+    while ref.shape[0] < g:
+        ref = np.kron(_B4, ref)
+    assert np.array_equal(R, ref)
+    # closed form: (-1)^(number of base-4 digit positions where i and j agree)
+    k = int(round(np.log(g) / np.log(4)))
+    i = np.arange(g)[:, None]
+    j = np.arange(g)[None, :]
+    same = sum(((i >> (2 * d)) & 3) == ((j >> (2 * d)) & 3) for d in range(k))
+    assert np.array_equal(R, np.where(same % 2 == 0, 1, -1))
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_regular_is_a_regular_hadamard_matrix(g):
+    R = oracle.regular_hadamard(g).astype(np.int64)
+    assert np.array_equal(R @ R.T, g * np.eye(g, dtype=np.int64))      # Hadamard
+    s = int(round(np.sqrt(g)))
+    assert np.all(R.sum(axis=1) == s) and np.all(R.sum(axis=0) == s)   # constant row / column sums
+    assert np.array_equal(R, R.T)
+    Rn = R.astype(np.float64) / np.sqrt(g)
+    assert np.array_equal(Rn @ Rn.T, np.eye(g))
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_regular_is_sylvester_up_to_signed_permutations(g):
+    """The issue's section 2 claim, checked by search: for some sign vector q,
+    the rows of R diag(q) are the rows of the Sylvester matrix up to order and
+    sign, i.e. R = P H Q with signed permutations P, Q."""
+    R = oracle.regular_hadamard(g).astype(np.int64)
+    H = scipy.linalg.hadamard(g).astype(np.int64)
+    h_rows = {tuple(r): n for n, r in enumerate(H)}
+    found = False
+    for i0 in range(g):
+        q = R[i0]                                   # makes row i0 all ones
+        hit = []
+        for r in R * q[None, :]:
+            t = tuple(r)
+            n = h_rows.get(t, h_rows.get(tuple(-r)))
+            if n is None:
+                break
+            hit.append(n)
+        if len(hit) == g and len(set(hit)) == g:
+            found = True
+            break
+    assert found
+    assert not np.array_equal(np.abs(R @ H.T), g * np.eye(g, dtype=np.int64))  # not the same matrix
+
+
 # --------------------------------------------------------------------------
 # Grouped rotation
 # --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g,K", [(64, 128), (256, 512)])
+def test_regular_rotation_equals_kronecker_operator(g, K):
+    x = synth.random_bf16((4, K), seed=21, outliers=3)
+    B = _B4
+    while B.shape[0] < g:
+        B = np.kron(_B4, B)
+    R = np.kron(np.eye(K // g), B).astype(np.float64) / np.sqrt(g)
+    ref = (synth.bf16_bits_to_f32(x).astype(np.float64) @ R).astype(np.float32)
+    assert np.array_equal(oracle.rotate_rows(x, g | oracle.REGULAR), ref)
+
+
+@pytest.mark.parametrize("g,K", [(64, 192), (256, 512)])
+def test_regular_rotation_invariance_exact_on_integers(g, K):
+    rng = np.random.default_rng(6)
+    X = rng.integers(-8, 9, size=(5, K)).astype(np.float32)
+    W = rng.integers(-8, 9, size=(6, K)).astype(np.float32)
+    RX = oracle.rotate_rows(_bits_of(X), g | oracle.REGULAR).astype(np.float64)
+    RW = oracle.rotate_rows(_bits_of(W), g | oracle.REGULAR).astype(np.float64)
+    assert np.array_equal(RX @ RW.T, (X.astype(np.int64) @ W.astype(np.int64).T).astype(np.float64))
+
+
+def test_regular_rotation_rejects_non_power_of_four():
+    x = synth.random_bf16((2, 128), seed=1)
+    with pytest.raises(ValueError):
+        oracle.rotate_rows(x, 32 | oracle.REGULAR)
 
 @pytest.mark.parametrize("g,K", [(64, 64), (64, 320), (256, 256), (256, 1024)])
 def test_rotation_equals_kronecker_operator(g, K):
