@@ -5,9 +5,10 @@
  * The operation (convrot-mlx README, "What is included"; comfy-quants issue
  * "convrot is ... QuaRot Stage 1c", section 1):
  *   Y[M,N] = bf16( (Q(X R) . Q(W R)^T) * sx[m] * sw[n] + bias[n] )
- * where R = I_G (x) H_g / sqrt(g) is the block-diagonal normalized Sylvester
- * Hadamard rotation over contiguous groups of g in {64, 256} input channels,
- * and Q quantizes each rotated row symmetrically to signed 4-bit codes in
+ * where R = I_G (x) H_g / sqrt(g) is the block-diagonal normalized Hadamard
+ * rotation over contiguous groups of g in {64, 256} input channels -- H_g the
+ * Sylvester matrix, or the regular one when g carries
+ * CONVROT_REGULAR_HADAMARD (below) -- and Q quantizes each rotated row symmetrically to signed 4-bit codes in
  * [-7, 7] with one scale s = absmax(row) / 7 per row (codes rint(r / s),
  * ties to even; an all-zero row has s = 0 and codes 0).  The product is an
  * exact integer dot product; the epilogue is fmaf(float(acc) * sx[m], sw[n],
@@ -53,6 +54,16 @@ const char* convrot_status_string(int status);
 
 /* Library version string, e.g. "convrot-gfx950 1.0". */
 const char* convrot_version(void);
+
+/* Rotation flag for every g argument: g = 64 or 256 selects the normalized
+ * Sylvester matrix H_g / sqrt(g); g = (64 or 256) | CONVROT_REGULAR_HADAMARD
+ * selects the normalized regular Hadamard matrix (J_4 - 2 I_4)^(x k) / sqrt(g),
+ * g = 4^k, whose rows all sum to sqrt(g) (convrot-mlx README, "What is
+ * included": normalized regular-Hadamard rotation; comfy-quants issue,
+ * section 2: for 4^k it equals the Sylvester matrix up to signed permutations
+ * of rows and columns).  A weight image is valid only with the g it was
+ * prepared with: convrot_linear must be given the same value. */
+#define CONVROT_REGULAR_HADAMARD 0x10000
 
 /* ---- sizes (host only, no HIP call) ----------------------------------- */
 

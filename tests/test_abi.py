@@ -38,6 +38,11 @@ def test_workspace_image_offset_matches_header():
     assert m and int(m.group(1)) == B.WORKSPACE_IMAGE_OFFSET
 
 
+def test_regular_flag_matches_header():
+    m = re.search(r"#define\s+CONVROT_REGULAR_HADAMARD\s+(0x[0-9a-fA-F]+)", open(HEADER).read())
+    assert m and int(m.group(1), 16) == B.CONVROT_REGULAR_HADAMARD
+
+
 def test_version_and_status_strings():
     assert B.convrot_version().startswith("convrot-gfx950")
     for code in (0, 1, 2, 3, 4):
@@ -104,6 +109,12 @@ def test_validate_linear_statuses():
     assert _validate_linear() == B.CONVROT_OK
     assert _validate_linear(bias=2) == B.CONVROT_OK
     assert _validate_linear(g=128) == B.CONVROT_EINVAL
+    R = B.CONVROT_REGULAR_HADAMARD
+    assert _validate_linear(g=256 | R) == B.CONVROT_OK
+    assert _validate_linear(g=64 | R) == B.CONVROT_OK
+    assert _validate_linear(g=128 | R) == B.CONVROT_EINVAL
+    assert _validate_linear(g=256 | (R << 1)) == B.CONVROT_EINVAL    # unknown flag
+    assert _validate_linear(g=R) == B.CONVROT_EINVAL
     assert _validate_linear(K=1000) == B.CONVROT_EINVAL
     assert _validate_linear(X=0) == B.CONVROT_EINVAL
     assert _validate_linear(Y=0) == B.CONVROT_EINVAL

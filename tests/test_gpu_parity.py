@@ -42,6 +42,11 @@ PREP_SHAPES = [
 ]
 
 
+REG = 0x10000  # the library's regular-Hadamard flag (checked against the header in test_abi)
+PREP_SHAPES += [(5, 256, 256 | REG), (37, 3072, 256 | REG), (2, 16384, 256 | REG), (7, 192, 64 | REG),
+                (33, 1024, 64 | REG), (1, 64, 64 | REG)]
+
+
 @pytest.mark.parametrize("rows,K,g", PREP_SHAPES)
 def test_prepare_rows_parity(gpu, rows, K, g):
     x = synth.random_bf16((rows, K), seed=rows * 7 + K + g, outliers=max(1, K // 200))
@@ -202,7 +207,11 @@ def test_linear_small_workloads_full(gpu, name):
                                      (33, 64, 192, 64), (257, 300, 2048, 64), (2, 2, 64, 64),
                                      # M <= 4: the single-kernel path (1..3 strips per workgroup, 1..4 waves per row)
                                      (1, 100, 1024, 256), (3, 5000, 4096, 256), (4, 33, 512, 64),
-                                     (2, 17000, 2048, 64), (4, 48, 1280, 256), (1, 12288, 3072, 256)])
+                                     (2, 17000, 2048, 64), (4, 48, 1280, 256), (1, 12288, 3072, 256),
+                                     # the regular Hadamard matrix, both paths
+                                     (37, 70, 512, 256 | REG), (257, 300, 2048, 64 | REG),
+                                     (1, 100, 1024, 256 | REG), (4, 33, 512, 64 | REG),
+                                     (3, 5000, 4096, 256 | REG)])
 def test_linear_ragged_shapes(gpu, M, N, K, g):
     x = synth.random_bf16((M, K), seed=M + N, outliers=3)
     w = synth.random_bf16((N, K), seed=N + K, std=0.02)
@@ -249,14 +258,16 @@ FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_ml
         "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL + ["flux_qkv_m1536_k3072_n9216+regular"])
 def test_linear_full_size_sampled(gpu, name):
     """Full shapes, the launch configuration the benchmark times; the oracle
-    recomputes sampled rows x sampled columns from scratch."""
+    recomputes sampled rows x sampled columns from scratch.  "+regular": the
+    same inputs rotated with the regular Hadamard matrix."""
     import torch
-    inp = synth.make(name)
+    base, _, variant = name.partition("+")
+    inp = synth.make(base)
     wl = inp["workload"]
-    M, N, K, g = wl.M, wl.N, wl.K, wl.g
+    M, N, K, g = wl.M, wl.N, wl.K, wl.g | (REG if variant == "regular" else 0)
     W = _dev(inp["w"])
     image, sw = gpu.convrot_prepare_weight(W, g)
     ws = gpu.new_workspace(M, K, N, g)

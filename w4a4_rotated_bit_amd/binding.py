@@ -24,6 +24,8 @@ CONVROT_EINVAL = 1
 CONVROT_EWORKSPACE = 2
 CONVROT_EHIP = 3
 CONVROT_EDEVICE = 4
+# OR'd into a group size g: rotate with the regular Hadamard matrix
+CONVROT_REGULAR_HADAMARD = 0x10000
 
 _lock = threading.Lock()
 _lib = None

@@ -9,13 +9,16 @@
 
 using namespace convrot;
 
+static_assert(CONVROT_REGULAR_HADAMARD == kRegularHadamard, "header and library agree on the rotation flag");
+
 namespace convrot {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_shape(int64_t rows, int64_t K, int g)
 {
-    if (g != 64 && g != 256) return CONVROT_EINVAL;
+    if ((g & ~kRegularHadamard) != 64 && (g & ~kRegularHadamard) != 256) return CONVROT_EINVAL;
+    g &= ~kRegularHadamard;
     if (K < 1 || K > kMaxK || K % g != 0) return CONVROT_EINVAL;
     if (rows < 0 || rows > kMaxRows) return CONVROT_EINVAL;
     return CONVROT_OK;

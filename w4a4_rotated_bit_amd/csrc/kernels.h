@@ -37,6 +37,7 @@ struct GemmArgs {
     int32_t* partial;    // (splits - 1) partial tiles per tile
 };
 
+// g: group size, optionally with kRegularHadamard (the rotation matrix)
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
 // Whole linear in one launch when single_kernel_linear(M, K, g) holds; see

@@ -193,13 +193,81 @@ __device__ inline void zero_unless(bool has_data, uint4 (&w)[P / 8])
         if (!has_data) w[c] = make_uint4(0, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Regular Hadamard rotation.  The order-4 regular matrix B = J_4 - 2 I_4 is
+// Pi D H_4 D, with H_4 the order-4 Sylvester matrix, D = diag(1, 1, 1, -1) and
+// Pi the exchange of rows 0 and 3; so its k-th Kronecker power, the regular
+// matrix of order g = 4^k, is (Pi D)^(x k) H_g D^(x k).  Rotating a group x by
+// it is therefore: flip the sign of x_j when the base-4 digits of j hold an
+// odd number of 3s (D^(x k)), apply the Sylvester butterflies, and take output
+// o from Sylvester output pi(o), pi exchanging digits 0 and 3 in every base-4
+// position, with the sign flipped when o has an odd number of 0 digits
+// ((Pi D)^(x k)).  Sign flips and permutations are exact, so the rounded
+// result is as exact as the Sylvester one.
+// ---------------------------------------------------------------------------
+
+// parity of the number of base-4 digits equal to 3 in x
+__host__ __device__ constexpr uint32_t threes_parity(uint32_t x)
+{
+    return (uint32_t)__builtin_popcount(x & (x >> 1) & 0x55555555u) & 1u;
+}
+
+__device__ inline double negate_if(double v, uint32_t neg)
+{
+    return __hiloint2double(__double2hiint(v) ^ (int)(neg << 31), __double2loint(v));
+}
+
+__device__ inline float negate_if(float v, uint32_t neg) { return __uint_as_float(__float_as_uint(v) ^ (neg << 31)); }
+
+// D^(x k) on the P inputs k0 .. k0 + P - 1 of a lane (k0 a multiple of P).
+// With P = 16 the lane's two low digits are its own; with P = 8 digit 1 is
+// split between bit 2 of the element and bit 3 of k0.
+template <int G, int P>
+__device__ inline void regular_input_signs(int64_t k0, double (&v)[P])
+{
+    const uint32_t hi = (uint32_t)(k0 % G);
+    const uint32_t l0 = threes_parity(hi), l4 = threes_parity(hi | 4u);
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const uint32_t neg = (P == 16) ? (l0 ^ threes_parity((uint32_t)e))
+                                       : (((e & 4) ? l4 : l0) ^ threes_parity((uint32_t)(e & 3)));
+        v[e] = negate_if(v[e], neg);
+    }
+}
+
+// (Pi D)^(x k) on the way back to phase-1 order: lf holds this lane group's
+// normalized Sylvester outputs z in natural order (z[i] at row i / P, column
+// i % P of the group's rows starting at gbase).  Output o = 4 c + d of the
+// lane takes z[4 pi(c) + pi(d)], pi(d) = 3, 1, 2, 0 for d = 0 .. 3, with the
+// sign of (-1)^(zero digits of c) and one more flip for d == 0.
+template <int G, int P, int RUN>
+__device__ inline void regular_output_permutation(const float* lf, int gbase, int64_t k0, float (&r)[P])
+{
+    constexpr uint32_t kDigits = (G == 256) ? 3 : 2;              // base-4 digits of a block index c
+    constexpr uint32_t kLow = 0x55555555u & ((1u << (2 * kDigits)) - 1);
+    const uint32_t c0 = (uint32_t)(k0 % G) >> 2;                  // block index of the lane's first output
+#pragma unroll
+    for (int b = 0; b < P / 4; ++b) {
+        const uint32_t c = c0 + (uint32_t)b;
+        const uint32_t same = ~(c ^ (c >> 1)) & kLow;               // digits 0 or 3
+        const uint32_t pc = c ^ (same | (same << 1));
+        const uint32_t zpar = (uint32_t)__builtin_popcount(~(c | (c >> 1)) & kLow) & 1u;
+        const uint32_t src = 4 * pc;
+        const float4 q = *(const float4*)(lf + (gbase + (int)(src / P)) * RUN + (int)(src % P));
+        r[4 * b + 0] = negate_if(q.w, zpar ^ 1u);
+        r[4 * b + 1] = negate_if(q.y, zpar);
+        r[4 * b + 2] = negate_if(q.z, zpar);
+        r[4 * b + 3] = negate_if(q.x, zpar);
+    }
+}
+
 // One row of the prep kernel: rotation, absmax, quantization and the write
 // of the codes in the layout of MODE.  w holds the lane's P bf16 values.
 // A team of more than 64 lanes is waves team_w0 .. team_w0 + team_nw - 1 of
 // the workgroup.  OUT_LDS writes the image rows of a small row block into
 // shared memory: row r of 128-K unit kb at ((kb * LDS_ROWS + r) * 64) with
 // the image's in-row layout.
-template <int G, int MODE, int LDS_ROWS = 0>
+template <int G, int MODE, int LDS_ROWS = 0, bool REG = false>
 __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape<G>::P / 8], int64_t row, int t,
                                          int64_t k0, int lane, int wave, double* ld, uint32_t (*red)[16], int parity,
                                          int team_w0, int team_nw)
@@ -221,6 +289,7 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
         v[8 * c + 4] = bf16_lo(w[c].z); v[8 * c + 5] = bf16_hi(w[c].z);
         v[8 * c + 6] = bf16_lo(w[c].w); v[8 * c + 7] = bf16_hi(w[c].w);
     }
+    if constexpr (REG) regular_input_signs<G, P>(k0, v);
 #pragma unroll
     for (int b = 1; b < P; b <<= 1)
 #pragma unroll
@@ -275,10 +344,14 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     float r[P];
+    if constexpr (!REG) {
 #pragma unroll
-    for (int e = 0; e < P; e += 4) {
-        const float4 q = *(const float4*)(lf + lane * S::kRunF + e);
-        r[e] = q.x; r[e + 1] = q.y; r[e + 2] = q.z; r[e + 3] = q.w;
+        for (int e = 0; e < P; e += 4) {
+            const float4 q = *(const float4*)(lf + lane * S::kRunF + e);
+            r[e] = q.x; r[e + 1] = q.y; r[e + 2] = q.z; r[e + 3] = q.w;
+        }
+    } else {
+        regular_output_permutation<G, P, S::kRunF>(lf, gbase, k0, r);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next row rewrites the region
@@ -347,8 +420,8 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     }
 }
 
-template <int G, int MODE>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void prep_kernel(PrepArgs a)
+template <int G, int MODE, bool REG>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(REG ? 5 : 6))) void prep_kernel(PrepArgs a)
 {
     using S = PrepShape<G>;
     constexpr int P = S::P;
@@ -389,12 +462,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
     for (int64_t it = 0; it < n_it; it += 2) {
         int64_t nx = row + row_step;
         load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wb);
-        prep_row<G, MODE>(a, wa, row, t, k0, lane, wave, ld, red, 0, 0, blockDim.x >> 6);
+        prep_row<G, MODE, 0, REG>(a, wa, row, t, k0, lane, wave, ld, red, 0, 0, blockDim.x >> 6);
         row = nx;
         if (it + 1 >= n_it) break;
         nx = row + row_step;
         load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wa);
-        prep_row<G, MODE>(a, wb, row, t, k0, lane, wave, ld, red, 1, 0, blockDim.x >> 6);
+        prep_row<G, MODE, 0, REG>(a, wb, row, t, k0, lane, wave, ld, red, 1, 0, blockDim.x >> 6);
         row = nx;
     }
 }
@@ -1107,7 +1180,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kSmallUnits = 8;     // 128-K units per wave: K <= 4096 over four waves
 
-template <int G, int SW>
+template <int G, int SW, bool REG>
 __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArgs a, PrepArgs p)
 {
     using PS = PrepShape<G>;
@@ -1183,7 +1256,8 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
         pl.scales = sxl;
         const int passes = (int)((a.M + teams - 1) / teams);  // rows 0 .. M - 1
         if (live && team < a.M)  // uniform over the team's waves
-            prep_row<G, OUT_LDS, kSmallRows>(pl, xw, team, t, k0, lane, wave, ld, pred, 0, team * team_nw, team_nw);
+            prep_row<G, OUT_LDS, kSmallRows, REG>(pl, xw, team, t, k0, lane, wave, ld, pred, 0, team * team_nw,
+                                                   team_nw);
         else if (p.team > 64)
             __syncthreads();
         for (int pass = 1; pass < passes; ++pass) {
@@ -1191,7 +1265,7 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
             const bool active = live && row < a.M;
             load_run<P>(p.X, row, p.K, k0, active && k0 < p.K, xw);
             if (active)
-                prep_row<G, OUT_LDS, kSmallRows>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
+                prep_row<G, OUT_LDS, kSmallRows, REG>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
                                                   team_nw);
             else if (p.team > 64)
                 __syncthreads();
@@ -1315,7 +1389,7 @@ static int device_cus()
     return n;
 }
 
-template <int G, int MODE>
+template <int G, int MODE, bool REG>
 static void launch_prep_g(PrepArgs a, hipStream_t s)
 {
     constexpr int P = PrepShape<G>::P;
@@ -1336,7 +1410,7 @@ static void launch_prep_g(PrepArgs a, hipStream_t s)
     const size_t lds = (size_t)(block / 64) * PrepShape<G>::kWaveLdsBytes;
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)&prep_kernel<G, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (void)hipFuncSetAttribute((const void*)&prep_kernel<G, MODE, REG>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   16 * PrepShape<G>::kWaveLdsBytes);
         attr_set = true;
     }
@@ -1346,7 +1420,7 @@ static void launch_prep_g(PrepArgs a, hipStream_t s)
     const int waves = block / 64;
     int per_cu = per_cu_cache[waves].load(std::memory_order_relaxed);
     if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)&prep_kernel<G, MODE>, block, lds) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)&prep_kernel<G, MODE, REG>, block, lds) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -1355,16 +1429,18 @@ static void launch_prep_g(PrepArgs a, hipStream_t s)
     const int64_t need = (a.rows_pad + row_slots - 1) / row_slots;
     const int64_t resident = (int64_t)device_cus() * per_cu;
     const unsigned grid = (unsigned)(need < resident ? need : resident);
-    hipLaunchKernelGGL((prep_kernel<G, MODE>), dim3(grid), dim3(block), lds, s, a);
+    hipLaunchKernelGGL((prep_kernel<G, MODE, REG>), dim3(grid), dim3(block), lds, s, a);
 }
 
 template <int MODE>
 static void launch_prep_mode(int g, const PrepArgs& a, hipStream_t s)
 {
+    const bool reg = (g & kRegularHadamard) != 0;
+    g &= ~kRegularHadamard;
     if (g == 256)
-        launch_prep_g<256, MODE>(a, s);
+        reg ? launch_prep_g<256, MODE, true>(a, s) : launch_prep_g<256, MODE, false>(a, s);
     else
-        launch_prep_g<64, MODE>(a, s);
+        reg ? launch_prep_g<64, MODE, true>(a, s) : launch_prep_g<64, MODE, false>(a, s);
 }
 
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
@@ -1423,13 +1499,13 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     }
 }
 
-template <int G>
+template <int G, bool REG>
 static void launch_small_m_g(int sw, const GemmArgs& a, const PrepArgs& p, dim3 grid, hipStream_t s)
 {
     switch (sw) {
-        case 1: hipLaunchKernelGGL((small_m_kernel<G, 1>), grid, dim3(1 * kSkinnyWaves * 64), 0, s, a, p); break;
-        case 2: hipLaunchKernelGGL((small_m_kernel<G, 2>), grid, dim3(2 * kSkinnyWaves * 64), 0, s, a, p); break;
-        default: hipLaunchKernelGGL((small_m_kernel<G, 3>), grid, dim3(3 * kSkinnyWaves * 64), 0, s, a, p); break;
+        case 1: hipLaunchKernelGGL((small_m_kernel<G, 1, REG>), grid, dim3(1 * kSkinnyWaves * 64), 0, s, a, p); break;
+        case 2: hipLaunchKernelGGL((small_m_kernel<G, 2, REG>), grid, dim3(2 * kSkinnyWaves * 64), 0, s, a, p); break;
+        default: hipLaunchKernelGGL((small_m_kernel<G, 3, REG>), grid, dim3(3 * kSkinnyWaves * 64), 0, s, a, p); break;
     }
 }
 
@@ -1439,13 +1515,15 @@ void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s)
     const int64_t strips = (a.N + 15) / 16;
     const int cus = device_cus();
     const int sw = (int)std::min<int64_t>(3, std::max<int64_t>(1, (strips + cus - 1) / cus));
+    const bool reg = (g & kRegularHadamard) != 0;
+    g &= ~kRegularHadamard;
     p.team = (int)(p.K_pad / (g == 256 ? 16 : 8));  // lanes per row (whole waves: 64 .. 256)
     p.rows_pad = kSmallRows;
     const dim3 grid((unsigned)((strips + sw - 1) / sw));
     if (g == 256)
-        launch_small_m_g<256>(sw, a, p, grid, s);
+        reg ? launch_small_m_g<256, true>(sw, a, p, grid, s) : launch_small_m_g<256, false>(sw, a, p, grid, s);
     else
-        launch_small_m_g<64>(sw, a, p, grid, s);
+        reg ? launch_small_m_g<64, true>(sw, a, p, grid, s) : launch_small_m_g<64, false>(sw, a, p, grid, s);
 }
 
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,

@@ -70,6 +70,11 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
            (size_t)((ks % 2) * 8 + d * 4);
 }
 
+// ---- rotation ---------------------------------------------------------------
+// The group-size argument g is 64 or 256, optionally with this flag: rotate
+// with the regular Hadamard matrix instead of the Sylvester one.
+constexpr int kRegularHadamard = 0x10000;
+
 // ---- GEMM plan -------------------------------------------------------------
 // The GEMM covers the output with one of four block tiles: shape 0 is
 // 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192, shape 3 is
@@ -137,7 +142,7 @@ CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
 constexpr int kSmallRows = 4;
 CONVROT_HD inline bool single_kernel_linear(int64_t M, int64_t K, int g)
 {
-    const int64_t lanes = round_up(K, kTileK) / (g == 256 ? 16 : 8);
+    const int64_t lanes = round_up(K, kTileK) / ((g & ~kRegularHadamard) == 256 ? 16 : 8);
     return M >= 1 && M <= kSmallRows && lanes >= 64 && lanes <= 256;
 }
 
