@@ -68,7 +68,7 @@ def read_traffic(workload: str, gemm_ops_unit_launches: int):
         return None
 
 
-def cpu_baseline(inp, target_s: float):
+def cpu_baseline(inp, target_s: float, g: int):
     """The oracle's linear on a bounded sample of the workload: as many rows of
     X as fit in about target_s seconds (the whole X, repeated, when one pass is
     shorter).  The weight is prepared by the oracle beforehand, untimed, like
@@ -77,11 +77,11 @@ def cpu_baseline(inp, target_s: float):
     wl = inp["workload"]
     threads = oracle.default_threads()
     t0 = time.perf_counter()
-    qw, sw = oracle.prepare_weight(inp["w"], wl.g, threads=threads)
+    qw, sw = oracle.prepare_weight(inp["w"], g, threads=threads)
     log(f"cpu baseline: oracle weight preparation {time.perf_counter() - t0:.1f} s (untimed)")
     probe = min(wl.M, 8)
     t0 = time.perf_counter()
-    oracle.linear(inp["x"][:probe], qw, sw, inp["bias"], wl.g, threads=threads)
+    oracle.linear(inp["x"][:probe], qw, sw, inp["bias"], g, threads=threads)
     dt = time.perf_counter() - t0
     rows = int(max(probe, min(wl.M, probe * target_s / max(dt, 1e-6))))
     reps = 1
@@ -89,7 +89,7 @@ def cpu_baseline(inp, target_s: float):
         reps = int(max(1, min(20, target_s / max(dt * wl.M / probe, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(reps):
-        oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], wl.g, threads=threads)
+        oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], g, threads=threads)
     dt = time.perf_counter() - t0
     tops = 2.0 * rows * reps * wl.N * wl.K / dt / 1e12
     return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--cold-bytes", type=float, default=512 * 2**20, help="total bytes of rotating buffer sets")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps one by one instead of as a graph")
+    ap.add_argument("--rotation", choices=("sylvester", "regular"), default="sylvester",
+                    help="Hadamard matrix of the rotation (the regular one adds sign flips and a permutation)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,7 +144,9 @@ def main():
     inp = synth.make(args.workload)
     wl = inp["workload"]
     M, N, K, g = wl.M, wl.N, wl.K, wl.g
-    log(f"workload {wl.name}: M={M} N={N} K={K} g={g}")
+    if args.rotation == "regular":
+        g |= binding.CONVROT_REGULAR_HADAMARD
+    log(f"workload {wl.name}: M={M} N={N} K={K} g={wl.g} rotation={args.rotation}")
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -263,7 +267,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, g)
 
     rec = {
         "metric": METRIC,
@@ -278,7 +282,8 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": g, "x_kind": wl.x_kind,
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": wl.g, "rotation": args.rotation,
+                   "x_kind": wl.x_kind,
                    "outlier_channels": wl.outlier_count, "cold_buffer_sets": n_sets,
                    "timed_as": "hip_graph" if graph is not None else "stream_launches"},
         "gbps": round(gbs, 1),

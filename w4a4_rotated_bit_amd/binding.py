@@ -70,11 +70,17 @@ _SIGNATURES = {
 
 
 def load():
-    """Load libconvrot.so (building it only if nothing is built)."""
+    """Load libconvrot.so (building it only if nothing is built).
+
+    torch is imported first: it brings its own HIP runtime library, and the
+    library's HIP dependency must resolve to that same, already loaded copy --
+    loaded the other way round, the process would hold two HIP runtimes and
+    torch's device pointers and streams would be foreign to the library's."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
+        import torch  # noqa: F401  (see above)
         if not os.path.exists(LIB_PATH):
             _build.build()
         lib = ctypes.CDLL(LIB_PATH)
