@@ -87,6 +87,8 @@ def _load():
         lib.oracle_epilogue.restype = None
         lib.oracle_linear.argtypes = [P, I64, I64, P, P, P, I64, I, P, P, P, P, I]
         lib.oracle_linear.restype = I
+        lib.oracle_linear_w4a16.argtypes = [P, I64, I64, P, P, P, I64, I, P, P, I]
+        lib.oracle_linear_w4a16.restype = I
         _lib = lib
         return lib
 
@@ -267,3 +269,20 @@ def linear(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, 
     if want_parts:
         return y, {"qx": qx, "sx": sx, "acc": acc}
     return y
+
+
+def linear_w4a16(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, want_rotated: bool = False):
+    """W4A16: rotated activation rows rounded to bf16, times the INT4 weight
+    codes (exact products, binary64 sum), y = fmaf(fl32(sum), sw, bias) to bf16.
+    Returns Y as bf16 bits [M, N] (and, if asked, the bf16 rotated X)."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    qw = _c(qw_codes, np.int8)
+    N = qw.shape[0]
+    swa = _c(sw, np.float32)
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    y = np.empty((M, N), dtype=np.uint16)
+    xr = np.empty((M, K), dtype=np.uint16) if want_rotated else None
+    _check(_load().oracle_linear_w4a16(_ptr(x), M, K, _ptr(qw), _ptr(swa), _ptr(b), N, int(g), _ptr(y), _ptr(xr),
+                                       threads or default_threads()), "linear_w4a16")
+    return (y, xr) if want_rotated else y

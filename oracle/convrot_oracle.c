@@ -40,6 +40,11 @@
  *        [convrot-mlx README, "Install and test": the complete linear path is
  *         rotation, activation quantization, integer product, scaling, bias]
  *
+ *   W4A16 variant (weight-only INT4): the activation rows are rotated as in
+ *   step 1 and rounded to bf16 instead of being quantized, then multiplied by
+ *   the same INT4 weight codes; y = fmaf(fl32(sum), sw[n], bias[n]) to bf16.
+ *        [convrot-mlx README, "What is included": the W4A16 path beside W4A4]
+ *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes):
  *   - rotation is computed in double as a dense g x g product per group and
@@ -451,5 +456,53 @@ int oracle_linear(const uint16_t* X, int64_t M, int64_t K, const int8_t* QW, con
     if (!QX_out) free(QX);
     if (!SX_out) free(SX);
     if (!ACC_out) free(ACC);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8. W4A16: rotated activations rounded to bf16, INT4 weight codes           */
+/* ------------------------------------------------------------------------ */
+
+struct w4a16_ctx {
+    const uint16_t* XR; /* bf16 rotated activations [M][K] */
+    const int8_t* QW;
+    const float* SW;
+    const uint16_t* BIAS;
+    int64_t N, K;
+    uint16_t* Y;
+};
+
+static void w4a16_one_row(void* p, int64_t m)
+{
+    struct w4a16_ctx* c = (struct w4a16_ctx*)p;
+    const uint16_t* x = c->XR + m * c->K;
+    for (int64_t n = 0; n < c->N; ++n) {
+        const int8_t* q = c->QW + n * c->K;
+        double acc = 0.0; /* each product is exact; |sum| is far below 2^53 ulps of the terms */
+        for (int64_t k = 0; k < c->K; ++k) acc += (double)oracle_bf16_to_f32(x[k]) * (double)q[k];
+        float b = c->BIAS ? oracle_bf16_to_f32(c->BIAS[n]) : 0.0f;
+        c->Y[m * c->N + n] = oracle_f32_to_bf16(fmaf((float)acc, c->SW[n], b));
+    }
+}
+
+/* X: bf16 [M][K]; QW: int8 codes [N][K]; SW: [N]; BIAS: bf16 [N] or NULL;
+ * Y: bf16 [M][N]; XR_out (optional): the bf16 rotated activations [M][K].
+ * g as for oracle_rotate_rows.  Returns 0 on success. */
+int oracle_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, const int8_t* QW, const float* SW,
+                        const uint16_t* BIAS, int64_t N, int g, uint16_t* Y, uint16_t* XR_out, int nthreads)
+{
+    if (M < 0 || N < 0 || K <= 0) return -1;
+    size_t mk = (size_t)(M > 0 ? M : 1) * (size_t)K;
+    float* R = (float*)malloc(mk * sizeof(float));
+    uint16_t* XR = XR_out ? XR_out : (uint16_t*)malloc(mk * sizeof(uint16_t));
+    int rc = (!R || !XR) ? -2 : 0;
+    if (rc == 0) rc = oracle_rotate_rows(X, M, K, g, R, nthreads);
+    if (rc == 0) {
+        for (size_t i = 0; i < (size_t)M * (size_t)K; ++i) XR[i] = oracle_f32_to_bf16(R[i]);
+        struct w4a16_ctx c = {XR, QW, SW, BIAS, N, K, Y};
+        parallel_rows(w4a16_one_row, &c, M, nthreads);
+    }
+    free(R);
+    if (!XR_out) free(XR);
     return rc;
 }

@@ -28,12 +28,14 @@ MUTATIONS = [
     ("epilogue_operand", "float t = (float)ACC[m * N + n] * SX[m];", "float t = (float)ACC[m * N + n] * SW[n];"),
     ("dropped_bias", "float y = fmaf(t, SW[n], b);", "float y = fmaf(t, SW[n], 0.0f);"),
     ("bf16_truncation", "if (d_lo < d_hi) return toward_zero;", "return toward_zero;"),
-    ("dropped_k_term", "for (int64_t k = 0; k < c->K; ++k) acc +=", "for (int64_t k = 0; k < c->K - 1; ++k) acc +="),
+    ("dropped_k_term", "for (int64_t k = 0; k < c->K; ++k) acc += (int64_t)", "for (int64_t k = 0; k < c->K - 1; ++k) acc += (int64_t)"),
     ("clamp_6", "if (t > 7.0f) t = 7.0f;", "if (t > 6.0f) t = 6.0f;"),
     ("regular_base_sign", "{{-1, 1, 1, 1}, {1, -1, 1, 1},", "{{1, 1, 1, 1}, {1, -1, 1, 1},"),
     ("regular_block_sign", "(int8_t)(B[a][b] * H[(int64_t)i * g + j])", "(int8_t)((a == b ? 1 : B[a][b]) * H[(int64_t)i * g + j])"),
     ("regular_as_sylvester", "(regular ? oracle_regular_hadamard(g, H) : oracle_sylvester(g, H))",
      "oracle_sylvester(g, H)"),
+    ("w4a16_no_bf16_rounding", "XR[i] = oracle_f32_to_bf16(R[i]);", "XR[i] = (uint16_t)(oracle_f32_to_bf16(R[i]) ^ 1u);"),
+    ("w4a16_dropped_scale", "fmaf((float)acc, c->SW[n], b)", "fmaf((float)acc, 1.0f, b)"),
     ("first_group_only", "for (int64_t base = 0; base < c->K; base += g) {",
      "for (int64_t base = 0; base < c->K; base += g) { if (base) { for (int j = 0; j < g; ++j) "
      "r[base + j] = r[j]; continue; }"),

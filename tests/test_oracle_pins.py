@@ -433,3 +433,43 @@ def test_linear_thread_count_does_not_change_result():
     y1 = oracle.linear(inp["x"], qw, sw, inp["bias"][:256], 64, threads=1)
     y7 = oracle.linear(inp["x"], qw, sw, inp["bias"][:256], 64, threads=7)
     assert np.array_equal(y1, y7)
+
+
+# --------------------------------------------------------------------------
+# W4A16 variant (convrot-mlx README, "What is included": the W4A16 path)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [64, 256, 256 | oracle.REGULAR])
+def test_w4a16_exact_rational_small(g):
+    """Y = bf16(fmaf(fl32(sum_k bf16(r[m,k]) q[n,k]), sw[n], b[n])), recomputed
+    with exact rationals from the separately pinned rotation, numpy's bf16
+    rounding and the weight codes."""
+    K = 2 * (g & 0xFFFF)
+    x = synth.random_bf16((3, K), seed=31, outliers=2)
+    w = synth.random_bf16((5, K), seed=32, std=0.02)
+    b = synth.random_bf16((5,), seed=33, std=0.01)
+    qw, sw = oracle.prepare_weight(w, g)
+    y, xr = oracle.linear_w4a16(x, qw, sw, b, g, want_rotated=True)
+    xr_ref = synth.to_bf16_bits(oracle.rotate_rows(x, g))
+    assert np.array_equal(xr, xr_ref)
+    xv = synth.bf16_bits_to_f32(xr_ref)
+    bv = synth.bf16_bits_to_f32(b)
+    for m in range(3):
+        for n in range(5):
+            acc = sum(Fraction(float(xv[m, k])) * int(qw[n, k]) for k in range(K))
+            a32 = _round_to_f32_exact(acc)
+            yf = _round_to_f32_exact(Fraction(float(a32)) * Fraction(float(sw[n])) + Fraction(float(bv[n])))
+            assert y[m, n] == oracle.f32_to_bf16(np.array([yf]))[0]
+
+
+def test_w4a16_tracks_dense_product_better_than_w4a4():
+    """Only the weights are quantized, so W4A16 is closer to X W^T + b than W4A4."""
+    x = synth.random_bf16((16, 1024), seed=41, outliers=4)
+    w = synth.random_bf16((96, 1024), seed=42, std=0.02)
+    b = synth.random_bf16((96,), seed=43, std=0.01)
+    qw, sw = oracle.prepare_weight(w, 256)
+    ref = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+           + synth.bf16_bits_to_f32(b))
+    e16 = np.linalg.norm(synth.bf16_bits_to_f32(oracle.linear_w4a16(x, qw, sw, b, 256)) - ref) / np.linalg.norm(ref)
+    e4 = np.linalg.norm(synth.bf16_bits_to_f32(oracle.linear(x, qw, sw, b, 256)) - ref) / np.linalg.norm(ref)
+    assert e16 < e4 and e16 < 0.2
