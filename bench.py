@@ -68,7 +68,7 @@ def read_traffic(workload: str, gemm_ops_unit_launches: int):
         return None
 
 
-def cpu_baseline(inp, target_s: float, g: int):
+def cpu_baseline(inp, target_s: float, g: int, path: str = "w4a4"):
     """The oracle's linear on a bounded sample of the workload: as many rows of
     X as fit in about target_s seconds (the whole X, repeated, when one pass is
     shorter).  The weight is prepared by the oracle beforehand, untimed, like
@@ -81,7 +81,8 @@ def cpu_baseline(inp, target_s: float, g: int):
     log(f"cpu baseline: oracle weight preparation {time.perf_counter() - t0:.1f} s (untimed)")
     probe = min(wl.M, 8)
     t0 = time.perf_counter()
-    oracle.linear(inp["x"][:probe], qw, sw, inp["bias"], g, threads=threads)
+    run = oracle.linear_w4a16 if path == "w4a16" else oracle.linear
+    run(inp["x"][:probe], qw, sw, inp["bias"], g, threads=threads)
     dt = time.perf_counter() - t0
     rows = int(max(probe, min(wl.M, probe * target_s / max(dt, 1e-6))))
     reps = 1
@@ -89,12 +90,14 @@ def cpu_baseline(inp, target_s: float, g: int):
         reps = int(max(1, min(20, target_s / max(dt * wl.M / probe, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(reps):
-        oracle.linear(inp["x"][:rows], qw, sw, inp["bias"], g, threads=threads)
+        run(inp["x"][:rows], qw, sw, inp["bias"], g, threads=threads)
     dt = time.perf_counter() - t0
     tops = 2.0 * rows * reps * wl.N * wl.K / dt / 1e12
     return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {wl.M} rows of X x {reps} pass(es) against the full {wl.N}x{wl.K} weight "
-                      f"(complete linear: rotation, quantization, int64 dot products, epilogue), {dt:.2f} s"}
+                      + ("(W4A16 linear: rotation, bf16 rounding, binary64 dot products, epilogue)" if path == "w4a16"
+                         else "(complete linear: rotation, quantization, int64 dot products, epilogue)")
+                      + f", {dt:.2f} s"}
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -120,12 +123,14 @@ def main():
     ap.add_argument("--cold-bytes", type=float, default=512 * 2**20, help="total bytes of rotating buffer sets")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps one by one instead of as a graph")
+    ap.add_argument("--path", choices=("w4a4", "w4a16"), default="w4a4",
+                    help="w4a16: weight-only INT4 with bf16 rotated activations (M <= 32)")
     ap.add_argument("--rotation", choices=("sylvester", "regular"), default="sylvester",
                     help="Hadamard matrix of the rotation (the regular one adds sign flips and a permutation)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
@@ -163,7 +168,12 @@ def main():
     torch.cuda.synchronize()
     weight_prep_ms = ev0.elapsed_time(ev1) / 3
 
-    ws_bytes = binding.convrot_workspace_bytes(M, K, N, g)
+    w4a16 = args.path == "w4a16"
+    if w4a16 and M > 32:
+        log(f"--path w4a16 covers M <= 32 (the weight-bound regime); {wl.name} has M = {M}")
+        sys.exit(2)
+    ws_bytes = (binding.convrot_w4a16_workspace_bytes(M, K, g) if w4a16
+                else binding.convrot_workspace_bytes(M, K, N, g))
     set_bytes = X0.numel() * 2 + image0.numel() + sw0.numel() * 4 + B0.numel() * 2 + M * N * 2 + ws_bytes
     n_sets = int(min(64, max(1, -(-args.cold_bytes // set_bytes))))
     sets = []
@@ -175,9 +185,11 @@ def main():
     torch.cuda.synchronize()
     log(f"{n_sets} buffer sets of {set_bytes / 2**20:.1f} MiB each")
 
+    linear = binding.convrot_linear_w4a16 if w4a16 else binding.convrot_linear
+
     def step(i):
         s = sets[i % n_sets]
-        binding.convrot_linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
+        linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
 
     for i in range(args.warmup):
         step(i)
@@ -210,7 +222,8 @@ def main():
     # and over the same buffer rotation as the timed steps.  A bounded spin
     # kernel holds the stream while the host enqueues, so that no event
     # measures the host's launch latency.
-    single = binding.convrot_linear_kernel_count(M, K, N, g) == 1
+    # (the W4A16 path is timed as one unit: its bf16 activation rows and their product)
+    single = w4a16 or binding.convrot_linear_kernel_count(M, K, N, g) == 1
 
     def launch_avg_ms(n):
         """Average launch durations: (prep, gemm) for the two-kernel path,
@@ -227,7 +240,7 @@ def main():
             e[0].record()
             if single:
                 e[1].record()
-                binding.convrot_linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
+                linear(s["X"], s["image"], s["sw"], s["bias"], N, g, Y=s["Y"], workspace=s["ws"])
             else:
                 binding.convrot_prepare_activations(s["X"], g, s["ws"])
                 e[1].record()
@@ -249,7 +262,7 @@ def main():
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
     gbs = wl.bytes_alg / (ms_per_step * 1e-3) / 1e9
-    traffic = read_traffic(wl.name, 1)
+    traffic = None if w4a16 else read_traffic(wl.name, 1)
     # Roofline of the GEMM kernel: the matrix-core peak for compute-bound
     # shapes; for weight-streaming shapes (arithmetic intensity below the ridge
     # point) the HBM peak, with the kernel's algorithmic bytes: packed weight
@@ -267,7 +280,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds, g)
+        cpu = cpu_baseline(inp, args.cpu_seconds, g, args.path)
 
     rec = {
         "metric": METRIC,
@@ -280,9 +293,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "bf16" if w4a16 else "int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": wl.g, "rotation": args.rotation,
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": wl.g, "path": args.path,
+                   "rotation": args.rotation,
                    "x_kind": wl.x_kind,
                    "outlier_channels": wl.outlier_count, "cold_buffer_sets": n_sets,
                    "timed_as": "hip_graph" if graph is not None else "stream_launches"},

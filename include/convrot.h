@@ -161,6 +161,31 @@ int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_de
                    const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
                    void* stream);
 
+/* ---- W4A16 variant (weight-only INT4) ------------------------------------ */
+/* The weight-bandwidth-bound regime, M <= 32 (convrot-mlx README, "What is
+ * included": a W4A16 path beside W4A4).  The activation rows are rotated as
+ * in convrot_linear and rounded to bf16 (nearest even) instead of being
+ * quantized; the product runs against the same weight image:
+ *   Y[m][n] = bf16( fmaf(sum_k bf16(r[m][k]) * qw[n][k], sw[n], bias[n]) ),
+ * the sum accumulated in binary32 by the bf16 matrix cores (so Y is close to,
+ * not bit-identical with, the same formula summed exactly).
+ * Bytes of workspace for M x K: round_up(M * K * 2, 256); it receives the
+ * bf16 rotated rows, row-major [M][K].  M must be <= 32; otherwise, and for
+ * the shape rules of convrot_linear, CONVROT_EINVAL. */
+int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
+
+/* The checks convrot_linear_w4a16 performs.  Returns a status code. */
+int convrot_validate_linear_w4a16(const void* X_dev, int64_t M, int64_t K, const void* image_dev,
+                                  const float* sw_dev, const void* bias_dev, int64_t N, int g, const void* Y_dev,
+                                  const void* workspace_dev, size_t ws_bytes);
+
+/* The W4A16 linear: arguments as convrot_linear (image_dev and sw_dev from
+ * convrot_prepare_weight with the same g), workspace of at least
+ * convrot_w4a16_workspace_bytes(M, K, g).  Two kernels on the stream. */
+int convrot_linear_w4a16(const void* X_dev, int64_t M, int64_t K, const void* image_dev, const float* sw_dev,
+                         const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
+                         void* stream);
+
 /* The two halves of convrot_linear, for callers that want to time or reuse
  * them separately.  convrot_prepare_activations writes the activation codes
  * and scales of X into the workspace (rotation, row absmax, quantization);

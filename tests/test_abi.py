@@ -128,6 +128,30 @@ def test_validate_linear_statuses():
     assert _validate_linear(M=-1) == B.CONVROT_EINVAL
 
 
+def test_w4a16_sizes_and_statuses():
+    assert B.convrot_w4a16_workspace_bytes(1, 3072, 256) == 6144
+    assert B.convrot_w4a16_workspace_bytes(32, 12288, 256) == 32 * 12288 * 2
+    assert B.convrot_w4a16_workspace_bytes(3, 192, 64) == 1280          # 1152 rounded up to 256
+    assert B.convrot_w4a16_workspace_bytes(0, 1024, 256) == 0
+    with pytest.raises(B.ConvRotError):
+        B.convrot_w4a16_workspace_bytes(33, 1024, 256)                    # M > 32: the W4A4 path's regime
+    ok = B.convrot_w4a16_workspace_bytes(16, 1024, 256)
+
+    def v(**over):
+        args = dict(X=4096, M=16, K=1024, image=8192, sw=16384, bias=0, N=1024, g=256, Y=32768, ws=65536,
+                    ws_bytes=ok)
+        args.update(over)
+        return B.convrot_validate_linear_w4a16(*[args[k] for k in ("X", "M", "K", "image", "sw", "bias", "N", "g",
+                                                                     "Y", "ws", "ws_bytes")])
+
+    assert v() == B.CONVROT_OK
+    assert v(M=33) == B.CONVROT_EINVAL
+    assert v(g=256 | B.CONVROT_REGULAR_HADAMARD) == B.CONVROT_OK
+    assert v(ws_bytes=ok - 1) == B.CONVROT_EWORKSPACE
+    assert v(X=4100) == B.CONVROT_EINVAL
+    assert v(M=0, X=0, Y=0) == B.CONVROT_OK
+
+
 def test_validate_weight_statuses():
     assert B.convrot_validate_weight(4096, 1024, 1024, 256, 8192, 16384) == B.CONVROT_OK
     assert B.convrot_validate_weight(4096, 1024, 1024, 32, 8192, 16384) == B.CONVROT_EINVAL

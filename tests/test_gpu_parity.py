@@ -254,6 +254,36 @@ def test_linear_rejects_bad_arguments(gpu):
     assert e.value.status == gpu.CONVROT_EWORKSPACE
 
 
+# --------------------------------------------------------------------------
+# W4A16 variant (M <= 32)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 96, 256, 256), (4, 5000, 3072, 256), (16, 12288, 3072, 256),
+                                     (17, 300, 1024, 64), (32, 1000, 2048, 256 | REG), (5, 70, 192, 64),
+                                     (3, 17000, 512, 64 | REG), (1, 12288, 3072, 256)])
+def test_linear_w4a16(gpu, M, N, K, g):
+    """The bf16 rotated rows are bit-exact (one rounding of the exact
+    rotation); Y is within the path's tolerance of the oracle, whose sum is
+    exact where the matrix cores accumulate in binary32."""
+    import torch
+    x = synth.random_bf16((M, K), seed=M * 3 + K, outliers=3)
+    w = synth.random_bf16((N, K), seed=N + 5, std=0.02)
+    b = synth.random_bf16((N,), seed=N + 6, std=0.01)
+    oq_w, osw = oracle.prepare_weight(w, g)
+    y_or, xr_or = oracle.linear_w4a16(x, oq_w, osw, b, g, want_rotated=True)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), g)
+    ws = torch.zeros(gpu.convrot_w4a16_workspace_bytes(M, K, g), dtype=torch.uint8, device="cuda")
+    Y = gpu.convrot_linear_w4a16(_dev(x), image, sw, _dev(b), N, g, workspace=ws)
+    torch.cuda.synchronize()
+    xr = ws[: M * K * 2].cpu().numpy().view(np.uint16).reshape(M, K)
+    assert np.array_equal(xr, xr_or), "bf16 rotated rows differ"
+    gy = synth.bf16_bits_to_f32(_host_bits(Y)).astype(np.float64)
+    oy = synth.bf16_bits_to_f32(y_or).astype(np.float64)
+    err = np.abs(gy - oy).max() / np.abs(oy).max()
+    assert err <= 1e-2, f"max |dY| / max |Y| = {err:.3g}"
+    assert np.mean(gy == oy) > 0.5          # most values round to the same bf16
+
+
 FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_mlp_down_m1536_k12288_n3072",
         "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
 

@@ -58,6 +58,9 @@ _SIGNATURES = {
     "convrot_prepare_activations": ([_P, _I64, _I64, _I, _P, _SZ, _P], _I),
     "convrot_gemm": ([_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P], _I),
     "convrot_prepare_rows": ([_P, _I64, _I64, _I, _P, _P, _P, _P], _I),
+    "convrot_w4a16_workspace_bytes": ([_I64, _I64, _I, _P], _I),
+    "convrot_validate_linear_w4a16": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
+    "convrot_linear_w4a16": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ, _P], _I),
     "convrot_gemm_i32": ([_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P], _I),
     "convrot_host_pack_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_unpack_nk": ([_P, _I64, _I64, _P], _I),
@@ -333,3 +336,35 @@ def convrot_host_act_image_to_codes(image, M: int, K: int) -> np.ndarray:
     out = np.empty((M, K), np.int8)
     _call("convrot_host_act_image_to_codes", _hp(p), M, K, _hp(out))
     return out
+
+
+# --------------------------------------------------------------------------
+# W4A16 variant (M <= 32)
+# --------------------------------------------------------------------------
+
+def convrot_w4a16_workspace_bytes(M: int, K: int, g: int) -> int:
+    out = ctypes.c_size_t()
+    _call("convrot_w4a16_workspace_bytes", M, K, g, ctypes.byref(out))
+    return out.value
+
+
+def convrot_validate_linear_w4a16(X_ptr, M, K, image_ptr, sw_ptr, bias_ptr, N, g, Y_ptr, ws_ptr, ws_bytes) -> int:
+    """Raw pointer values (ints); returns the status code."""
+    return load().convrot_validate_linear_w4a16(X_ptr, M, K, image_ptr, sw_ptr, bias_ptr, N, g, Y_ptr, ws_ptr,
+                                                ws_bytes)
+
+
+def convrot_linear_w4a16(X, image, sw, bias, N: int, g: int, Y=None, workspace=None, stream=None):
+    """Y = X W^T + bias with INT4 weights and bf16 rotated activations (M <= 32).
+    The workspace receives the bf16 rotated rows [M, K]."""
+    import torch
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_w4a16_workspace_bytes(M, K, g), 1), dtype=torch.uint8, device=X.device)
+    bias_p = None if bias is None else _dev(bias, torch.bfloat16, "bias")
+    _call("convrot_linear_w4a16", _dev(X, torch.bfloat16, "X"), M, K, _dev(image, torch.uint8, "image"),
+          _dev(sw, torch.float32, "sw"), bias_p, N, g, _dev(Y, torch.bfloat16, "Y"),
+          _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return Y

@@ -78,6 +78,7 @@ GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, cons
     a.out = Y;
     a.M = M;
     a.N = N;
+    a.K = K;
     a.MT = (int)(round_up(M, kTileRows) / kTileRows);
     a.NT = (int)(round_up(N, kTileRows) / kTileRows);
     a.KB = (int)(round_up(K, kTileK) / kTileK);
@@ -191,6 +192,29 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
     }
     if ((rc = enqueue_prepare_activations(X, M, K, g, ws, s))) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, ws, M, K, image, sw, bias, N, Y, s);
+}
+
+int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
+                         int64_t N, int g, void* Y, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = convrot_validate_linear_w4a16(X, M, K, image, sw, bias, N, g, Y, ws, ws_bytes);
+    if (rc || M == 0 || N == 0) return rc;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = as_stream(stream);
+    // 1. the rotated activation rows, rounded to bf16, into the workspace
+    PrepArgs a{};
+    a.X = (const uint16_t*)X;
+    a.rows = M;
+    a.rows_pad = M;
+    a.K = K;
+    a.K_pad = K;
+    a.out = (uint8_t*)ws;
+    launch_prep(g, OUT_ROTATED_BF16, a, s);
+    if ((rc = launched())) return rc;
+    // 2. their product with the weight image, scale and bias
+    GemmArgs ga = gemm_args(ws, M, K, image, sw, bias, N, Y);
+    launch_w4a16(ga, (const uint16_t*)ws, s);
+    return launched();
 }
 
 int convrot_prepare_rows(const void* X, int64_t rows, int64_t K, int g, int8_t* codes, float* scales,

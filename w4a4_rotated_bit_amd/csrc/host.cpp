@@ -116,6 +116,31 @@ int convrot_validate_linear(const void* X, int64_t M, int64_t K, const void* ima
     return CONVROT_OK;
 }
 
+int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes)
+{
+    if (!bytes) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, g);
+    if (rc) return rc;
+    if (M > kW4A16MaxRows) return CONVROT_EINVAL;
+    *bytes = (size_t)round_up(M * K * 2, 256);
+    return CONVROT_OK;
+}
+
+int convrot_validate_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image, const float* sw,
+                                  const void* bias, int64_t N, int g, const void* Y, const void* ws, size_t ws_bytes)
+{
+    size_t need = 0;
+    int rc = convrot_w4a16_workspace_bytes(M, K, g, &need);
+    if (rc) return rc;
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    if (M == 0 || N == 0) return CONVROT_OK;
+    if (!X || !image || !sw || !Y || !ws) return CONVROT_EINVAL;
+    if (!aligned(X, 16) || !aligned(image, 16) || !aligned(Y, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
+    if (!aligned(sw, 4) || (bias && !aligned(bias, 2))) return CONVROT_EINVAL;
+    if (ws_bytes < need) return CONVROT_EWORKSPACE;
+    return CONVROT_OK;
+}
+
 // ---- host layout tools ---------------------------------------------------
 
 static inline uint8_t lo4(int8_t q) { return (uint8_t)q & 0x0F; }

@@ -5,7 +5,7 @@
 
 namespace convrot {
 
-enum PrepOut { OUT_IMAGE = 0, OUT_ROWMAJOR = 2, OUT_NK = 3, OUT_LDS = 4 };
+enum PrepOut { OUT_IMAGE = 0, OUT_ROWMAJOR = 2, OUT_NK = 3, OUT_LDS = 4, OUT_ROTATED_BF16 = 5 };
 enum GemmOut { GEMM_OUT_BF16 = 0, GEMM_OUT_I32 = 1 };
 
 struct PrepArgs {
@@ -29,6 +29,7 @@ struct GemmArgs {
     const uint16_t* bias;  // bf16 [N] or nullptr
     void* out;           // bf16 or int32 [M][N]
     int64_t M, N;
+    int64_t K;           // reduction length (the W4A16 activation rows are K long)
     int MT, NT, KB;      // 32-row tiles, 32-column tiles, 128-K blocks
     int shape;           // block tile shape, tiles and K splits (gemm_plan)
     int tiles_m, tiles_n;
@@ -40,6 +41,9 @@ struct GemmArgs {
 // g: group size, optionally with kRegularHadamard (the rotation matrix)
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
+// W4A16 product for M <= 32: bf16 rotated activation rows xr [M][K] times the
+// weight image (act, sx and the split fields of a are unused).
+void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s);
 // Whole linear in one launch when single_kernel_linear(M, K, g) holds; see
 // kernels.hip.
 void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s);

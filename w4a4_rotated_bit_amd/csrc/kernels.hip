@@ -357,6 +357,20 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next row rewrites the region
     __builtin_amdgcn_wave_barrier();
 
+    // W4A16: the rotated row, rounded to bf16 (nearest even), row-major; no
+    // scale and no codes.  Rows are K values long, K % 64 == 0, so every
+    // lane's P values are whole 16-byte words.
+    if constexpr (MODE == OUT_ROTATED_BF16) {
+        if (has_data) {
+            uint4* dst = (uint4*)(a.out + ((size_t)row * a.K + k0) * 2);
+#pragma unroll
+            for (int c = 0; c < P / 8; ++c)
+                dst[c] = make_uint4(pack_bf16x2(r[8 * c], r[8 * c + 1]), pack_bf16x2(r[8 * c + 2], r[8 * c + 3]),
+                                    pack_bf16x2(r[8 * c + 4], r[8 * c + 5]), pack_bf16x2(r[8 * c + 6], r[8 * c + 7]));
+        }
+        return;
+    }
+
     // ---- row absmax over the team ----
     float lane_max = 0.0f;
 #pragma unroll
@@ -1162,6 +1176,143 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// w4a16_kernel: weight-only INT4 product for M <= 32 (MH 16-row halves).
+//
+// Same work split as skinny_kernel -- one workgroup per 16-column strip, its
+// four waves splitting K, weight chunks streamed into registers -- but the
+// activations are the bf16 rotated rows (no activation codes) and the
+// product runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Lane quad
+// q holds 16-byte chunk q of its weight row in a 128-K unit: four words, word
+// j being the eight consecutive codes from k = 32 (2 (q / 2) + j / 2) +
+// 16 (q % 2) + 8 (j % 2) (the image layout), low nibbles first.  Word j of
+// every quad feeds MFMA j, and the activation operand of lane (r, q) is the
+// eight bf16 values of row r at the same k: both operands agree on k, so the
+// sum over the four MFMAs is the dot product over the unit.  Codes become
+// bf16 exactly (signed bit-field extract, convert, pack).  The four partial
+// tiles are summed through LDS in wave order and the epilogue is
+// fmaf(acc, sw[n], bias[n]) rounded to bf16.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// eight INT4 codes (low nibbles k..k+3, high nibbles k+4..k+7) -> bf16 in k order
+__device__ inline bf16x8_t dequant8_bf16(uint32_t w)
+{
+    float f[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // the builtin's result type is unsigned: convert the sign-extended bits as int
+        f[b] = (float)(int)__builtin_amdgcn_sbfe((int)w, 8 * b, 4);
+        f[4 + b] = (float)(int)__builtin_amdgcn_sbfe((int)w, 8 * b + 4, 4);
+    }
+    const uint4 p = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                               pack_bf16x2(f[6], f[7]));
+    return __builtin_bit_cast(bf16x8_t, p);
+}
+
+template <int MH, int BATCH>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void w4a16_kernel(GemmArgs a, const uint16_t* xr)
+{
+    __shared__ __attribute__((aligned(16))) float red[kSkinnyWaves - 1][MH][4][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int strip = blockIdx.x;                   // output columns 16 strip .. 16 strip + 15
+    const int nt = strip >> 1, half = strip & 1;
+    const int KB = a.KB;
+    const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int kb0 = wave * per, kb1 = min(KB, kb0 + per);
+    const int wrow = 16 * half + r16;
+    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + wrow * 64 + ((q ^ row_swizzle(wrow)) * 16);
+    int kst[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kst[j] = 32 * (2 * (q >> 1) + (j >> 1)) + 16 * (q & 1) + 8 * (j & 1);
+    const uint16_t* xrow[MH];
+    bool xok[MH];
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh) {
+        const int64_t m = 16 * mh + r16;
+        xok[mh] = m < a.M;
+        xrow[mh] = xr + (xok[mh] ? m : 0) * a.K;
+    }
+
+    f32x4_t acc[MH];
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh) acc[mh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = kb0; kb < kb1; kb += BATCH) {
+        uint4 wq[BATCH];
+        uint4 xa[BATCH][4][MH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const bool in = kb + u < kb1;
+            wq[u] = in ? load_stream16(wbase + (size_t)(kb + u) * kUnitBytes) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mh = 0; mh < MH; ++mh) {
+                    const int64_t k = (int64_t)(kb + u) * kTileK + kst[j];
+                    xa[u][j][mh] = (in && xok[mh] && k < a.K) ? *(const uint4*)(xrow[mh] + k) : make_uint4(0, 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            if (kb + u >= kb1) break;
+            const uint32_t ww[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8_t wf = dequant8_bf16(ww[j]);
+#pragma unroll
+                for (int mh = 0; mh < MH; ++mh)
+                    acc[mh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8_t, xa[u][j][mh]),
+                                                                      acc[mh], 0, 0, 0);
+            }
+        }
+    }
+
+    // sum the partial tiles of the waves, in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wave - 1][mh][j][lane] = acc[mh][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mh][j] += red[w][mh][j][lane];
+
+    // lane holds, per half mh, output row m = 16 mh + r16 and the four
+    // consecutive columns n = 16 strip + 4 q + (0..3)
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    if (n0 >= a.N) return;
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh) {
+        const int64_t m = 16 * mh + r16;
+        if (m >= a.M) continue;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
+            const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
+            y[j] = __builtin_fmaf(acc[mh][j], a.sw[n], bn);
+        }
+        const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
+        uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
+        if ((a.N % 4) == 0) {
+            *(uint2*)dst = make_uint2(p01, p23);
+        } else {
+            const uint16_t yb[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+            for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = yb[j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // small_m_kernel: the whole linear in one launch for M <= kSmallRows, when a
 // row's prep team is whole waves (64 <= K / P <= 256).
 //
@@ -1448,6 +1599,7 @@ void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
     switch (mode) {
         case OUT_IMAGE: launch_prep_mode<OUT_IMAGE>(g, a, s); break;
         case OUT_NK: launch_prep_mode<OUT_NK>(g, a, s); break;
+        case OUT_ROTATED_BF16: launch_prep_mode<OUT_ROTATED_BF16>(g, a, s); break;
         default: launch_prep_mode<OUT_ROWMAJOR>(g, a, s); break;
     }
 }
@@ -1524,6 +1676,15 @@ void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s)
         reg ? launch_small_m_g<256, true>(sw, a, p, grid, s) : launch_small_m_g<256, false>(sw, a, p, grid, s);
     else
         reg ? launch_small_m_g<64, true>(sw, a, p, grid, s) : launch_small_m_g<64, false>(sw, a, p, grid, s);
+}
+
+void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.N + 15) / 16)), block(kSkinnyWaves * 64);
+    if (a.M <= 16)
+        hipLaunchKernelGGL((w4a16_kernel<1, 6>), grid, block, 0, s, a, xr);
+    else
+        hipLaunchKernelGGL((w4a16_kernel<2, 3>), grid, block, 0, s, a, xr);
 }
 
 void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,

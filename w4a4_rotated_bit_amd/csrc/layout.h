@@ -75,6 +75,10 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
 // with the regular Hadamard matrix instead of the Sylvester one.
 constexpr int kRegularHadamard = 0x10000;
 
+// ---- W4A16 -----------------------------------------------------------------
+// The weight-only INT4 variant is the weight-bandwidth-bound regime: M <= 32.
+constexpr int64_t kW4A16MaxRows = 32;
+
 // ---- GEMM plan -------------------------------------------------------------
 // The GEMM covers the output with one of four block tiles: shape 0 is
 // 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192, shape 3 is
