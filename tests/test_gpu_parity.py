@@ -325,3 +325,36 @@ def test_linear_full_size_sampled(gpu, name):
     rows_ok = np.all(gq_x == oq_x, axis=1) & (n_w == 0)
     compare_y(gy[np.ix_(rows, cols)], y_or, rows_ok)
     print(f"{name}: code mismatches x={n_x} w={n_w}")
+
+
+# --------------------------------------------------------------------------
+# ConvRotLinear module: leading dimensions, both paths
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lead,K,N,rotation,path", [((2, 7), 512, 200, "sylvester", "w4a4"),
+                                                     ((3, 40), 1024, 96, "regular", "w4a4"),
+                                                     ((1, 4), 256, 130, "regular", "w4a16")])
+def test_module_matches_the_c_abi(gpu, lead, K, N, rotation, path):
+    import torch
+    from w4a4_rotated_bit_amd.module import ConvRotLinear
+    torch.manual_seed(0)
+    lin = torch.nn.Linear(K, N, bias=True).cuda().to(torch.bfloat16)
+    mod = ConvRotLinear.from_linear(lin, 256, rotation, path)
+    x = torch.randn(*lead, K, device="cuda").to(torch.bfloat16)
+    y = mod(x)
+    assert y.shape == (*lead, N) and y.dtype == torch.bfloat16
+    g = 256 | (REG if rotation == "regular" else 0)
+    x2 = x.reshape(-1, K).contiguous()
+    fn = gpu.convrot_linear_w4a16 if path == "w4a16" else gpu.convrot_linear
+    ref = fn(x2, mod.image, mod.sw, mod.bias, N, g)
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(-1, N), ref)
+    # and the oracle agrees on the linear as a whole
+    xb = _host_bits(x2)
+    wb = _host_bits(lin.weight.detach().contiguous())
+    bb = _host_bits(lin.bias.detach().contiguous())
+    oq_w, osw = oracle.prepare_weight(wb, g)
+    y_or = oracle.linear_w4a16(xb, oq_w, osw, bb, g) if path == "w4a16" else oracle.linear(xb, oq_w, osw, bb, g)
+    gy = synth.bf16_bits_to_f32(_host_bits(ref)).astype(np.float64)
+    oy = synth.bf16_bits_to_f32(y_or).astype(np.float64)
+    assert np.abs(gy - oy).max() <= 1e-2 * np.abs(oy).max()
