@@ -132,6 +132,12 @@ def f32_to_bf16(values) -> np.ndarray:
 REGULAR = 0x10000
 
 
+def rotated_width(K: int, g: int) -> int:
+    """Rows are zero-padded to a whole number of groups: K rounded up to g."""
+    gs = g & ~REGULAR
+    return -(-K // gs) * gs
+
+
 def sylvester(g: int) -> np.ndarray:
     """Integer Sylvester Hadamard matrix H_g (entries +-1), natural order."""
     H = np.empty((g, g), dtype=np.int8)
@@ -151,7 +157,7 @@ def rotate_rows(x_bf16, g: int, threads: int | None = None) -> np.ndarray:
     binary32; H is Sylvester, or regular when g carries REGULAR."""
     x = _c(x_bf16, np.uint16)
     rows, K = x.shape
-    r = np.empty((rows, K), dtype=np.float32)
+    r = np.empty((rows, rotated_width(K, g)), dtype=np.float32)
     _check(_load().oracle_rotate_rows(_ptr(x), rows, K, int(g), _ptr(r), threads or default_threads()),
            "rotate_rows")
     return r
@@ -175,9 +181,10 @@ def prepare_rows(x_bf16, g: int, threads: int | None = None, want_rotated: bool 
     binary32 rotated values."""
     x = _c(x_bf16, np.uint16)
     rows, K = x.shape
-    q = np.empty((rows, K), dtype=np.int8)
+    Kr = rotated_width(K, g)
+    q = np.empty((rows, Kr), dtype=np.int8)
     s = np.empty((rows,), dtype=np.float32)
-    r = np.empty((rows, K), dtype=np.float32) if want_rotated else None
+    r = np.empty((rows, Kr), dtype=np.float32) if want_rotated else None
     _check(_load().oracle_prepare_rows(_ptr(x), rows, K, int(g), _ptr(q), _ptr(s), _ptr(r),
                                        threads or default_threads()), "prepare_rows")
     return (q, s, r) if want_rotated else (q, s)
@@ -255,10 +262,12 @@ def linear(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, 
     M, K = x.shape
     qw = _c(qw_codes, np.int8)
     N = qw.shape[0]
+    if qw.shape[1] != rotated_width(K, g):
+        raise ValueError("weight codes must be K rounded up to g wide")
     swa = _c(sw, np.float32)
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     y = np.empty((M, N), dtype=np.uint16)
-    qx = np.empty((M, K), dtype=np.int8) if want_parts else None
+    qx = np.empty((M, rotated_width(K, g)), dtype=np.int8) if want_parts else None
     sx = np.empty((M,), dtype=np.float32) if want_parts else None
     acc = np.empty((M, N), dtype=np.int32) if want_parts else None
     rc = _load().oracle_linear(_ptr(x), M, K, _ptr(qw), _ptr(swa), _ptr(b), N, int(g), _ptr(y), _ptr(qx),
@@ -279,10 +288,12 @@ def linear_w4a16(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = 
     M, K = x.shape
     qw = _c(qw_codes, np.int8)
     N = qw.shape[0]
+    if qw.shape[1] != rotated_width(K, g):
+        raise ValueError("weight codes must be K rounded up to g wide")
     swa = _c(sw, np.float32)
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     y = np.empty((M, N), dtype=np.uint16)
-    xr = np.empty((M, K), dtype=np.uint16) if want_rotated else None
+    xr = np.empty((M, rotated_width(K, g)), dtype=np.uint16) if want_rotated else None
     _check(_load().oracle_linear_w4a16(_ptr(x), M, K, _ptr(qw), _ptr(swa), _ptr(b), N, int(g), _ptr(y), _ptr(xr),
                                        threads or default_threads()), "linear_w4a16")
     return (y, xr) if want_rotated else y

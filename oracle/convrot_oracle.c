@@ -45,6 +45,12 @@
  *   the same INT4 weight codes; y = fmaf(fl32(sum), sw[n], bias[n]) to bf16.
  *        [convrot-mlx README, "What is included": the W4A16 path beside W4A4]
  *
+ * Row length: when K is not a multiple of g the rows are padded with zeros to
+ * K_rot = round_up(K, g) before the rotation, and every later step works on
+ * the K_rot rotated values (the padded X and W rows give the same X W^T).
+ *        [comfy-quants issue, section 1: K = G N0, "or after padding the last
+ *         block if necessary"]
+ *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes):
  *   - rotation is computed in double as a dense g x g product per group and
@@ -212,7 +218,8 @@ int oracle_regular_hadamard(int g, int8_t* H)
 
 struct rot_ctx {
     const uint16_t* X;
-    int64_t K;
+    int64_t K_in; /* elements per input row */
+    int64_t K;    /* rotated row length: K_in rounded up to g */
     int g;
     const int8_t* H;
     double inv_norm; /* 1 / sqrt(g): 1/8 or 1/16, exact in double */
@@ -222,34 +229,44 @@ struct rot_ctx {
 static void rotate_one_row(void* p, int64_t m)
 {
     struct rot_ctx* c = (struct rot_ctx*)p;
-    const uint16_t* x = c->X + m * c->K;
+    const uint16_t* x = c->X + m * c->K_in;
     float* r = c->R + m * c->K;
     const int g = c->g;
     for (int64_t base = 0; base < c->K; base += g) {
         for (int j = 0; j < g; ++j) {
             double acc = 0.0;
-            for (int t = 0; t < g; ++t)
-                acc += (double)oracle_bf16_to_f32(x[base + t]) * (double)c->H[(int64_t)t * g + j];
+            for (int t = 0; t < g; ++t) {
+                const double v = base + t < c->K_in ? (double)oracle_bf16_to_f32(x[base + t]) : 0.0; /* zero pad */
+                acc += v * (double)c->H[(int64_t)t * g + j];
+            }
             r[base + j] = (float)(acc * c->inv_norm); /* one rounding to binary32 */
         }
     }
 }
 
-/* X: bf16 bits [rows][K]; R: binary32 [rows][K].  g_arg is the group size,
- * optionally with ORACLE_REGULAR.  Returns 0, or -1 on bad arguments (g not a
- * power of two -- of four for the regular matrix --, K not a multiple of g). */
+/* Rotated row length for K input values and group argument g_arg. */
+int64_t oracle_rotated_width(int64_t K, int g_arg)
+{
+    const int64_t g = g_arg & ~ORACLE_REGULAR;
+    return g > 0 ? (K + g - 1) / g * g : K;
+}
+
+/* X: bf16 bits [rows][K]; R: binary32 [rows][K_rot], K_rot = K rounded up to
+ * g.  g_arg is the group size, optionally with ORACLE_REGULAR.  Returns 0, or
+ * -1 on bad arguments (g not a power of two -- of four for the regular
+ * matrix). */
 int oracle_rotate_rows(const uint16_t* X, int64_t rows, int64_t K, int g_arg, float* R, int nthreads)
 {
     const int regular = (g_arg & ORACLE_REGULAR) != 0;
     const int g = g_arg & ~ORACLE_REGULAR;
-    if (g < 2 || (g & (g - 1)) != 0 || g > 4096 || K <= 0 || K % g != 0 || rows < 0) return -1;
+    if (g < 2 || (g & (g - 1)) != 0 || g > 4096 || K <= 0 || rows < 0) return -1;
     int8_t* H = (int8_t*)malloc((size_t)g * g);
     if (!H) return -2;
     if ((regular ? oracle_regular_hadamard(g, H) : oracle_sylvester(g, H)) != 0) {
         free(H);
         return -1;
     }
-    struct rot_ctx c = {X, K, g, H, 1.0 / sqrt((double)g), R};
+    struct rot_ctx c = {X, K, oracle_rotated_width(K, g_arg), g, H, 1.0 / sqrt((double)g), R};
     parallel_rows(rotate_one_row, &c, rows, nthreads);
     free(H);
     return 0;
@@ -300,17 +317,19 @@ int oracle_quantize_rows(const float* R, int64_t rows, int64_t K, int8_t* Q, flo
 }
 
 /* Rotate + quantize: the whole per-row preparation (used for both the
- * activation rows X and the weight rows W). */
+ * activation rows X and the weight rows W).  X is [rows][K]; Q and R are
+ * [rows][K_rot]. */
 int oracle_prepare_rows(const uint16_t* X, int64_t rows, int64_t K, int g, int8_t* Q, float* S,
                         float* R_or_null, int nthreads)
 {
+    const int64_t Kr = oracle_rotated_width(K, g);
     float* R = R_or_null;
     if (!R) {
-        R = (float*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)K * sizeof(float));
+        R = (float*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)Kr * sizeof(float));
         if (!R) return -2;
     }
     int rc = oracle_rotate_rows(X, rows, K, g, R, nthreads);
-    if (rc == 0) rc = oracle_quantize_rows(R, rows, K, Q, S, nthreads);
+    if (rc == 0) rc = oracle_quantize_rows(R, rows, Kr, Q, S, nthreads);
     if (!R_or_null) free(R);
     return rc;
 }
@@ -437,21 +456,23 @@ void oracle_epilogue(const int32_t* ACC, const float* SX, const float* SW, const
 /* ------------------------------------------------------------------------ */
 
 /* X: bf16 [M][K]; QW: int8 codes [N][K]; SW: [N]; BIAS: bf16 [N] or NULL.
- * Optional outputs QX_out [M][K], SX_out [M], ACC_out [M][N] may be NULL.
- * Returns 0 on success. */
+ * Optional outputs QX_out [M][K_rot], SX_out [M], ACC_out [M][N] may be NULL.
+ * QW is [N][K_rot] (weight rows prepared with the same g).  Returns 0 on
+ * success. */
 int oracle_linear(const uint16_t* X, int64_t M, int64_t K, const int8_t* QW, const float* SW,
                   const uint16_t* BIAS, int64_t N, int g, uint16_t* Y, int8_t* QX_out, float* SX_out,
                   int32_t* ACC_out, int nthreads)
 {
     if (M < 0 || N < 0 || K <= 0) return -1;
-    size_t mk = (size_t)(M > 0 ? M : 1) * (size_t)K;
+    const int64_t Kr = oracle_rotated_width(K, g);
+    size_t mk = (size_t)(M > 0 ? M : 1) * (size_t)Kr;
     size_t mn = (size_t)(M > 0 ? M : 1) * (size_t)(N > 0 ? N : 1);
     int8_t* QX = QX_out ? QX_out : (int8_t*)malloc(mk);
     float* SX = SX_out ? SX_out : (float*)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
     int32_t* ACC = ACC_out ? ACC_out : (int32_t*)malloc(mn * sizeof(int32_t));
     int rc = (!QX || !SX || !ACC) ? -2 : 0;
     if (rc == 0) rc = oracle_prepare_rows(X, M, K, g, QX, SX, NULL, nthreads);
-    if (rc == 0) rc = oracle_gemm_i32(QX, QW, M, N, K, ACC, nthreads);
+    if (rc == 0) rc = oracle_gemm_i32(QX, QW, M, N, Kr, ACC, nthreads);
     if (rc == 0) oracle_epilogue(ACC, SX, SW, BIAS, M, N, Y);
     if (!QX_out) free(QX);
     if (!SX_out) free(SX);
@@ -485,21 +506,22 @@ static void w4a16_one_row(void* p, int64_t m)
     }
 }
 
-/* X: bf16 [M][K]; QW: int8 codes [N][K]; SW: [N]; BIAS: bf16 [N] or NULL;
- * Y: bf16 [M][N]; XR_out (optional): the bf16 rotated activations [M][K].
+/* X: bf16 [M][K]; QW: int8 codes [N][K_rot]; SW: [N]; BIAS: bf16 [N] or NULL;
+ * Y: bf16 [M][N]; XR_out (optional): the bf16 rotated activations [M][K_rot].
  * g as for oracle_rotate_rows.  Returns 0 on success. */
 int oracle_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, const int8_t* QW, const float* SW,
                         const uint16_t* BIAS, int64_t N, int g, uint16_t* Y, uint16_t* XR_out, int nthreads)
 {
     if (M < 0 || N < 0 || K <= 0) return -1;
-    size_t mk = (size_t)(M > 0 ? M : 1) * (size_t)K;
+    const int64_t Kr = oracle_rotated_width(K, g);
+    size_t mk = (size_t)(M > 0 ? M : 1) * (size_t)Kr;
     float* R = (float*)malloc(mk * sizeof(float));
     uint16_t* XR = XR_out ? XR_out : (uint16_t*)malloc(mk * sizeof(uint16_t));
     int rc = (!R || !XR) ? -2 : 0;
     if (rc == 0) rc = oracle_rotate_rows(X, M, K, g, R, nthreads);
     if (rc == 0) {
-        for (size_t i = 0; i < (size_t)M * (size_t)K; ++i) XR[i] = oracle_f32_to_bf16(R[i]);
-        struct w4a16_ctx c = {XR, QW, SW, BIAS, N, K, Y};
+        for (size_t i = 0; i < (size_t)M * (size_t)Kr; ++i) XR[i] = oracle_f32_to_bf16(R[i]);
+        struct w4a16_ctx c = {XR, QW, SW, BIAS, N, Kr, Y};
         parallel_rows(w4a16_one_row, &c, M, nthreads);
     }
     free(R);

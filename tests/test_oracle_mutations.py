@@ -21,8 +21,8 @@ MUTATIONS = [
     ("scale_div6", "float s = a / 7.0f;", "float s = a / 6.0f;"),
     ("wrong_norm", "1.0 / sqrt((double)g)", "1.0 / (double)g"),
     ("h_sign", "H[(int64_t)(i + n) * g + (j + n)] = (int8_t)-v;", "H[(int64_t)(i + n) * g + (j + n)] = v;"),
-    ("h_index", "x[base + t]) * (double)c->H[(int64_t)t * g + j]",
-     "x[base + t]) * (double)c->H[(int64_t)j * g + ((t + 1) % g)]"),
+    ("h_index", "acc += v * (double)c->H[(int64_t)t * g + j];",
+     "acc += v * (double)c->H[(int64_t)j * g + ((t + 1) % g)];"),
     ("nibble_order", "(uint8_t)(nibble(Q[n * K + 2 * j]) | (nibble(Q[n * K + 2 * j + 1]) << 4))",
      "(uint8_t)(nibble(Q[n * K + 2 * j + 1]) | (nibble(Q[n * K + 2 * j]) << 4))"),
     ("epilogue_operand", "float t = (float)ACC[m * N + n] * SX[m];", "float t = (float)ACC[m * N + n] * SW[n];"),
@@ -36,6 +36,8 @@ MUTATIONS = [
      "oracle_sylvester(g, H)"),
     ("w4a16_no_bf16_rounding", "XR[i] = oracle_f32_to_bf16(R[i]);", "XR[i] = (uint16_t)(oracle_f32_to_bf16(R[i]) ^ 1u);"),
     ("w4a16_dropped_scale", "fmaf((float)acc, c->SW[n], b)", "fmaf((float)acc, 1.0f, b)"),
+    ("nonzero_padding", "base + t < c->K_in ? (double)oracle_bf16_to_f32(x[base + t]) : 0.0",
+     "base + t < c->K_in ? (double)oracle_bf16_to_f32(x[base + t]) : 1.0"),
     ("first_group_only", "for (int64_t base = 0; base < c->K; base += g) {",
      "for (int64_t base = 0; base < c->K; base += g) { if (base) { for (int j = 0; j < g; ++j) "
      "r[base + j] = r[j]; continue; }"),

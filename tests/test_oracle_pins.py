@@ -221,10 +221,54 @@ def test_rotation_preserves_group_norms(g):
     np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(xf, axis=-1), rtol=1e-6)
 
 
-def test_rotation_rejects_bad_group():
-    x = synth.random_bf16((2, 100), seed=1)
+@pytest.mark.parametrize("K,g", [(100, 64), (320, 256), (8, 64), (3000, 256), (200, 64 | oracle.REGULAR),
+                                 (776, 256 | oracle.REGULAR)])
+def test_padded_rotation_is_the_dense_operator_on_zero_padded_rows(K, g):
+    """K not a multiple of g: the rows are padded with zeros to a whole number
+    of groups (comfy-quants issue, section 1), i.e. the dense operator
+    I (x) H / sqrt(g) applied to [x, 0]."""
+    gs = g & ~oracle.REGULAR
+    Kr = -(-K // gs) * gs
+    x = synth.random_bf16((3, K), seed=K, outliers=2)
+    base = scipy.linalg.hadamard(gs) if not g & oracle.REGULAR else None
+    if base is None:
+        base = _B4
+        while base.shape[0] < gs:
+            base = np.kron(_B4, base)
+    R = np.kron(np.eye(Kr // gs), base).astype(np.float64) / np.sqrt(gs)
+    xp = np.zeros((3, Kr))
+    xp[:, :K] = synth.bf16_bits_to_f32(x)
+    got = oracle.rotate_rows(x, g)
+    assert got.shape == (3, Kr)
+    assert np.array_equal(got, (xp @ R).astype(np.float32))
+
+
+def test_padded_rotation_invariance_exact_on_integers():
+    rng = np.random.default_rng(8)
+    K, g = 200, 64
+    X = rng.integers(-8, 9, size=(4, K)).astype(np.float32)
+    W = rng.integers(-8, 9, size=(5, K)).astype(np.float32)
+    RX = oracle.rotate_rows(_bits_of(X), g).astype(np.float64)
+    RW = oracle.rotate_rows(_bits_of(W), g).astype(np.float64)
+    assert RX.shape == (4, 256)
+    assert np.array_equal(RX @ RW.T, (X.astype(np.int64) @ W.astype(np.int64).T).astype(np.float64))
+
+
+def test_padded_linear_tracks_dense_product():
+    x = synth.random_bf16((8, 320), seed=51, outliers=2)
+    w = synth.random_bf16((40, 320), seed=52, std=0.02)
+    b = synth.random_bf16((40,), seed=53, std=0.01)
+    qw, sw = oracle.prepare_weight(w, 256)
+    assert qw.shape == (40, 512)
+    ref = (synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+           + synth.bf16_bits_to_f32(b))
+    y = synth.bf16_bits_to_f32(oracle.linear(x, qw, sw, b, 256))
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.35
     with pytest.raises(ValueError):
-        oracle.rotate_rows(x, 64)      # K not a multiple of g
+        oracle.linear(x, qw[:, :320], sw, b, 256)   # codes must be K_rot wide
+
+
+def test_rotation_rejects_bad_group():
     with pytest.raises(ValueError):
         oracle.rotate_rows(synth.random_bf16((2, 96), seed=1), 48)  # not a power of two
 
