@@ -24,8 +24,14 @@
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Device
  *     entry points only enqueue work on it and return; nothing is synchronised.
  *   - Device buffers must be 16-byte aligned except sw/sx/bias (4/4/2 bytes).
- *   - Sizes: 1 <= K <= 16384 with K % g == 0; 0 <= M, N <= 16777216.  M == 0 or
- *     N == 0 is a no-op that returns CONVROT_OK.
+ *   - Sizes: K % 8 == 0 and K_rot <= 16384, where K_rot = K rounded up to a
+ *     multiple of g; 0 <= M, N <= 16777216.  M == 0 or N == 0 is a no-op that
+ *     returns CONVROT_OK.
+ *   - When g does not divide K, every row of X and W is zero-padded to K_rot
+ *     before the rotation (comfy-quants issue, section 1: "after padding the
+ *     last block"), and codes, scales and the product cover the K_rot rotated
+ *     values; the result is still X W^T up to quantization.  Outputs that are
+ *     rows of codes or rotated values are K_rot wide; X and W stay K wide.
  *   - All arguments are checked before anything is launched; on any error
  *     nothing is enqueued and an error status is returned.  There is no
  *     fallback path of any kind.
@@ -68,10 +74,11 @@ const char* convrot_version(void);
 /* ---- sizes (host only, no HIP call) ----------------------------------- */
 
 /* Bytes of the packed INT4 weight image for an N x K weight:
- * round_up(N, 32) * round_up(K, 128) / 2.  Layout: 32-column x 128-K units
- * in MFMA fragment order (convrot-mlx README, "What is included": the K x
- * packed-N family of layouts, here tiled for CDNA4 matrix cores).  g must be
- * 64 or 256 and K % g == 0.  Returns CONVROT_OK or CONVROT_EINVAL. */
+ * round_up(N, 32) * round_up(K_rot, 128) / 2.  Layout: 32-column x 128-K
+ * units in MFMA fragment order (convrot-mlx README, "What is included": the
+ * K x packed-N family of layouts, here tiled for CDNA4 matrix cores).  g must
+ * be 64 or 256 (with or without CONVROT_REGULAR_HADAMARD).  Returns
+ * CONVROT_OK or CONVROT_EINVAL. */
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
 /* Bytes of workspace convrot_linear needs for an M x K input and N outputs.
@@ -127,7 +134,7 @@ int convrot_prepare_weight(const void* W_dev, int64_t N, int64_t K, int g, void*
 
 /* The same rotation and quantization, writing the portable N x packed-K form
  * (convrot-mlx README, "What is included": reversible N x packed-K layout):
- * qweight_nk_dev is uint8 [N][K/2], byte j of row n holding code 2j in its low
+ * qweight_nk_dev is uint8 [N][K_rot/2], byte j of row n holding code 2j in its low
  * nibble and code 2j+1 in its high nibble (two's complement).  sw_dev float [N]. */
 int convrot_quantize_weight(const void* W_dev, int64_t N, int64_t K, int g, uint8_t* qweight_nk_dev,
                             float* sw_dev, void* stream);
@@ -169,8 +176,8 @@ int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_de
  *   Y[m][n] = bf16( fmaf(sum_k bf16(r[m][k]) * qw[n][k], sw[n], bias[n]) ),
  * the sum accumulated in binary32 by the bf16 matrix cores (so Y is close to,
  * not bit-identical with, the same formula summed exactly).
- * Bytes of workspace for M x K: round_up(M * K * 2, 256); it receives the
- * bf16 rotated rows, row-major [M][K].  M must be <= 32; otherwise, and for
+ * Bytes of workspace for M x K: round_up(M * K_rot * 2, 256); it receives the
+ * bf16 rotated rows, row-major [M][K_rot].  M must be <= 32; otherwise, and for
  * the shape rules of convrot_linear, CONVROT_EINVAL. */
 int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
 
@@ -193,7 +200,9 @@ int convrot_linear_w4a16(const void* X_dev, int64_t M, int64_t K, const void* im
  * image, then the scale + bias epilogue into Y.  Same arguments and rules as
  * convrot_linear, except that convrot_prepare_activations needs only the
  * first three parts of the workspace (it does not know N).  convrot_gemm
- * leaves the workspace valid for another convrot_gemm. */
+ * does not know g: its K is the code width K_rot of the prepared rows (equal
+ * to K when g divides K).  It leaves the workspace valid for another
+ * convrot_gemm. */
 int convrot_prepare_activations(const void* X_dev, int64_t M, int64_t K, int g, void* workspace_dev,
                                 size_t ws_bytes, void* stream);
 int convrot_gemm(const void* workspace_dev, size_t ws_bytes, int64_t M, int64_t K, const void* image_dev,
@@ -202,8 +211,8 @@ int convrot_gemm(const void* workspace_dev, size_t ws_bytes, int64_t M, int64_t 
 /* ---- parity hooks (same kernels, exposed intermediate results) ---------- */
 
 /* Rotation + row absmax + quantization of `rows` bf16 rows, with plain
- * row-major outputs: codes_dev int8 [rows][K], scales_dev float [rows], and,
- * if rotated_dev is not NULL, the rotated rows as float [rows][K] (convrot-mlx
+ * row-major outputs: codes_dev int8 [rows][K_rot], scales_dev float [rows], and,
+ * if rotated_dev is not NULL, the rotated rows as float [rows][K_rot] (convrot-mlx
  * README, "What is included": the rotation and the rowwise quantizer). */
 int convrot_prepare_rows(const void* X_dev, int64_t rows, int64_t K, int g, int8_t* codes_dev, float* scales_dev,
                          float* rotated_dev, void* stream);

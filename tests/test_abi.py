@@ -77,6 +77,9 @@ def test_workspace_bytes():
     assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 524288 + 1024 + 2048 + 4 * 147456
     # 5 x 192 -> N: M <= 32
     assert B.convrot_workspace_bytes(5, 192, 100, 64) == 32 * 256 // 2 + 256 + 2048
+    # K not a multiple of g: sizes follow the rotated width (1000 -> 1024)
+    assert B.convrot_workspace_bytes(64, 1000, 1024, 256) == B.convrot_workspace_bytes(64, 1024, 1024, 256)
+    assert B.convrot_weight_image_bytes(100, 328, 256) == 128 * 512 // 2
     # N = 0: nothing to split
     assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 9437184 + 6144 + 2048
 
@@ -115,7 +118,9 @@ def test_validate_linear_statuses():
     assert _validate_linear(g=128 | R) == B.CONVROT_EINVAL
     assert _validate_linear(g=256 | (R << 1)) == B.CONVROT_EINVAL    # unknown flag
     assert _validate_linear(g=R) == B.CONVROT_EINVAL
-    assert _validate_linear(K=1000) == B.CONVROT_EINVAL
+    assert _validate_linear(K=1000) == B.CONVROT_OK               # last group zero-padded to 1024
+    assert _validate_linear(K=1004) == B.CONVROT_EINVAL           # rows are whole 16-byte runs
+    assert _validate_linear(K=16392) == B.CONVROT_EINVAL          # rotated width above the maximum
     assert _validate_linear(X=0) == B.CONVROT_EINVAL
     assert _validate_linear(Y=0) == B.CONVROT_EINVAL
     assert _validate_linear(image=0) == B.CONVROT_EINVAL
@@ -156,7 +161,8 @@ def test_validate_weight_statuses():
     assert B.convrot_validate_weight(4096, 1024, 1024, 256, 8192, 16384) == B.CONVROT_OK
     assert B.convrot_validate_weight(4096, 1024, 1024, 32, 8192, 16384) == B.CONVROT_EINVAL
     assert B.convrot_validate_weight(0, 1024, 1024, 256, 8192, 16384) == B.CONVROT_EINVAL
-    assert B.convrot_validate_weight(4096, 1024, 1000, 64, 8192, 16384) == B.CONVROT_EINVAL
+    assert B.convrot_validate_weight(4096, 1024, 1000, 64, 8192, 16384) == B.CONVROT_OK     # padded to 1024
+    assert B.convrot_validate_weight(4096, 1024, 1001, 64, 8192, 16384) == B.CONVROT_EINVAL  # K % 8 != 0
     assert B.convrot_validate_weight(0, 0, 1024, 256, 0, 0) == B.CONVROT_OK
 
 

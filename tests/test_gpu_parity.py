@@ -44,7 +44,9 @@ PREP_SHAPES = [
 
 REG = 0x10000  # the library's regular-Hadamard flag (checked against the header in test_abi)
 PREP_SHAPES += [(5, 256, 256 | REG), (37, 3072, 256 | REG), (2, 16384, 256 | REG), (7, 192, 64 | REG),
-                (33, 1024, 64 | REG), (1, 64, 64 | REG)]
+                (33, 1024, 64 | REG), (1, 64, 64 | REG),
+                # K not a multiple of g (zero-padded last group), both matrices
+                (6, 328, 256), (3, 3000, 256), (9, 200, 64), (2, 8, 64), (4, 776, 256 | REG), (5, 1000, 64 | REG)]
 
 
 @pytest.mark.parametrize("rows,K,g", PREP_SHAPES)
@@ -84,9 +86,12 @@ def test_prepare_rows_golden_ties(gpu):
 # weight preparation and layouts (K1 + K3)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N,K,g", [(70, 512, 256), (32, 256, 256), (45, 192, 64), (256, 1024, 64)])
+@pytest.mark.parametrize("N,K,g", [(70, 512, 256), (32, 256, 256), (45, 192, 64), (256, 1024, 64),
+                                   # K not a multiple of g: the last group is zero-padded
+                                   (33, 328, 256), (40, 200, 64)])
 def test_weight_image_and_nk_parity(gpu, N, K, g):
     w = synth.random_bf16((N, K), seed=N + K, std=0.02)
+    K = gpu.rotated_width(K, g)   # code width
     oq, osw = oracle.prepare_weight(w, g)
     onk = oracle.pack_nk(oq)
     W = _dev(w)
@@ -184,8 +189,9 @@ def _linear_parity(gpu, x, w, bias, g):
     ws = gpu.new_workspace(x.shape[0], K, N, g)
     Y = gpu.convrot_linear(_dev(x), image, sw, None if bias is None else _dev(bias), N, g, workspace=ws)
     gy = _host_bits(Y)
-    # codes of X (from the workspace) and of W (from the image)
+    # codes of X (from the workspace) and of W (from the image), K_rot wide
     M = x.shape[0]
+    K = gpu.rotated_width(K, g)
     qx = gpu.workspace_act_codes(ws, M, K)
     orx = oracle.rotate_rows(x, g)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
@@ -211,7 +217,10 @@ def test_linear_small_workloads_full(gpu, name):
                                      # the regular Hadamard matrix, both paths
                                      (37, 70, 512, 256 | REG), (257, 300, 2048, 64 | REG),
                                      (1, 100, 1024, 256 | REG), (4, 33, 512, 64 | REG),
-                                     (3, 5000, 4096, 256 | REG)])
+                                     (3, 5000, 4096, 256 | REG),
+                                     # K not a multiple of g, both paths
+                                     (37, 70, 328, 256), (300, 520, 1000, 64), (1, 100, 1000, 256),
+                                     (4, 33, 2000, 64 | REG), (65, 200, 3000, 256 | REG)])
 def test_linear_ragged_shapes(gpu, M, N, K, g):
     x = synth.random_bf16((M, K), seed=M + N, outliers=3)
     w = synth.random_bf16((N, K), seed=N + K, std=0.02)
@@ -260,7 +269,7 @@ def test_linear_rejects_bad_arguments(gpu):
 
 @pytest.mark.parametrize("M,N,K,g", [(1, 96, 256, 256), (4, 5000, 3072, 256), (16, 12288, 3072, 256),
                                      (17, 300, 1024, 64), (32, 1000, 2048, 256 | REG), (5, 70, 192, 64),
-                                     (3, 17000, 512, 64 | REG), (1, 12288, 3072, 256)])
+                                     (3, 17000, 512, 64 | REG), (1, 12288, 3072, 256), (2, 300, 1000, 256)])
 def test_linear_w4a16(gpu, M, N, K, g):
     """The bf16 rotated rows are bit-exact (one rounding of the exact
     rotation); Y is within the path's tolerance of the oracle, whose sum is
@@ -275,7 +284,8 @@ def test_linear_w4a16(gpu, M, N, K, g):
     ws = torch.zeros(gpu.convrot_w4a16_workspace_bytes(M, K, g), dtype=torch.uint8, device="cuda")
     Y = gpu.convrot_linear_w4a16(_dev(x), image, sw, _dev(b), N, g, workspace=ws)
     torch.cuda.synchronize()
-    xr = ws[: M * K * 2].cpu().numpy().view(np.uint16).reshape(M, K)
+    Kr = gpu.rotated_width(K, g)
+    xr = ws[: M * Kr * 2].cpu().numpy().view(np.uint16).reshape(M, Kr)
     assert np.array_equal(xr, xr_or), "bf16 rotated rows differ"
     gy = synth.bf16_bits_to_f32(_host_bits(Y)).astype(np.float64)
     oy = synth.bf16_bits_to_f32(y_or).astype(np.float64)

@@ -27,6 +27,13 @@ CONVROT_EDEVICE = 4
 # OR'd into a group size g: rotate with the regular Hadamard matrix
 CONVROT_REGULAR_HADAMARD = 0x10000
 
+
+def rotated_width(K: int, g: int) -> int:
+    """Codes and rotated values are K rounded up to a whole number of groups wide
+    (the missing values of the last group are zero)."""
+    gs = g & ~CONVROT_REGULAR_HADAMARD
+    return -(-K // gs) * gs
+
 _lock = threading.Lock()
 _lib = None
 
@@ -181,10 +188,10 @@ def convrot_prepare_weight(W, g: int, image=None, sw=None, stream=None):
 
 
 def convrot_quantize_weight(W, g: int, stream=None):
-    """W: bf16 [N, K] -> (N x packed-K uint8 [N, K/2], sw float32 [N])."""
+    """W: bf16 [N, K] -> (N x packed-K uint8 [N, K_rot/2], sw float32 [N]), K_rot = rotated_width(K, g)."""
     import torch
     N, K = W.shape
-    nk = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    nk = torch.empty((N, rotated_width(K, g) // 2), dtype=torch.uint8, device=W.device)
     sw = torch.empty(N, dtype=torch.float32, device=W.device)
     _call("convrot_quantize_weight", _dev(W, torch.bfloat16, "W"), N, K, g, _dev(nk, torch.uint8, "nk"),
           _dev(sw, torch.float32, "sw"), _stream(stream))
@@ -239,12 +246,14 @@ def convrot_gemm(workspace, M: int, K: int, image, sw, bias, N: int, Y=None, str
 
 
 def convrot_prepare_rows(X, g: int, want_rotated: bool = False, stream=None):
-    """Rotation + quantization of bf16 rows -> (codes int8 [rows, K], scales f32 [rows], rotated f32 or None)."""
+    """Rotation + quantization of bf16 rows -> (codes int8 [rows, K_rot], scales f32 [rows],
+    rotated f32 [rows, K_rot] or None), K_rot = rotated_width(K, g)."""
     import torch
     rows, K = X.shape
-    codes = torch.empty((rows, K), dtype=torch.int8, device=X.device)
+    Kr = rotated_width(K, g)
+    codes = torch.empty((rows, Kr), dtype=torch.int8, device=X.device)
     scales = torch.empty(rows, dtype=torch.float32, device=X.device)
-    rot = torch.empty((rows, K), dtype=torch.float32, device=X.device) if want_rotated else None
+    rot = torch.empty((rows, Kr), dtype=torch.float32, device=X.device) if want_rotated else None
     _call("convrot_prepare_rows", _dev(X, torch.bfloat16, "X"), rows, K, g, _dev(codes, torch.int8, "codes"),
           _dev(scales, torch.float32, "scales"), None if rot is None else _dev(rot, torch.float32, "rotated"),
           _stream(stream))
@@ -326,7 +335,8 @@ WORKSPACE_IMAGE_OFFSET = 2048
 
 
 def workspace_act_codes(workspace, M: int, K: int) -> np.ndarray:
-    """Activation codes int8 [M, K] decoded from a workspace (tensor or array)."""
+    """Activation codes int8 [M, K] decoded from a workspace (tensor or array); K is
+    the code width (the rotated width of the prepared rows)."""
     ws = workspace.cpu().numpy() if hasattr(workspace, "cpu") else np.asarray(workspace)
     return convrot_host_act_image_to_codes(ws[WORKSPACE_IMAGE_OFFSET:], M, K)
 

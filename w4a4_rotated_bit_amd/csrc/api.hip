@@ -51,14 +51,16 @@ int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
 
 int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, hipStream_t s)
 {
+    const int64_t Kr = rotated_width(K, g);
     PrepArgs a{};
     a.X = (const uint16_t*)X;
+    a.ld = K;
     a.rows = M;
     a.rows_pad = round_up(M, kTileRows);
-    a.K = K;
-    a.K_pad = round_up(K, kTileK);
+    a.K = Kr;
+    a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)ws + workspace_image_offset();
-    a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
+    a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
     a.zero_count = 2 * kSplitCounters;
@@ -108,12 +110,14 @@ int convrot_prepare_weight(const void* W, int64_t N, int64_t K, int g, void* ima
     int rc = convrot_validate_weight(W, N, K, g, image, sw);
     if (rc || N == 0) return rc;
     if ((rc = check_device())) return rc;
+    const int64_t Kr = rotated_width(K, g);
     PrepArgs a{};
     a.X = (const uint16_t*)W;
+    a.ld = K;
     a.rows = N;
     a.rows_pad = round_up(N, kTileRows);
-    a.K = K;
-    a.K_pad = round_up(K, kTileK);
+    a.K = Kr;
+    a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)image;
     a.scales = sw;
     launch_prep(g, OUT_IMAGE, a, as_stream(stream));
@@ -128,10 +132,11 @@ int convrot_quantize_weight(const void* W, int64_t N, int64_t K, int g, uint8_t*
     if ((rc = check_device())) return rc;
     PrepArgs a{};
     a.X = (const uint16_t*)W;
+    a.ld = K;
     a.rows = N;
     a.rows_pad = N;
-    a.K = K;
-    a.K_pad = K;
+    a.K = rotated_width(K, g);
+    a.K_pad = a.K;
     a.out = qweight_nk;
     a.scales = sw;
     launch_prep(g, OUT_NK, a, as_stream(stream));
@@ -155,7 +160,7 @@ int convrot_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     int rc = validate_rows_out(X, M, K, g);
     if (rc || M == 0) return rc;
     if (!ws || !aligned(ws, 16)) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_partial_offset(M, K)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_partial_offset(M, rotated_width(K, g))) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     return enqueue_prepare_activations(X, M, K, g, ws, as_stream(stream));
 }
@@ -177,21 +182,23 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
     if (rc || M == 0 || N == 0) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    if (single_kernel_linear(M, K, g)) {
+    const int64_t Kr = rotated_width(K, g);
+    if (single_kernel_linear(M, Kr, g)) {
         // one kernel: each workgroup quantizes the few activation rows itself
-        GemmArgs ga = gemm_args(ws, M, K, image, sw, bias, N, Y);
+        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
         PrepArgs pa{};
         pa.X = (const uint16_t*)X;
+        pa.ld = K;
         pa.rows = M;
-        pa.K = K;
-        pa.K_pad = round_up(K, kTileK);
+        pa.K = Kr;
+        pa.K_pad = round_up(Kr, kTileK);
         pa.out = (uint8_t*)ws + workspace_image_offset();
-        pa.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, K));
+        pa.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
         launch_small_m(g, ga, pa, s);
         return launched();
     }
     if ((rc = enqueue_prepare_activations(X, M, K, g, ws, s))) return rc;
-    return enqueue_gemm(GEMM_OUT_BF16, ws, M, K, image, sw, bias, N, Y, s);
+    return enqueue_gemm(GEMM_OUT_BF16, ws, M, Kr, image, sw, bias, N, Y, s);
 }
 
 int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
@@ -202,17 +209,19 @@ int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image,
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
     // 1. the rotated activation rows, rounded to bf16, into the workspace
+    const int64_t Kr = rotated_width(K, g);
     PrepArgs a{};
     a.X = (const uint16_t*)X;
+    a.ld = K;
     a.rows = M;
     a.rows_pad = M;
-    a.K = K;
-    a.K_pad = K;
+    a.K = Kr;
+    a.K_pad = Kr;
     a.out = (uint8_t*)ws;
     launch_prep(g, OUT_ROTATED_BF16, a, s);
     if ((rc = launched())) return rc;
     // 2. their product with the weight image, scale and bias
-    GemmArgs ga = gemm_args(ws, M, K, image, sw, bias, N, Y);
+    GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
     launch_w4a16(ga, (const uint16_t*)ws, s);
     return launched();
 }
@@ -226,10 +235,11 @@ int convrot_prepare_rows(const void* X, int64_t rows, int64_t K, int g, int8_t* 
     if ((rc = check_device())) return rc;
     PrepArgs a{};
     a.X = (const uint16_t*)X;
+    a.ld = K;
     a.rows = rows;
     a.rows_pad = rows;
-    a.K = K;
-    a.K_pad = K;
+    a.K = rotated_width(K, g);
+    a.K_pad = a.K;
     a.out = (uint8_t*)codes;
     a.scales = scales;
     a.rotated = rotated;

@@ -18,8 +18,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int check_shape(int64_t rows, int64_t K, int g)
 {
     if ((g & ~kRegularHadamard) != 64 && (g & ~kRegularHadamard) != 256) return CONVROT_EINVAL;
-    g &= ~kRegularHadamard;
-    if (K < 1 || K > kMaxK || K % g != 0) return CONVROT_EINVAL;
+    // rows of X and W are 16-byte aligned runs of bf16; the rotated width
+    // (K rounded up to g, the rest zero padding) is at most kMaxK
+    if (K < 1 || K % 8 != 0 || rotated_width(K, g) > kMaxK) return CONVROT_EINVAL;
     if (rows < 0 || rows > kMaxRows) return CONVROT_EINVAL;
     return CONVROT_OK;
 }
@@ -68,7 +69,7 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
     if (!bytes) return CONVROT_EINVAL;
     int rc = check_shape(N, K, g);
     if (rc) return rc;
-    *bytes = image_bytes(N, K);
+    *bytes = image_bytes(N, rotated_width(K, g));
     return CONVROT_OK;
 }
 
@@ -78,7 +79,7 @@ int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* byte
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
-    *bytes = workspace_bytes(M, K, N);
+    *bytes = workspace_bytes(M, rotated_width(K, g), N);
     return CONVROT_OK;
 }
 
@@ -88,7 +89,7 @@ int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* cou
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
-    *count = (M == 0 || N == 0) ? 0 : single_kernel_linear(M, K, g) ? 1 : 2;
+    *count = (M == 0 || N == 0) ? 0 : single_kernel_linear(M, rotated_width(K, g), g) ? 1 : 2;
     return CONVROT_OK;
 }
 
@@ -112,7 +113,7 @@ int convrot_validate_linear(const void* X, int64_t M, int64_t K, const void* ima
     if (!X || !image || !sw || !Y || !ws) return CONVROT_EINVAL;
     if (!aligned(X, 16) || !aligned(image, 16) || !aligned(Y, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
     if (!aligned(sw, 4) || (bias && !aligned(bias, 2))) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_bytes(M, rotated_width(K, g), N)) return CONVROT_EWORKSPACE;
     return CONVROT_OK;
 }
 
@@ -122,7 +123,7 @@ int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes)
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (M > kW4A16MaxRows) return CONVROT_EINVAL;
-    *bytes = (size_t)round_up(M * K * 2, 256);
+    *bytes = (size_t)round_up(M * rotated_width(K, g) * 2, 256);
     return CONVROT_OK;
 }
 

@@ -12,7 +12,8 @@ struct PrepArgs {
     const uint16_t* X;   // bf16 [rows][K]
     int64_t rows;        // rows holding data
     int64_t rows_pad;    // rows written (image mode: rows rounded up to 32)
-    int64_t K, K_pad;    // K_pad = K rounded up to 128 (image mode)
+    int64_t K, K_pad;    // K: rotated row length (a whole number of groups); K_pad: K rounded up to 128 (image mode)
+    int64_t ld;          // elements per row of X (<= K: the rest of a row is zero padding)
     uint8_t* out;        // codes in the layout of the mode
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr

@@ -171,26 +171,30 @@ struct PrepShape {
         (32 * kRunD * 8 > 64 * kRunF * 4) ? 32 * kRunD * 8 : 64 * kRunF * 4;
 };
 
-// Loads of the P bf16 values of a lane's phase-1 run.  The loads are always
-// issued (from row 0, element 0 when the lane has no data -- a valid address,
-// since rows >= 1 and K >= 64 whenever the kernel runs) and then replaced by
-// zeros, so the number of loads in flight is the same on every path and the
-// wait for a prefetched row does not have to drain the newer loads.
+// Loads of the P bf16 values of a lane's phase-1 run, in 16-byte chunks of 8
+// values.  A row of X holds ld values (ld % 8 == 0); chunks past it are the
+// zero padding of the last group.  The loads are always issued (from row 0,
+// element 0 for a chunk without data -- a valid address) and such chunks are
+// replaced by zeros (zero_unless), so the number of loads in flight is the
+// same on every path and the wait for a prefetched row does not have to drain
+// the newer loads.
 template <int P>
-__device__ inline void load_run(const uint16_t* X, int64_t row, int64_t K, int64_t k0, bool has_data,
+__device__ inline void load_run(const uint16_t* X, int64_t row, int64_t ld, int64_t k0, bool has_row,
                                 uint4 (&w)[P / 8])
 {
-    const uint16_t* src = X + (has_data ? row * K + k0 : 0);
 #pragma unroll
-    for (int c = 0; c < P / 8; ++c) w[c] = *(const uint4*)(src + 8 * c);
+    for (int c = 0; c < P / 8; ++c) {
+        const bool ok = has_row && k0 + 8 * c < ld;
+        w[c] = *(const uint4*)(X + (ok ? row * ld + k0 + 8 * c : 0));
+    }
 }
 
 template <int P>
-__device__ inline void zero_unless(bool has_data, uint4 (&w)[P / 8])
+__device__ inline void zero_unless(bool has_row, int64_t ld, int64_t k0, uint4 (&w)[P / 8])
 {
 #pragma unroll
     for (int c = 0; c < P / 8; ++c)
-        if (!has_data) w[c] = make_uint4(0, 0, 0, 0);
+        if (!(has_row && k0 + 8 * c < ld)) w[c] = make_uint4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -280,7 +284,7 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     const bool row_valid = row < a.rows;  // row holds data
     const bool has_data = row_valid && k0 < a.K;
     // ---- phase 1: P consecutive elements, butterflies over the low bits ----
-    zero_unless<P>(has_data, w);
+    zero_unless<P>(row_valid, a.ld, k0, w);
     double v[P];
 #pragma unroll
     for (int c = 0; c < P / 8; ++c) {
@@ -469,18 +473,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(REG ? 5 : 
     const int64_t n_it = first < a.rows_pad ? (a.rows_pad - first + row_step - 1) / row_step : 0;
     const int64_t k0 = (int64_t)t * P;  // first element of the phase-1 run
     double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
-    const bool lane_k = k0 < a.K;
-
     uint4 wa[P / 8], wb[P / 8];
-    load_run<P>(a.X, row, a.K, k0, row < a.rows && lane_k, wa);
+    load_run<P>(a.X, row, a.ld, k0, row < a.rows, wa);
     for (int64_t it = 0; it < n_it; it += 2) {
         int64_t nx = row + row_step;
-        load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wb);
+        load_run<P>(a.X, nx, a.ld, k0, nx < a.rows, wb);
         prep_row<G, MODE, 0, REG>(a, wa, row, t, k0, lane, wave, ld, red, 0, 0, blockDim.x >> 6);
         row = nx;
         if (it + 1 >= n_it) break;
         nx = row + row_step;
-        load_run<P>(a.X, nx, a.K, k0, nx < a.rows && lane_k, wa);
+        load_run<P>(a.X, nx, a.ld, k0, nx < a.rows, wa);
         prep_row<G, MODE, 0, REG>(a, wb, row, t, k0, lane, wave, ld, red, 1, 0, blockDim.x >> 6);
         row = nx;
     }
@@ -1372,7 +1374,7 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
     //    loads -- and the wait for the activation values, issued first, does
     //    not wait for the weights)
     uint4 xw[P / 8];
-    load_run<P>(p.X, live ? team : 0, p.K, k0, live && team < p.rows && k0 < p.K, xw);
+    load_run<P>(p.X, live ? team : 0, p.ld, k0, live && team < p.rows, xw);
     // the epilogue's column scales and biases (clamped columns: every lane
     // issues the same loads; only the first wave of each strip uses them)
     const int64_t n0 = (int64_t)strip * 16 + 4 * q;
@@ -1414,7 +1416,7 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
         for (int pass = 1; pass < passes; ++pass) {
             const int64_t row = (int64_t)pass * teams + (live ? team : 0);
             const bool active = live && row < a.M;
-            load_run<P>(p.X, row, p.K, k0, active && k0 < p.K, xw);
+            load_run<P>(p.X, row, p.ld, k0, active, xw);
             if (active)
                 prep_row<G, OUT_LDS, kSmallRows, REG>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1, team * team_nw,
                                                   team_nw);

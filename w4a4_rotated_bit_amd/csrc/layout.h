@@ -75,6 +75,14 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
 // with the regular Hadamard matrix instead of the Sylvester one.
 constexpr int kRegularHadamard = 0x10000;
 
+// A row of K values is rotated as K rounded up to a whole number of groups,
+// the missing values being zero; codes, scales and the product use that width.
+CONVROT_HD inline int64_t rotated_width(int64_t K, int g)
+{
+    const int64_t gs = g & ~kRegularHadamard;
+    return (K + gs - 1) / gs * gs;
+}
+
 // ---- W4A16 -----------------------------------------------------------------
 // The weight-only INT4 variant is the weight-bandwidth-bound regime: M <= 32.
 constexpr int64_t kW4A16MaxRows = 32;
