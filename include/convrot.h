@@ -28,8 +28,8 @@
  *     multiple of g; 0 <= M, N <= 16777216.  M == 0 or N == 0 is a no-op that
  *     returns CONVROT_OK.
  *   - When g does not divide K, every row of X and W is zero-padded to K_rot
- *     before the rotation (comfy-quants issue, section 1: "after padding the
- *     last block"), and codes, scales and the product cover the K_rot rotated
+ *     before the rotation (comfy-quants issue, section 1, which pads the last
+ *     block when needed), and codes, scales and the product cover the K_rot rotated
  *     values; the result is still X W^T up to quantization.  Outputs that are
  *     rows of codes or rotated values are K_rot wide; X and W stay K wide.
  *   - All arguments are checked before anything is launched; on any error

@@ -166,6 +166,15 @@ def test_validate_weight_statuses():
     assert B.convrot_validate_weight(0, 0, 1024, 256, 0, 0) == B.CONVROT_OK
 
 
+def test_binding_size_limits_match_the_library():
+    v = B.convrot_validate_weight
+    assert v(4096, 1, B.MAX_K, 256, 8192, 16384) == B.CONVROT_OK
+    assert v(4096, 1, B.MAX_K + 8, 256, 8192, 16384) == B.CONVROT_EINVAL
+    assert v(4096, 1, B.MAX_K - 8, 256, 8192, 16384) == B.CONVROT_OK       # rotated width MAX_K
+    assert v(4096, B.MAX_ROWS, 1024, 256, 8192, 16384) == B.CONVROT_OK
+    assert v(4096, B.MAX_ROWS + 1, 1024, 256, 8192, 16384) == B.CONVROT_EINVAL
+
+
 # --------------------------------------------------------------------------
 # host layout tools vs the oracle
 # --------------------------------------------------------------------------

@@ -298,16 +298,23 @@ FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_ml
         "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
 
 
-@pytest.mark.parametrize("name", FULL + ["flux_qkv_m1536_k3072_n9216+regular"])
+@pytest.mark.parametrize("name", FULL + ["flux_qkv_m1536_k3072_n9216+regular", "flux_qkv_m1536_k3072_n9216+zero_rows",
+                                         "decode_m4_k3072_n12288+zero_rows"])
 def test_linear_full_size_sampled(gpu, name):
     """Full shapes, the launch configuration the benchmark times; the oracle
     recomputes sampled rows x sampled columns from scratch.  "+regular": the
-    same inputs rotated with the regular Hadamard matrix."""
+    same inputs rotated with the regular Hadamard matrix.  "+zero_rows": a
+    few rows of X set to zero, whose scale and codes must be zero and whose
+    output must be the bias exactly."""
     import torch
     base, _, variant = name.partition("+")
     inp = synth.make(base)
     wl = inp["workload"]
     M, N, K, g = wl.M, wl.N, wl.K, wl.g | (REG if variant == "regular" else 0)
+    zero_rows = np.array(sorted({1 % M, M // 2, M - 1})) if variant == "zero_rows" else np.array([], int)
+    if zero_rows.size:
+        inp["x"] = inp["x"].copy()
+        inp["x"][zero_rows] = 0
     W = _dev(inp["w"])
     image, sw = gpu.convrot_prepare_weight(W, g)
     ws = gpu.new_workspace(M, K, N, g)
@@ -318,7 +325,7 @@ def test_linear_full_size_sampled(gpu, name):
     assert np.array_equal(gy, _host_bits(Y2)), "two runs differ"
     assert np.all(np.isfinite(synth.bf16_bits_to_f32(gy)))
     rng = np.random.default_rng(2024)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 24), replace=False)]))
+    rows = np.unique(np.concatenate([[0, M - 1], zero_rows, rng.choice(M, size=min(M, 24), replace=False)]))
     cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=192, replace=False)]))
     oq_x, osx, orx = oracle.prepare_rows(inp["x"][rows], g, want_rotated=True)
     oq_w, osw, orw = oracle.prepare_rows(inp["w"][cols], g, want_rotated=True)
@@ -334,6 +341,10 @@ def test_linear_full_size_sampled(gpu, name):
     y_or = oracle.epilogue(oracle.gemm_i32(oq_x, oq_w), osx, osw, inp["bias"][cols])
     rows_ok = np.all(gq_x == oq_x, axis=1) & (n_w == 0)
     compare_y(gy[np.ix_(rows, cols)], y_or, rows_ok)
+    if zero_rows.size:
+        assert np.all(osx[np.searchsorted(rows, zero_rows)] == 0)
+        assert np.all(gq_x[np.searchsorted(rows, zero_rows)] == 0)
+        assert np.all(gy[zero_rows] == inp["bias"][None, :]), "zero rows must give the bias"
     print(f"{name}: code mismatches x={n_x} w={n_w}")
 
 
@@ -368,3 +379,17 @@ def test_module_matches_the_c_abi(gpu, lead, K, N, rotation, path):
     gy = synth.bf16_bits_to_f32(_host_bits(ref)).astype(np.float64)
     oy = synth.bf16_bits_to_f32(y_or).astype(np.float64)
     assert np.abs(gy - oy).max() <= 1e-2 * np.abs(oy).max()
+
+
+@pytest.mark.parametrize("rotation", ["sylvester", "regular"])
+def test_flux_block_swap(gpu, rotation):
+    """Every linear of a small FLUX-shaped block is swapped; the block still
+    runs and stays close to the dense block.  The bound is loose on purpose:
+    each W4A4 linear alone is about 0.2 off the dense product (relative
+    Frobenius), and the residual connections carry the unquantized input."""
+    from w4a4_rotated_bit_amd.flux_block import run
+    r = run(T=96, hidden=512, group_size=256, rotation=rotation, iters=0)
+    print(r)
+    assert r["finite"] and r["swapped"] == ["down", "proj", "qkv", "up"]
+    assert r["rel_err_update"] < 0.5
+    assert r["rel_err_block"] < 0.2

@@ -26,6 +26,8 @@ CONVROT_EHIP = 3
 CONVROT_EDEVICE = 4
 # OR'd into a group size g: rotate with the regular Hadamard matrix
 CONVROT_REGULAR_HADAMARD = 0x10000
+MAX_K = 16384           # largest rotated width K_rot
+MAX_ROWS = 16777216     # largest M or N
 
 
 def rotated_width(K: int, g: int) -> int:

@@ -62,3 +62,30 @@ class ConvRotLinear(torch.nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, bias={self.bias is not None}, "
                 f"group_size={self.group_size}, rotation={self.rotation}, path={self.path}")
+
+
+def eligible(linear: torch.nn.Linear, group_size: int = 256) -> bool:
+    """Whether the library takes this linear: K a multiple of 8 whose rotated
+    width fits, and N within the row limit."""
+    K, N = linear.in_features, linear.out_features
+    return K % 8 == 0 and binding.rotated_width(K, group_size) <= binding.MAX_K and 1 <= N <= binding.MAX_ROWS
+
+
+@torch.no_grad()
+def convert_linears(model: torch.nn.Module, group_size: int = 256, rotation: str = "sylvester", path: str = "w4a4",
+                    include=None) -> list[str]:
+    """Replace, in place, every eligible ``nn.Linear`` of ``model`` (and whose
+    qualified name ``include(name)`` accepts, when given) by a ConvRotLinear
+    built from it -- the module swap of the convrot-mlx README, "What is
+    included".  Returns the names of the replaced linears."""
+    done = []
+    for name, parent in list(model.named_modules()):
+        for child_name, child in list(parent.named_children()):
+            full = f"{name}.{child_name}" if name else child_name
+            if type(child) is not torch.nn.Linear or not eligible(child, group_size):
+                continue
+            if include is not None and not include(full):
+                continue
+            setattr(parent, child_name, ConvRotLinear.from_linear(child, group_size, rotation, path))
+            done.append(full)
+    return done
