@@ -2,8 +2,10 @@
 """Benchmark of the ConvRot W4A4 linear on one MI355X.
 
 One step = one complete ``convrot_linear`` call (rotation, row absmax and
-INT4 quantization of the activations, INT8-MFMA product against the packed
-INT4 weight image, scale + bias epilogue to bf16) over one batch of seeded
+INT4 quantization of the activations, the integer product against the weight
+image -- on the FP6 matrix cores, where the INT4 codes are exact e2m3 values,
+or on the INT8 ones, as the library's plan picks -- and the scale + bias
+epilogue to bf16) over one batch of seeded
 synthetic input already resident in HBM.  The weight is prepared once before
 timing (an offline step; its time is reported separately).  Steps cycle
 through enough independent buffer sets (>= 512 MiB in total) that the 256 MiB
@@ -13,8 +15,9 @@ Prints one JSON line on stdout.  ``value`` is effective TOPS = 2*M*N*K per
 step time (the K timed steps run as one HIP graph).  ``roofline`` rates the
 dominant kernel -- the GEMM, or the whole linear where it is a single kernel
 (M <= 4) -- from its average launch duration (a pair of HIP events on the
-launch stream around each launch) against the dense
-INT8 matrix-core peak (or, for weight-streaming shapes, the HBM peak);
+launch stream around each launch) against the dense peak of the matrix
+cores it runs on (FP6 10.1 POP/s, INT8 5.0) or, for weight-streaming shapes,
+the HBM peak;
 ``traffic`` comes from the committed rocprofv3 byte counters when they match
 the current kernel source.  ``cpu_baseline`` is the CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvRot W4A4 linear effective TOPS + GB/s and % of roofline, FLUX shapes"
 DEFAULT_WORKLOAD = "flux_qkv_m1536_k3072_n9216"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 matrix-core peak, 5.0 POP/s
+PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 matrix-core peak, 10.1 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 KERNEL_SOURCE = os.path.join(ROOT, "w4a4_rotated_bit_amd", "csrc", "kernels.hip")
 
@@ -269,10 +273,12 @@ def main():
     # and activation codes, weight/activation scales, bias and Y.
     # (a single-kernel linear moves the whole path's algorithmic bytes)
     gemm_bytes = wl.bytes_alg if single else N * K // 2 + M * K // 2 + 4 * M + 4 * N + 2 * N + 2 * M * N
-    if ops / wl.bytes_alg >= PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+    kind = 0 if w4a16 else binding.convrot_linear_mfma_kind(M, K, N, g)
+    peak = PEAK_FP6_TOPS if kind == binding.CONVROT_MFMA_FP6 else PEAK_INT8_TOPS
+    if ops / wl.bytes_alg >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         ach = ops / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TOP/s",
+                "frac": round(ach / peak, 4), "traffic": traffic}
     else:
         ach = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -293,7 +299,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w4a16 else "int8",
+        "dtype": "bf16" if w4a16 else ("fp6" if kind == binding.CONVROT_MFMA_FP6 else "int8"),
         "data": "synthetic",
         "config": {"workload": wl.name, "M": M, "K": K, "N": N, "group": wl.g, "path": args.path,
                    "rotation": args.rotation,
@@ -302,7 +308,8 @@ def main():
                    "timed_as": "hip_graph" if graph is not None else "stream_launches"},
         "gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "int8_frac": round(value / PEAK_INT8_TOPS, 4),
+        "mfma_peak_tops": peak,
+        "mfma_frac": round(value / peak, 4),
         "kernel_us": ({"linear": round(gemm_ms * 1e3, 2)} if single else
                       {"prep": round(prep_ms * 1e3, 2), "gemm": round(gemm_ms * 1e3, 2)}),
         "weight_prep_ms": round(weight_prep_ms, 4),

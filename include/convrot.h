@@ -73,12 +73,14 @@ const char* convrot_version(void);
 
 /* ---- sizes (host only, no HIP call) ----------------------------------- */
 
-/* Bytes of the packed INT4 weight image for an N x K weight:
- * round_up(N, 32) * round_up(K_rot, 128) / 2.  Layout: 32-column x 128-K
+/* Bytes of the weight image for an N x K weight: the packed INT4 codes,
+ * round_up(N, 32) * round_up(K_rot, 128) / 2 bytes in 32-column x 128-K
  * units in MFMA fragment order (convrot-mlx README, "What is included": the
- * K x packed-N family of layouts, here tiled for CDNA4 matrix cores).  g must
- * be 64 or 256 (with or without CONVROT_REGULAR_HADAMARD).  Returns
- * CONVROT_OK or CONVROT_EINVAL. */
+ * K x packed-N family of layouts, here tiled for CDNA4 matrix cores), followed
+ * by the same codes as FP6 e2m3 values (every integer in [-7, 7] is exact in
+ * e2m3), round_up(N, 32) * round_up(K_rot, 128) * 3 / 4 bytes, for the FP6
+ * matrix cores of the large-M product.  g must be 64 or 256 (with or without
+ * CONVROT_REGULAR_HADAMARD).  Returns CONVROT_OK or CONVROT_EINVAL. */
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
 /* Bytes of workspace convrot_linear needs for an M x K input and N outputs.
@@ -87,14 +89,16 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
  *      convrot_prepare_activations, left cleared by every GEMM; at the same
  *      offset for every shape);
  *   2. offset CONVROT_WORKSPACE_IMAGE_OFFSET: the activation-code image,
- *      round_up(M, 32) * round_up(K, 128) / 2 bytes, INT4 codes in the same
- *      layout as the weight image;
- *   3. the activation scales sx: round_up(M, 32) floats;
- *   4. split-K partial tiles: when M > 32 and the 256 x 256 output tiles are
- *      too few to occupy the GPU, each tile's K range is shared by S
- *      workgroups and S - 1 int32 partial tiles of 256 KB per output tile
- *      live here (0 bytes otherwise).
- * Parts 1-3 depend on M and K only; convrot_prepare_activations needs only
+ *      round_up(M, 32) * round_up(K_rot, 128) / 2 bytes, INT4 codes in the
+ *      same layout as the weight image;
+ *   3. when M > 32, the same codes as FP6: round_up(M, 32) *
+ *      round_up(K_rot, 128) * 3 / 4 bytes;
+ *   4. the activation scales sx: round_up(M, 32) floats;
+ *   5. split-K partial tiles: when M > 32 and the output tiles are too few
+ *      to occupy the GPU, each tile's K range is shared by S workgroups and
+ *      S - 1 partial tiles of 4-byte sums per output tile live here (0 bytes
+ *      otherwise).
+ * Parts 1-4 depend on M and K only; convrot_prepare_activations needs only
  * them.  Returns CONVROT_OK or CONVROT_EINVAL. */
 #define CONVROT_WORKSPACE_IMAGE_OFFSET 2048
 int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes_host);
@@ -104,6 +108,15 @@ int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* byte
  * 2 (activation kernel, then GEMM), or 0 (M or N is 0).  Returns CONVROT_OK
  * or CONVROT_EINVAL. */
 int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* count_host);
+
+/* *kind = the matrix cores convrot_linear's integer product runs on for this
+ * shape: CONVROT_MFMA_I8 (INT8 MFMA on codes widened from INT4),
+ * CONVROT_MFMA_FP6 (FP6 e2m3 MFMA on the FP6 copy of the codes; exact: the
+ * codes are exact e2m3 values and the binary32 sums are exact integers), or
+ * 0 when M or N is 0.  Returns CONVROT_OK or CONVROT_EINVAL. */
+#define CONVROT_MFMA_I8 1
+#define CONVROT_MFMA_FP6 2
+int convrot_linear_mfma_kind(int64_t M, int64_t K, int64_t N, int g, int* kind_host);
 
 /* ---- argument checks (host only, no HIP call) ------------------------- */
 
@@ -241,6 +254,12 @@ int convrot_host_image_to_nk(const uint8_t* image_host, int64_t N, int64_t K, ui
 /* Activation-code image (workspace + CONVROT_WORKSPACE_IMAGE_OFFSET) -> int8
  * codes [M][K]. */
 int convrot_host_act_image_to_codes(const uint8_t* image_host, int64_t M, int64_t K, int8_t* codes_host);
+/* The FP6 copies, decoded: the FP6 part of a weight image -> N x packed-K,
+ * and the FP6 activation image of a workspace (whole workspace, M > 32) ->
+ * int8 codes [M][K].  K is the code width, a multiple of 64.  CONVROT_EINVAL
+ * also when a field is not the e2m3 pattern of an integer in [-7, 7]. */
+int convrot_host_image_fp6_to_nk(const uint8_t* image_host, int64_t N, int64_t K, uint8_t* nk_host);
+int convrot_host_workspace_fp6_codes(const uint8_t* workspace_host, int64_t M, int64_t K, int8_t* codes_host);
 
 #ifdef __cplusplus
 }

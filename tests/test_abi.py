@@ -43,6 +43,13 @@ def test_regular_flag_matches_header():
     assert m and int(m.group(1), 16) == B.CONVROT_REGULAR_HADAMARD
 
 
+def test_mfma_kinds_match_header():
+    text = open(HEADER).read()
+    for name in ("CONVROT_MFMA_I8", "CONVROT_MFMA_FP6"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(B, name)
+
+
 def test_version_and_status_strings():
     assert B.convrot_version().startswith("convrot-gfx950")
     for code in (0, 1, 2, 3, 4):
@@ -50,38 +57,60 @@ def test_version_and_status_strings():
     assert B.convrot_status_string(99) == "unknown status"
 
 
-@pytest.mark.parametrize("N,K,g,want", [
+def _int4_plane(rows, K):
+    """Bytes of the INT4 part of a weight image (rows padded to 32, K to 128)."""
+    return -(-rows // 32) * 32 * (-(-K // 128) * 128) // 2
+
+
+@pytest.mark.parametrize("N,K,g,int4", [
     (1024, 1024, 256, 1024 * 1024 // 2),
     (9216, 3072, 256, 9216 * 3072 // 2),
     (33, 192, 64, 64 * 256 // 2),        # N padded to 64, K to 256
 ])
-def test_weight_image_bytes(N, K, g, want):
-    assert B.convrot_weight_image_bytes(N, K, g) == want
+def test_weight_image_bytes(N, K, g, int4):
+    # the INT4 codes, then the same codes as FP6 (six bits each)
+    assert _int4_plane(N, K) == int4
+    assert B.convrot_weight_image_bytes(N, K, g) == int4 + int4 * 3 // 2
+
+
+def test_mfma_kind():
+    assert B.convrot_linear_mfma_kind(1536, 3072, 9216, 256) == B.CONVROT_MFMA_FP6     # 216 FP6 tiles
+    assert B.convrot_linear_mfma_kind(4096, 3072, 3072, 256) == B.CONVROT_MFMA_FP6
+    assert B.convrot_linear_mfma_kind(1536, 3072, 12288, 256) == B.CONVROT_MFMA_I8     # INT8 192 x 384
+    assert B.convrot_linear_mfma_kind(1536, 12288, 3072, 256) == B.CONVROT_MFMA_I8     # INT8 192 x 192, split
+    assert B.convrot_linear_mfma_kind(16, 3072, 12288, 256) == B.CONVROT_MFMA_I8       # weight streaming
+    assert B.convrot_linear_mfma_kind(0, 3072, 12288, 256) == 0
+    with pytest.raises(B.ConvRotError):
+        B.convrot_linear_mfma_kind(64, 1001, 64, 256)
 
 
 def test_workspace_bytes():
-    # image (M up to 32 rows, K up to 128, INT4) | sx | 512 counters | split-K partials,
+    # 512 counters (2048 B) | activation INT4 image (M up to 32 rows, K up to 128) |
+    # the same codes as FP6 when M > 32 (3/4 byte each) | sx | split-K partials,
     # each part 256-byte aligned (values worked out by hand from that layout)
-    # M <= 32: weight streaming, never split
-    assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 49152 + 256 + 2048
-    # 1536 x 3072 -> 9216: 216 tiles of 256 x 256 fill the GPU, no split
-    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 2359296 + 6144 + 2048
+    # M <= 32: weight streaming, never split, no FP6 image
+    assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 2048 + 49152 + 256
+    # 1536 x 3072 -> 9216: 216 FP6 tiles of 256 x 256 fill the GPU, no split
+    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 2048 + 2359296 + 3538944 + 6144
     # 1536 x 12288 -> 3072: 128 tiles of 192 x 192, K split 2 ways -> 1 partial tile of
-    # 192 x 192 int32 per tile (fewer partial bytes than 72 tiles of 256 x 256 split 3 ways)
-    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 9437184 + 6144 + 2048 + 128 * 147456
+    # 192 x 192 4-byte sums per tile (fewer partial bytes than 72 tiles of 256 x 256
+    # split 3 ways)
+    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 2048 + 9437184 + 14155776 + 6144 + 128 * 147456
     # 1536 x 3072 -> 12288: 288 tiles of 256 x 256 would take two rounds; 256 tiles
     # of 192 x 384 take one, unsplit
-    assert B.convrot_workspace_bytes(1536, 3072, 12288, 256) == 2359296 + 6144 + 2048
+    assert B.convrot_workspace_bytes(1536, 3072, 12288, 256) == 2048 + 2359296 + 3538944 + 6144
+    # 4096 x 3072 -> 3072: 192 FP6 tiles of 256 x 256, unsplit
+    assert B.convrot_workspace_bytes(4096, 3072, 3072, 256) == 2048 + 6291456 + 9437184 + 16384
     # 256 x 4096 -> 256: 2 x 2 tiles of 192 x 192; 32 K blocks split 2 ways (at least
     # 16 K blocks per split) -> 1 partial tile each
-    assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 524288 + 1024 + 2048 + 4 * 147456
+    assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 2048 + 524288 + 786432 + 1024 + 4 * 147456
     # 5 x 192 -> N: M <= 32
-    assert B.convrot_workspace_bytes(5, 192, 100, 64) == 32 * 256 // 2 + 256 + 2048
+    assert B.convrot_workspace_bytes(5, 192, 100, 64) == 2048 + 32 * 256 // 2 + 256
     # K not a multiple of g: sizes follow the rotated width (1000 -> 1024)
     assert B.convrot_workspace_bytes(64, 1000, 1024, 256) == B.convrot_workspace_bytes(64, 1024, 1024, 256)
-    assert B.convrot_weight_image_bytes(100, 328, 256) == 128 * 512 // 2
+    assert B.convrot_weight_image_bytes(100, 328, 256) == 128 * 512 // 2 * 5 // 2
     # N = 0: nothing to split
-    assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 9437184 + 6144 + 2048
+    assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 2048 + 9437184 + 14155776 + 6144
 
 
 @pytest.mark.parametrize("M,K,N,g,want", [(1, 3072, 12288, 256, 1), (4, 4096, 64, 256, 1), (5, 3072, 64, 256, 2),
@@ -200,9 +229,11 @@ def test_host_image_round_trip(N, K):
     image = B.convrot_host_nk_to_image(nk, N, K)
     assert image.size == B.convrot_weight_image_bytes(N, K, 64)
     assert np.array_equal(B.convrot_host_image_to_nk(image, N, K), nk)
-    # every code lands somewhere and the padding is zero: the image holds
+    assert np.array_equal(B.convrot_host_image_fp6_to_nk(image, N, K), nk)
+    # every code lands somewhere and the padding is zero: the INT4 part holds
     # exactly the nibbles of nk (as a multiset) plus zeros
-    nz_img = np.count_nonzero(np.concatenate([image & 0xF, image >> 4]))
+    int4 = image[:_int4_plane(N, K)]
+    nz_img = np.count_nonzero(np.concatenate([int4 & 0xF, int4 >> 4]))
     nz_nk = np.count_nonzero(np.concatenate([nk & 0xF, nk >> 4]))
     assert nz_img == nz_nk
 
@@ -214,9 +245,50 @@ def test_host_image_widening_property():
     rng = np.random.default_rng(1)
     codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
     image = B.convrot_host_nk_to_image(oracle.pack_nk(codes), N, K)
-    words = image.view(np.uint32)
+    words = image[:_int4_plane(N, K)].view(np.uint32)
     lo = ((words << 4) & 0xF0F0F0F0).astype(np.uint32).view(np.int8).astype(np.int32)
     hi = (words & 0xF0F0F0F0).astype(np.uint32).view(np.int8).astype(np.int32)
     assert np.all(lo % 16 == 0) and np.all(hi % 16 == 0)
     got = np.sort(np.concatenate([lo, hi]) // 16)
     assert np.array_equal(got, np.sort(codes.ravel().astype(np.int32)))
+
+
+def _e2m3_value(v):
+    """OCP MX FP6 E2M3: sign bit 5, exponent bits 4..3 (bias 1), mantissa bits
+    2..0; exponent 0 is subnormal (m / 8)."""
+    sign = -1.0 if v & 0x20 else 1.0
+    e, m = (v >> 3) & 3, v & 7
+    return sign * (m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 8.0))
+
+
+@pytest.mark.parametrize("N,K", [(32, 128), (70, 192), (5, 64)])
+def test_host_image_fp6_plane_by_definition(N, K):
+    """The FP6 part of a weight image, decoded here from its documented layout
+    (32-row x 128-K units of 3072 bytes; row r at 96 r; four 24-byte blocks per
+    row, block b holding codes 32 b + e at bit 6 e, stored at block position
+    b ^ f(r), f(r) = 2 r3 + (r2 xor r4) from the bits of r) with the OCP e2m3
+    value rule, gives back every code; padding decodes to 0."""
+    rng = np.random.default_rng(N + 3 * K)
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = B.convrot_host_nk_to_image(oracle.pack_nk(codes), N, K)
+    plane = image[_int4_plane(N, K):]
+    Np, Kp = -(-N // 32) * 32, -(-K // 128) * 128
+    assert plane.size == Np * Kp * 3 // 4
+    KB = Kp // 128
+    got = np.zeros((Np, Kp))
+    for n in range(Np):
+        for kb in range(KB):
+            base = ((n // 32) * KB + kb) * 3072 + (n % 32) * 96
+            phys = plane[base:base + 96]
+            logical = np.empty(96, np.uint8)
+            r = n % 32
+            f = (((r >> 3) & 1) << 1) | (((r >> 2) ^ (r >> 4)) & 1)
+            for blk in range(4):
+                src = blk ^ f
+                logical[24 * blk:24 * blk + 24] = phys[24 * src:24 * src + 24]
+            bits = np.unpackbits(logical, bitorder="little")
+            for kl in range(128):
+                v = int(sum(int(bits[6 * kl + i]) << i for i in range(6)))
+                got[n, kb * 128 + kl] = _e2m3_value(v)
+    assert np.array_equal(got[:N, :K], codes.astype(np.float64))
+    assert np.all(got[N:] == 0) and np.all(got[:, K:] == 0)

@@ -102,6 +102,8 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
     img = image.cpu().numpy()
     compare_codes(oracle.unpack_nk(gpu.convrot_host_image_to_nk(img, N, K), K), oq, osr, osw, "image codes")
     compare_codes(oracle.unpack_nk(nk.cpu().numpy(), K), oq, osr, osw, "nk codes")
+    # the FP6 copy in the image holds the same codes
+    assert np.array_equal(gpu.convrot_host_image_fp6_to_nk(img, N, K), gpu.convrot_host_image_to_nk(img, N, K))
     # the device repack of N x packed-K is byte-identical to the direct image
     image2 = gpu.convrot_repack_nk_to_image(nk, N, K)
     assert np.array_equal(image2.cpu().numpy(), img)
@@ -121,11 +123,12 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
 GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
                (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072),
                (256, 512, 8192), (100, 300, 6144), (20, 9000, 1024), (7, 17000, 256),
-               # 256 x 256 block tiles (216 of them, also ragged), 192 x 384 (256 of them, also
-               # ragged), 192 x 192 split 2 ways along K and 256 x 192 (256 of them, also
-               # ragged): the shapes the plan picks here
+               # FP6 256 x 256 block tiles (216 and 192 of them, also ragged), INT8 192 x 384
+               # (256 of them, also ragged), INT8 192 x 192 split 2 ways along K, and FP6
+               # 256 x 256 split 8 ways (also ragged): the shapes the plan picks here
                (1536, 9216, 128), (1500, 9000, 256), (1536, 12288, 128), (1500, 12000, 384),
-               (1536, 3072, 8192), (4096, 3072, 128), (4000, 3000, 256)]
+               (1536, 3072, 8192), (4096, 3072, 128), (4000, 3000, 256), (256, 3072, 16384),
+               (200, 3011, 16384)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -149,7 +152,7 @@ def test_gemm_i32_integer_edges(gpu):
     assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (64, 1024, 8192), (300, 700, 4096)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (64, 1024, 8192), (300, 700, 4096), (256, 4096, 12288)])
 def test_split_k_workspace_reuse(gpu, M, N, K):
     """Shapes whose tiles are split along K: a workspace full of garbage is
     cleared by the activation step, and repeated GEMMs on one workspace (the
@@ -195,6 +198,8 @@ def _linear_parity(gpu, x, w, bias, g):
     qx = gpu.workspace_act_codes(ws, M, K)
     orx = oracle.rotate_rows(x, g)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
+    if M > 32:  # the FP6 copy the block-tile GEMM reads holds the same codes
+        assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), qx)
     qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     compare_codes(qw, oq_w, oracle.rotate_rows(w, g), osw, "weight codes")
     rows_ok = np.all(qx == parts["qx"], axis=1) & bool(np.array_equal(qw, oq_w))

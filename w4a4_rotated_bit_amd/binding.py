@@ -58,6 +58,7 @@ _SIGNATURES = {
     "convrot_weight_image_bytes": ([_I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_workspace_bytes": ([_I64, _I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_linear_kernel_count": ([_I64, _I64, _I64, _I, ctypes.POINTER(_I)], _I),
+    "convrot_linear_mfma_kind": ([_I64, _I64, _I64, _I, ctypes.POINTER(_I)], _I),
     "convrot_validate_weight": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_validate_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_prepare_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
@@ -78,6 +79,8 @@ _SIGNATURES = {
     "convrot_host_nk_to_image": ([_P, _I64, _I64, _P], _I),
     "convrot_host_image_to_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_act_image_to_codes": ([_P, _I64, _I64, _P], _I),
+    "convrot_host_image_fp6_to_nk": ([_P, _I64, _I64, _P], _I),
+    "convrot_host_workspace_fp6_codes": ([_P, _I64, _I64, _P], _I),
 }
 
 
@@ -156,6 +159,17 @@ def convrot_workspace_bytes(M: int, K: int, N: int, g: int) -> int:
 def convrot_linear_kernel_count(M: int, K: int, N: int, g: int) -> int:
     out = _I(0)
     _call("convrot_linear_kernel_count", M, K, N, g, ctypes.byref(out))
+    return out.value
+
+
+CONVROT_MFMA_I8 = 1
+CONVROT_MFMA_FP6 = 2
+
+
+def convrot_linear_mfma_kind(M: int, K: int, N: int, g: int) -> int:
+    """CONVROT_MFMA_I8 or CONVROT_MFMA_FP6: the matrix cores of the product (0 if M or N is 0)."""
+    out = ctypes.c_int()
+    _call("convrot_linear_mfma_kind", M, K, N, g, ctypes.byref(out))
     return out.value
 
 
@@ -328,6 +342,23 @@ def convrot_host_image_to_nk(image, N: int, K: int) -> np.ndarray:
     p = _np(image, np.uint8)
     out = np.empty((N, K // 2), np.uint8)
     _call("convrot_host_image_to_nk", _hp(p), N, K, _hp(out))
+    return out
+
+
+def convrot_host_image_fp6_to_nk(image, N: int, K: int) -> np.ndarray:
+    """The FP6 copy of the codes in a weight image, as N x packed-K."""
+    p = _np(image, np.uint8)
+    out = np.empty((N, K // 2), np.uint8)
+    _call("convrot_host_image_fp6_to_nk", _hp(p), N, K, _hp(out))
+    return out
+
+
+def convrot_host_workspace_fp6_codes(workspace, M: int, K: int) -> np.ndarray:
+    """The FP6 activation codes of a workspace (M > 32), as int8 [M, K]."""
+    ws = workspace.cpu().numpy() if hasattr(workspace, "cpu") else np.asarray(workspace)
+    p = _np(ws, np.uint8)
+    out = np.empty((M, K), np.int8)
+    _call("convrot_host_workspace_fp6_codes", _hp(p), M, K, _hp(out))
     return out
 
 

@@ -60,6 +60,7 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)ws + workspace_image_offset();
+    a.out6 = act_has_fp6(M) ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
@@ -74,6 +75,8 @@ GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, cons
     GemmArgs a{};
     a.act = (const uint8_t*)ws + workspace_image_offset();
     a.wgt = (const uint8_t*)image;
+    a.act6 = (const uint8_t*)ws + workspace_image6_offset(M, K);
+    a.wgt6 = (const uint8_t*)image + weight_image6_offset(N, K);
     a.sx = (const float*)((const uint8_t*)ws + workspace_sx_offset(M, K));
     a.sw = sw;
     a.bias = (const uint16_t*)bias;
@@ -119,6 +122,7 @@ int convrot_prepare_weight(const void* W, int64_t N, int64_t K, int g, void* ima
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)image;
+    a.out6 = (uint8_t*)image + weight_image6_offset(N, Kr);
     a.scales = sw;
     launch_prep(g, OUT_IMAGE, a, as_stream(stream));
     return launched();
@@ -150,7 +154,8 @@ int convrot_repack_nk_to_image(const uint8_t* qweight_nk, int64_t N, int64_t K, 
     if (N == 0) return CONVROT_OK;
     if (!qweight_nk || !image || !aligned(qweight_nk, 16) || !aligned(image, 16)) return CONVROT_EINVAL;
     if ((rc = check_device())) return rc;
-    launch_repack_nk(qweight_nk, N, K, (uint8_t*)image, as_stream(stream));
+    launch_repack_nk(qweight_nk, N, K, (uint8_t*)image, (uint8_t*)image + weight_image6_offset(N, K),
+                     as_stream(stream));
     return launched();
 }
 
@@ -259,7 +264,8 @@ int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, 
     if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    launch_act_relayout(qx, M, K, (uint8_t*)ws + workspace_image_offset(), (uint32_t*)ws,
+    uint8_t* image6 = act_has_fp6(M) ? (uint8_t*)ws + workspace_image6_offset(M, K) : nullptr;
+    launch_act_relayout(qx, M, K, (uint8_t*)ws + workspace_image_offset(), image6, (uint32_t*)ws,
                         2 * kSplitCounters, s);
     if ((rc = launched())) return rc;
     return enqueue_gemm(GEMM_OUT_I32, ws, M, K, image, nullptr, nullptr, N, acc, s);

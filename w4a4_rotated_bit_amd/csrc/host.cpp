@@ -27,13 +27,19 @@ int check_shape(int64_t rows, int64_t K, int g)
 
 // Workspace layout (each part 256-byte aligned): the split-K counters at
 // offset 0 -- the same place for every shape, so a workspace reused across
-// shapes keeps them cleared -- then the activation image, sx, and the split-K
-// partial tiles.
+// shapes keeps them cleared -- then the activation INT4 image, the activation
+// FP6 image (M > 32), sx, and the split-K partial tiles.
 size_t workspace_image_offset() { return CONVROT_WORKSPACE_IMAGE_OFFSET; }
+
+size_t workspace_image6_offset(int64_t M, int64_t K)
+{
+    return (size_t)round_up((int64_t)(workspace_image_offset() + image_bytes(M, K)), 256);
+}
 
 size_t workspace_sx_offset(int64_t M, int64_t K)
 {
-    return (size_t)round_up((int64_t)(workspace_image_offset() + image_bytes(M, K)), 256);
+    const size_t fp6 = act_has_fp6(M) ? image6_bytes(M, K) : 0;
+    return (size_t)round_up((int64_t)(workspace_image6_offset(M, K) + fp6), 256);
 }
 
 size_t workspace_partial_offset(int64_t M, int64_t K)
@@ -69,7 +75,7 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
     if (!bytes) return CONVROT_EINVAL;
     int rc = check_shape(N, K, g);
     if (rc) return rc;
-    *bytes = image_bytes(N, rotated_width(K, g));
+    *bytes = weight_image_bytes(N, rotated_width(K, g));
     return CONVROT_OK;
 }
 
@@ -90,6 +96,22 @@ int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* cou
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
     *count = (M == 0 || N == 0) ? 0 : single_kernel_linear(M, rotated_width(K, g), g) ? 1 : 2;
+    return CONVROT_OK;
+}
+
+int convrot_linear_mfma_kind(int64_t M, int64_t K, int64_t N, int g, int* kind)
+{
+    if (!kind) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, g);
+    if (rc) return rc;
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    if (M == 0 || N == 0) {
+        *kind = 0;
+        return CONVROT_OK;
+    }
+    // M <= 32 streams the weight through the INT8 16x16x64 MFMA
+    const bool fp6 = M > 32 && gemm_shape_fp6(gemm_plan(M, N, rotated_width(K, g)).shape);
+    *kind = fp6 ? CONVROT_MFMA_FP6 : CONVROT_MFMA_I8;
     return CONVROT_OK;
 }
 
@@ -196,17 +218,77 @@ int convrot_host_kn_to_nk(const uint8_t* kn, int64_t N, int64_t K, uint8_t* nk)
     return CONVROT_OK;
 }
 
+// Six-bit field of code (row, k) in an FP6 image: bit i of the field is bit
+// 6 (k % 128) + i of the row's logical byte string.
+static void fp6_put(uint8_t* image6, int64_t row, int64_t k, int64_t K_pad, uint32_t v)
+{
+    for (int i = 0; i < 6; ++i) {
+        const int bit = 6 * (int)(k % kTileK) + i;
+        uint8_t* p = image6 + image6_byte_offset(row, k / kTileK, bit >> 3, K_pad);
+        *p = (uint8_t)((*p & ~(1u << (bit & 7))) | (((v >> i) & 1u) << (bit & 7)));
+    }
+}
+
+static uint32_t fp6_get(const uint8_t* image6, int64_t row, int64_t k, int64_t K_pad)
+{
+    uint32_t v = 0;
+    for (int i = 0; i < 6; ++i) {
+        const int bit = 6 * (int)(k % kTileK) + i;
+        v |= (uint32_t)((image6[image6_byte_offset(row, k / kTileK, bit >> 3, K_pad)] >> (bit & 7)) & 1u) << i;
+    }
+    return v;
+}
+
+// e2m3 bit pattern -> code in [-7, 7]; -128 for a pattern that is no such code
+static int8_t fp6_code(uint32_t v)
+{
+    for (int q = -7; q <= 7; ++q)
+        if (fp6_e2m3(q) == v) return (int8_t)q;
+    return (int8_t)-128;
+}
+
 int convrot_host_nk_to_image(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image)
 {
     if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
     const int64_t K_pad = round_up(K, kTileK);
-    memset(image, 0, image_bytes(N, K));
+    memset(image, 0, weight_image_bytes(N, K));
+    uint8_t* image6 = image + weight_image6_offset(N, K);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; k += 8) {
             uint32_t word = 0;
             for (int b = 0; b < 4; ++b)
                 word |= (uint32_t)(nk_nib(nk, K, n, k + b) | (nk_nib(nk, K, n, k + 4 + b) << 4)) << (8 * b);
             memcpy(image + image_word_offset(n, k, K_pad), &word, 4);
+            for (int e = 0; e < 8; ++e) fp6_put(image6, n, k + e, K_pad, fp6_e2m3(sext4(nk_nib(nk, K, n, k + e))));
+        }
+    return CONVROT_OK;
+}
+
+int convrot_host_image_fp6_to_nk(const uint8_t* image, int64_t N, int64_t K, uint8_t* nk)
+{
+    if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
+    const int64_t K_pad = round_up(K, kTileK);
+    const uint8_t* image6 = image + weight_image6_offset(N, K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j) {
+            const int8_t c0 = fp6_code(fp6_get(image6, n, 2 * j, K_pad));
+            const int8_t c1 = fp6_code(fp6_get(image6, n, 2 * j + 1, K_pad));
+            if (c0 == -128 || c1 == -128) return CONVROT_EINVAL;
+            nk[n * (K / 2) + j] = (uint8_t)(((uint8_t)c0 & 0x0F) | (((uint8_t)c1 & 0x0F) << 4));
+        }
+    return CONVROT_OK;
+}
+
+int convrot_host_workspace_fp6_codes(const uint8_t* workspace, int64_t M, int64_t K, int8_t* codes)
+{
+    if (!workspace || !codes || M <= 32 || M > kMaxRows || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
+    const int64_t K_pad = round_up(K, kTileK);
+    const uint8_t* image6 = workspace + workspace_image6_offset(M, K);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            const int8_t c = fp6_code(fp6_get(image6, m, k, K_pad));
+            if (c == -128) return CONVROT_EINVAL;
+            codes[m * K + k] = c;
         }
     return CONVROT_OK;
 }

@@ -15,6 +15,7 @@ struct PrepArgs {
     int64_t K, K_pad;    // K: rotated row length (a whole number of groups); K_pad: K rounded up to 128 (image mode)
     int64_t ld;          // elements per row of X (<= K: the rest of a row is zero padding)
     uint8_t* out;        // codes in the layout of the mode
+    uint8_t* out6;       // OUT_IMAGE only: the FP6 image of the same codes, or nullptr
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
     uint32_t* zero;      // words cleared by workgroup 0 (split-K counters) or nullptr
@@ -23,8 +24,10 @@ struct PrepArgs {
 };
 
 struct GemmArgs {
-    const uint8_t* act;  // operand image of the activation codes
-    const uint8_t* wgt;  // operand image of the weight codes
+    const uint8_t* act;  // INT4 operand image of the activation codes
+    const uint8_t* wgt;  // INT4 operand image of the weight codes
+    const uint8_t* act6; // FP6 images of the same codes (block-tile FP6 shape)
+    const uint8_t* wgt6;
     const float* sx;     // [M]
     const float* sw;     // [N]
     const uint16_t* bias;  // bf16 [N] or nullptr
@@ -36,7 +39,7 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int splits;
     uint32_t* counters;  // 2 * kSplitCounters zeroed words (tickets, then finished writers)
-    int32_t* partial;    // (splits - 1) partial tiles per tile
+    int32_t* partial;    // (splits - 1) partial tiles per tile (int32 or binary32 sums)
 };
 
 // g: group size, optionally with kRegularHadamard (the rotation matrix)
@@ -48,8 +51,9 @@ void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s);
 // Whole linear in one launch when single_kernel_linear(M, K, g) holds; see
 // kernels.hip.
 void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s);
-void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
-                         hipStream_t s);
-void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s);
+// Layout moves into the INT4 image and, when image6 is not null, the FP6 image.
+void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint8_t* image6, uint32_t* zero,
+                         int zero_count, hipStream_t s);
+void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, uint8_t* image6, hipStream_t s);
 
 }  // namespace convrot

@@ -104,6 +104,28 @@ __device__ inline uint32_t image_word(const uint32_t* f)
     return (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u);
 }
 
+// The FP6 (e2m3) fields of P = 8 or 16 codes, six bits each in code order, in
+// the low 6 P bits of the result.  The hardware conversion takes two sets of
+// 16 binary32 values and interleaves them (field 2i from the first set, 2i + 1
+// from the second), so the even codes go in the first set and the odd codes in
+// the second; the slots past P / 2 only feed fields that are not kept.  The
+// inputs are the integer codes themselves (1.5 * 2^23 + code minus 1.5 * 2^23,
+// exact), so the conversion with unit scale is exact.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+template <int P>
+__device__ inline u32x6_t fp6_fields(const uint32_t (&f)[P])
+{
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    f32x16_t ev = __builtin_nondeterministic_value(ev), od = __builtin_nondeterministic_value(od);
+#pragma unroll
+    for (int i = 0; i < P / 2; ++i) {
+        ev[i] = __uint_as_float(f[2 * i]) - kMagic;
+        od[i] = __uint_as_float(f[2 * i + 1]) - kMagic;
+    }
+    return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+}
+
 // Max over a wave-row of DPP lanes.
 template <int CTRL>
 __device__ inline uint32_t max_dpp(uint32_t v)
@@ -404,6 +426,23 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
                 *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
             else
                 *(uint32_t*)dst = image_word(f);
+            if (a.out6) {
+                // the same codes into the FP6 image: 6 P bits from logical
+                // byte 24 (k0 % 128 / 32) + 6 P / 8 (k0 % 32 / P) of the row
+                const u32x6_t fp = fp6_fields<P>(f);
+                const int64_t kb = k0 / kTileK;
+                const int kl = (int)(k0 % kTileK);
+                const int b0 = 24 * (kl / 32) + (6 * P / 8) * ((kl % 32) / P);
+                if constexpr (P == 16) {
+                    // 12 bytes inside one 24-byte block: contiguous after the swizzle
+                    *(uint3*)(a.out6 + image6_byte_offset(row, kb, b0, a.K_pad)) = make_uint3(fp[0], fp[1], fp[2]);
+                } else {
+                    const uint16_t hw[3] = {(uint16_t)fp[0], (uint16_t)(fp[0] >> 16), (uint16_t)fp[1]};
+#pragma unroll
+                    for (int d = 0; d < 3; ++d)
+                        *(uint16_t*)(a.out6 + image6_byte_offset(row, kb, b0 + 2 * d, a.K_pad)) = hw[d];
+                }
+            }
         } else if constexpr (MODE == OUT_LDS) {
             const size_t unit_off = image_word_offset(row, k0, a.K_pad) % kUnitBytes;  // in-unit offset of row, k0
             uint8_t* dst = a.out + ((k0 / kTileK) * LDS_ROWS + row) * 64 + (unit_off % 64);
@@ -491,17 +530,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(REG ? 5 : 
 // ---------------------------------------------------------------------------
 // gemm_kernel
 //
-// Two block-tile shapes (GemmShape, chosen per problem by gemm_plan):
-//   shape 0: 256 (M) x 256 (N), eight waves (two per SIMD) in a 2 x 4 grid,
-//            each owning 128 x 64 = 4 x 2 MFMA tiles;
-//   shape 1: 192 (M) x 384 (N), eight waves in a 2 x 4 grid, each owning
-//            96 x 96 = 3 x 3 MFMA tiles -- the shape that covers
-//            1536 x 12288 in exactly 256 tiles;
-//   shape 2: 192 (M) x 192 (N), four waves (one per SIMD) in a 2 x 2 grid,
+// The INT8 block-tile shapes (GemmShape, chosen per problem by gemm_plan):
+//   shape 0: 192 (M) x 384 (N), eight waves (two per SIMD) in a 2 x 4 grid,
+//            each owning 96 x 96 = 3 x 3 MFMA tiles -- the shape that covers
+//            1536 x 12288 in exactly 256 tiles (the FP6 tile of 256 x 256
+//            would need two rounds);
+//   shape 1: 192 (M) x 192 (N), four waves (one per SIMD) in a 2 x 2 grid,
 //            each owning 96 x 96 -- 1536 x 3072 in 128 tiles, two K splits
-//            each, with half the partial-tile bytes of larger tiles;
-//   shape 3: 256 (M) x 192 (N), four waves in a 2 x 2 grid, each owning
-//            128 x 96 = 4 x 3 MFMA tiles -- 4096 x 3072 in exactly 256.
+//            each, with half the partial-tile bytes of larger tiles.
 // K advances 128 at a time through a ring of four LDS stages, each holding
 // the tile's activation units and then its weight units of the operand image
 // (2 KB each).  The image is stored in exactly the LDS order, so every
@@ -519,20 +555,13 @@ template <int SHAPE>
 struct GemmShape;
 template <>
 struct GemmShape<0> {
-    static constexpr int NW = 8, NWM = 2, BI = 4, BJ = 2;
-};
-template <>
-struct GemmShape<1> {
     static constexpr int NW = 8, NWM = 2, BI = 3, BJ = 3;
 };
 template <>
-struct GemmShape<2> {
+struct GemmShape<1> {
     static constexpr int NW = 4, NWM = 2, BI = 3, BJ = 3;
 };
-template <>
-struct GemmShape<3> {
-    static constexpr int NW = 4, NWM = 2, BI = 4, BJ = 3;
-};
+constexpr int kStages = 4;
 template <int SHAPE>
 struct GemmGeom : GemmShape<SHAPE> {
     using S = GemmShape<SHAPE>;
@@ -544,9 +573,9 @@ struct GemmGeom : GemmShape<SHAPE> {
     static constexpr int kStageA = UA * kUnitBytes;     // activation part of a stage
     static constexpr int kStage = (UA + UB) * kUnitBytes;
     static constexpr int COPIES = (2 * (UA + UB) + S::NW - 1) / S::NW;  // 1 KB copies per wave per stage
+    static constexpr int kLdsBytes = kStages * kStage;
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
 };
-constexpr int kStages = 4;
 
 // Global -> LDS copy of 16 bytes per lane from base + voff (voff per lane):
 // lane l's bytes land at LDS address M0 + 16 l.  Written as inline asm so
@@ -731,19 +760,38 @@ __device__ inline void lds_copy16_coherent(const uint8_t* g, uint32_t lds_addr)
                  : "memory", "m0");
 }
 
-template <int SHAPE>
+// The accumulators of the two matrix-core paths: the INT8 path enters both
+// operands times 16, so its int32 sums are 256 times the dot products; the
+// FP6 path's binary32 sums are the dot products themselves (exact integers).
+typedef float v16f __attribute__((ext_vector_type(16)));
+template <typename ACC>
+struct AccOps;
+template <>
+struct AccOps<v16i> {
+    __device__ static float value(const v16i& a, int r) { return (float)(a[r] >> 8); }
+    __device__ static int32_t ivalue(const v16i& a, int r) { return a[r] >> 8; }
+    __device__ static uint32_t bits(const v16i& a, int r) { return (uint32_t)a[r]; }
+    __device__ static void add(v16i& a, int r, uint32_t w) { a[r] += (int32_t)w; }
+};
+template <>
+struct AccOps<v16f> {
+    __device__ static float value(const v16f& a, int r) { return a[r]; }
+    __device__ static int32_t ivalue(const v16f& a, int r) { return (int32_t)a[r]; }
+    __device__ static uint32_t bits(const v16f& a, int r) { return __float_as_uint(a[r]); }
+    __device__ static void add(v16f& a, int r, uint32_t w) { a[r] += __uint_as_float(w); }  // exact: integers < 2^24
+};
+
+template <typename G, typename ACC>
 __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, int wave, int lane, uint32_t lds0,
-                                        const uint8_t* smem,
-                                        v16i (&acc)[GemmShape<SHAPE>::BJ][GemmShape<SHAPE>::BI])
+                                        const uint8_t* smem, ACC (&acc)[G::BJ][G::BI])
 {
-    using G = GemmGeom<SHAPE>;
     constexpr int BI = G::BI, BJ = G::BJ;
     constexpr int kThreads = G::NW * 64;
     constexpr int kWords = BJ * BI * 8;                // 8-byte words per thread
     constexpr int kSlotBytes = kThreads * kWords * 8;  // BM x BN int32
     constexpr int kHalf = kSlotBytes / 2;              // fits the stage ring
-    static_assert(kHalf <= kStages * G::kStage, "half a partial tile must fit in LDS");
-    static_assert(kSlotBytes == G::BM * G::BN * 4, "slot = one int32 tile");
+    static_assert(kHalf <= G::kLdsBytes, "half a partial tile must fit in LDS");
+    static_assert(kSlotBytes == G::BM * G::BN * 4, "slot = one tile of 4-byte sums");
     __shared__ int ticket_sh;
     uint32_t* tickets = a.counters + tile;
     uint32_t* finished = a.counters + kSplitCounters + tile;
@@ -761,7 +809,8 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int u = (j * BI + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
-                    const uint64_t v = (uint64_t)(uint32_t)acc[j][i][2 * q] | ((uint64_t)(uint32_t)acc[j][i][2 * q + 1] << 32);
+                    const uint64_t v = (uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q) |
+                                       ((uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q + 1) << 32);
                     __hip_atomic_store(dst + (size_t)u * kThreads + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
         __builtin_amdgcn_s_waitcnt(0);  // every store of this wave has completed
@@ -796,8 +845,8 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
                 const int u = half * (kWords / 2) + u2;
                 const int j = u / (BI * 8), i = (u / 8) % BI, q = u % 8;
                 const uint2 w = *(const uint2*)(smem + ((size_t)u2 * kThreads + tid) * 8);
-                acc[j][i][2 * q] += (int32_t)w.x;
-                acc[j][i][2 * q + 1] += (int32_t)w.y;
+                AccOps<ACC>::add(acc[j][i], 2 * q, w.x);
+                AccOps<ACC>::add(acc[j][i], 2 * q + 1, w.y);
             }
             __syncthreads();  // every read of this half is done before the next copy
         }
@@ -813,11 +862,133 @@ struct Const {
     static constexpr int value = V;
 };
 
+// Epilogue of a block tile: int32 stores (parity hook) or scale + bias to bf16
+// through LDS (every copy has landed and every wave is past its last LDS
+// read of the K loop when this runs).
+template <typename G, int OUT, typename ACC>
+__device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, int wn, int tid, int wave, int lane,
+                                     uint8_t* smem, const ACC (&acc)[G::BJ][G::BI])
+{
+    constexpr int NW = G::NW, BI = G::BI, BJ = G::BJ, WN = G::WN;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int64_t m_base = (int64_t)tm * G::BM + wm * (32 * BI);
+    const int64_t n_base = (int64_t)tn * G::BN + wn * WN;
+
+    // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
+    // register (row / 8) * 4 + row % 4; here rows are output columns n and
+    // columns are output rows m, so lane l holds row m = l % 32 and, per group
+    // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
+    if constexpr (OUT == GEMM_OUT_I32) {
+        const bool vec_ok = (a.N % 4) == 0;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+            const int64_t m = m_base + 32 * i + r32;
+            if (m >= a.M) continue;
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t n0 = n_base + 32 * j + 8 * t + 4 * h;
+                    if (n0 >= a.N) continue;
+                    int32_t v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = AccOps<ACC>::ivalue(acc[j][i], 4 * t + u);
+                    int32_t* dst = (int32_t*)a.out + m * a.N + n0;
+                    if (vec_ok) {
+                        *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
+                    } else {
+                        for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
+                    }
+                }
+        }
+    } else {
+        // The block's BN column scales and biases and BM row scales go
+        // through LDS (free again: every copy has landed and every wave has
+        // passed the last stage barrier) -- one cooperative load instead of
+        // per-lane scattered loads.  Then the bf16 output goes through a
+        // per-wave LDS tile of 32 rows x WN columns, one MFMA tile row at a
+        // time, and is stored as 16-byte row segments.  Row pitch 2*WN + 16
+        // bytes (36 banks modulo 64) keeps rows 16-byte aligned; rows r and
+        // r + 16 would still meet on the same banks, so in rows with
+        // half_swap(r) the two 8-byte halves of every 16-byte chunk trade
+        // places: the 8-byte writes of 16 (32-bank LDS) or 32 (64-bank LDS)
+        // consecutive lanes then hit distinct banks.
+        float* p_sw = (float*)smem;
+        float* p_b = p_sw + G::BN;
+        float* p_sx = p_b + G::BN;
+        constexpr int kPitch = 2 * WN + 16;
+        constexpr int kParamBytes = 4096;
+        constexpr int kChunks = WN / 8;              // 16-byte chunks per tile row
+        constexpr int kReads = 32 * kChunks / 64;    // chunks per lane per tile row block
+        static_assert(kReads * 64 == 32 * kChunks, "row chunks divide evenly over the lanes");
+        static_assert((2 * G::BN + G::BM) * 4 <= kParamBytes, "scales and biases fit");
+        static_assert(kParamBytes + NW * 32 * kPitch <= G::kLdsBytes, "epilogue staging must fit in LDS");
+        __syncthreads();
+        for (int e = tid; e < G::BN + G::BM; e += NW * 64) {
+            if (e < G::BN) {
+                const int64_t n = (int64_t)tn * G::BN + e;
+                const int64_t nc = n < a.N ? n : a.N - 1;
+                p_sw[e] = a.sw[nc];
+                p_b[e] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
+            } else {
+                const int64_t m = (int64_t)tm * G::BM + (e - G::BN);
+                p_sx[e - G::BN] = a.sx[m < a.M ? m : a.M - 1];
+            }
+        }
+        __syncthreads();
+        uint8_t* tile_lds = smem + kParamBytes + wave * (32 * kPitch);
+        const bool vec8 = (a.N % 8) == 0;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+            const float sxm = p_sx[wm * (32 * BI) + 32 * i + r32];
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
+                    const float4 sw4 = *(const float4*)(p_sw + wn * WN + nl);
+                    const float4 b4 = *(const float4*)(p_b + wn * WN + nl);
+                    const float sc[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        y[u] = __builtin_fmaf(AccOps<ACC>::value(acc[j][i], 4 * t + u) * sxm, sc[u], bb[u]);
+                    }
+                    *(uint2*)(tile_lds + r32 * kPitch + ((nl * 2) ^ half_swap(r32))) =
+                        make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+                }
+            // read back row segments: lane l takes the 16-byte chunks l + 64 s
+            // of the tile row block (row rho = chunk / kChunks)
+#pragma unroll
+            for (int sr = 0; sr < kReads; ++sr) {
+                const int idx = lane + 64 * sr;
+                const int rho = idx / kChunks;
+                const int c = idx % kChunks;
+                uint4 w = *(const uint4*)(tile_lds + rho * kPitch + c * 16);
+                if (half_swap(rho)) w = make_uint4(w.z, w.w, w.x, w.y);
+                const int64_t m = m_base + 32 * i + rho;
+                const int64_t n = n_base + 8 * c;
+                if (m >= a.M || n >= a.N) continue;
+                uint16_t* dst = (uint16_t*)a.out + m * a.N + n;
+                if (vec8 && n + 8 <= a.N) {
+                    // streaming store: Y is not read back by this kernel, and
+                    // keeping it out of the caches shortens the final drain
+                    __builtin_nontemporal_store(v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w}, (v4i*)dst);
+                } else {
+                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                    for (int u = 0; u < 8 && n + u < a.N; ++u) dst[u] = (uint16_t)(ww[u >> 1] >> (16 * (u & 1)));
+                }
+            }
+        }
+    }
+}
+
 template <int OUT, int SHAPE>
 __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(GemmArgs a)
 {
     using G = GemmGeom<SHAPE>;
-    constexpr int NW = G::NW, BI = G::BI, BJ = G::BJ, WN = G::WN;
+    constexpr int BI = G::BI, BJ = G::BJ;
     constexpr int kStage = G::kStage;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
@@ -925,120 +1096,228 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if (a.splits > 1 && !split_k_exchange<SHAPE>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
+}
 
-    const int64_t m_base = (int64_t)tm * G::BM + wm * (32 * BI);
-    const int64_t n_base = (int64_t)tn * G::BN + wn * WN;
+// ---------------------------------------------------------------------------
+// gemm6_kernel: the block-tile product on the FP6 matrix cores.
+//
+// The codes come from the FP6 images (layout.h): every integer code in
+// [-7, 7] is an exact e2m3 value, v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// block scales multiplies them exactly, and the binary32 sums are the exact
+// integer dot products (|dot| <= 802816 < 2^24), at twice the INT8 rate and
+// with no widening in registers.
+// Block tile 256 x 256 (Gemm6Geom: waves, their grid and MFMA tiles per wave).
+// K advances 128 at a time through a ring of three 48 KB LDS stages filled by
+// global -> LDS copies, two stages ahead.  A stage is two k-steps of 64; a lane's fragment
+// for one k-step is 24 bytes (32 codes), read as three ds_read_b64:
+//   k-step 0 fragments (X registers) feed 16 MFMAs while the k-step 1
+//     fragments of the same stage are read into Y;
+//   barrier: the next stage has landed everywhere and every wave is done
+//     reading this stage, whose buffer then takes the copy three stages on;
+//   Y feeds 16 MFMAs while the next stage's k-step 0 fragments are read into X.
+// Each stage so starts and ends with the same registers, and the body is
+// straight-line code.
+// ---------------------------------------------------------------------------
+template <int NW_, int NWM_, int BI_, int BJ_, int SHAPE_>
+struct Gemm6Geom {
+    static constexpr int NW = NW_, NWM = NWM_, BI = BI_, BJ = BJ_, SHAPE = SHAPE_;
+    static constexpr int NWN = NW / NWM;
+    static constexpr int BM = NWM * 32 * BI, BN = NWN * 32 * BJ, WN = 32 * BJ;
+    static constexpr int UA = BM / 32, UB = BN / 32;
+    static constexpr int kStageA = UA * kUnit6Bytes;
+    static constexpr int kStage = (UA + UB) * kUnit6Bytes;
+    static constexpr int kStages = 3;
+    static constexpr int kLdsBytes = kStages * kStage;
+    static constexpr int UPW = (UA + UB) / NW;          // units copied per wave per stage
+    static constexpr int COPIES = 3 * UPW;              // 1 KB copies per wave per stage
+    static_assert(UPW * NW == UA + UB && UA % UPW == 0, "a wave copies whole units of one operand");
+    static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
+};
+// Shape 2: eight waves, two per SIMD, each owning 128 x 64.  (Four waves of
+// 128 x 128 read a third fewer LDS bytes per MFMA, but with one wave per SIMD
+// every LDS wait stalls the matrix core: measured 14% slower on 1536 x 3072 x
+// 9216, and its epilogue has twice the work per wave.)
+using Gemm6W8 = Gemm6Geom<8, 2, 4, 2, 2>;
 
-    // D[row][col] of a 32x32 MFMA tile sits in lane col + 32 * ((row / 4) % 2),
-    // register (row / 8) * 4 + row % 4; here rows are output columns n and
-    // columns are output rows m, so lane l holds row m = l % 32 and, per group
-    // of four registers t, the four consecutive columns n = 8 t + 4 h + (0..3).
-    if constexpr (OUT == GEMM_OUT_I32) {
-        const bool vec_ok = (a.N % 4) == 0;
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// one lane's fragment (three 8-byte slots) as the MFMA operand: e2m3 reads
+// six registers
+__device__ inline v8i fp6_operand(const uint2 (&p)[3])
+{
+    v8i r = __builtin_nondeterministic_value(r);
+    r[0] = (int)p[0].x;
+    r[1] = (int)p[0].y;
+    r[2] = (int)p[1].x;
+    r[3] = (int)p[1].y;
+    r[4] = (int)p[2].x;
+    r[5] = (int)p[2].y;
+    return r;
+}
+
+// Wait until at most IN_FLIGHT stages of this wave's copies are outstanding
+// and its LDS reads have returned, then synchronise the workgroup.
+template <int COPIES, int IN_FLIGHT>
+__device__ inline void wait6_and_barrier()
+{
+    static_assert(IN_FLIGHT >= 0 && IN_FLIGHT * COPIES <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(IN_FLIGHT * COPIES) : "memory");
+}
+
+template <int OUT, typename G>
+__global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
+{
+    constexpr int BI = G::BI, BJ = G::BJ;
+    constexpr int kStage = G::kStage;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G::kLdsBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % G::NWM, wn = wave / G::NWM;
+
+    // XCD-aware order, as in gemm_kernel
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int total = tiles * a.splits;
+    const int wg = blockIdx.x;
+    const int qx = total / 8, rx = total % 8;
+    const int xcd = wg % 8, idx = wg / 8;
+    const int vid = xcd * qx + (xcd < rx ? xcd : rx) + idx;
+    const int split = vid / tiles, tile = vid % tiles;
+    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
+    const int kb0 = (int)((int64_t)split * a.KB / a.splits);
+    const int KC = (int)((int64_t)(split + 1) * a.KB / a.splits) - kb0;
+
+    v16f acc[BJ][BI];
 #pragma unroll
-        for (int i = 0; i < BI; ++i) {
-            const int64_t m = m_base + 32 * i + r32;
-            if (m >= a.M) continue;
+    for (int j = 0; j < BJ; ++j)
 #pragma unroll
-            for (int j = 0; j < BJ; ++j)
+        for (int i = 0; i < BI; ++i)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int64_t n0 = n_base + 32 * j + 8 * t + 4 * h;
-                    if (n0 >= a.N) continue;
-                    int32_t v[4];
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    // Copies: wave w moves units UPW w .. UPW (w + 1) - 1 of each stage
+    // (activation units 0 .. UA - 1, then the weight units), three 1 KB runs
+    // per unit.  Units past the end of the matrix re-read the last valid unit
+    // (their products land in rows / columns that are never stored).
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const bool copies_a = wave * G::UPW < G::UA;
+    const uint8_t* copy_src[G::UPW];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
-                    int32_t* dst = (int32_t*)a.out + m * a.N + n0;
-                    if (vec_ok) {
-                        *(int4*)dst = make_int4(v[0], v[1], v[2], v[3]);
-                    } else {
-                        for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
-                    }
-                }
-        }
-    } else {
-        // The block's BN column scales and biases and BM row scales go
-        // through LDS (free again: every copy has landed and every wave has
-        // passed the last stage barrier) -- one cooperative load instead of
-        // per-lane scattered loads.  Then the bf16 output goes through a
-        // per-wave LDS tile of 32 rows x WN columns, one MFMA tile row at a
-        // time, and is stored as 16-byte row segments.  Row pitch 2*WN + 16
-        // bytes (36 banks modulo 64) keeps rows 16-byte aligned; rows r and
-        // r + 16 would still meet on the same banks, so in rows with
-        // half_swap(r) the two 8-byte halves of every 16-byte chunk trade
-        // places: the 8-byte writes of 16 (32-bank LDS) or 32 (64-bank LDS)
-        // consecutive lanes then hit distinct banks.
-        float* p_sw = (float*)smem;
-        float* p_b = p_sw + G::BN;
-        float* p_sx = p_b + G::BN;
-        constexpr int kPitch = 2 * WN + 16;
-        constexpr int kParamBytes = 4096;
-        constexpr int kChunks = WN / 8;              // 16-byte chunks per tile row
-        constexpr int kReads = 32 * kChunks / 64;    // chunks per lane per tile row block
-        static_assert(kReads * 64 == 32 * kChunks, "row chunks divide evenly over the lanes");
-        static_assert((2 * G::BN + G::BM) * 4 <= kParamBytes, "scales and biases fit");
-        static_assert(kParamBytes + NW * 32 * kPitch <= kStages * kStage, "epilogue staging must fit in LDS");
-        __syncthreads();
-        for (int e = tid; e < G::BN + G::BM; e += NW * 64) {
-            if (e < G::BN) {
-                const int64_t n = (int64_t)tn * G::BN + e;
-                const int64_t nc = n < a.N ? n : a.N - 1;
-                p_sw[e] = a.sw[nc];
-                p_b[e] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
-            } else {
-                const int64_t m = (int64_t)tm * G::BM + (e - G::BN);
-                p_sx[e - G::BN] = a.sx[m < a.M ? m : a.M - 1];
-            }
-        }
-        __syncthreads();
-        uint8_t* tile_lds = smem + kParamBytes + wave * (32 * kPitch);
-        const bool vec8 = (a.N % 8) == 0;
-#pragma unroll
-        for (int i = 0; i < BI; ++i) {
-            const float sxm = p_sx[wm * (32 * BI) + 32 * i + r32];
-#pragma unroll
-            for (int j = 0; j < BJ; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
-                    const float4 sw4 = *(const float4*)(p_sw + wn * WN + nl);
-                    const float4 b4 = *(const float4*)(p_b + wn * WN + nl);
-                    const float sc[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-                    float y[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int32_t v = acc[j][i][4 * t + u] >> 8;  // both operands entered x 16
-                        y[u] = __builtin_fmaf((float)v * sxm, sc[u], bb[u]);
-                    }
-                    *(uint2*)(tile_lds + r32 * kPitch + ((nl * 2) ^ half_swap(r32))) =
-                        make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-                }
-            // read back row segments: lane l takes the 16-byte chunks l + 64 s
-            // of the tile row block (row rho = chunk / kChunks)
-#pragma unroll
-            for (int sr = 0; sr < kReads; ++sr) {
-                const int idx = lane + 64 * sr;
-                const int rho = idx / kChunks;
-                const int c = idx % kChunks;
-                uint4 w = *(const uint4*)(tile_lds + rho * kPitch + c * 16);
-                if (half_swap(rho)) w = make_uint4(w.z, w.w, w.x, w.y);
-                const int64_t m = m_base + 32 * i + rho;
-                const int64_t n = n_base + 8 * c;
-                if (m >= a.M || n >= a.N) continue;
-                uint16_t* dst = (uint16_t*)a.out + m * a.N + n;
-                if (vec8 && n + 8 <= a.N) {
-                    // streaming store: Y is not read back by this kernel, and
-                    // keeping it out of the caches shortens the final drain
-                    __builtin_nontemporal_store(v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w}, (v4i*)dst);
-                } else {
-                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-                    for (int u = 0; u < 8 && n + u < a.N; ++u) dst[u] = (uint16_t)(ww[u >> 1] >> (16 * (u & 1)));
-                }
-            }
-        }
+    for (int u = 0; u < G::UPW; ++u) {
+        const int ug = wave * G::UPW + u;
+        const int row_tile = copies_a ? min(tm * G::UA + ug, a.MT - 1) : min(tn * G::UB + ug - G::UA, a.NT - 1);
+        copy_src[u] = (copies_a ? a.act6 : a.wgt6) + (size_t)row_tile * a.KB * kUnit6Bytes;
     }
+    auto issue = [&](uint32_t stage, int kb) __attribute__((always_inline)) {
+        const uint32_t voff = (uint32_t)kb * kUnit6Bytes + lane * 16;
+#pragma unroll
+        for (int u = 0; u < G::UPW; ++u)
+#pragma unroll
+            for (int part = 0; part < 3; ++part)
+                lds_copy16(copy_src[u] + part * 1024, voff,
+                           stage + (G::UPW * wave + u) * kUnit6Bytes + part * 1024);
+    };
+
+    // Fragments: lane (r32, h) reads row r32 of its tiles' units, block
+    // 2 s + h for k-step s: three 8-byte slots at consecutive addresses.  The
+    // per-tile offsets are hidden from the compiler (an empty asm), so that it
+    // pairs the slots of one fragment (which land in operand order) rather
+    // than the same slot of two tiles (which would need register moves).
+    const int r32 = lane & 31, h = lane >> 5;
+    int ta[BI], tb[BJ];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        ta[i] = (wm * BI + i) * kUnit6Bytes + r32 * kRow6Bytes;
+        asm volatile("" : "+v"(ta[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+        tb[j] = G::kStageA + (wn * BJ + j) * kUnit6Bytes + r32 * kRow6Bytes;
+        asm volatile("" : "+v"(tb[j]));
+    }
+    const int blk[2] = {((0 + h) ^ row_swizzle6(r32)) * 24, ((2 + h) ^ row_swizzle6(r32)) * 24};
+    uint2 xa[BI][3], xb[BJ][3], ya[BI][3], yb[BJ][3];
+    auto read = [&](const uint8_t* stage, int st, uint2 (&ra)[BI][3], uint2 (&rb)[BJ][3]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+            const uint8_t* p = stage + ta[i] + blk[st];
+#pragma unroll
+            for (int x = 0; x < 3; ++x) ra[i][x] = *(const uint2*)(p + 8 * x);
+        }
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+            const uint8_t* p = stage + tb[j] + blk[st];
+#pragma unroll
+            for (int x = 0; x < 3; ++x) rb[j][x] = *(const uint2*)(p + 8 * x);
+        }
+    };
+    // acc[j][i] += W_j . X_i^T for one k-step (e2m3 x e2m3, unit scales)
+    auto mma = [&](const uint2 (&ra)[BI][3], const uint2 (&rb)[BJ][3]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int i = 0; i < BI; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(rb[j]), fp6_operand(ra[i]),
+                                                                            acc[j][i], 2, 2, 0, 127, 0, 127);
+    };
+    // each MFMA followed by its share of the 24 fragment reads of a phase
+    auto hints = [&](int reads) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < BI * BJ; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (reads > 0) {
+                if (m % 2 == 0)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                else
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+    };
+
+    // prologue: up to three stages in flight; wait for stage 0
+    const int first = KC < G::kStages ? KC : G::kStages;
+    for (int st = 0; st < first; ++st) issue(lds0 + st * kStage, kb0 + st);
+    if (first >= 3)
+        wait6_and_barrier<G::COPIES, 2>();
+    else if (first == 2)
+        wait6_and_barrier<G::COPIES, 1>();
+    else
+        wait6_and_barrier<G::COPIES, 0>();
+    read(smem, 0, xa, xb);
+
+    // One stage.  ISSUE: copy stage kr + 3 into this stage's buffer;
+    // IN_FLIGHT: stages that may still be in flight at the barrier; MORE: a
+    // stage kr + 1 follows.
+    auto step = [&](int kr, auto issue_c, auto in_flight_c, auto more_c) __attribute__((always_inline)) {
+        constexpr bool ISSUE = decltype(issue_c)::value != 0;
+        constexpr int IN_FLIGHT = decltype(in_flight_c)::value;
+        constexpr bool MORE = decltype(more_c)::value != 0;
+        const int slot_kr = kr % G::kStages;
+        const uint8_t* cur = smem + slot_kr * kStage;
+        read(cur, 1, ya, yb);
+        mma(xa, xb);
+        hints(24);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MORE) {
+            wait6_and_barrier<G::COPIES, IN_FLIGHT>();
+            if constexpr (ISSUE) issue(lds0 + slot_kr * kStage, kb0 + kr + G::kStages);
+            read(smem + ((kr + 1) % G::kStages) * kStage, 0, xa, xb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ya, yb);
+        hints(MORE ? 24 : 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kr = 0; kr < KC - G::kStages; ++kr) step(kr, Const<1>{}, Const<1>{}, Const<1>{});
+    if (KC >= 3) step(KC - 3, Const<0>{}, Const<1>{}, Const<1>{});
+    if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
+    step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
+
+    if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1481,9 +1760,23 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
 // layout kernels
 // ---------------------------------------------------------------------------
 
-// int8 codes [M][K] -> operand image (zero padding); one thread per 8 codes.
+// The FP6 fields of codes k .. k+7 (code e at bits 6 e) into the FP6 image:
+// three 16-bit pieces from logical byte 24 (k % 128 / 32) + 6 (k % 32 / 8).
+__device__ inline void store_fp6_8(uint8_t* image6, int64_t row, int64_t k, int64_t K_pad, const int (&q)[8])
+{
+    uint64_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v |= (uint64_t)fp6_e2m3(q[e]) << (6 * e);
+    const int kl = (int)(k % kTileK);
+    const int b0 = 24 * (kl / 32) + 6 * ((kl % 32) / 8);
+#pragma unroll
+    for (int d = 0; d < 3; ++d)
+        *(uint16_t*)(image6 + image6_byte_offset(row, k / kTileK, b0 + 2 * d, K_pad)) = (uint16_t)(v >> (16 * d));
+}
+
+// int8 codes [M][K] -> operand images (zero padding); one thread per 8 codes.
 __global__ void act_relayout_kernel(const int8_t* codes, int64_t M, int64_t K, int64_t M_pad, int64_t K_pad,
-                                    uint8_t* image, uint32_t* zero, int zero_count)
+                                    uint8_t* image, uint8_t* image6, uint32_t* zero, int zero_count)
 {
     const int64_t words_per_row = K_pad / 8;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1491,6 +1784,7 @@ __global__ void act_relayout_kernel(const int8_t* codes, int64_t M, int64_t K, i
     if (t >= M_pad * words_per_row) return;
     const int64_t m = t / words_per_row, k = (t % words_per_row) * 8;
     uint32_t out = 0;
+    int q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (m < M && k < K) {
         const uint2 in = *(const uint2*)(codes + m * K + k);  // codes k..k+7, one per byte
 #pragma unroll
@@ -1498,20 +1792,24 @@ __global__ void act_relayout_kernel(const int8_t* codes, int64_t M, int64_t K, i
             const uint32_t c_lo = (in.x >> (8 * b)) & 0xFu;  // code k + b
             const uint32_t c_hi = (in.y >> (8 * b)) & 0xFu;  // code k + 4 + b
             out |= (c_lo | (c_hi << 4)) << (8 * b);
+            q[b] = (int)(int8_t)(in.x >> (8 * b));
+            q[4 + b] = (int)(int8_t)(in.y >> (8 * b));
         }
     }
     *(uint32_t*)(image + image_word_offset(m, k, K_pad)) = out;
+    if (image6) store_fp6_8(image6, m, k, K_pad, q);
 }
 
-// N x packed-K [N][K/2] -> operand image (zero padding); one thread per 8 codes.
+// N x packed-K [N][K/2] -> operand images (zero padding); one thread per 8 codes.
 __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_t N_pad, int64_t K_pad,
-                                 uint8_t* image)
+                                 uint8_t* image, uint8_t* image6)
 {
     const int64_t words_per_col = K_pad / 8;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= N_pad * words_per_col) return;
     const int64_t n = t / words_per_col, k = (t % words_per_col) * 8;
     uint32_t out = 0;
+    int q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n < N && k < K) {
         const uint32_t in = *(const uint32_t*)(nk + n * (K / 2) + k / 2);  // codes k..k+7, two per byte
 #pragma unroll
@@ -1519,9 +1817,12 @@ __global__ void repack_nk_kernel(const uint8_t* nk, int64_t N, int64_t K, int64_
             const uint32_t c_lo = (in >> (4 * b)) & 0xFu;        // code k + b
             const uint32_t c_hi = (in >> (4 * (b + 4))) & 0xFu;  // code k + 4 + b
             out |= (c_lo | (c_hi << 4)) << (8 * b);
+            q[b] = ((int)(c_lo << 28)) >> 28;
+            q[4 + b] = ((int)(c_hi << 28)) >> 28;
         }
     }
     *(uint32_t*)(image + image_word_offset(n, k, K_pad)) = out;
+    if (image6) store_fp6_8(image6, n, k, K_pad, q);
 }
 
 // ---------------------------------------------------------------------------
@@ -1626,30 +1927,24 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     }
     if (a.splits < 1) a.splits = 1;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
-    if (a.shape == 0) {
+    if (a.shape == 2) {
+        const dim3 block(Gemm6W8::NW * 64);
+        if (out_mode == GEMM_OUT_I32)
+            hipLaunchKernelGGL((gemm6_kernel<GEMM_OUT_I32, Gemm6W8>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm6_kernel<GEMM_OUT_BF16, Gemm6W8>), grid, block, 0, s, a);
+    } else if (a.shape == 0) {
         const dim3 block(GemmShape<0>::NW * 64);
         if (out_mode == GEMM_OUT_I32)
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 0>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 0>), grid, block, 0, s, a);
-    } else if (a.shape == 1) {
+    } else {
         const dim3 block(GemmShape<1>::NW * 64);
         if (out_mode == GEMM_OUT_I32)
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
-    } else if (a.shape == 2) {
-        const dim3 block(GemmShape<2>::NW * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 2>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 2>), grid, block, 0, s, a);
-    } else {
-        const dim3 block(GemmShape<3>::NW * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 3>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 3>), grid, block, 0, s, a);
     }
 }
 
@@ -1689,22 +1984,22 @@ void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s)
         hipLaunchKernelGGL((w4a16_kernel<2, 3>), grid, block, 0, s, a, xr);
 }
 
-void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint32_t* zero, int zero_count,
-                         hipStream_t s)
+void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* image, uint8_t* image6, uint32_t* zero,
+                         int zero_count, hipStream_t s)
 {
     const int64_t M_pad = round_up(M, kTileRows), K_pad = round_up(K, kTileK);
     int64_t n = M_pad * (K_pad / 8);
     if (n < zero_count) n = zero_count;
     hipLaunchKernelGGL(act_relayout_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, M, K, M_pad,
-                       K_pad, image, zero, zero_count);
+                       K_pad, image, image6, zero, zero_count);
 }
 
-void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, hipStream_t s)
+void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, uint8_t* image6, hipStream_t s)
 {
     const int64_t N_pad = round_up(N, kTileRows), K_pad = round_up(K, kTileK);
     const int64_t n = N_pad * (K_pad / 8);
     hipLaunchKernelGGL(repack_nk_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, nk, N, K, N_pad, K_pad,
-                       image);
+                       image, image6);
 }
 
 }  // namespace convrot

@@ -70,6 +70,65 @@ CONVROT_HD inline size_t image_word_offset(int64_t row, int64_t k, int64_t K_pad
            (size_t)((ks % 2) * 8 + d * 4);
 }
 
+// ---- FP6 operand image ------------------------------------------------------
+// The same codes once more, as FP6 values for the FP6 matrix cores: OCP e2m3
+// (sign, two exponent bits with bias 1, three mantissa bits) holds every
+// integer in [-7, 7] exactly, and binary32 sums of their products are exact
+// integers while below 2^24 (|dot| <= 49 K <= 802816).
+//
+//   unit (rt, kb) = rows [32 rt, 32 rt + 32) x k [128 kb, 128 kb + 128),
+//   3072 bytes at ((rt * KB) + kb) * 3072; row r owns bytes [96 r, 96 r + 96).
+//   The row is four 24-byte blocks: block b holds codes 32 b .. 32 b + 31, six
+//   bits each, code 32 b + e at bit 6 e of the block read as one little-endian
+//   bit string -- exactly the six registers one lane feeds to a 32x32x64 FP6
+//   MFMA.  Block b is stored at block position b ^ row_swizzle6(r).
+//
+// Swizzle: a fragment is read as three 8-byte slots (0, 1, 2 of its block);
+// each read has the lanes of a half wave read the same slot of the same
+// logical block of 32 consecutive rows (96-byte stride).  Row r's block b
+// sits at b ^ f(r), f(r) = 2 r3 + (r2 ^ r4) (bits of r).  In 8-byte units the
+// slot addresses are 12 r + 3 (b ^ f(r)) + slot: modulo 16 (a 128-byte window)
+// they differ for any 16 consecutive rows, because f tells apart the four rows
+// of each residue r mod 4 (r2, r3 vary), and modulo 32 (a 256-byte window) for
+// all 32 rows, because f tells apart the four rows of each residue r mod 8
+// (r3, r4 vary): free of bank conflicts whether the LDS serves 16 lanes from
+// 32 banks or 32 lanes from 64 banks per cycle.
+constexpr int kUnit6Bytes = 3072;  // 32 rows x 128 codes x 6 bits
+constexpr int kRow6Bytes = 96;
+
+CONVROT_HD inline int row_swizzle6(int r) { return (((r >> 3) & 1) << 1) | (((r >> 2) ^ (r >> 4)) & 1); }
+
+CONVROT_HD inline size_t image6_bytes(int64_t rows, int64_t K)
+{
+    return (size_t)round_up(rows, kTileRows) * (size_t)round_up(K, kTileK) * 3 / 4;
+}
+
+// Byte offset of logical byte b (0 .. 95) of row `row`, 128-K block kb.
+CONVROT_HD inline size_t image6_byte_offset(int64_t row, int64_t kb, int b, int64_t K_pad)
+{
+    const int64_t KB = K_pad / kTileK;
+    const int64_t rt = row / kTileRows, r = row % kTileRows;
+    return (size_t)(rt * KB + kb) * kUnit6Bytes + (size_t)r * kRow6Bytes +
+           (size_t)(((b / 24) ^ row_swizzle6((int)r)) * 24 + b % 24);
+}
+
+// OCP FP6 e2m3 bit pattern of an integer code in [-7, 7].
+CONVROT_HD inline uint32_t fp6_e2m3(int q)
+{
+    const uint32_t mag = (uint32_t)(q < 0 ? -q : q);
+    const uint32_t enc = (0xFEDCA840u >> (4 * mag)) & 0xFu;  // |q| = 0..7 -> 0, 4, 8, 10, 12, 13, 14, 15 (halved)
+    return (q < 0 ? 0x20u : 0u) | (enc << 1);
+}
+
+// The weight image: the INT4 image of the N rows (read by the weight-streaming
+// kernels), then the FP6 image of the same codes (read by the FP6 GEMM).
+CONVROT_HD inline size_t weight_image_bytes(int64_t N, int64_t K) { return image_bytes(N, K) + image6_bytes(N, K); }
+CONVROT_HD inline size_t weight_image6_offset(int64_t N, int64_t K) { return image_bytes(N, K); }
+
+// Activations get an FP6 image too when the product goes to the block-tile
+// GEMM (M > 32 rows).
+CONVROT_HD inline bool act_has_fp6(int64_t M) { return M > 32; }
+
 // ---- rotation ---------------------------------------------------------------
 // The group-size argument g is 64 or 256, optionally with this flag: rotate
 // with the regular Hadamard matrix instead of the Sylvester one.
@@ -88,27 +147,34 @@ CONVROT_HD inline int64_t rotated_width(int64_t K, int g)
 constexpr int64_t kW4A16MaxRows = 32;
 
 // ---- GEMM plan -------------------------------------------------------------
-// The GEMM covers the output with one of four block tiles: shape 0 is
-// 256 x 256, shape 1 is 192 x 384, shape 2 is 192 x 192, shape 3 is
-// 256 x 192.  When there are too
-// few tiles to fill the chip, each tile's K range is split over S workgroups
-// (the integer partial sums are exact in any order): S is the largest value
-// <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks per split.
-// Of the shapes the plan takes the one with the smallest estimated time:
-// rounds of workgroups x 128-K blocks per workgroup x tile area at about
-// 24 ns per 1024 outputs per block, one prologue + epilogue (about 4 us) per
-// round, and for a split the exchange of (S - 1) int32 partial tiles per tile
-// through memory (written and read back at about 4 TB/s, plus 3 us).
-// M <= 32 goes to the weight-streaming kernels and is never split.
+// The GEMM covers the output with one of three block tiles.  Shapes 0 and 1
+// run on the INT8 matrix cores from the INT4 image: shape 0 is 192 x 384,
+// shape 1 is 192 x 192.  Shape 2 is 256 x 256 on the FP6 matrix cores from
+// the FP6 image (twice the INT8 rate; bound by LDS bandwidth rather than by
+// the matrix cores), the fastest per output where its tiles fill the chip.
+// When there are too few tiles to fill the chip, each tile's K range is split
+// over S workgroups (the integer partial sums are exact in any order): S is the
+// largest value <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks
+// per split.  Of the shapes the plan takes the one with the smallest estimated
+// time: rounds of workgroups x 128-K blocks per workgroup x tile area at
+// gemm_shape_ns per 1024 outputs per block (measured on MI355X on the FLUX
+// shapes), one prologue +
+// epilogue (about 4 us) per round, and for a split the exchange of (S - 1)
+// 4-byte partial tiles per tile through memory (written and read back at
+// about 4 TB/s, plus 3 us).  M <= 32 goes to the weight-streaming kernels and
+// is never split.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
 constexpr int kSplitCounters = 256;    // counter slots (tiles of a split launch <= 128)
-constexpr int kGemmShapes = 4;
+constexpr int kGemmShapes = 3;
 
-CONVROT_HD constexpr int gemm_tile_m(int shape) { return (shape == 0 || shape == 3) ? 256 : 192; }
-CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 256 : (shape == 1 ? 384 : 192); }
+CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 2 ? 256 : 192; }
+CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 384 : (shape == 1 ? 192 : 256); }
+CONVROT_HD constexpr bool gemm_shape_fp6(int shape) { return shape == 2; }
+// nanoseconds per 1024 outputs per 128-K block, by shape
+CONVROT_HD constexpr int gemm_shape_ns(int shape) { return shape == 0 ? 29 : (shape == 1 ? 26 : 20); }
 
 struct GemmPlan {
-    int shape;             // block tile shape (0 .. 3)
+    int shape;             // block tile shape (0 .. 2)
     int tiles_m, tiles_n;  // block tiles along M and N
     int splits;            // workgroups per tile along K
 };
@@ -126,7 +192,7 @@ CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
         int S = 1;
         while (S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
         const int64_t rounds = (tiles * S + kSplitTargetWGs - 1) / kSplitTargetWGs;
-        int64_t ns = rounds * ((KB + S - 1) / S) * (bm * bn / 1024) * 24 + rounds * 4000;
+        int64_t ns = rounds * ((KB + S - 1) / S) * (bm * bn / 1024) * gemm_shape_ns(shape) + rounds * 4000;
         if (S > 1) ns += tiles * (S - 1) * bm * bn * 8 / 4000 + 3000;
         if (best_ns < 0 || ns < best_ns) {
             best_ns = ns;
@@ -138,7 +204,7 @@ CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
 
 CONVROT_HD inline int gemm_splits(int64_t M, int64_t N, int64_t K) { return gemm_plan(M, N, K).splits; }
 
-// Bytes of split-K partial tiles: (S - 1) int32 block tiles per tile.
+// Bytes of split-K partial tiles: (S - 1) block tiles of 4-byte sums per tile.
 CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
 {
     const GemmPlan p = gemm_plan(M, N, K);
