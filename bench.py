@@ -273,7 +273,7 @@ def main():
     # and activation codes, weight/activation scales, bias and Y.
     # (a single-kernel linear moves the whole path's algorithmic bytes)
     gemm_bytes = wl.bytes_alg if single else N * K // 2 + M * K // 2 + 4 * M + 4 * N + 2 * N + 2 * M * N
-    kind = 0 if w4a16 else binding.convrot_linear_mfma_kind(M, K, N, g)
+    kind = 0 if w4a16 else binding.convrot_linear_plan(M, K, N, g)["mfma"]
     peak = PEAK_FP6_TOPS if kind == binding.CONVROT_MFMA_FP6 else PEAK_INT8_TOPS
     if ops / wl.bytes_alg >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         ach = ops / (gemm_ms * 1e-3) / 1e12

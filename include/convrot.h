@@ -109,14 +109,18 @@ int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* byte
  * or CONVROT_EINVAL. */
 int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* count_host);
 
-/* *kind = the matrix cores convrot_linear's integer product runs on for this
- * shape: CONVROT_MFMA_I8 (INT8 MFMA on codes widened from INT4),
- * CONVROT_MFMA_FP6 (FP6 e2m3 MFMA on the FP6 copy of the codes; exact: the
- * codes are exact e2m3 values and the binary32 sums are exact integers), or
- * 0 when M or N is 0.  Returns CONVROT_OK or CONVROT_EINVAL. */
+/* The plan of convrot_linear's integer product for this shape, into host
+ * ints: *mfma_kind = the matrix cores it runs on, CONVROT_MFMA_I8 (INT8 MFMA
+ * on codes widened from INT4) or CONVROT_MFMA_FP6 (FP6 e2m3 MFMA on the FP6
+ * copy of the codes; exact: the codes are exact e2m3 values and the binary32
+ * sums are exact integers), 0 when M or N is 0; *tile_m x *tile_n = the block
+ * tile when M > 32 (0 x 0 for the weight-streaming kernels of M <= 32);
+ * *splits = workgroups sharing each tile's K range (1 when not split).
+ * Returns CONVROT_OK or CONVROT_EINVAL. */
 #define CONVROT_MFMA_I8 1
 #define CONVROT_MFMA_FP6 2
-int convrot_linear_mfma_kind(int64_t M, int64_t K, int64_t N, int g, int* kind_host);
+int convrot_linear_plan(int64_t M, int64_t K, int64_t N, int g, int* mfma_kind_host, int* tile_m_host,
+                        int* tile_n_host, int* splits_host);
 
 /* ---- argument checks (host only, no HIP call) ------------------------- */
 

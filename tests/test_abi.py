@@ -73,15 +73,24 @@ def test_weight_image_bytes(N, K, g, int4):
     assert B.convrot_weight_image_bytes(N, K, g) == int4 + int4 * 3 // 2
 
 
-def test_mfma_kind():
-    assert B.convrot_linear_mfma_kind(1536, 3072, 9216, 256) == B.CONVROT_MFMA_FP6     # 216 FP6 tiles
-    assert B.convrot_linear_mfma_kind(4096, 3072, 3072, 256) == B.CONVROT_MFMA_FP6
-    assert B.convrot_linear_mfma_kind(1536, 3072, 12288, 256) == B.CONVROT_MFMA_I8     # INT8 192 x 384
-    assert B.convrot_linear_mfma_kind(1536, 12288, 3072, 256) == B.CONVROT_MFMA_I8     # INT8 192 x 192, split
-    assert B.convrot_linear_mfma_kind(16, 3072, 12288, 256) == B.CONVROT_MFMA_I8       # weight streaming
-    assert B.convrot_linear_mfma_kind(0, 3072, 12288, 256) == 0
+def test_plan_of_the_flux_shapes():
+    """The block tile each FLUX-shaped linear gets (measured choices on MI355X:
+    the FP6 tile where its 256 x 256 tiles fill one round, 192 x 384 INT8 where
+    256 x 256 would need two rounds, the split 192 x 192 INT8 tile for the long
+    reduction of the down-projection)."""
+    FP6, I8 = B.CONVROT_MFMA_FP6, B.CONVROT_MFMA_I8
+    assert B.convrot_linear_plan(1536, 3072, 9216, 256) == {"mfma": FP6, "tile": (256, 256), "splits": 1}
+    assert B.convrot_linear_plan(4096, 3072, 3072, 256) == {"mfma": FP6, "tile": (256, 256), "splits": 1}
+    assert B.convrot_linear_plan(1536, 3072, 12288, 256) == {"mfma": I8, "tile": (192, 384), "splits": 1}
+    assert B.convrot_linear_plan(1536, 12288, 3072, 256) == {"mfma": I8, "tile": (192, 192), "splits": 2}
+    assert B.convrot_linear_plan(16, 3072, 12288, 256) == {"mfma": I8, "tile": (0, 0), "splits": 1}
+    assert B.convrot_linear_plan(0, 3072, 12288, 256) == {"mfma": 0, "tile": (0, 0), "splits": 1}
+    # only the 192 x 192 tile is ever split
+    for M, N, K in [(256, 3072, 16384), (1024, 1024, 8192), (300, 9000, 12288), (64, 64, 16384)]:
+        p = B.convrot_linear_plan(M, K, N, 256)
+        assert p["splits"] == 1 or p["tile"] == (192, 192), (M, N, K, p)
     with pytest.raises(B.ConvRotError):
-        B.convrot_linear_mfma_kind(64, 1001, 64, 256)
+        B.convrot_linear_plan(64, 1001, 64, 256)
 
 
 def test_workspace_bytes():

@@ -124,8 +124,9 @@ GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), 
                (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072),
                (256, 512, 8192), (100, 300, 6144), (20, 9000, 1024), (7, 17000, 256),
                # FP6 256 x 256 block tiles (216 and 192 of them, also ragged), INT8 192 x 384
-               # (256 of them, also ragged), INT8 192 x 192 split 2 ways along K, and FP6
-               # 256 x 256 split 8 ways (also ragged): the shapes the plan picks here
+               # (256 of them, also ragged), INT8 192 x 192 split 2 ways along K, and
+               # 192 x 192 split 8 ways (256 workgroups, also ragged): the shapes the plan
+               # picks here (convrot_linear_plan)
                (1536, 9216, 128), (1500, 9000, 256), (1536, 12288, 128), (1500, 12000, 384),
                (1536, 3072, 8192), (4096, 3072, 128), (4000, 3000, 256), (256, 3072, 16384),
                (200, 3011, 16384)]

@@ -58,7 +58,7 @@ _SIGNATURES = {
     "convrot_weight_image_bytes": ([_I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_workspace_bytes": ([_I64, _I64, _I64, _I, ctypes.POINTER(_SZ)], _I),
     "convrot_linear_kernel_count": ([_I64, _I64, _I64, _I, ctypes.POINTER(_I)], _I),
-    "convrot_linear_mfma_kind": ([_I64, _I64, _I64, _I, ctypes.POINTER(_I)], _I),
+    "convrot_linear_plan": ([_I64, _I64, _I64, _I] + [ctypes.POINTER(_I)] * 4, _I),
     "convrot_validate_weight": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_validate_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_prepare_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
@@ -166,11 +166,12 @@ CONVROT_MFMA_I8 = 1
 CONVROT_MFMA_FP6 = 2
 
 
-def convrot_linear_mfma_kind(M: int, K: int, N: int, g: int) -> int:
-    """CONVROT_MFMA_I8 or CONVROT_MFMA_FP6: the matrix cores of the product (0 if M or N is 0)."""
-    out = ctypes.c_int()
-    _call("convrot_linear_mfma_kind", M, K, N, g, ctypes.byref(out))
-    return out.value
+def convrot_linear_plan(M: int, K: int, N: int, g: int) -> dict:
+    """The product plan: {"mfma": CONVROT_MFMA_I8 / CONVROT_MFMA_FP6 (0 if M or N
+    is 0), "tile": (tile_m, tile_n) ((0, 0) for M <= 32), "splits": S}."""
+    v = [ctypes.c_int() for _ in range(4)]
+    _call("convrot_linear_plan", M, K, N, g, *[ctypes.byref(x) for x in v])
+    return {"mfma": v[0].value, "tile": (v[1].value, v[2].value), "splits": v[3].value}
 
 
 def convrot_validate_weight(W_ptr, N, K, g, image_ptr, sw_ptr) -> int:

@@ -99,19 +99,24 @@ int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* cou
     return CONVROT_OK;
 }
 
-int convrot_linear_mfma_kind(int64_t M, int64_t K, int64_t N, int g, int* kind)
+int convrot_linear_plan(int64_t M, int64_t K, int64_t N, int g, int* kind, int* tile_m, int* tile_n, int* splits)
 {
-    if (!kind) return CONVROT_EINVAL;
+    if (!kind || !tile_m || !tile_n || !splits) return CONVROT_EINVAL;
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
-    if (M == 0 || N == 0) {
-        *kind = 0;
-        return CONVROT_OK;
-    }
+    *kind = 0;
+    *tile_m = *tile_n = 0;
+    *splits = 1;
+    if (M == 0 || N == 0) return CONVROT_OK;
     // M <= 32 streams the weight through the INT8 16x16x64 MFMA
-    const bool fp6 = M > 32 && gemm_shape_fp6(gemm_plan(M, N, rotated_width(K, g)).shape);
-    *kind = fp6 ? CONVROT_MFMA_FP6 : CONVROT_MFMA_I8;
+    *kind = CONVROT_MFMA_I8;
+    if (M <= 32) return CONVROT_OK;
+    const GemmPlan p = gemm_plan(M, N, rotated_width(K, g));
+    if (gemm_shape_fp6(p.shape)) *kind = CONVROT_MFMA_FP6;
+    *tile_m = gemm_tile_m(p.shape);
+    *tile_n = gemm_tile_n(p.shape);
+    *splits = p.splits;
     return CONVROT_OK;
 }
 

@@ -574,6 +574,7 @@ struct GemmGeom : GemmShape<SHAPE> {
     static constexpr int kStage = (UA + UB) * kUnitBytes;
     static constexpr int COPIES = (2 * (UA + UB) + S::NW - 1) / S::NW;  // 1 KB copies per wave per stage
     static constexpr int kLdsBytes = kStages * kStage;
+    static constexpr bool kSplit = gemm_shape_splits(SHAPE);  // the plan may split K
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
 };
 
@@ -1096,7 +1097,8 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if constexpr (G::kSplit)
+        if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
     gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
 }
 
@@ -1133,6 +1135,7 @@ struct Gemm6Geom {
     static constexpr int UPW = (UA + UB) / NW;          // units copied per wave per stage
     static constexpr int COPIES = 3 * UPW;              // 1 KB copies per wave per stage
     static_assert(UPW * NW == UA + UB && UA % UPW == 0, "a wave copies whole units of one operand");
+    static constexpr bool kSplit = gemm_shape_splits(SHAPE);  // the plan may split K
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
 };
 // Shape 2: eight waves, two per SIMD, each owning 128 x 64.  (Four waves of
@@ -1316,7 +1319,8 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if constexpr (G::kSplit)
+        if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
     gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
 }
 

@@ -152,10 +152,11 @@ constexpr int64_t kW4A16MaxRows = 32;
 // shape 1 is 192 x 192.  Shape 2 is 256 x 256 on the FP6 matrix cores from
 // the FP6 image (twice the INT8 rate; bound by LDS bandwidth rather than by
 // the matrix cores), the fastest per output where its tiles fill the chip.
-// When there are too few tiles to fill the chip, each tile's K range is split
-// over S workgroups (the integer partial sums are exact in any order): S is the
-// largest value <= 8 with S * tiles <= kSplitTargetWGs and >= 16 128-K blocks
-// per split.  Of the shapes the plan takes the one with the smallest estimated
+// When there are too few tiles to fill the chip, the 192 x 192 tile's K range
+// is split over S workgroups (the integer partial sums are exact in any
+// order): S is the largest value <= 8 with S * tiles <= kSplitTargetWGs and
+// >= 16 128-K blocks per split.  The other two shapes are never split (a
+// split of them at 216 and 256 workgroups is not validated on the hardware).  Of the shapes the plan takes the one with the smallest estimated
 // time: rounds of workgroups x 128-K blocks per workgroup x tile area at
 // gemm_shape_ns per 1024 outputs per block (measured on MI355X on the FLUX
 // shapes), one prologue +
@@ -170,8 +171,9 @@ constexpr int kGemmShapes = 3;
 CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 2 ? 256 : 192; }
 CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 384 : (shape == 1 ? 192 : 256); }
 CONVROT_HD constexpr bool gemm_shape_fp6(int shape) { return shape == 2; }
-// nanoseconds per 1024 outputs per 128-K block, by shape
-CONVROT_HD constexpr int gemm_shape_ns(int shape) { return shape == 0 ? 29 : (shape == 1 ? 26 : 20); }
+// nanoseconds per 1024 outputs per 128-K block, by shape (MI355X, FLUX shapes)
+CONVROT_HD constexpr int gemm_shape_ns(int shape) { return shape == 0 ? 28 : (shape == 1 ? 30 : 19); }
+CONVROT_HD constexpr bool gemm_shape_splits(int shape) { return shape == 1; }
 
 struct GemmPlan {
     int shape;             // block tile shape (0 .. 2)
@@ -190,7 +192,7 @@ CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
         const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
         const int64_t tiles = tm * tn;
         int S = 1;
-        while (S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
+        while (gemm_shape_splits(shape) && S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
         const int64_t rounds = (tiles * S + kSplitTargetWGs - 1) / kSplitTargetWGs;
         int64_t ns = rounds * ((KB + S - 1) / S) * (bm * bn / 1024) * gemm_shape_ns(shape) + rounds * 4000;
         if (S > 1) ns += tiles * (S - 1) * bm * bn * 8 / 4000 + 3000;
