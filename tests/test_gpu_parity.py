@@ -300,6 +300,33 @@ def test_linear_w4a16(gpu, M, N, K, g):
     assert np.mean(gy == oy) > 0.5          # most values round to the same bf16
 
 
+@pytest.mark.parametrize("K,N,g", [(3072, 12288, 256), (1000, 700, 256), (512, 300, 64 | REG), (2048, 129, 64)])
+def test_single_kernel_paths_match_two_kernel_paths(gpu, K, N, g):
+    """Rows are independent, so the first four rows of a five-row input (two
+    launches: prep, then the weight-streaming product) and the same four rows
+    alone (one launch that rotates the rows in every workgroup) must agree bit
+    for bit -- for W4A4 and for W4A16, whose binary32 sums are taken in the
+    same order on both paths."""
+    x = synth.random_bf16((5, K), seed=K + N, outliers=2)
+    w = synth.random_bf16((N, K), seed=N + 1, std=0.02)
+    b = synth.random_bf16((N,), seed=N + 2, std=0.01)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), g)
+    Kr = gpu.rotated_width(K, g)
+    assert gpu.convrot_linear_kernel_count(4, K, N, g) == 1 and gpu.convrot_linear_kernel_count(5, K, N, g) == 2
+    for fn in (gpu.convrot_linear, gpu.convrot_linear_w4a16):
+        y5 = _host_bits(fn(_dev(x), image, sw, _dev(b), N, g))
+        y4 = _host_bits(fn(_dev(x[:4]), image, sw, _dev(b), N, g))
+        assert np.array_equal(y4, y5[:4]), fn.__name__
+    # the one-launch W4A16 path leaves the bf16 rows in the workspace as the two-launch path does
+    import torch
+    ws4 = torch.zeros(gpu.convrot_w4a16_workspace_bytes(4, K, g), dtype=torch.uint8, device="cuda")
+    ws5 = torch.zeros(gpu.convrot_w4a16_workspace_bytes(5, K, g), dtype=torch.uint8, device="cuda")
+    gpu.convrot_linear_w4a16(_dev(x[:4]), image, sw, _dev(b), N, g, workspace=ws4)
+    gpu.convrot_linear_w4a16(_dev(x), image, sw, _dev(b), N, g, workspace=ws5)
+    torch.cuda.synchronize()
+    assert np.array_equal(ws4[: 4 * Kr * 2].cpu().numpy(), ws5[: 4 * Kr * 2].cpu().numpy())
+
+
 FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_mlp_down_m1536_k12288_n3072",
         "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
 

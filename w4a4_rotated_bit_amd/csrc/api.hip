@@ -213,8 +213,21 @@ int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image,
     if (rc || M == 0 || N == 0) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    // 1. the rotated activation rows, rounded to bf16, into the workspace
     const int64_t Kr = rotated_width(K, g);
+    if (single_kernel_linear(M, Kr, g)) {
+        // one kernel: each workgroup rotates the few activation rows itself
+        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
+        PrepArgs pa{};
+        pa.X = (const uint16_t*)X;
+        pa.ld = K;
+        pa.rows = M;
+        pa.K = Kr;
+        pa.K_pad = round_up(Kr, kTileK);
+        pa.out = (uint8_t*)ws;
+        launch_small_w4a16(g, ga, pa, s);
+        return launched();
+    }
+    // 1. the rotated activation rows, rounded to bf16, into the workspace
     PrepArgs a{};
     a.X = (const uint16_t*)X;
     a.ld = K;

@@ -48,6 +48,9 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
 // W4A16 product for M <= 32: bf16 rotated activation rows xr [M][K] times the
 // weight image (act, sx and the split fields of a are unused).
 void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s);
+// The W4A16 linear in one launch when single_kernel_linear(M, K, g) holds:
+// p.out receives the bf16 rotated rows [M][K].
+void launch_small_w4a16(int g, GemmArgs a, PrepArgs p, hipStream_t s);
 // Whole linear in one launch when single_kernel_linear(M, K, g) holds; see
 // kernels.hip.
 void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s);

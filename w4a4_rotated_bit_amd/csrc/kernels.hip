@@ -1761,6 +1761,145 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
 }
 
 // ---------------------------------------------------------------------------
+// small_w4a16_kernel: the W4A16 linear in one launch, for the shapes of the
+// single-kernel W4A4 linear (M <= kSmallRows, a row's prep team whole waves).
+//
+// As in small_m_kernel, a workgroup first requests its whole weight range and,
+// while the weights stream in, rotates the M activation rows itself -- here
+// rounded to bf16, as the prep kernel's bf16 mode writes them -- into its own
+// shared memory.  The products then run exactly as in w4a16_kernel (the same
+// split of K over the four waves, the same MFMA order, the partial tiles
+// summed in wave order), with the activation operand from shared memory, so
+// the result equals the two-launch path's bit for bit.  Workgroup 0 also
+// writes the bf16 rows to the workspace.
+// ---------------------------------------------------------------------------
+template <int G, int SW, bool REG>
+__global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_w4a16_kernel(GemmArgs a, PrepArgs p)
+{
+    using PS = PrepShape<G>;
+    constexpr int P = PS::P;
+    constexpr int NWAVES = SW * kSkinnyWaves;
+    constexpr int kMaxRowK = kSmallUnits * kSkinnyWaves * kTileK;  // longest row: 4096 values
+    __shared__ __attribute__((aligned(16))) uint8_t plds[NWAVES * PS::kWaveLdsBytes];
+    __shared__ uint32_t pred[2][16];
+    __shared__ __attribute__((aligned(16))) uint16_t xr[kSmallRows * kMaxRowK];  // bf16 rows, K values apart
+    __shared__ __attribute__((aligned(16))) float red[SW][kSkinnyWaves - 1][4][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int sl = wave / kSkinnyWaves, kq = wave % kSkinnyWaves;  // strip within the workgroup, K quarter
+    const int r16 = lane & 15, q = lane >> 4;
+    const int strip = blockIdx.x * SW + sl;
+    const int nstrips = (int)((a.N + 15) / 16);
+    const int strip_c = min(strip, nstrips - 1);  // past the end: re-read the last strip, never stored
+    const int nt = strip_c >> 1, half = strip_c & 1;
+    const int KB = a.KB;
+    const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;  // <= kSmallUnits
+    const int kb0 = kq * per;
+    const int kn = max(0, min(KB, kb0 + per) - kb0);          // units of this wave
+    const int wrow = 16 * half + r16;
+    const uint8_t* wbase = a.wgt + (size_t)nt * KB * kUnitBytes + wrow * 64 + ((q ^ row_swizzle(wrow)) * 16);
+
+    const int team_nw = (int)(p.K_pad / P + 63) / 64;  // waves per row
+    const int teams = NWAVES / team_nw;
+    const int team = wave / team_nw;
+    const bool live = team < teams;
+    const int t = tid - team * team_nw * 64;
+    const int64_t k0 = (int64_t)t * P;
+
+    // 1. the first pass's activation values, the epilogue's scales and
+    //    biases, then the whole weight range: all in flight
+    uint4 xw[P / 8];
+    load_run<P>(p.X, live ? team : 0, p.ld, k0, live && team < p.rows, xw);
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    const uint16_t* bsrc = a.bias ? a.bias : (const uint16_t*)a.sw;  // a valid address either way
+    const uint32_t bmask = a.bias ? 0xFFFFu : 0u;
+    float swv[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = min(n0 + j, a.N - 1);
+        swv[j] = a.sw[n];
+        bv[j] = __uint_as_float(((uint32_t)bsrc[n] & bmask) << 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 wq[kSmallUnits];
+#pragma unroll
+    for (int u = 0; u < kSmallUnits; ++u) {
+        const int kb = min(kb0 + min(u, max(kn - 1, 0)), KB - 1);
+        wq[u] = load_stream16(wbase + (size_t)kb * kUnitBytes);
+    }
+
+    // 2. the bf16 rotated rows 0 .. M-1 into shared memory (the bf16 mode has
+    //    no team barrier: teams without a row skip it)
+    {
+        double* ld = (double*)(plds + wave * PS::kWaveLdsBytes);
+        PrepArgs pl = p;
+        pl.out = (uint8_t*)xr;
+        const int passes = (int)((a.M + teams - 1) / teams);
+        if (live && team < a.M)
+            prep_row<G, OUT_ROTATED_BF16, 0, REG>(pl, xw, team, t, k0, lane, wave, ld, pred, 0, team * team_nw,
+                                                  team_nw);
+        for (int pass = 1; pass < passes; ++pass) {
+            const int64_t row = (int64_t)pass * teams + (live ? team : 0);
+            const bool active = live && row < a.M;
+            load_run<P>(p.X, row, p.ld, k0, active, xw);
+            if (active)
+                prep_row<G, OUT_ROTATED_BF16, 0, REG>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1,
+                                                      team * team_nw, team_nw);
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int words = (int)(a.M * a.K / 8);  // 16-byte words of the M rows
+        for (int i = tid; i < words; i += NWAVES * 64) ((uint4*)p.out)[i] = ((const uint4*)xr)[i];
+    }
+
+    // 3. products, as in w4a16_kernel (MH = 1)
+    int kst[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kst[j] = 32 * (2 * (q >> 1) + (j >> 1)) + 16 * (q & 1) + 8 * (j & 1);
+    const bool act_row = r16 < a.M;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kSmallUnits; ++u) {
+        if (u >= kn) break;
+        const uint32_t ww[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t k = (int64_t)(kb0 + u) * kTileK + kst[j];
+            const uint4 x = (act_row && k < a.K) ? *(const uint4*)(xr + r16 * a.K + k) : make_uint4(0, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8_bf16(ww[j]), __builtin_bit_cast(bf16x8_t, x), acc,
+                                                          0, 0, 0);
+        }
+    }
+
+    // 4. the strip's partial tiles summed in wave order, epilogue
+    if (kq > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[sl][kq - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (kq != 0) return;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += red[sl][w][j][lane];
+    const int64_t m = r16;
+    if (n0 >= a.N || m >= a.M) return;
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = __builtin_fmaf(acc[j], swv[j], bv[j]);
+    const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
+    uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
+    if ((a.N % 4) == 0) {
+        *(uint2*)dst = make_uint2(p01, p23);
+    } else {
+        const uint16_t yb[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+        for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = yb[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // layout kernels
 // ---------------------------------------------------------------------------
 
@@ -1977,6 +2116,32 @@ void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s)
         reg ? launch_small_m_g<256, true>(sw, a, p, grid, s) : launch_small_m_g<256, false>(sw, a, p, grid, s);
     else
         reg ? launch_small_m_g<64, true>(sw, a, p, grid, s) : launch_small_m_g<64, false>(sw, a, p, grid, s);
+}
+
+template <int G, bool REG>
+static void launch_small_w4a16_g(int sw, const GemmArgs& a, const PrepArgs& p, dim3 grid, hipStream_t s)
+{
+    switch (sw) {
+        case 1: hipLaunchKernelGGL((small_w4a16_kernel<G, 1, REG>), grid, dim3(1 * kSkinnyWaves * 64), 0, s, a, p); break;
+        case 2: hipLaunchKernelGGL((small_w4a16_kernel<G, 2, REG>), grid, dim3(2 * kSkinnyWaves * 64), 0, s, a, p); break;
+        default: hipLaunchKernelGGL((small_w4a16_kernel<G, 3, REG>), grid, dim3(3 * kSkinnyWaves * 64), 0, s, a, p); break;
+    }
+}
+
+void launch_small_w4a16(int g, GemmArgs a, PrepArgs p, hipStream_t s)
+{
+    const int64_t strips = (a.N + 15) / 16;
+    const int cus = device_cus();
+    const int sw = (int)std::min<int64_t>(3, std::max<int64_t>(1, (strips + cus - 1) / cus));
+    const bool reg = (g & kRegularHadamard) != 0;
+    g &= ~kRegularHadamard;
+    p.team = (int)(p.K_pad / (g == 256 ? 16 : 8));
+    p.rows_pad = kSmallRows;
+    const dim3 grid((unsigned)((strips + sw - 1) / sw));
+    if (g == 256)
+        reg ? launch_small_w4a16_g<256, true>(sw, a, p, grid, s) : launch_small_w4a16_g<256, false>(sw, a, p, grid, s);
+    else
+        reg ? launch_small_w4a16_g<64, true>(sw, a, p, grid, s) : launch_small_w4a16_g<64, false>(sw, a, p, grid, s);
 }
 
 void launch_w4a16(GemmArgs a, const uint16_t* xr, hipStream_t s)
