@@ -426,3 +426,51 @@ def test_flux_block_swap(gpu, rotation):
     assert r["finite"] and r["swapped"] == ["down", "proj", "qkv", "up"]
     assert r["rel_err_update"] < 0.5
     assert r["rel_err_block"] < 0.2
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: every replay equals the eager result
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N,g,path", [(1536, 1024, 9216, 256, "w4a4"),     # FP6 256 x 256 tiles
+                                          (256, 4096, 256, 256, "w4a4"),       # 192 x 192, split K
+                                          (3, 3072, 1000, 256 | REG, "w4a4"),  # one kernel
+                                          (40, 1024, 500, 64, "w4a4"),         # prep + INT8 192 x 192
+                                          (4, 2048, 700, 256, "w4a16"),        # one kernel
+                                          (16, 1024, 300, 64, "w4a16")])       # prep + w4a16_kernel
+def test_graph_replays_match_eager(gpu, M, K, N, g, path):
+    """The linear captured once into a HIP graph and replayed several times,
+    with other work on the GPU in between (another linear on other buffers,
+    torch ops, host synchronisations): every replay's Y equals the eager
+    result bit for bit (the split-K counters are cleared by a kernel of the
+    captured work, not by a memset)."""
+    import torch
+    x = synth.random_bf16((M, K), seed=M + K + N, outliers=3)
+    w = synth.random_bf16((N, K), seed=N + 7, std=0.02)
+    b = synth.random_bf16((N,), seed=N + 8, std=0.01)
+    X, B = _dev(x), _dev(b)
+    image, sw = gpu.convrot_prepare_weight(_dev(w), g)
+    fn = gpu.convrot_linear_w4a16 if path == "w4a16" else gpu.convrot_linear
+    if path == "w4a16":
+        ws = torch.empty(max(gpu.convrot_w4a16_workspace_bytes(M, K, g), 256), dtype=torch.uint8, device="cuda")
+    else:
+        ws = gpu.new_workspace(M, K, N, g)
+    eager = _host_bits(fn(X, image, sw, B, N, g, workspace=ws))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(X, image, sw, B, N, g, Y=Y, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn(X, image, sw, B, N, g, Y=Y, workspace=ws)
+    other_ws = torch.empty_like(ws)
+    for rep in range(4):
+        Y.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_host_bits(Y), eager), f"replay {rep}"
+        # unrelated eager work between replays, on another workspace
+        fn(X, image, sw, B, N, g, workspace=other_ws)
+        (X.float() * 2).sum().item()
