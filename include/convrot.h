@@ -91,8 +91,10 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
  *   2. offset CONVROT_WORKSPACE_IMAGE_OFFSET: the activation-code image,
  *      round_up(M, 32) * round_up(K_rot, 128) / 2 bytes, INT4 codes in the
  *      same layout as the weight image;
- *   3. when M > 32, the same codes as FP6: round_up(M, 32) *
- *      round_up(K_rot, 128) * 3 / 4 bytes;
+ *   3. when M > 32, room for the same codes as FP6: round_up(M, 32) *
+ *      round_up(K_rot, 128) * 3 / 4 bytes (written by
+ *      convrot_prepare_activations always, by convrot_linear when its plan
+ *      runs on the FP6 matrix cores);
  *   4. the activation scales sx: round_up(M, 32) floats;
  *   5. split-K partial tiles: when M > 32 and the output tiles are too few
  *      to occupy the GPU, each tile's K range is shared by S workgroups and

@@ -171,6 +171,9 @@ def test_split_k_workspace_reuse(gpu, M, N, K):
     ws = gpu.new_workspace(M, K, N, 256)
     ws.fill_(0xFF)
     gpu.convrot_prepare_activations(_dev(x), 256, ws)
+    # not knowing N, the activation step writes both copies of the codes
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), gpu.workspace_act_codes(ws, M, K))
     outs = [gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N) for _ in range(3)]
     # a narrower GEMM on the same workspace, then the original again
     Nn = N // 2
@@ -199,7 +202,8 @@ def _linear_parity(gpu, x, w, bias, g):
     qx = gpu.workspace_act_codes(ws, M, K)
     orx = oracle.rotate_rows(x, g)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
-    if M > 32:  # the FP6 copy the block-tile GEMM reads holds the same codes
+    if M > 32 and gpu.convrot_linear_plan(M, w.shape[1], N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
+        # the FP6 copy the FP6 tile reads holds the same codes
         assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), qx)
     qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     compare_codes(qw, oq_w, oracle.rotate_rows(w, g), osw, "weight codes")

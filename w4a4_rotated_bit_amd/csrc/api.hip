@@ -49,7 +49,9 @@ int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
     return CONVROT_OK;
 }
 
-int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, hipStream_t s)
+// want_fp6: also write the FP6 copy of the codes (when the GEMM that follows
+// is unknown, or its plan reads that copy)
+int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, bool want_fp6, hipStream_t s)
 {
     const int64_t Kr = rotated_width(K, g);
     PrepArgs a{};
@@ -60,7 +62,7 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)ws + workspace_image_offset();
-    a.out6 = act_has_fp6(M) ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
+    a.out6 = act_has_fp6(M) && want_fp6 ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
@@ -167,7 +169,8 @@ int convrot_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     if (!ws || !aligned(ws, 16)) return CONVROT_EINVAL;
     if (ws_bytes < workspace_partial_offset(M, rotated_width(K, g))) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
-    return enqueue_prepare_activations(X, M, K, g, ws, as_stream(stream));
+    // the GEMM that will consume the workspace is not known: both copies
+    return enqueue_prepare_activations(X, M, K, g, ws, true, as_stream(stream));
 }
 
 int convrot_gemm(const void* ws, size_t ws_bytes, int64_t M, int64_t K, const void* image, const float* sw,
@@ -202,7 +205,8 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
         launch_small_m(g, ga, pa, s);
         return launched();
     }
-    if ((rc = enqueue_prepare_activations(X, M, K, g, ws, s))) return rc;
+    const bool fp6 = gemm_shape_fp6(gemm_plan(M, N, Kr).shape);
+    if ((rc = enqueue_prepare_activations(X, M, K, g, ws, fp6, s))) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, ws, M, Kr, image, sw, bias, N, Y, s);
 }
 
