@@ -1,15 +1,22 @@
 // kernels.hip -- gfx950 (CDNA4) kernels of the ConvRot W4A4 linear.
 //
-//   prep_kernel   rotation (grouped Sylvester Hadamard as fast Walsh-Hadamard
-//                 butterflies in binary64, rounded once to binary32), row
-//                 absmax, symmetric INT4 quantization; writes the codes as the
-//                 operand image (activations and weights alike) or in plain
-//                 layouts for parity checks.
-//   gemm_kernel   INT4 x INT4 products on the INT8 matrix cores
-//                 (v_mfma_i32_32x32x32_i8, codes widened to INT8 x 16 in
-//                 registers) with int32 accumulation and the scale + bias
-//                 epilogue to bf16 (or raw int32 for parity).
-//   relayout kernels: lossless layout moves into the operand image.
+//   prep_kernel   rotation (grouped Sylvester or regular Hadamard as fast
+//                 Walsh-Hadamard butterflies in binary64, rounded once to
+//                 binary32), row absmax, symmetric INT4 quantization; writes
+//                 the codes as the operand images (INT4, and FP6 e2m3 for
+//                 the FP6 matrix cores), in plain layouts for parity checks,
+//                 or the rotated rows as bf16 (W4A16).
+//   gemm6_kernel  the block-tile product on the FP6 matrix cores
+//                 (v_mfma_scale_f32_32x32x64_f8f6f4: the codes are exact
+//                 e2m3 values, the binary32 sums exact integers) with the
+//                 scale + bias epilogue to bf16 (or int32 for parity).
+//   gemm_kernel   the same on the INT8 matrix cores (v_mfma_i32_32x32x32_i8,
+//                 codes widened to INT8 x 16 in registers), two tile shapes,
+//                 one of them split along K.
+//   skinny_kernel, small_m_kernel, w4a16_kernel, small_w4a16_kernel:
+//                 the weight-streaming products of M <= 32 (one launch for
+//                 M <= 4, the rows rotated in every workgroup).
+//   relayout kernels: lossless layout moves into the operand images.
 //
 // Method: convrot-mlx README, "What is included" (normalized Hadamard
 // rotation over groups of 64 or 256, symmetric rowwise absmax INT4 in
