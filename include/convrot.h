@@ -195,9 +195,13 @@ int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_de
  *   Y[m][n] = bf16( fmaf(sum_k bf16(r[m][k]) * qw[n][k], sw[n], bias[n]) ),
  * the sum accumulated in binary32 by the bf16 matrix cores (so Y is close to,
  * not bit-identical with, the same formula summed exactly).
- * Bytes of workspace for M x K: round_up(M * K_rot * 2, 256); it receives the
- * bf16 rotated rows, row-major [M][K_rot].  M must be <= 32; otherwise, and for
- * the shape rules of convrot_linear, CONVROT_EINVAL. */
+ * Bytes of workspace for M x K: round_up(M, 16) * round_up(K_rot, 128) * 2.
+ * It receives the bf16 rotated rows in the order the matrix cores read them:
+ * value k of row m (kl = k % 128, b_i = bit i of kl, KB = round_up(K_rot,
+ * 128) / 128) is element kl % 8 of the 16-byte word number
+ *   ((((m / 16) * KB + k / 128) * 4 + 2 b5 + b3) * 4 + 2 b6 + b4) * 16 + m % 16;
+ * the words of padding rows and columns are not written.  M must be <= 32;
+ * otherwise, and for the shape rules of convrot_linear, CONVROT_EINVAL. */
 int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes_host);
 
 /* The checks convrot_linear_w4a16 performs.  Returns a status code. */

@@ -172,9 +172,11 @@ def test_validate_linear_statuses():
 
 
 def test_w4a16_sizes_and_statuses():
-    assert B.convrot_w4a16_workspace_bytes(1, 3072, 256) == 6144
+    # rows rounded up to 16 and K to 128, bf16 each
+    assert B.convrot_w4a16_workspace_bytes(1, 3072, 256) == 16 * 3072 * 2
     assert B.convrot_w4a16_workspace_bytes(32, 12288, 256) == 32 * 12288 * 2
-    assert B.convrot_w4a16_workspace_bytes(3, 192, 64) == 1280          # 1152 rounded up to 256
+    assert B.convrot_w4a16_workspace_bytes(3, 192, 64) == 16 * 256 * 2
+    assert B.convrot_w4a16_workspace_bytes(17, 1000, 256) == 32 * 1024 * 2   # K_rot = 1024
     assert B.convrot_w4a16_workspace_bytes(0, 1024, 256) == 0
     with pytest.raises(B.ConvRotError):
         B.convrot_w4a16_workspace_bytes(33, 1024, 256)                    # M > 32: the W4A4 path's regime

@@ -27,6 +27,21 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
+def _w16_rows(ws, M, Kr):
+    """The bf16 rotated rows [M][Kr] out of a W4A16 workspace, decoded by the
+    layout that include/convrot.h states for it (16-byte words in the order
+    of 16-row blocks, 128-K units, steps j, quarters q, rows)."""
+    words = ws.cpu().numpy().view(np.uint16).reshape(-1, 8)
+    KB = -(-Kr // 128)
+    m = np.arange(M)[:, None]
+    k = np.arange(0, Kr, 8)[None, :]
+    kl = k % 128
+    j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1)
+    q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1)
+    w = ((((m // 16) * KB + k // 128) * 4 + j) * 4 + q) * 16 + m % 16
+    return words[w].reshape(M, Kr)
+
+
 def _host_bits(t):
     import torch
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -295,8 +310,8 @@ def test_linear_w4a16(gpu, M, N, K, g):
     Y = gpu.convrot_linear_w4a16(_dev(x), image, sw, _dev(b), N, g, workspace=ws)
     torch.cuda.synchronize()
     Kr = gpu.rotated_width(K, g)
-    xr = ws[: M * Kr * 2].cpu().numpy().view(np.uint16).reshape(M, Kr)
-    assert np.array_equal(xr, xr_or), "bf16 rotated rows differ"
+    assert ws.numel() == -(-M // 16) * 16 * -(-Kr // 128) * 128 * 2
+    assert np.array_equal(_w16_rows(ws, M, Kr), xr_or), "bf16 rotated rows differ"
     gy = synth.bf16_bits_to_f32(_host_bits(Y)).astype(np.float64)
     oy = synth.bf16_bits_to_f32(y_or).astype(np.float64)
     err = np.abs(gy - oy).max() / np.abs(oy).max()
@@ -328,7 +343,7 @@ def test_single_kernel_paths_match_two_kernel_paths(gpu, K, N, g):
     gpu.convrot_linear_w4a16(_dev(x[:4]), image, sw, _dev(b), N, g, workspace=ws4)
     gpu.convrot_linear_w4a16(_dev(x), image, sw, _dev(b), N, g, workspace=ws5)
     torch.cuda.synchronize()
-    assert np.array_equal(ws4[: 4 * Kr * 2].cpu().numpy(), ws5[: 4 * Kr * 2].cpu().numpy())
+    assert np.array_equal(_w16_rows(ws4, 4, Kr), _w16_rows(ws5, 5, Kr)[:4])
 
 
 FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_mlp_down_m1536_k12288_n3072",

@@ -150,7 +150,7 @@ int convrot_w4a16_workspace_bytes(int64_t M, int64_t K, int g, size_t* bytes)
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (M > kW4A16MaxRows) return CONVROT_EINVAL;
-    *bytes = (size_t)round_up(M * rotated_width(K, g) * 2, 256);
+    *bytes = w16_rows_bytes(M, rotated_width(K, g));
     return CONVROT_OK;
 }
 

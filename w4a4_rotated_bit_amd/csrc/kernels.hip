@@ -390,16 +390,21 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next row rewrites the region
     __builtin_amdgcn_wave_barrier();
 
-    // W4A16: the rotated row, rounded to bf16 (nearest even), row-major; no
-    // scale and no codes.  Rows are K values long, K % 64 == 0, so every
-    // lane's P values are whole 16-byte words.
+    // W4A16: the rotated row, rounded to bf16 (nearest even); no scale and
+    // no codes.  K % 64 == 0, so every lane's P values are whole 16-byte
+    // words: in the matrix-core order of w16_word_offset in device memory,
+    // or row-major (rows K values apart) when LDS_ROWS > 0 (shared memory).
     if constexpr (MODE == OUT_ROTATED_BF16) {
         if (has_data) {
-            uint4* dst = (uint4*)(a.out + ((size_t)row * a.K + k0) * 2);
 #pragma unroll
-            for (int c = 0; c < P / 8; ++c)
-                dst[c] = make_uint4(pack_bf16x2(r[8 * c], r[8 * c + 1]), pack_bf16x2(r[8 * c + 2], r[8 * c + 3]),
-                                    pack_bf16x2(r[8 * c + 4], r[8 * c + 5]), pack_bf16x2(r[8 * c + 6], r[8 * c + 7]));
+            for (int c = 0; c < P / 8; ++c) {
+                const uint4 wd = make_uint4(pack_bf16x2(r[8 * c], r[8 * c + 1]), pack_bf16x2(r[8 * c + 2], r[8 * c + 3]),
+                                            pack_bf16x2(r[8 * c + 4], r[8 * c + 5]),
+                                            pack_bf16x2(r[8 * c + 6], r[8 * c + 7]));
+                const size_t off = LDS_ROWS > 0 ? ((size_t)row * a.K + k0 + 8 * c) * 2
+                                                : w16_word_offset(row, k0 + 8 * c, a.K);
+                *(uint4*)(a.out + off) = wd;
+            }
         }
         return;
     }
@@ -484,8 +489,15 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
     }
 }
 
+// Occupancy targets: the largest number of waves per SIMD at which the
+// instance keeps every value in registers (a spill costs more than the lost
+// wave: g = 256 runs 1.1 us faster on 1536 x 3072 at 5 waves than at 6).
+template <int G, bool REG>
+constexpr int kPrepWavesPerSimd = G == 256 ? (REG ? 4 : 5) : (REG ? 5 : 6);
+
 template <int G, int MODE, bool REG>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(REG ? 5 : 6))) void prep_kernel(PrepArgs a)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepWavesPerSimd<G, REG>))) void prep_kernel(
+    PrepArgs a)
 {
     using S = PrepShape<G>;
     constexpr int P = S::P;
@@ -1359,6 +1371,23 @@ __device__ inline uint4 load_stream16(const uint8_t* p)
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// The epilogue's column scales and biases of columns n0 .. n0 + 3 (clamped to
+// N - 1, so every lane issues the same loads), requested at the start of a
+// kernel so that they are not a chain of dependent round trips at its end.
+// No branch around the loads: the wait for a load issued inside a branch
+// would also wait for every load issued before it.
+__device__ inline void load_column_params(const GemmArgs& a, int64_t n0, float (&swv)[4], float (&bv)[4])
+{
+    const uint16_t* bsrc = a.bias ? a.bias : (const uint16_t*)a.sw;  // a valid address either way
+    const uint32_t bmask = a.bias ? 0xFFFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = min(n0 + j, a.N - 1);
+        swv[j] = a.sw[n];
+        bv[j] = __uint_as_float(((uint32_t)bsrc[n] & bmask) << 16);
+    }
+}
+
 template <int OUT, int MH>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 {
@@ -1380,6 +1409,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
         const int arow = 16 * mh + r16;
         abase[mh] = a.act + arow * 64 + ((q ^ row_swizzle(arow)) * 16);
         act_row[mh] = arow < a.M;  // rows past M are zero in the image: not loaded
+    }
+    // lane's output columns (n0 .. n0 + 3) and rows (16 mh + r16) in the epilogue
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    float swv[4], bv[4], sxv[MH];
+    if constexpr (OUT == GEMM_OUT_BF16) {
+        load_column_params(a, n0, swv, bv);
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) sxv[mh] = a.sx[min((int64_t)(16 * mh + r16), a.M - 1)];
+        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
     }
 
     v4i acc[MH];
@@ -1428,8 +1466,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
             for (int j = 0; j < 4; ++j) acc[mh][j] += red[w][mh][j][lane];
 
     // lane holds, per half mh, output row m = 16 mh + r16 and the four
-    // consecutive columns n = 16 strip + 4 q + (0..3)
-    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    // consecutive columns n = n0 + (0..3)
     if (n0 >= a.N) return;
     const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
@@ -1447,14 +1484,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
                 for (int j = 0; j < 4 && n0 + j < a.N; ++j) dst[j] = v[j];
             }
         } else {
-            const float sxm = a.sx[m];
             float y[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
-                const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-                y[j] = __builtin_fmaf((float)v[j] * sxm, a.sw[n], bn);
-            }
+            for (int j = 0; j < 4; ++j) y[j] = __builtin_fmaf((float)v[j] * sxv[mh], swv[j], bv[j]);
             const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
             uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
             if (vec_ok) {
@@ -1519,14 +1551,19 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void w4a16_kernel(GemmArgs a, co
     int kst[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kst[j] = 32 * (2 * (q >> 1) + (j >> 1)) + 16 * (q & 1) + 8 * (j & 1);
-    const uint16_t* xrow[MH];
+    // activation words in the order of w16_word_offset: for 16-row block mh,
+    // unit kb and step j, the wave reads 1 KB at ((mh KB + kb) 4 + j) KB + 16 lane
+    const uint8_t* xbase[MH];
     bool xok[MH];
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh) {
-        const int64_t m = 16 * mh + r16;
-        xok[mh] = m < a.M;
-        xrow[mh] = xr + (xok[mh] ? m : 0) * a.K;
+        xok[mh] = 16 * mh + r16 < a.M;
+        xbase[mh] = (const uint8_t*)xr + (size_t)mh * KB * 4096 + lane * 16;
     }
+    const int64_t n0 = (int64_t)strip * 16 + 4 * q;  // lane's output columns n0 .. n0 + 3
+    float swv[4], bv[4];
+    load_column_params(a, n0, swv, bv);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
 
     f32x4_t acc[MH];
 #pragma unroll
@@ -1544,7 +1581,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void w4a16_kernel(GemmArgs a, co
 #pragma unroll
                 for (int mh = 0; mh < MH; ++mh) {
                     const int64_t k = (int64_t)(kb + u) * kTileK + kst[j];
-                    xa[u][j][mh] = (in && xok[mh] && k < a.K) ? *(const uint4*)(xrow[mh] + k) : make_uint4(0, 0, 0, 0);
+                    xa[u][j][mh] = (in && xok[mh] && k < a.K)
+                                       ? *(const uint4*)(xbase[mh] + ((size_t)(kb + u) * 4 + j) * 1024)
+                                       : make_uint4(0, 0, 0, 0);
                 }
         }
 #pragma unroll
@@ -1579,8 +1618,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void w4a16_kernel(GemmArgs a, co
             for (int j = 0; j < 4; ++j) acc[mh][j] += red[w][mh][j][lane];
 
     // lane holds, per half mh, output row m = 16 mh + r16 and the four
-    // consecutive columns n = 16 strip + 4 q + (0..3)
-    const int64_t n0 = (int64_t)strip * 16 + 4 * q;
+    // consecutive columns n = n0 + (0..3)
     if (n0 >= a.N) return;
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh) {
@@ -1588,11 +1626,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void w4a16_kernel(GemmArgs a, co
         if (m >= a.M) continue;
         float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + j < a.N ? n0 + j : a.N - 1;
-            const float bn = a.bias ? __uint_as_float((uint32_t)a.bias[n] << 16) : 0.0f;
-            y[j] = __builtin_fmaf(acc[mh][j], a.sw[n], bn);
-        }
+        for (int j = 0; j < 4; ++j) y[j] = __builtin_fmaf(acc[mh][j], swv[j], bv[j]);
         const uint32_t p01 = pack_bf16x2(y[0], y[1]), p23 = pack_bf16x2(y[2], y[3]);
         uint16_t* dst = (uint16_t*)a.out + m * a.N + n0;
         if ((a.N % 4) == 0) {
@@ -1668,17 +1702,8 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_m_kernel(GemmArg
     // the epilogue's column scales and biases (clamped columns: every lane
     // issues the same loads; only the first wave of each strip uses them)
     const int64_t n0 = (int64_t)strip * 16 + 4 * q;
-    // (no branch around a load here: the wait for a load issued inside a
-    // branch would also wait for every load before it)
-    const uint16_t* bsrc = a.bias ? a.bias : (const uint16_t*)a.sw;  // a valid address either way
-    const uint32_t bmask = a.bias ? 0xFFFFu : 0u;
     float swv[4], bv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = min(n0 + j, a.N - 1);
-        swv[j] = a.sw[n];
-        bv[j] = __uint_as_float(((uint32_t)bsrc[n] & bmask) << 16);
-    }
+    load_column_params(a, n0, swv, bv);
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads
     uint4 wq[kSmallUnits];
 #pragma unroll
@@ -1819,15 +1844,8 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_w4a16_kernel(Gem
     uint4 xw[P / 8];
     load_run<P>(p.X, live ? team : 0, p.ld, k0, live && team < p.rows, xw);
     const int64_t n0 = (int64_t)strip * 16 + 4 * q;
-    const uint16_t* bsrc = a.bias ? a.bias : (const uint16_t*)a.sw;  // a valid address either way
-    const uint32_t bmask = a.bias ? 0xFFFFu : 0u;
     float swv[4], bv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = min(n0 + j, a.N - 1);
-        swv[j] = a.sw[n];
-        bv[j] = __uint_as_float(((uint32_t)bsrc[n] & bmask) << 16);
-    }
+    load_column_params(a, n0, swv, bv);
     __builtin_amdgcn_sched_barrier(0);
     uint4 wq[kSmallUnits];
 #pragma unroll
@@ -1844,21 +1862,24 @@ __global__ __launch_bounds__(SW * kSkinnyWaves * 64) void small_w4a16_kernel(Gem
         pl.out = (uint8_t*)xr;
         const int passes = (int)((a.M + teams - 1) / teams);
         if (live && team < a.M)
-            prep_row<G, OUT_ROTATED_BF16, 0, REG>(pl, xw, team, t, k0, lane, wave, ld, pred, 0, team * team_nw,
-                                                  team_nw);
+            prep_row<G, OUT_ROTATED_BF16, kSmallRows, REG>(pl, xw, team, t, k0, lane, wave, ld, pred, 0,
+                                                           team * team_nw, team_nw);
         for (int pass = 1; pass < passes; ++pass) {
             const int64_t row = (int64_t)pass * teams + (live ? team : 0);
             const bool active = live && row < a.M;
             load_run<P>(p.X, row, p.ld, k0, active, xw);
             if (active)
-                prep_row<G, OUT_ROTATED_BF16, 0, REG>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1,
-                                                      team * team_nw, team_nw);
+                prep_row<G, OUT_ROTATED_BF16, kSmallRows, REG>(pl, xw, row, t, k0, lane, wave, ld, pred, pass & 1,
+                                                               team * team_nw, team_nw);
         }
     }
     __syncthreads();
-    if (blockIdx.x == 0) {
-        const int words = (int)(a.M * a.K / 8);  // 16-byte words of the M rows
-        for (int i = tid; i < words; i += NWAVES * 64) ((uint4*)p.out)[i] = ((const uint4*)xr)[i];
+    if (blockIdx.x == 0) {  // the rows into the workspace, in the two-launch path's order
+        const int row_words = (int)(a.K / 8);  // 16-byte words of a row
+        for (int i = tid; i < (int)a.M * row_words; i += NWAVES * 64) {
+            const int m = i / row_words, k = (i % row_words) * 8;
+            *(uint4*)(p.out + w16_word_offset(m, k, a.K)) = ((const uint4*)xr)[i];
+        }
     }
 
     // 3. products, as in w4a16_kernel (MH = 1)

@@ -146,6 +146,27 @@ CONVROT_HD inline int64_t rotated_width(int64_t K, int g)
 // The weight-only INT4 variant is the weight-bandwidth-bound regime: M <= 32.
 constexpr int64_t kW4A16MaxRows = 32;
 
+// The bf16 rotated rows are kept in the order in which the bf16 matrix-core
+// product consumes them, so that every wave load is 1 KB of contiguous bytes:
+// blocks of 16 rows, then 128-K units, then the four 32-K steps j of a unit,
+// then the lane's quarter q of a step, then the 16 rows, each 16 bytes (8
+// values).  Within unit kb the value at kl = k % 128 sits in step
+// j = 2 b5 + b3 and quarter q = 2 b6 + b4 (b_i: bit i of kl), element kl % 8.
+// Rows are rounded up to 16 and K to 128; the padding is never read.
+CONVROT_HD inline size_t w16_rows_bytes(int64_t M, int64_t K)
+{
+    return (size_t)(round_up(M, 16) * round_up(K, kTileK) * 2);
+}
+// byte offset of the 16-byte word holding values k .. k+7 of row m (k % 8 == 0)
+CONVROT_HD inline size_t w16_word_offset(int64_t m, int64_t k, int64_t K)
+{
+    const int64_t KB = (K + kTileK - 1) / kTileK;
+    const int kl = (int)(k % kTileK);
+    const int j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1);
+    const int q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1);
+    return (size_t)((((((m >> 4) * KB + k / kTileK) * 4 + j) * 4 + q) * 16 + (m & 15)) * 16);
+}
+
 // ---- GEMM plan -------------------------------------------------------------
 // The GEMM covers the output with one of three block tiles.  Shapes 0 and 1
 // run on the INT8 matrix cores from the INT4 image: shape 0 is 192 x 384,
