@@ -882,12 +882,65 @@ struct Const {
     static constexpr int value = V;
 };
 
+// The block's epilogue parameters go straight from memory into a small LDS
+// array of their own, requested before the first stage's copies, so that the
+// epilogue starts without a round trip to memory: BN column scales (binary32),
+// BN biases (bf16 in the low half of a 4-byte slot), BM row scales
+// (binary32).  Like the stage copies they are global -> LDS DMA written as
+// inline asm (nothing returned, so the compiler does not wait for them); lane
+// l's element lands at M0 + 4 l, and the prologue's wait for the first stage
+// also covers these older requests.  Indices are clamped and a missing bias
+// reads another valid address.
+template <typename G>
+struct EpilogueParams {
+    static constexpr int kColChunks = G::BN / 64, kRowChunks = G::BM / 64;
+    static constexpr int kChunks = 2 * kColChunks + kRowChunks;  // 64 slots each
+    static constexpr int kCount = 64 * kChunks;
+    static_assert(G::BN % 64 == 0 && G::BM % 64 == 0, "whole 64-slot chunks");
+};
+
+__device__ inline void lds_copy4(const void* base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ inline void lds_copy2(const void* base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+template <typename G>
+__device__ inline void issue_epilogue_params(const GemmArgs& a, int tm, int tn, int wave, int lane, uint32_t params_lds)
+{
+    using E = EpilogueParams<G>;
+    const void* bsrc = a.bias ? (const void*)a.bias : (const void*)a.sw;  // a valid address either way
+    for (int c = wave; c < E::kChunks; c += G::NW) {  // uniform per wave
+        const uint32_t dst = params_lds + c * 256;
+        if (c < E::kColChunks) {
+            const int64_t n = min((int64_t)tn * G::BN + c * 64 + lane, a.N - 1);
+            lds_copy4(a.sw, (uint32_t)n * 4, dst);
+        } else if (c < 2 * E::kColChunks) {
+            const int64_t n = min((int64_t)tn * G::BN + (c - E::kColChunks) * 64 + lane, a.N - 1);
+            lds_copy2(bsrc, (uint32_t)n * 2, dst);
+        } else {
+            const int64_t m = min((int64_t)tm * G::BM + (c - 2 * E::kColChunks) * 64 + lane, a.M - 1);
+            lds_copy4(a.sx, (uint32_t)m * 4, dst);
+        }
+    }
+}
+
 // Epilogue of a block tile: int32 stores (parity hook) or scale + bias to bf16
 // through LDS (every copy has landed and every wave is past its last LDS
 // read of the K loop when this runs).
 template <typename G, int OUT, typename ACC>
 __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, int wn, int tid, int wave, int lane,
-                                     uint8_t* smem, const ACC (&acc)[G::BJ][G::BI])
+                                     uint8_t* smem, const float* params, const ACC (&acc)[G::BJ][G::BI])
 {
     constexpr int NW = G::NW, BI = G::BI, BJ = G::BJ, WN = G::WN;
     const int r32 = lane & 31, h = lane >> 5;
@@ -922,10 +975,8 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
                 }
         }
     } else {
-        // The block's BN column scales and biases and BM row scales go
-        // through LDS (free again: every copy has landed and every wave has
-        // passed the last stage barrier) -- one cooperative load instead of
-        // per-lane scattered loads.  Then the bf16 output goes through a
+        // The block's column scales, biases and row scales are in params
+        // (parked there before the K loop).  The bf16 output goes through a
         // per-wave LDS tile of 32 rows x WN columns, one MFMA tile row at a
         // time, and is stored as 16-byte row segments.  Row pitch 2*WN + 16
         // bytes (36 banks modulo 64) keeps rows 16-byte aligned; rows r and
@@ -933,30 +984,17 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
         // half_swap(r) the two 8-byte halves of every 16-byte chunk trade
         // places: the 8-byte writes of 16 (32-bank LDS) or 32 (64-bank LDS)
         // consecutive lanes then hit distinct banks.
-        float* p_sw = (float*)smem;
-        float* p_b = p_sw + G::BN;
-        float* p_sx = p_b + G::BN;
+        const float* p_sw = params;
+        const uint32_t* p_b = (const uint32_t*)params + G::BN;  // bf16 in the low half
+        const float* p_sx = params + 2 * G::BN;
+        const bool has_bias = a.bias != nullptr;
         constexpr int kPitch = 2 * WN + 16;
-        constexpr int kParamBytes = 4096;
         constexpr int kChunks = WN / 8;              // 16-byte chunks per tile row
         constexpr int kReads = 32 * kChunks / 64;    // chunks per lane per tile row block
         static_assert(kReads * 64 == 32 * kChunks, "row chunks divide evenly over the lanes");
-        static_assert((2 * G::BN + G::BM) * 4 <= kParamBytes, "scales and biases fit");
-        static_assert(kParamBytes + NW * 32 * kPitch <= G::kLdsBytes, "epilogue staging must fit in LDS");
-        __syncthreads();
-        for (int e = tid; e < G::BN + G::BM; e += NW * 64) {
-            if (e < G::BN) {
-                const int64_t n = (int64_t)tn * G::BN + e;
-                const int64_t nc = n < a.N ? n : a.N - 1;
-                p_sw[e] = a.sw[nc];
-                p_b[e] = a.bias ? __uint_as_float((uint32_t)a.bias[nc] << 16) : 0.0f;
-            } else {
-                const int64_t m = (int64_t)tm * G::BM + (e - G::BN);
-                p_sx[e - G::BN] = a.sx[m < a.M ? m : a.M - 1];
-            }
-        }
-        __syncthreads();
-        uint8_t* tile_lds = smem + kParamBytes + wave * (32 * kPitch);
+        static_assert(NW * 32 * kPitch <= G::kLdsBytes, "epilogue staging must fit in LDS");
+        __syncthreads();  // every wave is past its last read of the ring; params are visible
+        uint8_t* tile_lds = smem + wave * (32 * kPitch);
         const bool vec8 = (a.N % 8) == 0;
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
@@ -967,9 +1005,12 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
                 for (int t = 0; t < 4; ++t) {
                     const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
                     const float4 sw4 = *(const float4*)(p_sw + wn * WN + nl);
-                    const float4 b4 = *(const float4*)(p_b + wn * WN + nl);
+                    const uint4 b4 = *(const uint4*)(p_b + wn * WN + nl);
                     const float sc[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                    const float bb[4] = {has_bias ? __uint_as_float(b4.x << 16) : 0.0f,
+                                         has_bias ? __uint_as_float(b4.y << 16) : 0.0f,
+                                         has_bias ? __uint_as_float(b4.z << 16) : 0.0f,
+                                         has_bias ? __uint_as_float(b4.w << 16) : 0.0f};
                     float y[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -1011,6 +1052,7 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     constexpr int BI = G::BI, BJ = G::BJ;
     constexpr int kStage = G::kStage;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
+    __shared__ __attribute__((aligned(16))) float params[EpilogueParams<G>::kCount];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1050,7 +1092,11 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     f.swz = row_swizzle(r32);
     f.h = h;
 
-    // prologue: the first kStages stages in flight; wait for stage 0
+    // prologue: the epilogue's parameters, then the first kStages stages in
+    // flight; wait for stage 0 (and so for the older parameter copies)
+    if constexpr (OUT == GEMM_OUT_BF16)
+        issue_epilogue_params<G>(a, tm, tn, wave, lane,
+                                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)params));
     const int first = KC < kStages ? KC : kStages;
     const StageCopies<SHAPE> sc = stage_copies<SHAPE>(a, mt0, nt0, wave);
     for (int s = 0; s < first; ++s) issue_stage<SHAPE>(sc, lds0 + s * kStage, kb0 + s, lane);
@@ -1118,7 +1164,7 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
 
     if constexpr (G::kSplit)
         if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
-    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
+    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1194,6 +1240,7 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
     constexpr int BI = G::BI, BJ = G::BJ;
     constexpr int kStage = G::kStage;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[G::kLdsBytes];
+    __shared__ __attribute__((aligned(16))) float params[EpilogueParams<G>::kCount];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1299,7 +1346,11 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
         }
     };
 
-    // prologue: up to three stages in flight; wait for stage 0
+    // prologue: the epilogue's parameters, then up to three stages in
+    // flight; wait for stage 0 (and so for the older parameter copies)
+    if constexpr (OUT == GEMM_OUT_BF16)
+        issue_epilogue_params<G>(a, tm, tn, wave, lane,
+                                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)params));
     const int first = KC < G::kStages ? KC : G::kStages;
     for (int st = 0; st < first; ++st) issue(lds0 + st * kStage, kb0 + st);
     if (first >= 3)
@@ -1340,7 +1391,7 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
 
     if constexpr (G::kSplit)
         if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
-    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, acc);
+    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
 // ---------------------------------------------------------------------------
