@@ -171,6 +171,24 @@ def test_validate_linear_statuses():
     assert _validate_linear(M=-1) == B.CONVROT_EINVAL
 
 
+def test_w4a16_row_layout_fits_the_workspace():
+    """The bf16 row layout that include/convrot.h states for the W4A16
+    workspace (16-byte words ordered by 16-row block, 128-K unit, step j,
+    quarter q, row) places every 8-value word of every row at a distinct word
+    inside the size the query returns, for ragged M and for K_rot % 128 == 64."""
+    for M, K, g in [(1, 3072, 256), (5, 192, 64), (17, 1000, 256), (32, 2048, 256), (31, 4160, 64)]:
+        Kr = -(-K // g) * g
+        KB = -(-Kr // 128)
+        m = np.arange(M)[:, None]
+        k = np.arange(0, Kr, 8)[None, :]
+        kl = k % 128
+        j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1)
+        q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1)
+        w = ((((m // 16) * KB + k // 128) * 4 + j) * 4 + q) * 16 + m % 16
+        assert len(np.unique(w)) == w.size, (M, K, g)
+        assert w.max() * 16 + 16 <= B.convrot_w4a16_workspace_bytes(M, K, g), (M, K, g)
+
+
 def test_w4a16_sizes_and_statuses():
     # rows rounded up to 16 and K to 128, bf16 each
     assert B.convrot_w4a16_workspace_bytes(1, 3072, 256) == 16 * 3072 * 2
