@@ -85,9 +85,11 @@ def _load():
         lib.oracle_gemm_i32.restype = I
         lib.oracle_epilogue.argtypes = [P, P, P, P, I64, I64, P]
         lib.oracle_epilogue.restype = None
+        lib.oracle_epilogue_f32.argtypes = [P, P, P, P, I64, I64, P, P]
+        lib.oracle_epilogue_f32.restype = None
         lib.oracle_linear.argtypes = [P, I64, I64, P, P, P, I64, I, P, P, P, P, I]
         lib.oracle_linear.restype = I
-        lib.oracle_linear_w4a16.argtypes = [P, I64, I64, P, P, P, I64, I, P, P, I]
+        lib.oracle_linear_w4a16.argtypes = [P, I64, I64, P, P, P, I64, I, P, P, P, I]
         lib.oracle_linear_w4a16.restype = I
         _lib = lib
         return lib
@@ -237,16 +239,18 @@ def gemm_i32(qx, qw, threads: int | None = None) -> np.ndarray:
     return acc
 
 
-def epilogue(acc, sx, sw, bias_bf16=None) -> np.ndarray:
-    """Y = bf16(fmaf(float(acc) * sx[m], sw[n], bias[n])), returned as bf16 bits."""
+def epilogue(acc, sx, sw, bias_bf16=None, want_f32: bool = False):
+    """Y = bf16(fmaf(float(acc) * sx[m], sw[n], bias[n])), returned as bf16 bits
+    (and, if asked, the binary32 values before the bf16 rounding)."""
     a = _c(acc, np.int32)
     M, N = a.shape
     sxa = _c(sx, np.float32)
     swa = _c(sw, np.float32)
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     y = np.empty((M, N), dtype=np.uint16)
-    _load().oracle_epilogue(_ptr(a), _ptr(sxa), _ptr(swa), _ptr(b), M, N, _ptr(y))
-    return y
+    yf = np.empty((M, N), dtype=np.float32) if want_f32 else None
+    _load().oracle_epilogue_f32(_ptr(a), _ptr(sxa), _ptr(swa), _ptr(b), M, N, _ptr(y), _ptr(yf))
+    return (y, yf) if want_f32 else y
 
 
 def prepare_weight(w_bf16, g: int, threads: int | None = None):
@@ -280,10 +284,12 @@ def linear(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, 
     return y
 
 
-def linear_w4a16(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, want_rotated: bool = False):
+def linear_w4a16(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = None, want_rotated: bool = False,
+                 want_f32: bool = False):
     """W4A16: rotated activation rows rounded to bf16, times the INT4 weight
     codes (exact products, binary64 sum), y = fmaf(fl32(sum), sw, bias) to bf16.
-    Returns Y as bf16 bits [M, N] (and, if asked, the bf16 rotated X)."""
+    Returns Y as bf16 bits [M, N] (and, if asked, the bf16 rotated X and the
+    binary32 outputs before the bf16 rounding, in that order)."""
     x = _c(x_bf16, np.uint16)
     M, K = x.shape
     qw = _c(qw_codes, np.int8)
@@ -294,6 +300,8 @@ def linear_w4a16(x_bf16, qw_codes, sw, bias_bf16, g: int, threads: int | None = 
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     y = np.empty((M, N), dtype=np.uint16)
     xr = np.empty((M, rotated_width(K, g)), dtype=np.uint16) if want_rotated else None
+    yf = np.empty((M, N), dtype=np.float32) if want_f32 else None
     _check(_load().oracle_linear_w4a16(_ptr(x), M, K, _ptr(qw), _ptr(swa), _ptr(b), N, int(g), _ptr(y), _ptr(xr),
-                                       threads or default_threads()), "linear_w4a16")
-    return (y, xr) if want_rotated else y
+                                       _ptr(yf), threads or default_threads()), "linear_w4a16")
+    out = (y,) + ((xr,) if want_rotated else ()) + ((yf,) if want_f32 else ())
+    return out if len(out) > 1 else y

@@ -62,7 +62,8 @@
  *   - code q = clamp(rint(fl32(r / s)), -7, 7), round half to even.
  *   - nibbles are two's complement; the low nibble holds the even index.
  *   - epilogue y = fmaf(fl32(float(acc) * sx[m]), sw[n], bias[n]) and then
- *     bf16 round-to-nearest-even.
+ *     bf16 round-to-nearest-even; the binary32 value y is exposed
+ *     (oracle_epilogue_f32) so that its single rounding can be checked.
  *
  * Built with -O2 -ffp-contract=off so no multiply-add is fused behind the
  * source's back; the one fused multiply-add of the epilogue is an explicit
@@ -438,17 +439,33 @@ int oracle_gemm_i32(const int8_t* QX, const int8_t* QW, int64_t M, int64_t N, in
 /* 6. Epilogue: y = bf16(fmaf(float(acc) * sx[m], sw[n], bias[n]))           */
 /* ------------------------------------------------------------------------ */
 
-/* bias: bf16 bits [N] or NULL for zeros. */
-void oracle_epilogue(const int32_t* ACC, const float* SX, const float* SW, const uint16_t* BIAS, int64_t M,
-                     int64_t N, uint16_t* Y)
+/* The binary32 value that the epilogue rounds to bf16: the integer sum times
+ * the row scale, rounded once, then one fused multiply-add with the column
+ * scale and the bias (a single rounding). */
+static float epilogue_value(int32_t acc, float sx, float sw, float b)
+{
+    float t = (float)acc * sx;
+    return fmaf(t, sw, b);
+}
+
+/* bias: bf16 bits [N] or NULL for zeros.  Y: bf16 bits [M][N]; YF (may be
+ * NULL): the binary32 values before the bf16 rounding. */
+void oracle_epilogue_f32(const int32_t* ACC, const float* SX, const float* SW, const uint16_t* BIAS, int64_t M,
+                         int64_t N, uint16_t* Y, float* YF)
 {
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             float b = BIAS ? oracle_bf16_to_f32(BIAS[n]) : 0.0f;
-            float t = (float)ACC[m * N + n] * SX[m];
-            float y = fmaf(t, SW[n], b);
-            Y[m * N + n] = oracle_f32_to_bf16(y);
+            float y = epilogue_value(ACC[m * N + n], SX[m], SW[n], b);
+            if (YF) YF[m * N + n] = y;
+            if (Y) Y[m * N + n] = oracle_f32_to_bf16(y);
         }
+}
+
+void oracle_epilogue(const int32_t* ACC, const float* SX, const float* SW, const uint16_t* BIAS, int64_t M,
+                     int64_t N, uint16_t* Y)
+{
+    oracle_epilogue_f32(ACC, SX, SW, BIAS, M, N, Y, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -491,6 +508,7 @@ struct w4a16_ctx {
     const uint16_t* BIAS;
     int64_t N, K;
     uint16_t* Y;
+    float* YF; /* binary32 values before the bf16 rounding, or NULL */
 };
 
 static void w4a16_one_row(void* p, int64_t m)
@@ -502,15 +520,19 @@ static void w4a16_one_row(void* p, int64_t m)
         double acc = 0.0; /* each product is exact; |sum| is far below 2^53 ulps of the terms */
         for (int64_t k = 0; k < c->K; ++k) acc += (double)oracle_bf16_to_f32(x[k]) * (double)q[k];
         float b = c->BIAS ? oracle_bf16_to_f32(c->BIAS[n]) : 0.0f;
-        c->Y[m * c->N + n] = oracle_f32_to_bf16(fmaf((float)acc, c->SW[n], b));
+        float y = fmaf((float)acc, c->SW[n], b); /* sum rounded once to binary32, then one fused multiply-add */
+        if (c->YF) c->YF[m * c->N + n] = y;
+        c->Y[m * c->N + n] = oracle_f32_to_bf16(y);
     }
 }
 
 /* X: bf16 [M][K]; QW: int8 codes [N][K_rot]; SW: [N]; BIAS: bf16 [N] or NULL;
- * Y: bf16 [M][N]; XR_out (optional): the bf16 rotated activations [M][K_rot].
+ * Y: bf16 [M][N]; XR_out (optional): the bf16 rotated activations [M][K_rot];
+ * YF_out (optional): the binary32 outputs before the bf16 rounding [M][N].
  * g as for oracle_rotate_rows.  Returns 0 on success. */
 int oracle_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, const int8_t* QW, const float* SW,
-                        const uint16_t* BIAS, int64_t N, int g, uint16_t* Y, uint16_t* XR_out, int nthreads)
+                        const uint16_t* BIAS, int64_t N, int g, uint16_t* Y, uint16_t* XR_out, float* YF_out,
+                        int nthreads)
 {
     if (M < 0 || N < 0 || K <= 0) return -1;
     const int64_t Kr = oracle_rotated_width(K, g);
@@ -521,7 +543,7 @@ int oracle_linear_w4a16(const uint16_t* X, int64_t M, int64_t K, const int8_t* Q
     if (rc == 0) rc = oracle_rotate_rows(X, M, K, g, R, nthreads);
     if (rc == 0) {
         for (size_t i = 0; i < (size_t)M * (size_t)Kr; ++i) XR[i] = oracle_f32_to_bf16(R[i]);
-        struct w4a16_ctx c = {XR, QW, SW, BIAS, N, Kr, Y};
+        struct w4a16_ctx c = {XR, QW, SW, BIAS, N, Kr, Y, YF_out};
         parallel_rows(w4a16_one_row, &c, M, nthreads);
     }
     free(R);

@@ -25,8 +25,13 @@ MUTATIONS = [
      "acc += v * (double)c->H[(int64_t)j * g + ((t + 1) % g)];"),
     ("nibble_order", "(uint8_t)(nibble(Q[n * K + 2 * j]) | (nibble(Q[n * K + 2 * j + 1]) << 4))",
      "(uint8_t)(nibble(Q[n * K + 2 * j + 1]) | (nibble(Q[n * K + 2 * j]) << 4))"),
-    ("epilogue_operand", "float t = (float)ACC[m * N + n] * SX[m];", "float t = (float)ACC[m * N + n] * SW[n];"),
-    ("dropped_bias", "float y = fmaf(t, SW[n], b);", "float y = fmaf(t, SW[n], 0.0f);"),
+    ("epilogue_operand", "float t = (float)acc * sx;", "float t = (float)acc * sw;"),
+    ("dropped_bias", "return fmaf(t, sw, b);", "return fmaf(t, sw, 0.0f);"),
+    ("epilogue_mul_add", "return fmaf(t, sw, b);", "return t * sw + b;"),
+    ("epilogue_scale_order", "float t = (float)acc * sx;\n    return fmaf(t, sw, b);",
+     "float t = (float)acc * sw;\n    return fmaf(t, sx, b);"),
+    ("quantize_by_reciprocal", "float t = rintf(r[k] / s);", "float t = rintf(r[k] * (1.0f / s));"),
+    ("w4a16_mul_add", "float y = fmaf((float)acc, c->SW[n], b);", "float y = (float)acc * c->SW[n] + b;"),
     ("bf16_truncation", "if (d_lo < d_hi) return toward_zero;", "return toward_zero;"),
     ("dropped_k_term", "for (int64_t k = 0; k < c->K; ++k) acc += (int64_t)", "for (int64_t k = 0; k < c->K - 1; ++k) acc += (int64_t)"),
     ("clamp_6", "if (t > 7.0f) t = 7.0f;", "if (t > 6.0f) t = 6.0f;"),

@@ -438,6 +438,78 @@ def test_epilogue_exact_rational():
             assert y[m, n] == oracle.f32_to_bf16(np.array([yf]))[0]
 
 
+def test_epilogue_f32_is_one_rounding_of_the_fused_multiply_add():
+    """The binary32 value the epilogue rounds to bf16 is fl32(fl32(acc sx) sw + b):
+    the row scale applied first and rounded, then one rounding of the exact
+    product-plus-bias.  Recomputed with exact rationals; the random cases are
+    checked to include some where a separate multiply and add, or the other
+    scale order, gives a different binary32 value (so both readings are pinned)."""
+    rng = np.random.default_rng(12)
+    M, N = 24, 40
+    acc = rng.integers(-800000, 800000, size=(M, N)).astype(np.int32)
+    sx = rng.uniform(0.01, 5, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    bias = _bits_of(rng.standard_normal(N) * 0.01)
+    y, yf = oracle.epilogue(acc, sx, sw, bias, want_f32=True)
+    assert np.array_equal(y, oracle.f32_to_bf16(yf))
+    bf = synth.bf16_bits_to_f32(bias)
+    differs_mul_add = differs_order = 0
+    for m in range(M):
+        for n in range(N):
+            t = np.float32(np.float32(acc[m, n]) * sx[m])
+            want = _round_to_f32_exact(Fraction(float(t)) * Fraction(float(sw[n])) + Fraction(float(bf[n])))
+            assert yf[m, n] == want, (m, n)
+            mul_add = np.float32(np.float32(t * sw[n]) + bf[n])
+            t_other = np.float32(np.float32(acc[m, n]) * sw[n])
+            other = _round_to_f32_exact(Fraction(float(t_other)) * Fraction(float(sx[m])) + Fraction(float(bf[n])))
+            differs_mul_add += int(mul_add != want)
+            differs_order += int(other != want)
+    assert differs_mul_add > 20 and differs_order > 20, (differs_mul_add, differs_order)
+
+
+def _fma_midpoint_cases():
+    """Hand-built epilogue inputs (acc, sx = 1, sw, bias) for which the fused
+    multiply-add and a separate multiply and add give different bf16 outputs.
+    With bias b = -1 and p = fl32(acc sw) = 1 + 2^-10 + 2^-18 (or + 3 2^-18),
+    p + b is exactly a bf16 midpoint (Sterbenz), so the unfused result is that
+    midpoint and rounds to the even bf16; the exact acc sw differs from p by a
+    small e of known sign, so the fused result lies on one side of the
+    midpoint and rounds to the other bf16 when e points away from the even
+    one.  Found by exact rational search over small integers acc."""
+    cases = []
+    for frac_num, even_is_upper in ((1, False), (3, True)):
+        p = Fraction(1) + Fraction(1, 2**10) + Fraction(frac_num, 2**18)
+        mid = p - 1
+        lo = mid - Fraction(1, 2**18)                 # bf16 neighbours of the midpoint
+        hi = mid + Fraction(1, 2**18)
+        for acc in range(3, 400):
+            sw0 = np.float32(float(p / acc))
+            found = None
+            for cand in (np.nextafter(sw0, np.float32(-1)), sw0, np.nextafter(sw0, np.float32(2))):
+                exact = acc * Fraction(float(cand))
+                if _round_to_f32_exact(exact) != np.float32(float(p)):
+                    continue
+                e = exact - p
+                if (e > 0) != even_is_upper and e != 0:   # the fused value leaves the even side
+                    found = cand
+                    break
+            if found is not None:
+                fused = hi if not even_is_upper else lo
+                even = lo if not even_is_upper else hi
+                cases.append((acc, np.float32(found), fused, even))
+                break
+    assert len(cases) == 2
+    return cases
+
+
+def test_epilogue_fused_multiply_add_decides_the_bf16_output():
+    for acc, sw, fused, even in _fma_midpoint_cases():
+        a = np.array([[acc]], dtype=np.int32)
+        y = oracle.epilogue(a, np.ones(1, np.float32), np.array([sw]), _exact_bf16([-1.0]))
+        got = Fraction(float(synth.bf16_bits_to_f32(y)[0, 0]))
+        assert got == fused and got != even, (acc, float(sw), got)
+
+
 def test_epilogue_zero_row_gives_bias():
     acc = np.zeros((2, 5), dtype=np.int32)
     bias = _bits_of(np.array([0.5, -0.25, 1.0, 0.0, -3.0]))
@@ -504,6 +576,38 @@ def test_w4a16_exact_rational_small(g):
             a32 = _round_to_f32_exact(acc)
             yf = _round_to_f32_exact(Fraction(float(a32)) * Fraction(float(sw[n])) + Fraction(float(bv[n])))
             assert y[m, n] == oracle.f32_to_bf16(np.array([yf]))[0]
+
+
+@pytest.mark.parametrize("g", [64, 256])
+def test_w4a16_f32_is_one_rounding_of_the_fused_multiply_add(g):
+    """The W4A16 binary32 output is fl32(fl32(sum) sw + b): one rounding of the
+    exact sum, then one rounding of the exact product-plus-bias (exact
+    rationals); some cases must differ from a separate multiply and add."""
+    K = 2 * g
+    x = synth.random_bf16((6, K), seed=34, outliers=2)
+    w = synth.random_bf16((9, K), seed=35, std=0.02)
+    qw, sw = oracle.prepare_weight(w, g)
+    _, xr = oracle.linear_w4a16(x, qw, sw, None, g, want_rotated=True)
+    xv = synth.bf16_bits_to_f32(xr)
+    a32 = np.empty((6, 9), dtype=np.float32)
+    for m in range(6):
+        for n in range(9):
+            a32[m, n] = _round_to_f32_exact(sum(Fraction(float(xv[m, k])) * int(qw[n, k]) for k in range(K)))
+    # the bias cancels row 0's product to bf16 precision, so that the rounding
+    # of the product (present in a separate multiply and add, absent in the
+    # fused one) shows in the result; the other rows take plain random biases
+    b = synth.random_bf16((9,), seed=36, std=0.01)
+    b[:] = np.where(np.arange(9) % 3 == 0, b, _bits_of(-(a32[0] * sw)))
+    y, yf = oracle.linear_w4a16(x, qw, sw, b, g, want_f32=True)
+    assert np.array_equal(y, oracle.f32_to_bf16(yf))
+    bv = synth.bf16_bits_to_f32(b)
+    differs = 0
+    for m in range(6):
+        for n in range(9):
+            want = _round_to_f32_exact(Fraction(float(a32[m, n])) * Fraction(float(sw[n])) + Fraction(float(bv[n])))
+            assert yf[m, n] == want, (m, n)
+            differs += int(np.float32(np.float32(a32[m, n] * sw[n]) + bv[n]) != want)
+    assert differs >= 3, differs
 
 
 def test_w4a16_tracks_dense_product_better_than_w4a4():
