@@ -248,7 +248,7 @@ def main():
             else:
                 binding.convrot_prepare_activations(s["X"], g, s["ws"])
                 e[1].record()
-                binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, Y=s["Y"])
+                binding.convrot_gemm(s["ws"], M, K, s["image"], s["sw"], s["bias"], N, g, Y=s["Y"])
             e[2].record()
         host_ms = (time.perf_counter() - t0) * 1e3
         torch.cuda.synchronize()

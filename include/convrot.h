@@ -58,7 +58,7 @@ extern "C" {
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* convrot_status_string(int status);
 
-/* Library version string, e.g. "convrot-gfx950 1.0". */
+/* Library version string, e.g. "convrot-gfx950 1.1". */
 const char* convrot_version(void);
 
 /* Rotation flag for every g argument: g = 64 or 256 selects the normalized
@@ -71,38 +71,59 @@ const char* convrot_version(void);
  * prepared with: convrot_linear must be given the same value. */
 #define CONVROT_REGULAR_HADAMARD 0x10000
 
+/* Image flag for every g argument: the weight image holds the packed INT4
+ * codes only, 0.5 bytes per weight -- the memory saving the pages aim at
+ * (convrot-mlx README, "Why this repository exists") -- and every product
+ * runs on the INT8 matrix cores.  Without it the image also carries the same
+ * codes as FP6 e2m3 values (1.25 bytes per weight in all), which lets the
+ * large-M product run on the FP6 matrix cores at twice the INT8 rate.  The
+ * flag changes the sizes below and must be passed, like the rotation flag,
+ * with the same value to every call that uses the image. */
+#define CONVROT_INT4_IMAGE 0x20000
+
 /* ---- sizes (host only, no HIP call) ----------------------------------- */
 
 /* Bytes of the weight image for an N x K weight: the packed INT4 codes,
  * round_up(N, 32) * round_up(K_rot, 128) / 2 bytes in 32-column x 128-K
  * units in MFMA fragment order (convrot-mlx README, "What is included": the
  * K x packed-N family of layouts, here tiled for CDNA4 matrix cores), followed
- * by the same codes as FP6 e2m3 values (every integer in [-7, 7] is exact in
- * e2m3), round_up(N, 32) * round_up(K_rot, 128) * 3 / 4 bytes, for the FP6
- * matrix cores of the large-M product.  g must be 64 or 256 (with or without
- * CONVROT_REGULAR_HADAMARD).  Returns CONVROT_OK or CONVROT_EINVAL. */
+ * -- unless g carries CONVROT_INT4_IMAGE -- by the same codes as FP6 e2m3
+ * values (every integer in [-7, 7] is exact in e2m3), round_up(N, 32) *
+ * round_up(K_rot, 128) * 3 / 4 bytes, for the FP6 matrix cores of the
+ * large-M product.  g must be 64 or 256 (with or without the flags above).
+ * Returns CONVROT_OK or CONVROT_EINVAL. */
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
 
 /* Bytes of workspace convrot_linear needs for an M x K input and N outputs.
  * Layout, each part starting at a 256-byte boundary:
- *   1. offset 0: 512 uint32 counters of the split-K GEMM (cleared by
- *      convrot_prepare_activations, left cleared by every GEMM; at the same
- *      offset for every shape);
- *   2. offset CONVROT_WORKSPACE_IMAGE_OFFSET: the activation-code image,
+ *   1. offset 0: 512 uint32 counters of the split-K GEMM (cleared by the
+ *      activation step, left cleared by every GEMM; at the same offset for
+ *      every shape);
+ *   2. offset CONVROT_WORKSPACE_STATUS_OFFSET: a uint32 status word, cleared
+ *      by the activation step of every call (convrot_linear,
+ *      convrot_prepare_activations, convrot_gemm_i32) and set to
+ *      CONVROT_STATUS_SPLIT_TIMEOUT by a split-K GEMM whose last workgroup of
+ *      a tile stopped waiting for the others' partial sums (a bounded wait of
+ *      seconds; it then adds none of them, so that call's Y is wrong).  The
+ *      library never reads it: a caller that wants to know reads the word
+ *      after the call has completed;
+ *   3. offset CONVROT_WORKSPACE_IMAGE_OFFSET: the activation-code image,
  *      round_up(M, 32) * round_up(K_rot, 128) / 2 bytes, INT4 codes in the
  *      same layout as the weight image;
- *   3. when M > 32, room for the same codes as FP6: round_up(M, 32) *
- *      round_up(K_rot, 128) * 3 / 4 bytes (written by
- *      convrot_prepare_activations always, by convrot_linear when its plan
- *      runs on the FP6 matrix cores);
- *   4. the activation scales sx: round_up(M, 32) floats;
- *   5. split-K partial tiles: when M > 32 and the output tiles are too few
+ *   4. when M > 32 and g does not carry CONVROT_INT4_IMAGE, room for the same
+ *      codes as FP6: round_up(M, 32) * round_up(K_rot, 128) * 3 / 4 bytes
+ *      (written by convrot_prepare_activations always, by convrot_linear when
+ *      its plan runs on the FP6 matrix cores);
+ *   5. the activation scales sx: round_up(M, 32) floats;
+ *   6. split-K partial tiles: when M > 32 and the output tiles are too few
  *      to occupy the GPU, each tile's K range is shared by S workgroups and
  *      S - 1 partial tiles of 4-byte sums per output tile live here (0 bytes
  *      otherwise).
- * Parts 1-4 depend on M and K only; convrot_prepare_activations needs only
+ * Parts 1-5 depend on M, K and g only; convrot_prepare_activations needs only
  * them.  Returns CONVROT_OK or CONVROT_EINVAL. */
-#define CONVROT_WORKSPACE_IMAGE_OFFSET 2048
+#define CONVROT_WORKSPACE_STATUS_OFFSET 2048
+#define CONVROT_WORKSPACE_IMAGE_OFFSET 4096
+#define CONVROT_STATUS_SPLIT_TIMEOUT 1
 int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* bytes_host);
 
 /* *count = the number of kernels convrot_linear launches for this shape: 1
@@ -160,8 +181,10 @@ int convrot_quantize_weight(const void* W_dev, int64_t N, int64_t K, int g, uint
 
 /* Lossless repack of N x packed-K codes into the weight image (the analogue
  * of the pages' repack_nk_weight_for_mpp, convrot-mlx README, "Install and
- * test").  image_dev: convrot_weight_image_bytes(N, K, 64) bytes. */
-int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t K, void* image_dev,
+ * test").  qweight_nk_dev is uint8 [N][K_rot/2]; image_dev:
+ * convrot_weight_image_bytes(N, K, g) bytes (g only decides K_rot and whether
+ * the FP6 copy is written). */
+int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t K, int g, void* image_dev,
                                void* stream);
 
 /* ---- the linear ------------------------------------------------------- */
@@ -222,14 +245,13 @@ int convrot_linear_w4a16(const void* X_dev, int64_t M, int64_t K, const void* im
  * convrot_gemm consumes that workspace: integer products against the weight
  * image, then the scale + bias epilogue into Y.  Same arguments and rules as
  * convrot_linear, except that convrot_prepare_activations needs only the
- * first three parts of the workspace (it does not know N).  convrot_gemm
- * does not know g: its K is the code width K_rot of the prepared rows (equal
- * to K when g divides K).  It leaves the workspace valid for another
+ * first five parts of the workspace (it does not know N).  convrot_gemm takes
+ * the M, K, N and g of the linear.  It leaves the workspace valid for another
  * convrot_gemm. */
 int convrot_prepare_activations(const void* X_dev, int64_t M, int64_t K, int g, void* workspace_dev,
                                 size_t ws_bytes, void* stream);
 int convrot_gemm(const void* workspace_dev, size_t ws_bytes, int64_t M, int64_t K, const void* image_dev,
-                 const float* sw_dev, const void* bias_dev, int64_t N, void* Y_dev, void* stream);
+                 const float* sw_dev, const void* bias_dev, int64_t N, int g, void* Y_dev, void* stream);
 
 /* ---- parity hooks (same kernels, exposed intermediate results) ---------- */
 
@@ -241,12 +263,44 @@ int convrot_prepare_rows(const void* X_dev, int64_t rows, int64_t K, int g, int8
                          float* rotated_dev, void* stream);
 
 /* The integer product alone: acc_dev int32 [M][N] = qx . codes(image)^T for
- * activation codes qx_dev int8 [M][K] (values in [-7, 7]).  The codes are first
- * re-laid-out into the workspace (convrot_workspace_bytes(M, K, N, 64) bytes),
- * then the GEMM kernel of convrot_linear runs with its epilogue replaced by
- * an int32 store. */
+ * activation codes qx_dev int8 [M][K] (values in [-7, 7]; K the code width).
+ * The codes are first re-laid-out into the workspace
+ * (convrot_workspace_bytes(M, K, N, 64) bytes), then the GEMM kernel of
+ * convrot_linear runs with its epilogue replaced by an int32 store.  The
+ * image must carry its FP6 copy (prepared without CONVROT_INT4_IMAGE). */
 int convrot_gemm_i32(const int8_t* qx_dev, int64_t M, int64_t K, const void* image_dev, int64_t N,
                      int32_t* acc_dev, void* workspace_dev, size_t ws_bytes, void* stream);
+
+/* The same with the block-tile plan given instead of the library's choice
+ * (M > 32): tile_m x tile_n one of 192 x 384 and 192 x 192 (INT8 matrix
+ * cores, INT4 image part) or 256 x 256 (FP6 matrix cores, FP6 image part),
+ * and `splits` workgroups sharing each tile's K range (1 .. min(8, K_pad /
+ * 128); a split launch may have at most 256 tiles).  Lets a test reach every
+ * block tile, with and without the split-K exchange, at any shape.  The
+ * workspace must hold convrot_workspace_bytes_tiled(M, K, N, tile_m, tile_n,
+ * splits) bytes -- sized from the same plan, so the exchange's partial tiles
+ * fit.  test_flags: 0, or CONVROT_TEST_SPLIT_TIMEOUT to make the last
+ * workgroup of every split tile wait for one writer more than exist, with a
+ * tiny bound on the wait (it runs out, sets the status word and still ends
+ * normally; the test of that report).  CONVROT_EINVAL for any other value. */
+#define CONVROT_TEST_SPLIT_TIMEOUT 1
+int convrot_workspace_bytes_tiled(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits,
+                                  size_t* bytes_host);
+int convrot_gemm_i32_tiled(const int8_t* qx_dev, int64_t M, int64_t K, const void* image_dev, int64_t N,
+                           int32_t* acc_dev, int tile_m, int tile_n, int splits, int test_flags, void* workspace_dev,
+                           size_t ws_bytes, void* stream);
+
+/* Host-side check of the split-K exchange of such a plan (no HIP call): every
+ * byte offset the exchange stores to or copies from in the workspace's
+ * partial-tile area, every counter slot and every LDS offset of the
+ * finalizer's copies and reads, computed with the kernels' own address
+ * functions; returns one past the largest of each: *partial_end_host (bytes
+ * from the start of the partial area; to be <= the bytes that
+ * convrot_workspace_bytes_tiled sets aside), *counters_used_host (counter
+ * words; <= 512) and *lds_end_host (bytes of the stage ring).  All 0 when
+ * splits == 1. */
+int convrot_split_k_extent(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits,
+                           size_t* partial_end_host, int* counters_used_host, size_t* lds_end_host);
 
 /* ---- host layout tools (host memory, no HIP call) ----------------------- */
 

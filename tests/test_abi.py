@@ -43,6 +43,19 @@ def test_regular_flag_matches_header():
     assert m and int(m.group(1), 16) == B.CONVROT_REGULAR_HADAMARD
 
 
+def test_image_flag_status_word_and_test_flag_match_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+CONVROT_INT4_IMAGE\s+(0x[0-9a-fA-F]+)", text)
+    assert m and int(m.group(1), 16) == B.CONVROT_INT4_IMAGE
+    for name, value in (("CONVROT_WORKSPACE_STATUS_OFFSET", B.WORKSPACE_STATUS_OFFSET),
+                        ("CONVROT_STATUS_SPLIT_TIMEOUT", B.CONVROT_STATUS_SPLIT_TIMEOUT),
+                        ("CONVROT_TEST_SPLIT_TIMEOUT", B.CONVROT_TEST_SPLIT_TIMEOUT)):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
+    # the status word sits right after the 512 counters, before the activation image
+    assert B.WORKSPACE_STATUS_OFFSET == 512 * 4 < B.WORKSPACE_IMAGE_OFFSET
+
+
 def test_mfma_kinds_match_header():
     text = open(HEADER).read()
     for name in ("CONVROT_MFMA_I8", "CONVROT_MFMA_FP6"):
@@ -71,6 +84,9 @@ def test_weight_image_bytes(N, K, g, int4):
     # the INT4 codes, then the same codes as FP6 (six bits each)
     assert _int4_plane(N, K) == int4
     assert B.convrot_weight_image_bytes(N, K, g) == int4 + int4 * 3 // 2
+    # INT4 only: half a byte per (padded) weight, with either rotation
+    assert B.convrot_weight_image_bytes(N, K, g | B.CONVROT_INT4_IMAGE) == int4
+    assert B.convrot_weight_image_bytes(N, K, g | B.CONVROT_INT4_IMAGE | B.CONVROT_REGULAR_HADAMARD) == int4
 
 
 def test_plan_of_the_flux_shapes():
@@ -93,33 +109,123 @@ def test_plan_of_the_flux_shapes():
         B.convrot_linear_plan(64, 1001, 64, 256)
 
 
+def test_plan_of_the_flux_shapes_with_an_int4_image():
+    """Without the FP6 copy every product runs on the INT8 matrix cores: the
+    QKV and stress shapes move to INT8 block tiles, the others keep theirs."""
+    I8, F = B.CONVROT_MFMA_I8, B.CONVROT_INT4_IMAGE
+    assert B.convrot_linear_plan(1536, 3072, 9216, 256 | F) == {"mfma": I8, "tile": (192, 384), "splits": 1}
+    assert B.convrot_linear_plan(1536, 3072, 12288, 256 | F) == {"mfma": I8, "tile": (192, 384), "splits": 1}
+    assert B.convrot_linear_plan(1536, 12288, 3072, 256 | F) == {"mfma": I8, "tile": (192, 192), "splits": 2}
+    for M, N, K in [(4096, 3072, 3072), (64, 1024, 1024), (128, 2048, 2048), (300, 9000, 12288)]:
+        assert B.convrot_linear_plan(M, K, N, 256 | F)["mfma"] == I8, (M, N, K)
+
+
 def test_workspace_bytes():
-    # 512 counters (2048 B) | activation INT4 image (M up to 32 rows, K up to 128) |
-    # the same codes as FP6 when M > 32 (3/4 byte each) | sx | split-K partials,
-    # each part 256-byte aligned (values worked out by hand from that layout)
+    # 512 counters (2048 B) and the status word, the activation INT4 image at 4096
+    # (M up to 32 rows, K up to 128) | the same codes as FP6 when M > 32 (3/4 byte
+    # each) | sx | split-K partials, each part 256-byte aligned (values worked out
+    # by hand from that layout)
     # M <= 32: weight streaming, never split, no FP6 image
-    assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 2048 + 49152 + 256
+    assert B.convrot_workspace_bytes(1, 3072, 12288, 256) == 4096 + 49152 + 256
     # 1536 x 3072 -> 9216: 216 FP6 tiles of 256 x 256 fill the GPU, no split
-    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 2048 + 2359296 + 3538944 + 6144
+    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256) == 4096 + 2359296 + 3538944 + 6144
     # 1536 x 12288 -> 3072: 128 tiles of 192 x 192, K split 2 ways -> 1 partial tile of
     # 192 x 192 4-byte sums per tile (fewer partial bytes than 72 tiles of 256 x 256
     # split 3 ways)
-    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 2048 + 9437184 + 14155776 + 6144 + 128 * 147456
+    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256) == 4096 + 9437184 + 14155776 + 6144 + 128 * 147456
     # 1536 x 3072 -> 12288: 288 tiles of 256 x 256 would take two rounds; 256 tiles
     # of 192 x 384 take one, unsplit
-    assert B.convrot_workspace_bytes(1536, 3072, 12288, 256) == 2048 + 2359296 + 3538944 + 6144
+    assert B.convrot_workspace_bytes(1536, 3072, 12288, 256) == 4096 + 2359296 + 3538944 + 6144
     # 4096 x 3072 -> 3072: 192 FP6 tiles of 256 x 256, unsplit
-    assert B.convrot_workspace_bytes(4096, 3072, 3072, 256) == 2048 + 6291456 + 9437184 + 16384
+    assert B.convrot_workspace_bytes(4096, 3072, 3072, 256) == 4096 + 6291456 + 9437184 + 16384
     # 256 x 4096 -> 256: 2 x 2 tiles of 192 x 192; 32 K blocks split 2 ways (at least
     # 16 K blocks per split) -> 1 partial tile each
-    assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 2048 + 524288 + 786432 + 1024 + 4 * 147456
+    assert B.convrot_workspace_bytes(256, 4096, 256, 256) == 4096 + 524288 + 786432 + 1024 + 4 * 147456
     # 5 x 192 -> N: M <= 32
-    assert B.convrot_workspace_bytes(5, 192, 100, 64) == 2048 + 32 * 256 // 2 + 256
+    assert B.convrot_workspace_bytes(5, 192, 100, 64) == 4096 + 32 * 256 // 2 + 256
     # K not a multiple of g: sizes follow the rotated width (1000 -> 1024)
     assert B.convrot_workspace_bytes(64, 1000, 1024, 256) == B.convrot_workspace_bytes(64, 1024, 1024, 256)
     assert B.convrot_weight_image_bytes(100, 328, 256) == 128 * 512 // 2 * 5 // 2
     # N = 0: nothing to split
-    assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 2048 + 9437184 + 14155776 + 6144
+    assert B.convrot_workspace_bytes(1536, 12288, 0, 256) == 4096 + 9437184 + 14155776 + 6144
+    # INT4 image: no FP6 activation part; QKV on 192 x 384 unsplit, the
+    # down-projection on 192 x 192 split 2 ways as before
+    F = B.CONVROT_INT4_IMAGE
+    assert B.convrot_workspace_bytes(1536, 3072, 9216, 256 | F) == 4096 + 2359296 + 6144
+    assert B.convrot_workspace_bytes(1536, 12288, 3072, 256 | F) == 4096 + 9437184 + 6144 + 128 * 147456
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+_RING = {(192, 384): 4 * 18 * 2048, (192, 192): 4 * 12 * 2048, (256, 256): 3 * 16 * 3072}
+
+
+@pytest.mark.parametrize("M,K,N", [(1536, 12288, 3072), (1500, 12000, 3000), (256, 4096, 256), (64, 16384, 64)])
+@pytest.mark.parametrize("tile", [(192, 384), (192, 192), (256, 256)])
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
+def test_split_k_exchange_stays_inside_its_workspace(M, K, N, tile, splits):
+    """Every address of the split-K exchange, enumerated on the host through the
+    kernels' own address functions: the partial-tile stores and copies end
+    exactly at (S - 1) slots per tile, which is the room the same plan's
+    workspace size sets aside after its other parts; counters and LDS stay in
+    their arrays."""
+    tiles = _ceil(M, tile[0]) * _ceil(N, tile[1])
+    if splits > 1 and tiles > 256:
+        with pytest.raises(B.ConvRotError):
+            B.convrot_split_k_extent(M, K, N, tile, splits)
+        return
+    ext = B.convrot_split_k_extent(M, K, N, tile, splits)
+    slot = tile[0] * tile[1] * 4
+    assert ext["partial_end"] == tiles * (splits - 1) * slot
+    ws = B.convrot_workspace_bytes_tiled(M, K, N, tile, splits)
+    assert ws - B.convrot_workspace_bytes_tiled(M, K, N, tile, 1) == ext["partial_end"]
+    if splits > 1:
+        assert ext["counters_used"] == 256 + tiles <= 512
+        assert ext["lds_end"] == slot // 2 <= _RING[tile]
+    else:
+        assert ext == {"partial_end": 0, "counters_used": 0, "lds_end": 0}
+
+
+def test_split_k_fault_reading():
+    """The down-projection shape, with the block tiles and splits that a timing
+    probe once forced when the GPU faulted (192 x 384 split 4 ways, 256 x 256
+    split 3 ways): their exchange needs 56.6 MB and 37.7 MB of partial tiles,
+    while a workspace sized by the library's own plan for this shape (192 x 192
+    split 2 ways) has 18.9 MB of room -- a forced launch given such a workspace
+    writes tens of MB past its end.  The plan's own split fits exactly."""
+    M, K, N = 1536, 12288, 3072
+    room = B.convrot_workspace_bytes(M, K, N, 256) - B.convrot_workspace_bytes_tiled(M, K, N, (256, 256), 1)
+    assert room == 128 * 192 * 192 * 4 == 18874368
+    assert B.convrot_split_k_extent(M, K, N, (192, 192), 2)["partial_end"] == room
+    e4 = B.convrot_split_k_extent(M, K, N, (192, 384), 4)["partial_end"]
+    e3 = B.convrot_split_k_extent(M, K, N, (256, 256), 3)["partial_end"]
+    assert e4 == 64 * 3 * 192 * 384 * 4 == 56623104 and e4 - room == 37748736
+    assert e3 == 72 * 2 * 256 * 256 * 4 == 37748736 and e3 - room == 18874368
+
+
+def _gemm_i32_tiled_status(M, K, N, tile, splits, ws_bytes, flags=0):
+    lib = B.load()
+    p = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: the checks come first
+    return lib.convrot_gemm_i32_tiled(p, M, K, p, N, p, tile[0], tile[1], splits, flags, p, ws_bytes, None)
+
+
+def test_gemm_i32_tiled_checks():
+    M, K, N = 1536, 12288, 3072
+    need = B.convrot_workspace_bytes_tiled(M, K, N, (256, 256), 3)
+    assert _gemm_i32_tiled_status(M, K, N, (256, 256), 3, need - 1) == B.CONVROT_EWORKSPACE
+    # the plan-sized workspace is too small for the forced split
+    assert _gemm_i32_tiled_status(M, K, N, (256, 256), 3, B.convrot_workspace_bytes(M, K, N, 256)) == \
+        B.CONVROT_EWORKSPACE
+    for tile, splits in [((128, 128), 1), ((192, 384), 0), ((192, 384), 9), ((256, 256), -1)]:
+        assert _gemm_i32_tiled_status(M, K, N, tile, splits, 1 << 40) == B.CONVROT_EINVAL, (tile, splits)
+    assert _gemm_i32_tiled_status(32, K, N, (192, 192), 1, 1 << 40) == B.CONVROT_EINVAL       # M <= 32
+    assert _gemm_i32_tiled_status(M, 256, N, (192, 192), 3, 1 << 40) == B.CONVROT_EINVAL      # S > K blocks
+    assert _gemm_i32_tiled_status(4096, K, 9216, (192, 192), 2, 1 << 40) == B.CONVROT_EINVAL  # > 256 tiles split
+    assert _gemm_i32_tiled_status(M, K, N, (192, 192), 2, 1 << 40, flags=2) == B.CONVROT_EINVAL
+    with pytest.raises(B.ConvRotError):
+        B.convrot_workspace_bytes_tiled(M, K, N, (192, 96), 1)
 
 
 @pytest.mark.parametrize("M,K,N,g,want", [(1, 3072, 12288, 256, 1), (4, 4096, 64, 256, 1), (5, 3072, 64, 256, 2),
@@ -154,7 +260,8 @@ def test_validate_linear_statuses():
     assert _validate_linear(g=256 | R) == B.CONVROT_OK
     assert _validate_linear(g=64 | R) == B.CONVROT_OK
     assert _validate_linear(g=128 | R) == B.CONVROT_EINVAL
-    assert _validate_linear(g=256 | (R << 1)) == B.CONVROT_EINVAL    # unknown flag
+    assert _validate_linear(g=256 | (R << 2)) == B.CONVROT_EINVAL    # unknown flag
+    assert _validate_linear(g=256 | B.CONVROT_INT4_IMAGE | R) == B.CONVROT_OK
     assert _validate_linear(g=R) == B.CONVROT_EINVAL
     assert _validate_linear(K=1000) == B.CONVROT_OK               # last group zero-padded to 1024
     assert _validate_linear(K=1004) == B.CONVROT_EINVAL           # rows are whole 16-byte runs

@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded
-synthetic inputs.  Small shapes are compared element by element and span
-several tiles with ragged tails; the full diffusion-transformer shapes are
-compared on sampled rows and columns plus properties that hold at any size.
+synthetic inputs.  Small shapes span several tiles with ragged tails; the
+full diffusion-transformer shapes run in the launch configuration the
+benchmark times.  Every output is compared element by element.
 
 Method: convrot-mlx README, "What is included" (grouped normalized Hadamard
 rotation for g = 64/256, symmetric rowwise absmax INT4 in [-7, 7],
@@ -58,6 +58,7 @@ PREP_SHAPES = [
 
 
 REG = 0x10000  # the library's regular-Hadamard flag (checked against the header in test_abi)
+INT4 = 0x20000  # the library's INT4-only image flag (checked against the header in test_abi)
 PREP_SHAPES += [(5, 256, 256 | REG), (37, 3072, 256 | REG), (2, 16384, 256 | REG), (7, 192, 64 | REG),
                 (33, 1024, 64 | REG), (1, 64, 64 | REG),
                 # K not a multiple of g (zero-padded last group), both matrices
@@ -120,7 +121,7 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
     # the FP6 copy in the image holds the same codes
     assert np.array_equal(gpu.convrot_host_image_fp6_to_nk(img, N, K), gpu.convrot_host_image_to_nk(img, N, K))
     # the device repack of N x packed-K is byte-identical to the direct image
-    image2 = gpu.convrot_repack_nk_to_image(nk, N, K)
+    image2 = gpu.convrot_repack_nk_to_image(nk, N, K, g)
     assert np.array_equal(image2.cpu().numpy(), img)
     # and so is the host repack (layout definition shared by host and device)
     assert np.array_equal(gpu.convrot_host_nk_to_image(nk.cpu().numpy(), N, K), img)
@@ -144,7 +145,10 @@ GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), 
                # picks here (convrot_linear_plan)
                (1536, 9216, 128), (1500, 9000, 256), (1536, 12288, 128), (1500, 12000, 384),
                (1536, 3072, 8192), (4096, 3072, 128), (4000, 3000, 256), (256, 3072, 16384),
-               (200, 3011, 16384)]
+               (200, 3011, 16384),
+               # the FP6 and 192 x 384 tiles with at least eight 128-K blocks, so that their
+               # K loops run the steady state of the stage ring (aligned and ragged)
+               (1536, 9216, 1024), (1500, 9000, 1152), (1536, 12288, 1024), (1500, 12000, 1408)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -168,6 +172,84 @@ def test_gemm_i32_integer_edges(gpu):
     assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
 
 
+# (tile, splits, M, N, K): every block tile at shapes the plan would not give
+# it, unsplit and (192 x 192) split
+TILED = [((256, 256), 1, 300, 520, 1152), ((256, 256), 1, 33, 1000, 2048), ((256, 256), 1, 700, 300, 5120),
+         ((192, 384), 1, 300, 700, 2048), ((192, 384), 1, 1000, 400, 6144), ((192, 384), 1, 40, 3000, 1024),
+         ((192, 192), 1, 1536, 9216, 1024), ((192, 192), 3, 256, 600, 6144), ((192, 192), 8, 200, 3011, 16384),
+         ((192, 192), 5, 500, 260, 8192)]
+
+
+@pytest.mark.parametrize("tile,splits,M,N,K", TILED)
+def test_gemm_i32_every_block_tile(gpu, tile, splits, M, N, K):
+    rng = np.random.default_rng(M + 3 * N + 5 * K + splits)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), N, K))
+    acc, ws = gpu.convrot_gemm_i32_tiled(_dev(qx), image, N, tile, splits)
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(qx, qw))
+    assert gpu.workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("tile,splits", [((256, 256), 1), ((192, 384), 1), ((192, 192), 8), ((192, 192), 1)])
+def test_gemm_i32_saturated_codes_on_every_block_tile(gpu, tile, splits):
+    """Integer edges at the longest rows: every code +-7 and K = 16384, so that
+    |acc| reaches 49 K = 802,816 -- through each block tile (on the FP6 tile the
+    binary32 sums stay exact integers below 2^24)."""
+    K, M, N = 16384, 64, 96
+    rng = np.random.default_rng(7)
+    sx = rng.choice(np.array([-1, 1], np.int8), size=(M, K))
+    sw = rng.choice(np.array([-1, 1], np.int8), size=(N, K))
+    sx[0], sx[1], sw[0], sw[1] = 1, -1, 1, -1
+    sw[2] = sx[5]
+    qx, qw = (7 * sx).astype(np.int8), (7 * sw).astype(np.int8)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), N, K))
+    acc = gpu.convrot_gemm_i32_tiled(_dev(qx), image, N, tile, splits)[0].cpu().numpy()
+    assert acc[0, 0] == 49 * K and acc[0, 1] == -49 * K and acc[1, 0] == -49 * K and acc[1, 1] == 49 * K
+    assert acc[5, 2] == 49 * K
+    assert np.array_equal(acc, oracle.gemm_i32(qx, qw))
+
+
+@pytest.mark.parametrize("tile,splits,M,N,K", [((256, 256), 2, 300, 520, 4096), ((192, 384), 2, 300, 700, 4096),
+                                               ((256, 256), 3, 1536, 3072, 12288), ((192, 384), 4, 1536, 3072, 12288)])
+def test_gemm_i32_split_k_on_the_eight_wave_tiles(gpu, tile, splits, M, N, K):
+    """The split-K exchange on the two eight-wave block tiles, which the plan
+    itself never splits, including the down-projection shape with the splits
+    a timing probe once forced there when the GPU faulted.  Such a split needs
+    more partial-tile room than a workspace sized by the library's own plan
+    (checked on the CPU in test_abi); here the workspace is sized from the
+    forced plan, as the hook requires."""
+    rng = np.random.default_rng(M + N + K + splits)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), N, K))
+    assert gpu.convrot_split_k_extent(M, K, N, tile, splits)["partial_end"] > 0
+    acc, ws = gpu.convrot_gemm_i32_tiled(_dev(qx), image, N, tile, splits)
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(qx, qw))
+    assert gpu.workspace_status(ws) == 0
+
+
+def test_split_k_timeout_is_reported(gpu):
+    """The split-K finalizer's bounded wait, forced to run out from the host
+    (it waits for one writer more than exist, with a tiny bound): the kernel
+    still ends, the workspace's status word says so, and the next call on the
+    same workspace (whose activation step clears the counters and the status)
+    is exact again."""
+    import torch
+    M, N, K = 256, 600, 6144
+    rng = np.random.default_rng(11)
+    qx = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    image = _dev(gpu.convrot_host_nk_to_image(oracle.pack_nk(qw), N, K))
+    _, ws = gpu.convrot_gemm_i32_tiled(_dev(qx), image, N, (192, 192), 3, test_flags=gpu.CONVROT_TEST_SPLIT_TIMEOUT)
+    torch.cuda.synchronize()
+    assert gpu.workspace_status(ws) == gpu.CONVROT_STATUS_SPLIT_TIMEOUT
+    acc, ws = gpu.convrot_gemm_i32_tiled(_dev(qx), image, N, (192, 192), 3, workspace=ws)
+    torch.cuda.synchronize()
+    assert gpu.workspace_status(ws) == 0
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(qx, qw))
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (64, 1024, 8192), (300, 700, 4096), (256, 4096, 12288)])
 def test_split_k_workspace_reuse(gpu, M, N, K):
     """Shapes whose tiles are split along K: a workspace full of garbage is
@@ -189,11 +271,11 @@ def test_split_k_workspace_reuse(gpu, M, N, K):
     # not knowing N, the activation step writes both copies of the codes
     torch.cuda.synchronize()
     assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), gpu.workspace_act_codes(ws, M, K))
-    outs = [gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N) for _ in range(3)]
+    outs = [gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N, 256) for _ in range(3)]
     # a narrower GEMM on the same workspace, then the original again
     Nn = N // 2
-    gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), Nn)
-    outs.append(gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N))
+    gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), Nn, 256)
+    outs.append(gpu.convrot_gemm(ws, M, K, image, sw, _dev(b), N, 256))
     torch.cuda.synchronize()
     for Y in outs:
         assert np.array_equal(_host_bits(Y), y_or)
@@ -203,10 +285,17 @@ def test_split_k_workspace_reuse(gpu, M, N, K):
 # the whole linear
 # --------------------------------------------------------------------------
 
+def _oracle_g(g):
+    """The group argument for the oracle: the INT4-only image flag is a storage
+    choice of the library and has no arithmetic meaning."""
+    return g & ~INT4
+
+
 def _linear_parity(gpu, x, w, bias, g):
     N, K = w.shape
-    oq_w, osw = oracle.prepare_weight(w, g)
-    y_or, parts = oracle.linear(x, oq_w, osw, bias, g, want_parts=True)
+    og = _oracle_g(g)
+    oq_w, osw = oracle.prepare_weight(w, og)
+    y_or, parts = oracle.linear(x, oq_w, osw, bias, og, want_parts=True)
     image, sw = gpu.convrot_prepare_weight(_dev(w), g)
     ws = gpu.new_workspace(x.shape[0], K, N, g)
     Y = gpu.convrot_linear(_dev(x), image, sw, None if bias is None else _dev(bias), N, g, workspace=ws)
@@ -215,13 +304,13 @@ def _linear_parity(gpu, x, w, bias, g):
     M = x.shape[0]
     K = gpu.rotated_width(K, g)
     qx = gpu.workspace_act_codes(ws, M, K)
-    orx = oracle.rotate_rows(x, g)
+    orx = oracle.rotate_rows(x, og)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
     if M > 32 and gpu.convrot_linear_plan(M, w.shape[1], N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
         # the FP6 copy the FP6 tile reads holds the same codes
         assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), qx)
     qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
-    compare_codes(qw, oq_w, oracle.rotate_rows(w, g), osw, "weight codes")
+    compare_codes(qw, oq_w, oracle.rotate_rows(w, og), osw, "weight codes")
     rows_ok = np.all(qx == parts["qx"], axis=1) & bool(np.array_equal(qw, oq_w))
     compare_y(gy, y_or, rows_ok)
     return gy, y_or
@@ -251,6 +340,41 @@ def test_linear_ragged_shapes(gpu, M, N, K, g):
     w = synth.random_bf16((N, K), seed=N + K, std=0.02)
     b = synth.random_bf16((N,), seed=K, std=0.01)
     _linear_parity(gpu, x, w, b, g)
+
+
+@pytest.mark.parametrize("M,N,K,g,bias", [
+    # the FP6 256 x 256 tile and the INT8 192 x 384 tile through the whole linear, ragged
+    # M and N (N % 8 != 0: the epilogue's partial 16-byte stores), with and without bias
+    (1500, 9000, 3072, 256, True), (1501, 9004, 3072, 256, False), (1500, 12000, 3072, 256, True),
+    (1499, 12004, 3072, 256, False), (300, 700, 1152, 256, False),
+    # INT4-only weight images: every product on the INT8 matrix cores, including the
+    # shapes the FP6 tile takes otherwise, the weight-streaming and one-kernel paths
+    (1500, 9000, 3072, 256 | INT4, True), (300, 520, 1280, 256 | INT4, False), (40, 1000, 2048, 64 | INT4, True),
+    (16, 3000, 3072, 256 | INT4, True), (3, 5000, 4096, 256 | INT4 | REG, True), (65, 200, 3000, 256 | INT4, True)])
+def test_linear_block_tiles_and_image_formats(gpu, M, N, K, g, bias):
+    x = synth.random_bf16((M, K), seed=M + 2 * N, outliers=3)
+    w = synth.random_bf16((N, K), seed=N + 3 * K, std=0.02)
+    b = synth.random_bf16((N,), seed=K + 1, std=0.01) if bias else None
+    _linear_parity(gpu, x, w, b, g)
+
+
+def test_int4_image_is_the_int4_part_of_the_full_image(gpu):
+    """An INT4-only image is byte for byte the first part of the default image
+    (0.5 bytes per weight, padding included), and the linear on it gives the
+    same Y as the FP6 tile on the full image (both are exact integer products)."""
+    M, N, K = 1536, 9216, 1024
+    x = synth.random_bf16((M, K), seed=91, outliers=4)
+    w = synth.random_bf16((N, K), seed=92, std=0.02)
+    b = synth.random_bf16((N,), seed=93, std=0.01)
+    full, sw = gpu.convrot_prepare_weight(_dev(w), 256)
+    int4, sw4 = gpu.convrot_prepare_weight(_dev(w), 256 | INT4)
+    assert int4.numel() == N * K // 2 == gpu.convrot_weight_image_bytes(N, K, 256 | INT4)
+    assert np.array_equal(int4.cpu().numpy(), full.cpu().numpy()[:int4.numel()])
+    assert gpu.convrot_linear_plan(M, K, N, 256)["mfma"] == gpu.CONVROT_MFMA_FP6
+    assert gpu.convrot_linear_plan(M, K, N, 256 | INT4)["mfma"] == gpu.CONVROT_MFMA_I8
+    y6 = _host_bits(gpu.convrot_linear(_dev(x), full, sw, _dev(b), N, 256))
+    y4 = _host_bits(gpu.convrot_linear(_dev(x), int4, sw4, _dev(b), N, 256 | INT4))
+    assert np.array_equal(y6, y4)
 
 
 def test_linear_no_bias_and_zero_rows(gpu):
@@ -351,18 +475,21 @@ FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_ml
 
 
 @pytest.mark.parametrize("name", FULL + ["flux_qkv_m1536_k3072_n9216+regular", "flux_qkv_m1536_k3072_n9216+zero_rows",
-                                         "decode_m4_k3072_n12288+zero_rows"])
-def test_linear_full_size_sampled(gpu, name):
-    """Full shapes, the launch configuration the benchmark times; the oracle
-    recomputes sampled rows x sampled columns from scratch.  "+regular": the
-    same inputs rotated with the regular Hadamard matrix.  "+zero_rows": a
-    few rows of X set to zero, whose scale and codes must be zero and whose
-    output must be the bias exactly."""
+                                         "decode_m4_k3072_n12288+zero_rows", "flux_qkv_m1536_k3072_n9216+int4",
+                                         "flux_mlp_down_m1536_k12288_n3072+regular"])
+def test_linear_full_size(gpu, name):
+    """Full shapes, in the launch configuration the benchmark times, against
+    the oracle on every output: all activation and weight codes, the scales,
+    and Y element by element.  "+regular": the same inputs rotated with the
+    regular Hadamard matrix.  "+zero_rows": a few rows of X set to zero, whose
+    scale and codes must be zero and whose output must be the bias exactly.
+    "+int4": an INT4-only weight image (INT8 matrix cores)."""
     import torch
     base, _, variant = name.partition("+")
     inp = synth.make(base)
     wl = inp["workload"]
-    M, N, K, g = wl.M, wl.N, wl.K, wl.g | (REG if variant == "regular" else 0)
+    M, N, K = wl.M, wl.N, wl.K
+    g = wl.g | (REG if variant == "regular" else 0) | (INT4 if variant == "int4" else 0)
     zero_rows = np.array(sorted({1 % M, M // 2, M - 1})) if variant == "zero_rows" else np.array([], int)
     if zero_rows.size:
         inp["x"] = inp["x"].copy()
@@ -376,28 +503,26 @@ def test_linear_full_size_sampled(gpu, name):
     gy = _host_bits(Y)
     assert np.array_equal(gy, _host_bits(Y2)), "two runs differ"
     assert np.all(np.isfinite(synth.bf16_bits_to_f32(gy)))
-    rng = np.random.default_rng(2024)
-    rows = np.unique(np.concatenate([[0, M - 1], zero_rows, rng.choice(M, size=min(M, 24), replace=False)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=192, replace=False)]))
-    oq_x, osx, orx = oracle.prepare_rows(inp["x"][rows], g, want_rotated=True)
-    oq_w, osw, orw = oracle.prepare_rows(inp["w"][cols], g, want_rotated=True)
-    # scales and codes
-    assert np.array_equal(sw.cpu().numpy()[cols], osw)
+    og = _oracle_g(g)
+    oq_w, osw = oracle.prepare_weight(inp["w"], og)
+    y_or, parts = oracle.linear(inp["x"], oq_w, osw, inp["bias"], og, want_parts=True)
+    assert np.array_equal(sw.cpu().numpy(), osw), "weight scales"
     wsh = ws.cpu().numpy()
-    gq_x = gpu.workspace_act_codes(wsh, M, K)[rows]
-    n_x = compare_codes(gq_x, oq_x, orx, osx, "activation codes")
+    gq_x = gpu.workspace_act_codes(wsh, M, K)
+    n_x = compare_codes(gq_x, parts["qx"], oracle.rotate_rows(inp["x"], og), parts["sx"], "activation codes")
+    if M > 32 and gpu.convrot_linear_plan(M, K, N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
+        assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(wsh, M, K), gq_x)
     qw_all = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     assert qw_all.min() >= -7 and qw_all.max() <= 7
     assert np.all(np.abs(qw_all).max(axis=1) == 7)
-    n_w = compare_codes(qw_all[cols], oq_w, orw, osw, "weight codes")
-    y_or = oracle.epilogue(oracle.gemm_i32(oq_x, oq_w), osx, osw, inp["bias"][cols])
-    rows_ok = np.all(gq_x == oq_x, axis=1) & (n_w == 0)
-    compare_y(gy[np.ix_(rows, cols)], y_or, rows_ok)
+    n_w = compare_codes(qw_all, oq_w, oracle.rotate_rows(inp["w"], og), osw, "weight codes")
+    rows_ok = np.all(gq_x == parts["qx"], axis=1) & (n_w == 0)
+    n_y = compare_y(gy, y_or, rows_ok)
     if zero_rows.size:
-        assert np.all(osx[np.searchsorted(rows, zero_rows)] == 0)
-        assert np.all(gq_x[np.searchsorted(rows, zero_rows)] == 0)
+        assert np.all(parts["sx"][zero_rows] == 0)
+        assert np.all(gq_x[zero_rows] == 0)
         assert np.all(gy[zero_rows] == inp["bias"][None, :]), "zero rows must give the bias"
-    print(f"{name}: code mismatches x={n_x} w={n_w}")
+    print(f"{name}: code mismatches x={n_x} w={n_w}, Y differences {n_y} of {gy.size}")
 
 
 # --------------------------------------------------------------------------

@@ -26,6 +26,15 @@ CONVROT_EHIP = 3
 CONVROT_EDEVICE = 4
 # OR'd into a group size g: rotate with the regular Hadamard matrix
 CONVROT_REGULAR_HADAMARD = 0x10000
+# OR'd into a group size g: the weight image holds the INT4 codes only (0.5 bytes
+# per weight); every product then runs on the INT8 matrix cores
+CONVROT_INT4_IMAGE = 0x20000
+_GROUP_FLAGS = CONVROT_REGULAR_HADAMARD | CONVROT_INT4_IMAGE
+# workspace status word: offset, and the value a split-K wait that ran out leaves
+WORKSPACE_STATUS_OFFSET = 2048
+CONVROT_STATUS_SPLIT_TIMEOUT = 1
+# test flag of convrot_gemm_i32_tiled
+CONVROT_TEST_SPLIT_TIMEOUT = 1
 MAX_K = 16384           # largest rotated width K_rot
 MAX_ROWS = 16777216     # largest M or N
 
@@ -33,7 +42,7 @@ MAX_ROWS = 16777216     # largest M or N
 def rotated_width(K: int, g: int) -> int:
     """Codes and rotated values are K rounded up to a whole number of groups wide
     (the missing values of the last group are zero)."""
-    gs = g & ~CONVROT_REGULAR_HADAMARD
+    gs = g & ~_GROUP_FLAGS
     return -(-K // gs) * gs
 
 _lock = threading.Lock()
@@ -63,15 +72,19 @@ _SIGNATURES = {
     "convrot_validate_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_prepare_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_quantize_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
-    "convrot_repack_nk_to_image": ([_P, _I64, _I64, _P, _P], _I),
+    "convrot_repack_nk_to_image": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ, _P], _I),
     "convrot_prepare_activations": ([_P, _I64, _I64, _I, _P, _SZ, _P], _I),
-    "convrot_gemm": ([_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P], _I),
+    "convrot_gemm": ([_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P], _I),
     "convrot_prepare_rows": ([_P, _I64, _I64, _I, _P, _P, _P, _P], _I),
     "convrot_w4a16_workspace_bytes": ([_I64, _I64, _I, _P], _I),
     "convrot_validate_linear_w4a16": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ], _I),
     "convrot_linear_w4a16": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ, _P], _I),
     "convrot_gemm_i32": ([_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P], _I),
+    "convrot_workspace_bytes_tiled": ([_I64, _I64, _I64, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+    "convrot_gemm_i32_tiled": ([_P, _I64, _I64, _P, _I64, _P, _I, _I, _I, _I, _P, _SZ, _P], _I),
+    "convrot_split_k_extent": ([_I64, _I64, _I64, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_I),
+                                ctypes.POINTER(_SZ)], _I),
     "convrot_host_pack_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_unpack_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_nk_to_kn": ([_P, _I64, _I64, _P], _I),
@@ -215,10 +228,11 @@ def convrot_quantize_weight(W, g: int, stream=None):
     return nk, sw
 
 
-def convrot_repack_nk_to_image(nk, N: int, K: int, stream=None):
+def convrot_repack_nk_to_image(nk, N: int, K: int, g: int = 64, stream=None):
+    """N x packed-K uint8 [N, K_rot/2] -> weight image (the FP6 copy too unless g has CONVROT_INT4_IMAGE)."""
     import torch
-    image = torch.empty(convrot_weight_image_bytes(N, K, 64), dtype=torch.uint8, device=nk.device)
-    _call("convrot_repack_nk_to_image", _dev(nk, torch.uint8, "nk"), N, K, _dev(image, torch.uint8, "image"),
+    image = torch.empty(convrot_weight_image_bytes(N, K, g), dtype=torch.uint8, device=nk.device)
+    _call("convrot_repack_nk_to_image", _dev(nk, torch.uint8, "nk"), N, K, g, _dev(image, torch.uint8, "image"),
           _stream(stream))
     return image
 
@@ -251,13 +265,14 @@ def convrot_prepare_activations(X, g: int, workspace, stream=None):
     return workspace
 
 
-def convrot_gemm(workspace, M: int, K: int, image, sw, bias, N: int, Y=None, stream=None):
+def convrot_gemm(workspace, M: int, K: int, image, sw, bias, N: int, g: int, Y=None, stream=None):
+    """The GEMM half of convrot_linear (M, K, N, g as for the linear) on a prepared workspace."""
     import torch
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=workspace.device)
     bias_p = None if bias is None else _dev(bias, torch.bfloat16, "bias")
     _call("convrot_gemm", _dev(workspace, torch.uint8, "workspace"), workspace.numel(), M, K,
-          _dev(image, torch.uint8, "image"), _dev(sw, torch.float32, "sw"), bias_p, N,
+          _dev(image, torch.uint8, "image"), _dev(sw, torch.float32, "sw"), bias_p, N, g,
           _dev(Y, torch.bfloat16, "Y"), _stream(stream))
     return Y
 
@@ -288,6 +303,42 @@ def convrot_gemm_i32(qx, image, N: int, workspace=None, stream=None):
           _dev(acc, torch.int32, "acc"), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
           _stream(stream))
     return acc
+
+
+def convrot_workspace_bytes_tiled(M: int, K: int, N: int, tile, splits: int) -> int:
+    out = _SZ(0)
+    _call("convrot_workspace_bytes_tiled", M, K, N, tile[0], tile[1], splits, ctypes.byref(out))
+    return out.value
+
+
+def convrot_gemm_i32_tiled(qx, image, N: int, tile, splits: int, test_flags: int = 0, workspace=None, stream=None):
+    """convrot_gemm_i32 with the block tile (tile_m, tile_n) and the K split given.
+    Returns (acc int32 [M, N], workspace)."""
+    import torch
+    M, K = qx.shape
+    if workspace is None:
+        workspace = torch.empty(convrot_workspace_bytes_tiled(M, K, N, tile, splits), dtype=torch.uint8,
+                                device=qx.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=qx.device)
+    _call("convrot_gemm_i32_tiled", _dev(qx, torch.int8, "qx"), M, K, _dev(image, torch.uint8, "image"), N,
+          _dev(acc, torch.int32, "acc"), tile[0], tile[1], splits, test_flags,
+          _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return acc, workspace
+
+
+def convrot_split_k_extent(M: int, K: int, N: int, tile, splits: int) -> dict:
+    """Host check of a split-K plan's footprint: one past the largest partial-area
+    byte, counter word and LDS byte the exchange touches."""
+    pe, cu, le = _SZ(0), _I(0), _SZ(0)
+    _call("convrot_split_k_extent", M, K, N, tile[0], tile[1], splits, ctypes.byref(pe), ctypes.byref(cu),
+          ctypes.byref(le))
+    return {"partial_end": pe.value, "counters_used": cu.value, "lds_end": le.value}
+
+
+def workspace_status(workspace) -> int:
+    """The workspace's status word after a completed call (0, or CONVROT_STATUS_SPLIT_TIMEOUT)."""
+    import torch
+    return int(workspace[WORKSPACE_STATUS_OFFSET:WORKSPACE_STATUS_OFFSET + 4].view(torch.int32).item())
 
 
 # --------------------------------------------------------------------------
@@ -365,7 +416,7 @@ def convrot_host_workspace_fp6_codes(workspace, M: int, K: int) -> np.ndarray:
 
 # Offset of the activation-code image inside a workspace
 # (CONVROT_WORKSPACE_IMAGE_OFFSET in include/convrot.h).
-WORKSPACE_IMAGE_OFFSET = 2048
+WORKSPACE_IMAGE_OFFSET = 4096
 
 
 def workspace_act_codes(workspace, M: int, K: int) -> np.ndarray:

@@ -50,10 +50,12 @@ int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
 }
 
 // want_fp6: also write the FP6 copy of the codes (when the GEMM that follows
-// is unknown, or its plan reads that copy)
+// is unknown, or its plan reads that copy); fp6 = image_has_fp6(g): the
+// workspace has room for it.  Clears the split-K counters and the status word.
 int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, bool want_fp6, hipStream_t s)
 {
     const int64_t Kr = rotated_width(K, g);
+    const bool fp6 = image_has_fp6(g);
     PrepArgs a{};
     a.X = (const uint16_t*)X;
     a.ld = K;
@@ -62,24 +64,26 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)ws + workspace_image_offset();
-    a.out6 = act_has_fp6(M) && want_fp6 ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
-    a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
+    a.out6 = act_has_fp6(M, fp6) && want_fp6 ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
+    a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr, fp6));
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
-    a.zero_count = 2 * kSplitCounters;
+    a.zero_count = kZeroWords;
     launch_prep(g, OUT_IMAGE, a, s);
     return launched();
 }
 
+// K: the code width.  fp6: the workspace layout has the FP6 activation part
+// (and the weight image its FP6 copy).
 GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
-                   int64_t N, void* Y)
+                   int64_t N, void* Y, bool fp6, const GemmPlan& plan)
 {
     GemmArgs a{};
     a.act = (const uint8_t*)ws + workspace_image_offset();
     a.wgt = (const uint8_t*)image;
     a.act6 = (const uint8_t*)ws + workspace_image6_offset(M, K);
     a.wgt6 = (const uint8_t*)image + weight_image6_offset(N, K);
-    a.sx = (const float*)((const uint8_t*)ws + workspace_sx_offset(M, K));
+    a.sx = (const float*)((const uint8_t*)ws + workspace_sx_offset(M, K, fp6));
     a.sw = sw;
     a.bias = (const uint16_t*)bias;
     a.out = Y;
@@ -89,20 +93,36 @@ GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, cons
     a.MT = (int)(round_up(M, kTileRows) / kTileRows);
     a.NT = (int)(round_up(N, kTileRows) / kTileRows);
     a.KB = (int)(round_up(K, kTileK) / kTileK);
-    const GemmPlan plan = gemm_plan(M, N, K);
     a.shape = plan.shape;
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
     a.splits = plan.splits;
     a.counters = (uint32_t*)ws;
-    a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K));
+    a.partial = (int32_t*)((uint8_t*)ws + workspace_partial_offset(M, K, fp6));
+    a.status = (uint32_t*)((uint8_t*)ws + CONVROT_WORKSPACE_STATUS_OFFSET);
+    a.spin_limit = kSplitSpinLimit;
+    a.extra_wait = 0;
     return a;
 }
 
-int enqueue_gemm(int out_mode, const void* ws, int64_t M, int64_t K, const void* image, const float* sw,
-                 const void* bias, int64_t N, void* Y, hipStream_t s)
+GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
+                   int64_t N, void* Y, bool fp6)
 {
-    launch_gemm(out_mode, gemm_args(ws, M, K, image, sw, bias, N, Y), s);
+    return gemm_args(ws, M, K, image, sw, bias, N, Y, fp6, gemm_plan(M, N, K, fp6));
+}
+
+int enqueue_gemm(int out_mode, const GemmArgs& a, hipStream_t s)
+{
+    launch_gemm(out_mode, a, s);
+    return launched();
+}
+
+// int8 codes [M][K] into the workspace's activation images (the FP6 one when
+// fp6), clearing the counters and the status word
+int enqueue_act_relayout(const int8_t* qx, int64_t M, int64_t K, void* ws, bool fp6, hipStream_t s)
+{
+    uint8_t* image6 = act_has_fp6(M, fp6) ? (uint8_t*)ws + workspace_image6_offset(M, K) : nullptr;
+    launch_act_relayout(qx, M, K, (uint8_t*)ws + workspace_image_offset(), image6, (uint32_t*)ws, kZeroWords, s);
     return launched();
 }
 
@@ -124,7 +144,7 @@ int convrot_prepare_weight(const void* W, int64_t N, int64_t K, int g, void* ima
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
     a.out = (uint8_t*)image;
-    a.out6 = (uint8_t*)image + weight_image6_offset(N, Kr);
+    a.out6 = image_has_fp6(g) ? (uint8_t*)image + weight_image6_offset(N, Kr) : nullptr;
     a.scales = sw;
     launch_prep(g, OUT_IMAGE, a, as_stream(stream));
     return launched();
@@ -149,15 +169,16 @@ int convrot_quantize_weight(const void* W, int64_t N, int64_t K, int g, uint8_t*
     return launched();
 }
 
-int convrot_repack_nk_to_image(const uint8_t* qweight_nk, int64_t N, int64_t K, void* image, void* stream)
+int convrot_repack_nk_to_image(const uint8_t* qweight_nk, int64_t N, int64_t K, int g, void* image, void* stream)
 {
-    int rc = check_shape(N, K, 64);
+    int rc = check_shape(N, K, g);
     if (rc) return rc;
     if (N == 0) return CONVROT_OK;
     if (!qweight_nk || !image || !aligned(qweight_nk, 16) || !aligned(image, 16)) return CONVROT_EINVAL;
     if ((rc = check_device())) return rc;
-    launch_repack_nk(qweight_nk, N, K, (uint8_t*)image, (uint8_t*)image + weight_image6_offset(N, K),
-                     as_stream(stream));
+    const int64_t Kr = rotated_width(K, g);
+    launch_repack_nk(qweight_nk, N, Kr, (uint8_t*)image,
+                     image_has_fp6(g) ? (uint8_t*)image + weight_image6_offset(N, Kr) : nullptr, as_stream(stream));
     return launched();
 }
 
@@ -167,20 +188,22 @@ int convrot_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     int rc = validate_rows_out(X, M, K, g);
     if (rc || M == 0) return rc;
     if (!ws || !aligned(ws, 16)) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_partial_offset(M, rotated_width(K, g))) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_partial_offset(M, rotated_width(K, g), image_has_fp6(g))) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     // the GEMM that will consume the workspace is not known: both copies
     return enqueue_prepare_activations(X, M, K, g, ws, true, as_stream(stream));
 }
 
 int convrot_gemm(const void* ws, size_t ws_bytes, int64_t M, int64_t K, const void* image, const float* sw,
-                 const void* bias, int64_t N, void* Y, void* stream)
+                 const void* bias, int64_t N, int g, void* Y, void* stream)
 {
     // same checks as the linear, with the workspace standing in for X
-    int rc = convrot_validate_linear(ws, M, K, image, sw, bias, N, 64, Y, ws, ws_bytes);
+    int rc = convrot_validate_linear(ws, M, K, image, sw, bias, N, g, Y, ws, ws_bytes);
     if (rc || M == 0 || N == 0) return rc;
     if ((rc = check_device())) return rc;
-    return enqueue_gemm(GEMM_OUT_BF16, ws, M, K, image, sw, bias, N, Y, as_stream(stream));
+    const int64_t Kr = rotated_width(K, g);
+    return enqueue_gemm(GEMM_OUT_BF16, gemm_args(ws, M, Kr, image, sw, bias, N, Y, image_has_fp6(g)),
+                        as_stream(stream));
 }
 
 int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
@@ -191,9 +214,10 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
     const int64_t Kr = rotated_width(K, g);
+    const bool fp6 = image_has_fp6(g);
     if (single_kernel_linear(M, Kr, g)) {
         // one kernel: each workgroup quantizes the few activation rows itself
-        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
+        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y, fp6);
         PrepArgs pa{};
         pa.X = (const uint16_t*)X;
         pa.ld = K;
@@ -201,13 +225,13 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
         pa.K = Kr;
         pa.K_pad = round_up(Kr, kTileK);
         pa.out = (uint8_t*)ws + workspace_image_offset();
-        pa.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr));
+        pa.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr, fp6));
         launch_small_m(g, ga, pa, s);
         return launched();
     }
-    const bool fp6 = gemm_shape_fp6(gemm_plan(M, N, Kr).shape);
-    if ((rc = enqueue_prepare_activations(X, M, K, g, ws, fp6, s))) return rc;
-    return enqueue_gemm(GEMM_OUT_BF16, ws, M, Kr, image, sw, bias, N, Y, s);
+    const GemmPlan plan = gemm_plan(M, N, Kr, fp6);
+    if ((rc = enqueue_prepare_activations(X, M, K, g, ws, gemm_shape_fp6(plan.shape), s))) return rc;
+    return enqueue_gemm(GEMM_OUT_BF16, gemm_args(ws, M, Kr, image, sw, bias, N, Y, fp6, plan), s);
 }
 
 int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
@@ -220,7 +244,7 @@ int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image,
     const int64_t Kr = rotated_width(K, g);
     if (single_kernel_linear(M, Kr, g)) {
         // one kernel: each workgroup rotates the few activation rows itself
-        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
+        GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y, false);
         PrepArgs pa{};
         pa.X = (const uint16_t*)X;
         pa.ld = K;
@@ -243,7 +267,7 @@ int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image,
     launch_prep(g, OUT_ROTATED_BF16, a, s);
     if ((rc = launched())) return rc;
     // 2. their product with the weight image, scale and bias
-    GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y);
+    GemmArgs ga = gemm_args(ws, M, Kr, image, sw, bias, N, Y, false);
     launch_w4a16(ga, (const uint16_t*)ws, s);
     return launched();
 }
@@ -269,8 +293,8 @@ int convrot_prepare_rows(const void* X, int64_t rows, int64_t K, int g, int8_t* 
     return launched();
 }
 
-int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, int64_t N, int32_t* acc, void* ws,
-                     size_t ws_bytes, void* stream)
+static int check_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, int64_t N, const int32_t* acc,
+                          const void* ws)
 {
     int rc = check_shape(M, K, 64);
     if (rc) return rc;
@@ -278,14 +302,41 @@ int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, 
     if (M == 0 || N == 0) return CONVROT_OK;
     if (!qx || !image || !acc || !ws) return CONVROT_EINVAL;
     if (!aligned(qx, 16) || !aligned(image, 16) || !aligned(acc, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, K, N)) return CONVROT_EWORKSPACE;
+    return CONVROT_OK;
+}
+
+int convrot_gemm_i32(const int8_t* qx, int64_t M, int64_t K, const void* image, int64_t N, int32_t* acc, void* ws,
+                     size_t ws_bytes, void* stream)
+{
+    int rc = check_gemm_i32(qx, M, K, image, N, acc, ws);
+    if (rc || M == 0 || N == 0) return rc;
+    if (ws_bytes < workspace_bytes(M, K, N, true)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = as_stream(stream);
-    uint8_t* image6 = act_has_fp6(M) ? (uint8_t*)ws + workspace_image6_offset(M, K) : nullptr;
-    launch_act_relayout(qx, M, K, (uint8_t*)ws + workspace_image_offset(), image6, (uint32_t*)ws,
-                        2 * kSplitCounters, s);
-    if ((rc = launched())) return rc;
-    return enqueue_gemm(GEMM_OUT_I32, ws, M, K, image, nullptr, nullptr, N, acc, s);
+    if ((rc = enqueue_act_relayout(qx, M, K, ws, true, s))) return rc;
+    return enqueue_gemm(GEMM_OUT_I32, gemm_args(ws, M, K, image, nullptr, nullptr, N, acc, true), s);
+}
+
+int convrot_gemm_i32_tiled(const int8_t* qx, int64_t M, int64_t K, const void* image, int64_t N, int32_t* acc,
+                           int tile_m, int tile_n, int splits, int test_flags, void* ws, size_t ws_bytes,
+                           void* stream)
+{
+    int rc = check_gemm_i32(qx, M, K, image, N, acc, ws);
+    if (rc || M == 0 || N == 0) return rc;
+    if (test_flags & ~CONVROT_TEST_SPLIT_TIMEOUT) return CONVROT_EINVAL;
+    GemmPlan plan;
+    const bool fp6 = gemm_shape_of(tile_m, tile_n) == 2;
+    if ((rc = check_forced_plan(M, K, N, tile_m, tile_n, splits, fp6, &plan))) return rc;
+    if (ws_bytes < workspace_bytes_for(M, K, fp6, plan)) return CONVROT_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = as_stream(stream);
+    if ((rc = enqueue_act_relayout(qx, M, K, ws, fp6, s))) return rc;
+    GemmArgs a = gemm_args(ws, M, K, image, nullptr, nullptr, N, acc, fp6, plan);
+    if (test_flags & CONVROT_TEST_SPLIT_TIMEOUT) {
+        a.extra_wait = 1;  // one writer more than exist: every finalizer's wait runs out
+        a.spin_limit = 64;
+    }
+    return enqueue_gemm(GEMM_OUT_I32, a, s);
 }
 
 }  // extern "C"

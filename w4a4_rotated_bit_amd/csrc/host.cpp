@@ -10,6 +10,12 @@
 using namespace convrot;
 
 static_assert(CONVROT_REGULAR_HADAMARD == kRegularHadamard, "header and library agree on the rotation flag");
+static_assert(CONVROT_INT4_IMAGE == kInt4Image, "header and library agree on the image flag");
+static_assert(CONVROT_STATUS_SPLIT_TIMEOUT == (int)kStatusSplitTimeout, "header and library agree on the status");
+static_assert(CONVROT_WORKSPACE_STATUS_OFFSET == 4 * 2 * kSplitCounters, "status word right after the counters");
+static_assert(CONVROT_WORKSPACE_IMAGE_OFFSET >= CONVROT_WORKSPACE_STATUS_OFFSET + 4 &&
+                  CONVROT_WORKSPACE_IMAGE_OFFSET % 256 == 0,
+              "activation image after the status word");
 
 namespace convrot {
 
@@ -17,7 +23,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_shape(int64_t rows, int64_t K, int g)
 {
-    if ((g & ~kRegularHadamard) != 64 && (g & ~kRegularHadamard) != 256) return CONVROT_EINVAL;
+    if ((g & ~kGroupFlags) != 64 && (g & ~kGroupFlags) != 256) return CONVROT_EINVAL;
     // rows of X and W are 16-byte aligned runs of bf16; the rotated width
     // (K rounded up to g, the rest zero padding) is at most kMaxK
     if (K < 1 || K % 8 != 0 || rotated_width(K, g) > kMaxK) return CONVROT_EINVAL;
@@ -26,9 +32,10 @@ int check_shape(int64_t rows, int64_t K, int g)
 }
 
 // Workspace layout (each part 256-byte aligned): the split-K counters at
-// offset 0 -- the same place for every shape, so a workspace reused across
-// shapes keeps them cleared -- then the activation INT4 image, the activation
-// FP6 image (M > 32), sx, and the split-K partial tiles.
+// offset 0 and the status word after them -- the same place for every shape,
+// so a workspace reused across shapes keeps them cleared -- then the
+// activation INT4 image, the activation FP6 image (M > 32, FP6 images), sx,
+// and the split-K partial tiles.
 size_t workspace_image_offset() { return CONVROT_WORKSPACE_IMAGE_OFFSET; }
 
 size_t workspace_image6_offset(int64_t M, int64_t K)
@@ -36,20 +43,39 @@ size_t workspace_image6_offset(int64_t M, int64_t K)
     return (size_t)round_up((int64_t)(workspace_image_offset() + image_bytes(M, K)), 256);
 }
 
-size_t workspace_sx_offset(int64_t M, int64_t K)
+size_t workspace_sx_offset(int64_t M, int64_t K, bool fp6)
 {
-    const size_t fp6 = act_has_fp6(M) ? image6_bytes(M, K) : 0;
-    return (size_t)round_up((int64_t)(workspace_image6_offset(M, K) + fp6), 256);
+    const size_t part6 = act_has_fp6(M, fp6) ? image6_bytes(M, K) : 0;
+    return (size_t)round_up((int64_t)(workspace_image6_offset(M, K) + part6), 256);
 }
 
-size_t workspace_partial_offset(int64_t M, int64_t K)
+size_t workspace_partial_offset(int64_t M, int64_t K, bool fp6)
 {
-    return (size_t)round_up((int64_t)(workspace_sx_offset(M, K) + sizeof(float) * (size_t)round_up(M, kTileRows)), 256);
+    return (size_t)round_up((int64_t)(workspace_sx_offset(M, K, fp6) + sizeof(float) * (size_t)round_up(M, kTileRows)),
+                            256);
 }
 
-size_t workspace_bytes(int64_t M, int64_t K, int64_t N)
+size_t workspace_bytes_for(int64_t M, int64_t K, bool fp6, const GemmPlan& p)
 {
-    return workspace_partial_offset(M, K) + gemm_partial_bytes(M, N, K);
+    return workspace_partial_offset(M, K, fp6) + gemm_partial_bytes(p);
+}
+
+size_t workspace_bytes(int64_t M, int64_t K, int64_t N, bool fp6)
+{
+    return workspace_bytes_for(M, K, fp6, gemm_plan(M, N, K, fp6));
+}
+
+int check_forced_plan(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits, bool fp6, GemmPlan* plan)
+{
+    const int shape = gemm_shape_of(tile_m, tile_n);
+    if (shape < 0 || M <= 32 || N < 1 || K < 1) return CONVROT_EINVAL;
+    if (gemm_shape_fp6(shape) && !fp6) return CONVROT_EINVAL;
+    const int64_t KB = round_up(K, kTileK) / kTileK;
+    if (splits < 1 || splits > kMaxSplits || splits > KB) return CONVROT_EINVAL;
+    const GemmPlan p = gemm_plan_forced(M, N, shape, splits);
+    if (splits > 1 && (int64_t)p.tiles_m * p.tiles_n > kSplitCounters) return CONVROT_EINVAL;
+    *plan = p;
+    return CONVROT_OK;
 }
 
 }  // namespace convrot
@@ -68,14 +94,14 @@ const char* convrot_status_string(int status)
     }
 }
 
-const char* convrot_version(void) { return "convrot-gfx950 1.0"; }
+const char* convrot_version(void) { return "convrot-gfx950 1.1"; }
 
 int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes)
 {
     if (!bytes) return CONVROT_EINVAL;
     int rc = check_shape(N, K, g);
     if (rc) return rc;
-    *bytes = weight_image_bytes(N, rotated_width(K, g));
+    *bytes = weight_image_bytes(N, rotated_width(K, g), image_has_fp6(g));
     return CONVROT_OK;
 }
 
@@ -85,7 +111,64 @@ int convrot_workspace_bytes(int64_t M, int64_t K, int64_t N, int g, size_t* byte
     int rc = check_shape(M, K, g);
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
-    *bytes = workspace_bytes(M, rotated_width(K, g), N);
+    *bytes = workspace_bytes(M, rotated_width(K, g), N, image_has_fp6(g));
+    return CONVROT_OK;
+}
+
+int convrot_workspace_bytes_tiled(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits, size_t* bytes)
+{
+    if (!bytes) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, 64);
+    if (rc) return rc;
+    if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
+    GemmPlan p;
+    const bool fp6 = gemm_shape_of(tile_m, tile_n) == 2;
+    if ((rc = check_forced_plan(M, K, N, tile_m, tile_n, splits, fp6, &p))) return rc;
+    *bytes = workspace_bytes_for(M, K, fp6, p);
+    return CONVROT_OK;
+}
+
+int convrot_split_k_extent(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits, size_t* partial_end,
+                           int* counters_used, size_t* lds_end)
+{
+    if (!partial_end || !counters_used || !lds_end) return CONVROT_EINVAL;
+    int rc = check_shape(M, K, 64);
+    if (rc) return rc;
+    GemmPlan p;
+    if ((rc = check_forced_plan(M, K, N, tile_m, tile_n, splits, true, &p))) return rc;
+    const int shape = p.shape;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int threads = gemm_threads(shape), words = split_words_per_thread(shape);
+    const int chunks = (int)(split_slot_bytes(shape) / 2 / 1024);  // 1 KB copies per half slot
+    size_t pend = 0, lend = 0;
+    int cmax = -1;
+    if (splits > 1) {
+        // every address the exchange touches, through the kernels' own geometry
+        for (int tile = 0; tile < tiles; ++tile) {
+            cmax = tile + kSplitCounters > cmax ? tile + kSplitCounters : cmax;  // tickets[tile], finished[tile]
+            for (int ticket = 0; ticket < splits - 1; ++ticket)
+                for (int u = 0; u < words; ++u)
+                    for (int t = 0; t < threads; ++t) {
+                        const size_t end = split_store_offset(shape, tile, splits, ticket, u, t) + 8;
+                        pend = end > pend ? end : pend;
+                    }
+            for (int sl = 0; sl < splits - 1; ++sl)
+                for (int half = 0; half < 2; ++half)
+                    for (int c = 0; c < chunks; ++c)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const size_t end = split_copy_offset(shape, tile, splits, sl, half, c, lane) + 16;
+                            pend = end > pend ? end : pend;
+                            const size_t lds = (size_t)c * 1024 + (size_t)lane * 16 + 16;  // LDS ring offset
+                            lend = lds > lend ? lds : lend;
+                        }
+        }
+        // the finalizer's reads of the ring: word u2 < words / 2 of thread t
+        const size_t reads = ((size_t)(words / 2 - 1) * threads + (threads - 1)) * 8 + 8;
+        lend = reads > lend ? reads : lend;
+    }
+    *partial_end = pend;
+    *counters_used = cmax + 1;
+    *lds_end = lend;
     return CONVROT_OK;
 }
 
@@ -112,7 +195,7 @@ int convrot_linear_plan(int64_t M, int64_t K, int64_t N, int g, int* kind, int* 
     // M <= 32 streams the weight through the INT8 16x16x64 MFMA
     *kind = CONVROT_MFMA_I8;
     if (M <= 32) return CONVROT_OK;
-    const GemmPlan p = gemm_plan(M, N, rotated_width(K, g));
+    const GemmPlan p = gemm_plan(M, N, rotated_width(K, g), image_has_fp6(g));
     if (gemm_shape_fp6(p.shape)) *kind = CONVROT_MFMA_FP6;
     *tile_m = gemm_tile_m(p.shape);
     *tile_n = gemm_tile_n(p.shape);
@@ -140,7 +223,7 @@ int convrot_validate_linear(const void* X, int64_t M, int64_t K, const void* ima
     if (!X || !image || !sw || !Y || !ws) return CONVROT_EINVAL;
     if (!aligned(X, 16) || !aligned(image, 16) || !aligned(Y, 16) || !aligned(ws, 16)) return CONVROT_EINVAL;
     if (!aligned(sw, 4) || (bias && !aligned(bias, 2))) return CONVROT_EINVAL;
-    if (ws_bytes < workspace_bytes(M, rotated_width(K, g), N)) return CONVROT_EWORKSPACE;
+    if (ws_bytes < workspace_bytes(M, rotated_width(K, g), N, image_has_fp6(g))) return CONVROT_EWORKSPACE;
     return CONVROT_OK;
 }
 
@@ -256,7 +339,7 @@ int convrot_host_nk_to_image(const uint8_t* nk, int64_t N, int64_t K, uint8_t* i
 {
     if (!nk || !image || N < 0 || K < 64 || K % 64 || K > kMaxK) return CONVROT_EINVAL;
     const int64_t K_pad = round_up(K, kTileK);
-    memset(image, 0, weight_image_bytes(N, K));
+    memset(image, 0, weight_image_bytes(N, K, true));
     uint8_t* image6 = image + weight_image6_offset(N, K);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; k += 8) {

@@ -40,9 +40,12 @@ struct GemmArgs {
     int splits;
     uint32_t* counters;  // 2 * kSplitCounters zeroed words (tickets, then finished writers)
     int32_t* partial;    // (splits - 1) partial tiles per tile (int32 or binary32 sums)
+    uint32_t* status;    // the workspace's status word (set on a split-K wait that ran out)
+    int spin_limit;      // sleeps a split-K finalizer waits at most
+    int extra_wait;      // test hook: writers the finalizer waits for beyond those that exist (normally 0)
 };
 
-// g: group size, optionally with kRegularHadamard (the rotation matrix)
+// g: group size, optionally with the flags of layout.h (kRegularHadamard: the rotation matrix)
 void launch_prep(int g, int mode, PrepArgs a, hipStream_t s);
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s);
 // W4A16 product for M <= 32: bf16 rotated activation rows xr [M][K] times the

@@ -581,8 +581,9 @@ struct GemmShape<1> {
     static constexpr int NW = 4, NWM = 2, BI = 3, BJ = 3;
 };
 constexpr int kStages = 4;
-template <int SHAPE>
-struct GemmGeom : GemmShape<SHAPE> {
+template <int SHAPE_>
+struct GemmGeom : GemmShape<SHAPE_> {
+    static constexpr int SHAPE = SHAPE_;
     using S = GemmShape<SHAPE>;
     static constexpr int NWN = S::NW / S::NWM;          // waves along N
     static constexpr int BM = S::NWM * 32 * S::BI;      // block tile rows
@@ -593,8 +594,8 @@ struct GemmGeom : GemmShape<SHAPE> {
     static constexpr int kStage = (UA + UB) * kUnitBytes;
     static constexpr int COPIES = (2 * (UA + UB) + S::NW - 1) / S::NW;  // 1 KB copies per wave per stage
     static constexpr int kLdsBytes = kStages * kStage;
-    static constexpr bool kSplit = gemm_shape_splits(SHAPE);  // the plan may split K
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
+    static_assert(S::NW * 64 == gemm_threads(SHAPE) && kLdsBytes == gemm_ring_bytes(SHAPE), "host geometry agrees");
 };
 
 // Global -> LDS copy of 16 bytes per lane from base + voff (voff per lane):
@@ -755,9 +756,8 @@ __device__ inline void interleave_mfma_valu(int lds_reads)
 
 // ---------------------------------------------------------------------------
 // Split-K exchange.  Every workgroup of a split tile takes a ticket from the
-// tile's counter.  The first S - 1 ticket holders store their int32 partial
-// tile (one slot per ticket: 8-byte word u of thread t at (u * threads + t) *
-// 8, so each store instruction covers 512 contiguous bytes) with
+// tile's counter.  The first S - 1 ticket holders store their partial tile
+// (4-byte sums) into the slots laid out by split_store_offset (layout.h) with
 // device-coherent stores, wait until the stores have completed, and count
 // themselves finished.  The last ticket holder waits until S - 1 writers have
 // finished -- each of them already holds a ticket, so it is running and
@@ -765,6 +765,13 @@ __device__ inline void interleave_mfma_valu(int lds_reads)
 // half with device-coherent global -> LDS copies (all in flight at once), adds
 // it to its own tile (exact integer sums, any order) and goes on to the
 // epilogue; it also returns both counters to zero for the next launch.
+// The wait is bounded (a.spin_limit sleeps).  If it runs out, the finalizer
+// sets the workspace's status word to kStatusSplitTimeout, adds no slot (their
+// contents are not known to be written), leaves the counters as they are
+// (the next activation step clears them and the status word), and still runs
+// the epilogue, so the kernel ends normally and the caller can see the
+// failure.  a.extra_wait makes the finalizer wait for that many writers more
+// than exist (a test of this path: the wait then always runs out).
 // Device-coherent (agent-scope, sc1) accesses go to the level of the memory
 // system that every compute unit sees, so no cache-wide write-back or
 // invalidation is needed.  Returns true for the workgroup that finishes the
@@ -806,22 +813,23 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
                                         const uint8_t* smem, ACC (&acc)[G::BJ][G::BI])
 {
     constexpr int BI = G::BI, BJ = G::BJ;
+    constexpr int SHAPE = G::SHAPE;
     constexpr int kThreads = G::NW * 64;
     constexpr int kWords = BJ * BI * 8;                // 8-byte words per thread
-    constexpr int kSlotBytes = kThreads * kWords * 8;  // BM x BN int32
-    constexpr int kHalf = kSlotBytes / 2;              // fits the stage ring
+    constexpr int kHalf = (int)split_slot_bytes(SHAPE) / 2;
+    static_assert(kThreads == gemm_threads(SHAPE) && kWords == split_words_per_thread(SHAPE),
+                  "slot geometry of layout.h");
     static_assert(kHalf <= G::kLdsBytes, "half a partial tile must fit in LDS");
-    static_assert(kSlotBytes == G::BM * G::BN * 4, "slot = one tile of 4-byte sums");
     __shared__ int ticket_sh;
+    __shared__ int done_sh;
     uint32_t* tickets = a.counters + tile;
     uint32_t* finished = a.counters + kSplitCounters + tile;
     if (tid == 0) ticket_sh = (int)__hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // also: every wave is done with the stage ring
     const int ticket = ticket_sh;
     const int S = a.splits;
-    uint8_t* slots = (uint8_t*)a.partial + (size_t)tile * (S - 1) * kSlotBytes;
+    uint8_t* part = (uint8_t*)a.partial;
     if (ticket < S - 1) {
-        uint64_t* dst = (uint64_t*)(slots + (size_t)ticket * kSlotBytes);
 #pragma unroll
         for (int j = 0; j < BJ; ++j)
 #pragma unroll
@@ -831,7 +839,8 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
                     const int u = (j * BI + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
                     const uint64_t v = (uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q) |
                                        ((uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q + 1) << 32);
-                    __hip_atomic_store(dst + (size_t)u * kThreads + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store((uint64_t*)(part + split_store_offset(SHAPE, tile, S, ticket, u, tid)), v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
         __builtin_amdgcn_s_waitcnt(0);  // every store of this wave has completed
         __syncthreads();
@@ -840,24 +849,34 @@ __device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, in
     }
     if (tid == 0) {
         // bounded: the writers are running and never wait
-        for (int spin = 0; spin < (1 << 26); ++spin) {
-            if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(S - 1)) break;
+        const uint32_t need = (uint32_t)(S - 1 + a.extra_wait);
+        int done = 0;
+        for (int spin = 0; spin < a.spin_limit; ++spin) {
+            if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) {
+                done = 1;
+                break;
+            }
             __builtin_amdgcn_s_sleep(2);
         }
-        __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done) {
+            __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            __hip_atomic_store(a.status, kStatusSplitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        done_sh = done;
     }
     __syncthreads();
+    if (!done_sh) return true;  // flagged in the status word; the epilogue still runs
     constexpr int kChunksPerWave = kHalf / 1024 / G::NW;  // 1 KB per copy instruction
     static_assert(kChunksPerWave * 1024 * G::NW == kHalf, "copies divide evenly over the waves");
     for (int sl = 0; sl < S - 1; ++sl) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const uint8_t* src = slots + (size_t)sl * kSlotBytes + half * kHalf;
 #pragma unroll
             for (int c = 0; c < kChunksPerWave; ++c) {
                 const int chunk = wave * kChunksPerWave + c;
-                lds_copy16_coherent(src + chunk * 1024 + lane * 16, lds0 + chunk * 1024);
+                lds_copy16_coherent(part + split_copy_offset(SHAPE, tile, S, sl, half, chunk, lane), lds0 + chunk * 1024);
             }
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
@@ -1045,7 +1064,10 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
     }
 }
 
-template <int OUT, int SHAPE>
+// SPLIT: the instance that takes part in a split-K exchange (launched only
+// when a.splits > 1); the other instance has no exchange code at all, which
+// keeps its registers free of spills.
+template <int OUT, int SHAPE, bool SPLIT>
 __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(GemmArgs a)
 {
     using G = GemmGeom<SHAPE>;
@@ -1162,8 +1184,8 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if constexpr (G::kSplit)
-        if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if constexpr (SPLIT)
+        if (!split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
     gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
@@ -1200,8 +1222,8 @@ struct Gemm6Geom {
     static constexpr int UPW = (UA + UB) / NW;          // units copied per wave per stage
     static constexpr int COPIES = 3 * UPW;              // 1 KB copies per wave per stage
     static_assert(UPW * NW == UA + UB && UA % UPW == 0, "a wave copies whole units of one operand");
-    static constexpr bool kSplit = gemm_shape_splits(SHAPE);  // the plan may split K
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
+    static_assert(NW * 64 == gemm_threads(SHAPE) && kLdsBytes == gemm_ring_bytes(SHAPE), "host geometry agrees");
 };
 // Shape 2: eight waves, two per SIMD, each owning 128 x 64.  (Four waves of
 // 128 x 128 read a third fewer LDS bytes per MFMA, but with one wave per SIMD
@@ -1234,7 +1256,7 @@ __device__ inline void wait6_and_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(IN_FLIGHT * COPIES) : "memory");
 }
 
-template <int OUT, typename G>
+template <int OUT, typename G, bool SPLIT>
 __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
 {
     constexpr int BI = G::BI, BJ = G::BJ;
@@ -1389,8 +1411,8 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
-    if constexpr (G::kSplit)
-        if (a.splits > 1 && !split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
+    if constexpr (SPLIT)
+        if (!split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
     gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
@@ -2120,7 +2142,7 @@ template <int MODE>
 static void launch_prep_mode(int g, const PrepArgs& a, hipStream_t s)
 {
     const bool reg = (g & kRegularHadamard) != 0;
-    g &= ~kRegularHadamard;
+    g = group_size(g);
     if (g == 256)
         reg ? launch_prep_g<256, MODE, true>(a, s) : launch_prep_g<256, MODE, false>(a, s);
     else
@@ -2135,6 +2157,26 @@ void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
         case OUT_ROTATED_BF16: launch_prep_mode<OUT_ROTATED_BF16>(g, a, s); break;
         default: launch_prep_mode<OUT_ROWMAJOR>(g, a, s); break;
     }
+}
+
+template <typename G, int OUT, bool SPLIT>
+static void launch_block_tile_kernel(dim3 grid, const GemmArgs& a, hipStream_t s)
+{
+    if constexpr (G::SHAPE == 2)
+        hipLaunchKernelGGL((gemm6_kernel<OUT, G, SPLIT>), grid, dim3(G::NW * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<OUT, G::SHAPE, SPLIT>), grid, dim3(G::NW * 64), 0, s, a);
+}
+
+template <typename G>
+static void launch_block_tile(int out_mode, bool split, dim3 grid, const GemmArgs& a, hipStream_t s)
+{
+    if (out_mode == GEMM_OUT_I32)
+        split ? launch_block_tile_kernel<G, GEMM_OUT_I32, true>(grid, a, s)
+              : launch_block_tile_kernel<G, GEMM_OUT_I32, false>(grid, a, s);
+    else
+        split ? launch_block_tile_kernel<G, GEMM_OUT_BF16, true>(grid, a, s)
+              : launch_block_tile_kernel<G, GEMM_OUT_BF16, false>(grid, a, s);
 }
 
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
@@ -2157,25 +2199,13 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     }
     if (a.splits < 1) a.splits = 1;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.splits));
-    if (a.shape == 2) {
-        const dim3 block(Gemm6W8::NW * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((gemm6_kernel<GEMM_OUT_I32, Gemm6W8>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm6_kernel<GEMM_OUT_BF16, Gemm6W8>), grid, block, 0, s, a);
-    } else if (a.shape == 0) {
-        const dim3 block(GemmShape<0>::NW * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 0>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 0>), grid, block, 0, s, a);
-    } else {
-        const dim3 block(GemmShape<1>::NW * 64);
-        if (out_mode == GEMM_OUT_I32)
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
-    }
+    const bool split = a.splits > 1;
+    if (a.shape == 2)
+        launch_block_tile<Gemm6W8>(out_mode, split, grid, a, s);
+    else if (a.shape == 0)
+        launch_block_tile<GemmGeom<0>>(out_mode, split, grid, a, s);
+    else
+        launch_block_tile<GemmGeom<1>>(out_mode, split, grid, a, s);
 }
 
 template <int G, bool REG>
@@ -2195,7 +2225,7 @@ void launch_small_m(int g, GemmArgs a, PrepArgs p, hipStream_t s)
     const int cus = device_cus();
     const int sw = (int)std::min<int64_t>(3, std::max<int64_t>(1, (strips + cus - 1) / cus));
     const bool reg = (g & kRegularHadamard) != 0;
-    g &= ~kRegularHadamard;
+    g = group_size(g);
     p.team = (int)(p.K_pad / (g == 256 ? 16 : 8));  // lanes per row (whole waves: 64 .. 256)
     p.rows_pad = kSmallRows;
     const dim3 grid((unsigned)((strips + sw - 1) / sw));
@@ -2221,7 +2251,7 @@ void launch_small_w4a16(int g, GemmArgs a, PrepArgs p, hipStream_t s)
     const int cus = device_cus();
     const int sw = (int)std::min<int64_t>(3, std::max<int64_t>(1, (strips + cus - 1) / cus));
     const bool reg = (g & kRegularHadamard) != 0;
-    g &= ~kRegularHadamard;
+    g = group_size(g);
     p.team = (int)(p.K_pad / (g == 256 ? 16 : 8));
     p.rows_pad = kSmallRows;
     const dim3 grid((unsigned)((strips + sw - 1) / sw));

@@ -120,25 +120,39 @@ CONVROT_HD inline uint32_t fp6_e2m3(int q)
     return (q < 0 ? 0x20u : 0u) | (enc << 1);
 }
 
+// ---- flags carried by the group-size argument -------------------------------
+// g is 64 or 256, optionally with these flags:
+//   kRegularHadamard: rotate with the regular Hadamard matrix instead of the
+//                     Sylvester one;
+//   kInt4Image:       the weight image holds the INT4 codes only (0.5 bytes per
+//                     weight), so every product runs on the INT8 matrix cores;
+//                     without it the image also holds the FP6 copy (1.25 bytes
+//                     per weight) that the FP6 block tile reads.
+constexpr int kRegularHadamard = 0x10000;
+constexpr int kInt4Image = 0x20000;
+constexpr int kGroupFlags = kRegularHadamard | kInt4Image;
+CONVROT_HD inline int group_size(int g) { return g & ~kGroupFlags; }
+CONVROT_HD inline bool image_has_fp6(int g) { return (g & kInt4Image) == 0; }
+
 // The weight image: the INT4 image of the N rows (read by the weight-streaming
-// kernels), then the FP6 image of the same codes (read by the FP6 GEMM).
-CONVROT_HD inline size_t weight_image_bytes(int64_t N, int64_t K) { return image_bytes(N, K) + image6_bytes(N, K); }
+// kernels and the INT8 block tiles), then, unless the image is INT4 only, the
+// FP6 image of the same codes (read by the FP6 block tile).
+CONVROT_HD inline size_t weight_image_bytes(int64_t N, int64_t K, bool fp6)
+{
+    return image_bytes(N, K) + (fp6 ? image6_bytes(N, K) : 0);
+}
 CONVROT_HD inline size_t weight_image6_offset(int64_t N, int64_t K) { return image_bytes(N, K); }
 
 // Activations get an FP6 image too when the product goes to the block-tile
-// GEMM (M > 32 rows).
-CONVROT_HD inline bool act_has_fp6(int64_t M) { return M > 32; }
+// GEMM (M > 32 rows) and the weight image has its FP6 copy.
+CONVROT_HD inline bool act_has_fp6(int64_t M, bool fp6) { return fp6 && M > 32; }
 
 // ---- rotation ---------------------------------------------------------------
-// The group-size argument g is 64 or 256, optionally with this flag: rotate
-// with the regular Hadamard matrix instead of the Sylvester one.
-constexpr int kRegularHadamard = 0x10000;
-
 // A row of K values is rotated as K rounded up to a whole number of groups,
 // the missing values being zero; codes, scales and the product use that width.
 CONVROT_HD inline int64_t rotated_width(int64_t K, int g)
 {
-    const int64_t gs = g & ~kRegularHadamard;
+    const int64_t gs = group_size(g);
     return (K + gs - 1) / gs * gs;
 }
 
@@ -172,21 +186,23 @@ CONVROT_HD inline size_t w16_word_offset(int64_t m, int64_t k, int64_t K)
 // run on the INT8 matrix cores from the INT4 image: shape 0 is 192 x 384,
 // shape 1 is 192 x 192.  Shape 2 is 256 x 256 on the FP6 matrix cores from
 // the FP6 image (twice the INT8 rate; bound by LDS bandwidth rather than by
-// the matrix cores), the fastest per output where its tiles fill the chip.
+// the matrix cores), the fastest per output where its tiles fill the chip;
+// it is not a candidate when the weight image is INT4 only.
 // When there are too few tiles to fill the chip, the 192 x 192 tile's K range
 // is split over S workgroups (the integer partial sums are exact in any
 // order): S is the largest value <= 8 with S * tiles <= kSplitTargetWGs and
-// >= 16 128-K blocks per split.  The other two shapes are never split (a
-// split of them at 216 and 256 workgroups is not validated on the hardware).  Of the shapes the plan takes the one with the smallest estimated
-// time: rounds of workgroups x 128-K blocks per workgroup x tile area at
-// gemm_shape_ns per 1024 outputs per block (measured on MI355X on the FLUX
-// shapes), one prologue +
-// epilogue (about 4 us) per round, and for a split the exchange of (S - 1)
-// 4-byte partial tiles per tile through memory (written and read back at
-// about 4 TB/s, plus 3 us).  M <= 32 goes to the weight-streaming kernels and
-// is never split.
+// >= 16 128-K blocks per split.  The plan never splits the other two shapes;
+// a plan given from outside (gemm_plan_forced, a test hook) may.  Of the
+// shapes the plan takes the one with the smallest estimated time: rounds of
+// workgroups x 128-K blocks per workgroup x tile area at gemm_shape_ns per
+// 1024 outputs per block (measured on MI355X on the FLUX shapes), one
+// prologue + epilogue (about 4 us) per round, and for a split the exchange of
+// (S - 1) 4-byte partial tiles per tile through memory (written and read back
+// at about 4 TB/s, plus 3 us).  M <= 32 goes to the weight-streaming kernels
+// and is never split.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
-constexpr int kSplitCounters = 256;    // counter slots (tiles of a split launch <= 128)
+constexpr int kSplitCounters = 256;    // counter slots: a split launch has at most this many tiles
+constexpr int kMaxSplits = 8;
 constexpr int kGemmShapes = 3;
 
 CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 2 ? 256 : 192; }
@@ -194,7 +210,21 @@ CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 384 : (sha
 CONVROT_HD constexpr bool gemm_shape_fp6(int shape) { return shape == 2; }
 // nanoseconds per 1024 outputs per 128-K block, by shape (MI355X, FLUX shapes)
 CONVROT_HD constexpr int gemm_shape_ns(int shape) { return shape == 0 ? 28 : (shape == 1 ? 30 : 19); }
+// the shapes whose K range the plan splits
 CONVROT_HD constexpr bool gemm_shape_splits(int shape) { return shape == 1; }
+// threads of a block-tile workgroup, and bytes of its LDS stage ring
+CONVROT_HD constexpr int gemm_threads(int shape) { return shape == 1 ? 256 : 512; }
+CONVROT_HD constexpr int gemm_ring_bytes(int shape)
+{
+    return shape == 2 ? 3 * (256 / 32 + 256 / 32) * kUnit6Bytes
+                      : 4 * (gemm_tile_m(shape) / 32 + gemm_tile_n(shape) / 32) * kUnitBytes;
+}
+// the block tile of (tile_m, tile_n), or -1
+CONVROT_HD constexpr int gemm_shape_of(int tile_m, int tile_n)
+{
+    return (tile_m == 192 && tile_n == 384) ? 0 : (tile_m == 192 && tile_n == 192) ? 1
+                                                 : (tile_m == 256 && tile_n == 256) ? 2 : -1;
+}
 
 struct GemmPlan {
     int shape;             // block tile shape (0 .. 2)
@@ -202,18 +232,26 @@ struct GemmPlan {
     int splits;            // workgroups per tile along K
 };
 
-CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
+CONVROT_HD inline GemmPlan gemm_plan_forced(int64_t M, int64_t N, int shape, int splits)
+{
+    const int64_t bm = gemm_tile_m(shape), bn = gemm_tile_n(shape);
+    return GemmPlan{shape, (int)((M + bm - 1) / bm), (int)((N + bn - 1) / bn), splits};
+}
+
+CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool fp6)
 {
     GemmPlan best{0, 1, 1, 1};
     if (M <= 32 || M <= 0 || N <= 0) return best;
     const int64_t KB = (K + kTileK - 1) / kTileK;
     int64_t best_ns = -1;
     for (int shape = 0; shape < kGemmShapes; ++shape) {
+        if (gemm_shape_fp6(shape) && !fp6) continue;
         const int64_t bm = gemm_tile_m(shape), bn = gemm_tile_n(shape);
         const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
         const int64_t tiles = tm * tn;
         int S = 1;
-        while (gemm_shape_splits(shape) && S < 8 && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16) ++S;
+        while (gemm_shape_splits(shape) && S < kMaxSplits && (S + 1) * tiles <= kSplitTargetWGs && KB / (S + 1) >= 16)
+            ++S;
         const int64_t rounds = (tiles * S + kSplitTargetWGs - 1) / kSplitTargetWGs;
         int64_t ns = rounds * ((KB + S - 1) / S) * (bm * bn / 1024) * gemm_shape_ns(shape) + rounds * 4000;
         if (S > 1) ns += tiles * (S - 1) * bm * bn * 8 / 4000 + 3000;
@@ -225,15 +263,41 @@ CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
     return best;
 }
 
-CONVROT_HD inline int gemm_splits(int64_t M, int64_t N, int64_t K) { return gemm_plan(M, N, K).splits; }
-
-// Bytes of split-K partial tiles: (S - 1) block tiles of 4-byte sums per tile.
-CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
+// ---- split-K exchange geometry -----------------------------------------------
+// The S - 1 first workgroups (tickets) of a split tile each store their partial
+// tile of 4-byte sums into a slot of the workspace's partial area; the last
+// one copies every slot back into its LDS ring, half a slot at a time, and
+// adds it.  Slot (tile, ticket) is slot number tile (S - 1) + ticket; inside
+// it, 8-byte word u of thread t sits at (u threads + t) 8, so that one store
+// instruction of a wave covers 512 contiguous bytes.  The kernels and the
+// host-side footprint check (convrot_split_k_extent) address it through
+// these functions only.
+CONVROT_HD constexpr size_t split_slot_bytes(int shape) { return (size_t)gemm_tile_m(shape) * gemm_tile_n(shape) * 4; }
+CONVROT_HD constexpr int split_words_per_thread(int shape)
 {
-    const GemmPlan p = gemm_plan(M, N, K);
+    return (int)(split_slot_bytes(shape) / 8 / gemm_threads(shape));
+}
+CONVROT_HD inline size_t split_store_offset(int shape, int tile, int splits, int ticket, int word, int thread)
+{
+    return ((size_t)tile * (splits - 1) + ticket) * split_slot_bytes(shape) +
+           ((size_t)word * gemm_threads(shape) + thread) * 8;
+}
+// 16-byte piece `lane` of 1 KB chunk `chunk` of half `half` of slot `slot`
+CONVROT_HD inline size_t split_copy_offset(int shape, int tile, int splits, int slot, int half, int chunk, int lane)
+{
+    return ((size_t)tile * (splits - 1) + slot) * split_slot_bytes(shape) + (size_t)half * (split_slot_bytes(shape) / 2) +
+           (size_t)chunk * 1024 + (size_t)lane * 16;
+}
+// The workspace's status word (at a fixed offset, cleared by every activation
+// step): kStatusSplitTimeout when a split-K finalizer stopped waiting.
+constexpr uint32_t kStatusSplitTimeout = 1;
+constexpr int kSplitSpinLimit = 1 << 26;  // sleeps of 128 clocks: seconds, far beyond any real wait
+
+// Bytes of split-K partial tiles of a plan: (S - 1) slots per tile.
+CONVROT_HD inline size_t gemm_partial_bytes(const GemmPlan& p)
+{
     if (p.splits <= 1) return 0;
-    return (size_t)p.tiles_m * p.tiles_n * (size_t)(p.splits - 1) * (size_t)gemm_tile_m(p.shape) *
-           gemm_tile_n(p.shape) * 4;
+    return (size_t)p.tiles_m * p.tiles_n * (size_t)(p.splits - 1) * split_slot_bytes(p.shape);
 }
 
 // ---- single-kernel linear ---------------------------------------------------
@@ -243,7 +307,7 @@ CONVROT_HD inline size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K)
 constexpr int kSmallRows = 4;
 CONVROT_HD inline bool single_kernel_linear(int64_t M, int64_t K, int g)
 {
-    const int64_t lanes = round_up(K, kTileK) / ((g & ~kRegularHadamard) == 256 ? 16 : 8);
+    const int64_t lanes = round_up(K, kTileK) / (group_size(g) == 256 ? 16 : 8);
     return M >= 1 && M <= kSmallRows && lanes >= 64 && lanes <= 256;
 }
 
