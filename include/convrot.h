@@ -210,6 +210,24 @@ int convrot_linear(const void* X_dev, int64_t M, int64_t K, const void* image_de
                    const void* bias_dev, int64_t N, int g, void* Y_dev, void* workspace_dev, size_t ws_bytes,
                    void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same
+ * linear as convrot_linear (same arguments and checks, same kernels, same
+ * result bit for bit) with no workspace argument.  Its workspace is a
+ * library-owned device array of CONVROT_NOALLOC_MAX_WORKSPACE bytes, one per
+ * GPU, held until the process ends; the call allocates nothing (no hipMalloc,
+ * no allocating library routine).  Shapes whose convrot_workspace_bytes(M, K,
+ * N, g) exceeds that size return CONVROT_EWORKSPACE (every FLUX-shaped linear
+ * fits).  All calls on one GPU share the array: calls that may overlap on one
+ * GPU (different streams, or different host threads without ordering) race
+ * and must be serialized by the caller.  The array keeps the last call's
+ * contents; the parts that must start at zero (split-K counters, status
+ * word) are cleared by a kernel of every call, so the call can be captured
+ * in a HIP graph.  CONVROT_EHIP if the array's address cannot be found. */
+#define CONVROT_NOALLOC_MAX_WORKSPACE (48u << 20)
+int convrot_linear_noalloc(const void* X_dev, int64_t M, int64_t K, const void* image_dev, const float* sw_dev,
+                           const void* bias_dev, int64_t N, int g, void* Y_dev, void* stream);
+
 /* ---- W4A16 variant (weight-only INT4) ------------------------------------ */
 /* The weight-bandwidth-bound regime, M <= 32 (convrot-mlx README, "What is
  * included": a W4A16 path beside W4A4).  The activation rows are rotated as

@@ -74,6 +74,7 @@ _SIGNATURES = {
     "convrot_quantize_weight": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_repack_nk_to_image": ([_P, _I64, _I64, _I, _P, _P], _I),
     "convrot_linear": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, _SZ, _P], _I),
+    "convrot_linear_noalloc": ([_P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P], _I),
     "convrot_prepare_activations": ([_P, _I64, _I64, _I, _P, _SZ, _P], _I),
     "convrot_gemm": ([_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P], _I),
     "convrot_prepare_rows": ([_P, _I64, _I64, _I, _P, _P, _P, _P], _I),
@@ -254,6 +255,21 @@ def convrot_linear(X, image, sw, bias, N: int, g: int, Y=None, workspace=None, s
     _call("convrot_linear", _dev(X, torch.bfloat16, "X"), M, K, _dev(image, torch.uint8, "image"),
           _dev(sw, torch.float32, "sw"), bias_p, N, g, _dev(Y, torch.bfloat16, "Y"),
           _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return Y
+
+
+# the largest workspace convrot_linear_noalloc has (CONVROT_NOALLOC_MAX_WORKSPACE)
+NOALLOC_MAX_WORKSPACE = 48 << 20
+
+
+def convrot_linear_noalloc(X, image, sw, bias, N: int, g: int, Y, stream=None):
+    """convrot_linear with the library's own device workspace (no allocation in
+    the call; Y must be given).  Calls on one GPU share that workspace."""
+    import torch
+    M, K = X.shape
+    bias_p = None if bias is None else _dev(bias, torch.bfloat16, "bias")
+    _call("convrot_linear_noalloc", _dev(X, torch.bfloat16, "X"), M, K, _dev(image, torch.uint8, "image"),
+          _dev(sw, torch.float32, "sw"), bias_p, N, g, _dev(Y, torch.bfloat16, "Y"), _stream(stream))
     return Y
 
 

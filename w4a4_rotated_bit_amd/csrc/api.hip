@@ -1,7 +1,10 @@
 // api.hip -- device entry points of the ConvRot C ABI (declared in
 // include/convrot.h).  Each call checks its arguments on the host, checks that
 // the current device is a gfx950, enqueues kernels on the caller's stream and
-// returns; nothing here allocates, frees or synchronises.
+// returns; nothing here allocates, frees or synchronises.  The one piece of
+// state is the allocation-free linear's workspace: a file-scope device array
+// (each GPU holds its own copy for the life of the process) whose address is
+// looked up once per device.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -40,6 +43,26 @@ int launched()
 }
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// The workspace of convrot_linear_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the per-device address from
+// hipGetSymbolAddress (scratch_ptr) is ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)CONVROT_NOALLOC_MAX_WORKSPACE;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[64];
+
+// This device's copy of `scratch`, looked up on the first call on the device
+// (the device is current), or nullptr when the lookup fails.
+void* scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+    return p;
+}
 
 int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
 {
@@ -206,13 +229,11 @@ int convrot_gemm(const void* ws, size_t ws_bytes, int64_t M, int64_t K, const vo
                         as_stream(stream));
 }
 
-int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
-                   int64_t N, int g, void* Y, void* ws, size_t ws_bytes, void* stream)
+// convrot_linear after its checks: ws is a workspace of at least
+// convrot_workspace_bytes(M, K, N, g) bytes
+static int enqueue_linear(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
+                          int64_t N, int g, void* Y, void* ws, hipStream_t s)
 {
-    int rc = convrot_validate_linear(X, M, K, image, sw, bias, N, g, Y, ws, ws_bytes);
-    if (rc || M == 0 || N == 0) return rc;
-    if ((rc = check_device())) return rc;
-    hipStream_t s = as_stream(stream);
     const int64_t Kr = rotated_width(K, g);
     const bool fp6 = image_has_fp6(g);
     if (single_kernel_linear(M, Kr, g)) {
@@ -230,8 +251,32 @@ int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const
         return launched();
     }
     const GemmPlan plan = gemm_plan(M, N, Kr, fp6);
-    if ((rc = enqueue_prepare_activations(X, M, K, g, ws, gemm_shape_fp6(plan.shape), s))) return rc;
+    int rc = enqueue_prepare_activations(X, M, K, g, ws, gemm_shape_fp6(plan.shape), s);
+    if (rc) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, gemm_args(ws, M, Kr, image, sw, bias, N, Y, fp6, plan), s);
+}
+
+int convrot_linear(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
+                   int64_t N, int g, void* Y, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = convrot_validate_linear(X, M, K, image, sw, bias, N, g, Y, ws, ws_bytes);
+    if (rc || M == 0 || N == 0) return rc;
+    if ((rc = check_device())) return rc;
+    return enqueue_linear(X, M, K, image, sw, bias, N, g, Y, ws, as_stream(stream));
+}
+
+int convrot_linear_noalloc(const void* X, int64_t M, int64_t K, const void* image, const float* sw,
+                           const void* bias, int64_t N, int g, void* Y, void* stream)
+{
+    // the checks of convrot_linear, with a stand-in for the workspace (any
+    // non-null aligned value) and the size of the static one
+    static const uint8_t kStandIn alignas(256) = 0;
+    int rc = convrot_validate_linear(X, M, K, image, sw, bias, N, g, Y, &kStandIn, kScratchBytes);
+    if (rc || M == 0 || N == 0) return rc;
+    if ((rc = check_device())) return rc;
+    void* ws = scratch_ptr();
+    if (!ws) return CONVROT_EHIP;
+    return enqueue_linear(X, M, K, image, sw, bias, N, g, Y, ws, as_stream(stream));
 }
 
 int convrot_linear_w4a16(const void* X, int64_t M, int64_t K, const void* image, const float* sw, const void* bias,
