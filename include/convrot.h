@@ -112,8 +112,9 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
  *      same layout as the weight image;
  *   4. when M > 32 and g does not carry CONVROT_INT4_IMAGE, room for the same
  *      codes as FP6: round_up(M, 32) * round_up(K_rot, 128) * 3 / 4 bytes
- *      (written by convrot_prepare_activations always, by convrot_linear when
- *      its plan runs on the FP6 matrix cores);
+ *      (convrot_prepare_activations writes both copies; convrot_linear
+ *      writes only the one its plan reads: the FP6 copy when the plan runs on
+ *      the FP6 matrix cores, the INT4 image otherwise);
  *   5. the activation scales sx: round_up(M, 32) floats;
  *   6. split-K partial tiles: when M > 32 and the output tiles are too few
  *      to occupy the GPU, each tile's K range is shared by S workgroups and
@@ -200,7 +201,9 @@ int convrot_repack_nk_to_image(const uint8_t* qweight_nk_dev, int64_t N, int64_t
  *   Y_dev      bf16 [M][N], written.
  *   workspace_dev / ws_bytes: at least convrot_workspace_bytes(M, K, N, g);
  *              its contents on entry are ignored and on exit hold the
- *              activation codes and scales of X.
+ *              activation codes and scales of X: the codes in the copy the
+ *              product reads -- the FP6 copy when convrot_linear_plan reports
+ *              CONVROT_MFMA_FP6, the INT4 image otherwise.
  * For M <= 4 with 1024 <= K <= 4096 (g = 256) or 512 <= K <= 2048 (g = 64)
  * the whole linear is one kernel: every workgroup quantizes the few
  * activation rows itself, in shared memory, while its weight loads are in

@@ -285,6 +285,14 @@ def test_split_k_workspace_reuse(gpu, M, N, K):
 # the whole linear
 # --------------------------------------------------------------------------
 
+def _linear_act_codes(gpu, ws, M, K, N, g):
+    """The activation codes convrot_linear leaves in its workspace, from the copy
+    its plan reads (FP6 for the FP6 block tile, else the INT4 image)."""
+    if M > 32 and gpu.convrot_linear_plan(M, K, N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
+        return gpu.convrot_host_workspace_fp6_codes(ws, M, gpu.rotated_width(K, g))
+    return gpu.workspace_act_codes(ws, M, gpu.rotated_width(K, g))
+
+
 def _oracle_g(g):
     """The group argument for the oracle: the INT4-only image flag is a storage
     choice of the library and has no arithmetic meaning."""
@@ -300,15 +308,13 @@ def _linear_parity(gpu, x, w, bias, g):
     ws = gpu.new_workspace(x.shape[0], K, N, g)
     Y = gpu.convrot_linear(_dev(x), image, sw, None if bias is None else _dev(bias), N, g, workspace=ws)
     gy = _host_bits(Y)
-    # codes of X (from the workspace) and of W (from the image), K_rot wide
+    # codes of X (from the copy of the workspace the plan reads) and of W (from
+    # the image), K_rot wide
     M = x.shape[0]
+    qx = _linear_act_codes(gpu, ws, M, K, N, g)
     K = gpu.rotated_width(K, g)
-    qx = gpu.workspace_act_codes(ws, M, K)
     orx = oracle.rotate_rows(x, og)
     compare_codes(qx, parts["qx"], orx, parts["sx"], "activation codes")
-    if M > 32 and gpu.convrot_linear_plan(M, w.shape[1], N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
-        # the FP6 copy the FP6 tile reads holds the same codes
-        assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(ws, M, K), qx)
     qw = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     compare_codes(qw, oq_w, oracle.rotate_rows(w, og), osw, "weight codes")
     rows_ok = np.all(qx == parts["qx"], axis=1) & bool(np.array_equal(qw, oq_w))
@@ -508,10 +514,8 @@ def test_linear_full_size(gpu, name):
     y_or, parts = oracle.linear(inp["x"], oq_w, osw, inp["bias"], og, want_parts=True)
     assert np.array_equal(sw.cpu().numpy(), osw), "weight scales"
     wsh = ws.cpu().numpy()
-    gq_x = gpu.workspace_act_codes(wsh, M, K)
+    gq_x = _linear_act_codes(gpu, wsh, M, K, N, g)
     n_x = compare_codes(gq_x, parts["qx"], oracle.rotate_rows(inp["x"], og), parts["sx"], "activation codes")
-    if M > 32 and gpu.convrot_linear_plan(M, K, N, g)["mfma"] == gpu.CONVROT_MFMA_FP6:
-        assert np.array_equal(gpu.convrot_host_workspace_fp6_codes(wsh, M, K), gq_x)
     qw_all = oracle.unpack_nk(gpu.convrot_host_image_to_nk(image.cpu().numpy(), N, K), K)
     assert qw_all.min() >= -7 and qw_all.max() <= 7
     assert np.all(np.abs(qw_all).max(axis=1) == 7)

@@ -72,10 +72,12 @@ int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
     return CONVROT_OK;
 }
 
-// want_fp6: also write the FP6 copy of the codes (when the GEMM that follows
-// is unknown, or its plan reads that copy); fp6 = image_has_fp6(g): the
-// workspace has room for it.  Clears the split-K counters and the status word.
-int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, bool want_fp6, hipStream_t s)
+// want4 / want6: write the INT4 activation image / its FP6 copy (both when
+// the GEMM that follows is unknown; otherwise the one its plan reads).  The
+// FP6 copy exists only when act_has_fp6(M, image_has_fp6(g)).  Clears the
+// split-K counters and the status word.
+int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, bool want4, bool want6,
+                                hipStream_t s)
 {
     const int64_t Kr = rotated_width(K, g);
     const bool fp6 = image_has_fp6(g);
@@ -86,8 +88,8 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.rows_pad = round_up(M, kTileRows);
     a.K = Kr;
     a.K_pad = round_up(Kr, kTileK);
-    a.out = (uint8_t*)ws + workspace_image_offset();
-    a.out6 = act_has_fp6(M, fp6) && want_fp6 ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
+    a.out6 = act_has_fp6(M, fp6) && want6 ? (uint8_t*)ws + workspace_image6_offset(M, Kr) : nullptr;
+    a.out = want4 || !a.out6 ? (uint8_t*)ws + workspace_image_offset() : nullptr;
     a.scales = (float*)((uint8_t*)ws + workspace_sx_offset(M, Kr, fp6));
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
@@ -214,7 +216,7 @@ int convrot_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     if (ws_bytes < workspace_partial_offset(M, rotated_width(K, g), image_has_fp6(g))) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;
     // the GEMM that will consume the workspace is not known: both copies
-    return enqueue_prepare_activations(X, M, K, g, ws, true, as_stream(stream));
+    return enqueue_prepare_activations(X, M, K, g, ws, true, true, as_stream(stream));
 }
 
 int convrot_gemm(const void* ws, size_t ws_bytes, int64_t M, int64_t K, const void* image, const float* sw,
@@ -251,7 +253,8 @@ static int enqueue_linear(const void* X, int64_t M, int64_t K, const void* image
         return launched();
     }
     const GemmPlan plan = gemm_plan(M, N, Kr, fp6);
-    int rc = enqueue_prepare_activations(X, M, K, g, ws, gemm_shape_fp6(plan.shape), s);
+    const bool fp6_plan = gemm_shape_fp6(plan.shape);  // the GEMM reads only the FP6 copy, else only the INT4 image
+    int rc = enqueue_prepare_activations(X, M, K, g, ws, !fp6_plan, fp6_plan, s);
     if (rc) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, gemm_args(ws, M, Kr, image, sw, bias, N, Y, fp6, plan), s);
 }

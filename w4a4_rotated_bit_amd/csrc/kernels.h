@@ -14,8 +14,8 @@ struct PrepArgs {
     int64_t rows_pad;    // rows written (image mode: rows rounded up to 32)
     int64_t K, K_pad;    // K: rotated row length (a whole number of groups); K_pad: K rounded up to 128 (image mode)
     int64_t ld;          // elements per row of X (<= K: the rest of a row is zero padding)
-    uint8_t* out;        // codes in the layout of the mode
-    uint8_t* out6;       // OUT_IMAGE only: the FP6 image of the same codes, or nullptr
+    uint8_t* out;        // codes in the layout of the mode (OUT_IMAGE: the INT4 image, or nullptr)
+    uint8_t* out6;       // OUT_IMAGE only: the FP6 image of the same codes, or nullptr (not both null)
     float* scales;       // [rows]
     float* rotated;      // OUT_ROWMAJOR only: fp32 [rows][K] or nullptr
     uint32_t* zero;      // words cleared by workgroup 0 (split-K counters) or nullptr

@@ -434,10 +434,12 @@ __device__ __forceinline__ void prep_row(const PrepArgs& a, uint4 (&w)[PrepShape
         if constexpr (MODE == OUT_IMAGE) {
             // P/8 words for k0, k0 + 8 (adjacent dwords of one 8-byte group when P = 16)
             uint8_t* dst = a.out + image_word_offset(row, k0, a.K_pad);
-            if constexpr (P == 16)
-                *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
-            else
-                *(uint32_t*)dst = image_word(f);
+            if (a.out) {
+                if constexpr (P == 16)
+                    *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
+                else
+                    *(uint32_t*)dst = image_word(f);
+            }
             if (a.out6) {
                 // the same codes into the FP6 image: 6 P bits from logical
                 // byte 24 (k0 % 128 / 32) + 6 P / 8 (k0 % 32 / P) of the row
@@ -542,6 +544,272 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepWaves
         nx = row + row_step;
         load_run<P>(a.X, nx, a.ld, k0, nx < a.rows, wa);
         prep_row<G, MODE, 0, REG>(a, wb, row, t, k0, lane, wave, ld, red, 1, 0, blockDim.x >> 6);
+        row = nx;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep_team_kernel: the operand-image mode of prep_kernel for rows whose team
+// is whole waves (K_pad / P = 128 .. 1024 lanes: K_pad >= 2048 at g = 256,
+// >= 1024 at g = 64) -- the activations of every FLUX-shaped linear and the
+// rows of every weight.  One workgroup is one row's team and walks rows with
+// a grid stride, so the row index and every row base address are uniform
+// (scalar registers); the lanes only add 32-bit offsets.  The rotation is
+// prep_row's (the same binary64 butterflies and LDS transposes, the same
+// single rounding); the quantizer rounds the exact product r * rcp(s) with a
+// fused multiply-add and keeps prep_row's near-tie fallback to the IEEE
+// division; the FP6 fields reuse the rounded codes.  OUT4 / OUT6: write the
+// INT4 image / the FP6 image (a linear whose plan reads only one of them
+// writes only that one).
+// ---------------------------------------------------------------------------
+
+// clamp(rint(fl32(r / s)), -7, 7) for P values, as the bit patterns f of
+// 1.5 * 2^23 + code (low byte = the code) and as floats t.  fma(r, inv,
+// 1.5 * 2^23) rounds the exact product r * inv to an integer (the sum lies in
+// [2^23, 2^24), whose spacing is 1; ties to even), and fma(r, inv, -t) is that
+// product's distance to the integer, rounded once.  With inv = rcp(s) (one
+// ulp), r * inv is within 2^-20 of r / s and fl32(r / s) within 2^-21 of it
+// (|r / s| < 8); so when the distance is at most 0.5 - 2^-18 the integer is
+// rint(fl32(r / s)).  Otherwise -- and for a scale that is not a normal
+// number -- the element takes the correctly rounded division.
+template <int P>
+__device__ inline void quantize_fma(const float (&r)[P], float s, bool zero_row, uint32_t (&f)[P], float (&t)[P])
+{
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const bool exact_only = !(s >= 0x1p-126f);
+    const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
+    bool need = exact_only && !zero_row;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        const float fy = __builtin_fmaf(r[e], inv, kMagic);
+        t[e] = fy - kMagic;
+        need |= fabsf(__builtin_fmaf(r[e], inv, -t[e])) > 0.5f - 0x1p-18f;
+        f[e] = __float_as_uint(fy);
+    }
+    if (need && !zero_row) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const float fy = __builtin_fmaf(r[e], inv, kMagic);
+            const float te = fy - kMagic;
+            if (exact_only || fabsf(__builtin_fmaf(r[e], inv, -te)) > 0.5f - 0x1p-18f) {
+                const float q = __builtin_rintf(fminf(fmaxf(r[e] / s, -7.0f), 7.0f));  // IEEE division
+                f[e] = __float_as_uint(q + kMagic);
+                t[e] = __uint_as_float(f[e]) - kMagic;  // +0 for a zero code (rint may give -0)
+            }
+        }
+    }
+    if (zero_row) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            f[e] = __float_as_uint(kMagic);
+            t[e] = 0.0f;
+        }
+    }
+}
+
+// FP6 fields of P = 8 or 16 codes given as floats (see fp6_fields)
+template <int P>
+__device__ inline u32x6_t fp6_fields_of(const float (&t)[P])
+{
+    f32x16_t ev = __builtin_nondeterministic_value(ev), od = __builtin_nondeterministic_value(od);
+#pragma unroll
+    for (int i = 0; i < P / 2; ++i) {
+        ev[i] = t[2 * i];
+        od[i] = t[2 * i + 1];
+    }
+    return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+}
+
+// The lane's P bf16 values of row `row` (uniform), k0 .. k0 + P - 1, in
+// 16-byte chunks; chunks past the row's ld values or past its rows read the
+// row's first chunk (a valid address) and are zeroed by team_zero_unless.
+template <int P>
+__device__ inline void team_load(const PrepArgs& a, int64_t row, uint32_t k0, uint4 (&w)[P / 8])
+{
+    const bool has_row = row < a.rows;
+    const uint16_t* xr = a.X + (has_row ? row : 0) * a.ld;
+#pragma unroll
+    for (int c = 0; c < P / 8; ++c) {
+        const uint32_t k = k0 + 8 * c;
+        w[c] = *(const uint4*)(xr + (has_row && k < (uint32_t)a.ld ? k : 0u));
+    }
+}
+
+template <int P>
+__device__ inline void team_zero_unless(const PrepArgs& a, int64_t row, uint32_t k0, uint4 (&w)[P / 8])
+{
+    const bool has_row = row < a.rows;
+#pragma unroll
+    for (int c = 0; c < P / 8; ++c)
+        if (!(has_row && k0 + 8 * c < (uint32_t)a.ld)) w[c] = make_uint4(0, 0, 0, 0);
+}
+
+template <int G, bool REG, bool OUT4, bool OUT6>
+__device__ __forceinline__ void team_row(const PrepArgs& a, uint4 (&w)[PrepShape<G>::P / 8], int64_t row, uint32_t k0,
+                                         uint32_t off4, uint32_t off6, int lane, int wave, int nw, double* ld,
+                                         uint32_t (*red)[16], int parity)
+{
+    using S = PrepShape<G>;
+    constexpr int P = S::P;
+    const int gbase = (lane / P) * P;
+    const int lo = lane % P;
+    float* lf = (float*)ld;
+    team_zero_unless<P>(a, row, k0, w);
+    // ---- phase 1: P consecutive elements, butterflies over the low bits ----
+    double v[P];
+#pragma unroll
+    for (int c = 0; c < P / 8; ++c) {
+        v[8 * c + 0] = bf16_lo(w[c].x); v[8 * c + 1] = bf16_hi(w[c].x);
+        v[8 * c + 2] = bf16_lo(w[c].y); v[8 * c + 3] = bf16_hi(w[c].y);
+        v[8 * c + 4] = bf16_lo(w[c].z); v[8 * c + 5] = bf16_hi(w[c].z);
+        v[8 * c + 6] = bf16_lo(w[c].w); v[8 * c + 7] = bf16_hi(w[c].w);
+    }
+    if constexpr (REG) regular_input_signs<G, P>((int64_t)k0, v);
+#pragma unroll
+    for (int b = 1; b < P; b <<= 1)
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if (!(e & b)) {
+                const double x = v[e], y = v[e | b];
+                v[e] = x + y;
+                v[e | b] = x - y;
+            }
+    // ---- transpose through this wave's LDS region, half a group at a time ----
+    double u[P];
+    {
+        const int slot_base = (lane / P) * (P / 2);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            if (lo / (P / 2) == hh) {
+                double* dst = ld + (slot_base + lo % (P / 2)) * S::kRunD;
+#pragma unroll
+                for (int e = 0; e < P; e += 2) *(double2*)(dst + e) = make_double2(v[e], v[e + 1]);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+            for (int i = 0; i < P / 2; ++i) u[hh * (P / 2) + i] = ld[(slot_base + i) * S::kRunD + lo];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // every lane's reads are done before the region is rewritten
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    // ---- phase 2: butterflies over the high bits ----
+#pragma unroll
+    for (int b = 1; b < P; b <<= 1)
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            if (!(i & b)) {
+                const double x = u[i], y = u[i | b];
+                u[i] = x + y;
+                u[i | b] = x - y;
+            }
+    // ---- round once to binary32, back to phase-1 order through LDS ----
+    constexpr double kNorm = (G == 256) ? 0.0625 : 0.125;  // 1/sqrt(g), exact
+#pragma unroll
+    for (int i = 0; i < P; ++i) lf[(gbase + i) * S::kRunF + lo] = (float)(u[i] * kNorm);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    float r[P];
+    if constexpr (!REG) {
+#pragma unroll
+        for (int e = 0; e < P; e += 4) {
+            const float4 q = *(const float4*)(lf + lane * S::kRunF + e);
+            r[e] = q.x; r[e + 1] = q.y; r[e + 2] = q.z; r[e + 3] = q.w;
+        }
+    } else {
+        regular_output_permutation<G, P, S::kRunF>(lf, gbase, (int64_t)k0, r);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next row rewrites the region
+    __builtin_amdgcn_wave_barrier();
+    // ---- row absmax: the wave, then the team's waves through LDS ----
+    float lane_max = 0.0f;
+#pragma unroll
+    for (int e = 0; e < P; ++e) lane_max = fmaxf(lane_max, fabsf(r[e]));
+    uint32_t amax_bits = team_max(__float_as_uint(lane_max), 64);
+    if (lane == 0) red[parity][wave] = amax_bits;  // rewritten two rows later, after the next row's barrier
+    __syncthreads();
+    amax_bits = red[parity][0];
+    for (int wv = 1; wv < nw; ++wv) amax_bits = max(amax_bits, red[parity][wv]);
+    const float amax = __uint_as_float(amax_bits);
+    const bool zero_row = !(amax > 0.0f);
+    const float s = zero_row ? 0.0f : amax / 7.0f;  // IEEE binary32 division
+    if (row < a.rows && k0 == 0) a.scales[row] = s;
+    if (k0 >= (uint32_t)a.K_pad) return;
+    uint32_t f[P];
+    float t[P];
+    quantize_fma<P>(r, s, zero_row, f, t);
+    const int64_t rt = row >> 5;
+    const int rr = (int)(row & 31);
+    const int64_t KB = a.K_pad / kTileK;
+    if constexpr (OUT4) {
+        uint8_t* dst = a.out + (size_t)(rt * KB) * kUnitBytes + rr * 64 + (off4 ^ (row_swizzle(rr) << 4));
+        if constexpr (P == 16)
+            *(uint2*)dst = make_uint2(image_word(f), image_word(f + 8));
+        else
+            *(uint32_t*)dst = image_word(f);
+    }
+    if constexpr (OUT6) {
+        const u32x6_t fp = fp6_fields_of<P>(t);
+        uint8_t* base6 = a.out6 + (size_t)(rt * KB) * kUnit6Bytes + rr * kRow6Bytes;
+        // off6 holds the K-block part (kb * 3072) in its high bits and the block
+        // b and in-block byte in its low byte: block b goes to b ^ row_swizzle6
+        const uint32_t blk = (off6 >> 5) & 3, inb = off6 & 31, kbo = off6 >> 7;
+        uint8_t* dst = base6 + kbo + ((blk ^ (uint32_t)row_swizzle6(rr)) * 24 + inb);
+        if constexpr (P == 16) {
+            *(uint3*)dst = make_uint3(fp[0], fp[1], fp[2]);
+        } else {
+            const uint16_t hw[3] = {(uint16_t)fp[0], (uint16_t)(fp[0] >> 16), (uint16_t)fp[1]};
+#pragma unroll
+            for (int d = 0; d < 3; ++d) *(uint16_t*)(dst + 2 * d) = hw[d];
+        }
+    }
+}
+
+// Occupancy targets of the team kernel: as prep_kernel's, one wave fewer
+// for the g = 256 instance that writes both images (weights), which spills
+// at five.
+template <int G, bool REG, bool BOTH>
+constexpr int kPrepTeamWavesPerSimd = (G == 256 && BOTH && !REG) ? 4 : kPrepWavesPerSimd<G, REG>;
+
+template <int G, bool REG, bool OUT4, bool OUT6>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepTeamWavesPerSimd<G, REG, OUT4 && OUT6>))) void
+prep_team_kernel(PrepArgs a)
+{
+    using S = PrepShape<G>;
+    constexpr int P = S::P;
+    extern __shared__ __attribute__((aligned(16))) uint8_t prep_lds[];
+    __shared__ uint32_t red[2][16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = (int)(blockDim.x >> 6);
+    if (a.zero && blockIdx.x == 0)  // split-K counters and status word of the GEMM that consumes this workspace
+        for (int i = tid; i < a.zero_count; i += blockDim.x) a.zero[i] = 0;
+    // lane parts of the image offsets (32-bit; the row parts are uniform)
+    const uint32_t k0 = (uint32_t)tid * P;
+    const uint32_t kb = k0 / kTileK, kl = k0 % kTileK;
+    const uint32_t ks = kl / 32, h = (kl % 32) / 16, d = (kl % 16) / 8;
+    // INT4: unit kb, logical chunk 2 (ks / 2) + h (swizzled by the row at the
+    // store), 8-byte half ks % 2, dword d
+    const uint32_t off4 = kb * kUnitBytes + ((2 * (ks / 2) + h) << 4) + (ks % 2) * 8 + d * 4;
+    // FP6: unit kb, block ks (swizzled at the store), in-block byte 6 P / 8 (kl % 32 / P)
+    const uint32_t off6 = (kb * kUnit6Bytes) << 7 | (ks << 5) | ((6 * P / 8) * ((kl % 32) / P));
+    double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
+    int64_t row = blockIdx.x;
+    const int64_t step = gridDim.x;
+    uint4 wa[P / 8], wb[P / 8];
+    team_load<P>(a, row, k0, wa);
+    for (int parity = 0; row < a.rows_pad; parity ^= 1) {
+        const int64_t nx = row + step;
+        if (parity == 0) {
+            team_load<P>(a, nx, k0, wb);
+            team_row<G, REG, OUT4, OUT6>(a, wa, row, k0, off4, off6, lane, wave, nw, ld, red, 0);
+        } else {
+            team_load<P>(a, nx, k0, wa);
+            team_row<G, REG, OUT4, OUT6>(a, wb, row, k0, off4, off6, lane, wave, nw, ld, red, 1);
+        }
         row = nx;
     }
 }
@@ -2138,9 +2406,68 @@ static void launch_prep_g(PrepArgs a, hipStream_t s)
     hipLaunchKernelGGL((prep_kernel<G, MODE, REG>), dim3(grid), dim3(block), lds, s, a);
 }
 
+// Workgroups of one kernel instance resident per compute unit (cached per
+// instance and block size).
+template <typename KernelPtr>
+static int resident_per_cu(KernelPtr kernel, int block, size_t lds, std::atomic<int> (&cache)[17])
+{
+    const int waves = block / 64;
+    int per_cu = cache[waves].load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, block, lds) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        cache[waves].store(per_cu, std::memory_order_relaxed);
+    }
+    return per_cu;
+}
+
+template <int G, bool REG, bool OUT4, bool OUT6>
+static void launch_prep_team(const PrepArgs& a, int team, hipStream_t s)
+{
+    const size_t lds = (size_t)(team / 64) * PrepShape<G>::kWaveLdsBytes;
+    static bool attr_set = false;  // benign race: every caller sets the same value
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)&prep_team_kernel<G, REG, OUT4, OUT6>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 16 * PrepShape<G>::kWaveLdsBytes);
+        attr_set = true;
+    }
+    static std::atomic<int> cache[17];
+    const int per_cu = resident_per_cu(&prep_team_kernel<G, REG, OUT4, OUT6>, team, lds, cache);
+    const int64_t resident = (int64_t)device_cus() * per_cu;
+    const unsigned grid = (unsigned)(a.rows_pad < resident ? a.rows_pad : resident);
+    hipLaunchKernelGGL((prep_team_kernel<G, REG, OUT4, OUT6>), dim3(grid), dim3(team), lds, s, a);
+}
+
+template <int G, bool REG>
+static void launch_prep_team_out(PrepArgs a, hipStream_t s)
+{
+    constexpr int P = PrepShape<G>::P;
+    const int team = (int)((a.K_pad / P + 63) / 64 * 64);
+    a.team = team;
+    if (a.out && a.out6)
+        launch_prep_team<G, REG, true, true>(a, team, s);
+    else if (a.out)
+        launch_prep_team<G, REG, true, false>(a, team, s);
+    else
+        launch_prep_team<G, REG, false, true>(a, team, s);
+}
+
 template <int MODE>
 static void launch_prep_mode(int g, const PrepArgs& a, hipStream_t s)
 {
+    if constexpr (MODE == OUT_IMAGE) {
+        // rows of whole waves: the team kernel (scalar row addressing)
+        const bool reg = (g & kRegularHadamard) != 0;
+        const int gs = group_size(g);
+        if (a.K_pad / (gs == 256 ? 16 : 8) > 64) {
+            if (gs == 256)
+                reg ? launch_prep_team_out<256, true>(a, s) : launch_prep_team_out<256, false>(a, s);
+            else
+                reg ? launch_prep_team_out<64, true>(a, s) : launch_prep_team_out<64, false>(a, s);
+            return;
+        }
+    }
     const bool reg = (g & kRegularHadamard) != 0;
     g = group_size(g);
     if (g == 256)
