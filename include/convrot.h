@@ -116,7 +116,7 @@ int convrot_weight_image_bytes(int64_t N, int64_t K, int g, size_t* bytes_host);
  *      writes only the one its plan reads: the FP6 copy when the plan runs on
  *      the FP6 matrix cores, the INT4 image otherwise);
  *   5. the activation scales sx: round_up(M, 32) floats;
- *   6. split-K partial tiles: when M > 32 and the output tiles are too few
+ *   6. split-K partial tiles: when M > 128 and the output tiles are too few
  *      to occupy the GPU, each tile's K range is shared by S workgroups and
  *      S - 1 partial tiles of 4-byte sums per output tile live here (0 bytes
  *      otherwise).
@@ -138,7 +138,7 @@ int convrot_linear_kernel_count(int64_t M, int64_t K, int64_t N, int g, int* cou
  * on codes widened from INT4) or CONVROT_MFMA_FP6 (FP6 e2m3 MFMA on the FP6
  * copy of the codes; exact: the codes are exact e2m3 values and the binary32
  * sums are exact integers), 0 when M or N is 0; *tile_m x *tile_n = the block
- * tile when M > 32 (0 x 0 for the weight-streaming kernels of M <= 32);
+ * tile when M > 128 (0 x 0 for the weight-streaming kernel of M <= 128);
  * *splits = workgroups sharing each tile's K range (1 when not split).
  * Returns CONVROT_OK or CONVROT_EINVAL. */
 #define CONVROT_MFMA_I8 1

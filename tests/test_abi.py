@@ -100,6 +100,10 @@ def test_plan_of_the_flux_shapes():
     assert B.convrot_linear_plan(1536, 3072, 12288, 256) == {"mfma": I8, "tile": (192, 384), "splits": 1}
     assert B.convrot_linear_plan(1536, 12288, 3072, 256) == {"mfma": I8, "tile": (192, 192), "splits": 2}
     assert B.convrot_linear_plan(16, 3072, 12288, 256) == {"mfma": I8, "tile": (0, 0), "splits": 1}
+    # up to 128 rows the weight is streamed; from 129 on, block tiles
+    assert B.convrot_linear_plan(64, 1024, 1024, 256) == {"mfma": I8, "tile": (0, 0), "splits": 1}
+    assert B.convrot_linear_plan(128, 2048, 2048, 64) == {"mfma": I8, "tile": (0, 0), "splits": 1}
+    assert B.convrot_linear_plan(129, 2048, 2048, 64)["tile"] != (0, 0)
     assert B.convrot_linear_plan(0, 3072, 12288, 256) == {"mfma": 0, "tile": (0, 0), "splits": 1}
     # only the 192 x 192 tile is ever split
     for M, N, K in [(256, 3072, 16384), (1024, 1024, 8192), (300, 9000, 12288), (64, 64, 16384)]:

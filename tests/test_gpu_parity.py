@@ -148,7 +148,11 @@ GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), 
                (200, 3011, 16384),
                # the FP6 and 192 x 384 tiles with at least eight 128-K blocks, so that their
                # K loops run the steady state of the stage ring (aligned and ragged)
-               (1536, 9216, 1024), (1500, 9000, 1152), (1536, 12288, 1024), (1500, 12000, 1408)]
+               (1536, 9216, 1024), (1500, 9000, 1152), (1536, 12288, 1024), (1500, 12000, 1408),
+               # the weight stream with 2, 3 and 4 groups of 32 rows (M <= 128; strips padded
+               # to a multiple of 8), and the first M past it (block tiles)
+               (33, 130, 384), (64, 1000, 1152), (65, 512, 2048), (128, 2048, 2048), (127, 33, 640),
+               (129, 200, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -250,7 +254,7 @@ def test_split_k_timeout_is_reported(gpu):
     assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(qx, qw))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (64, 1024, 8192), (300, 700, 4096), (256, 4096, 12288)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 4096), (160, 1024, 8192), (300, 700, 4096), (256, 4096, 12288)])
 def test_split_k_workspace_reuse(gpu, M, N, K):
     """Shapes whose tiles are split along K: a workspace full of garbage is
     cleared by the activation step, and repeated GEMMs on one workspace (the

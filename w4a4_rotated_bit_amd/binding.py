@@ -182,7 +182,7 @@ CONVROT_MFMA_FP6 = 2
 
 def convrot_linear_plan(M: int, K: int, N: int, g: int) -> dict:
     """The product plan: {"mfma": CONVROT_MFMA_I8 / CONVROT_MFMA_FP6 (0 if M or N
-    is 0), "tile": (tile_m, tile_n) ((0, 0) for M <= 32), "splits": S}."""
+    is 0), "tile": (tile_m, tile_n) ((0, 0) for M <= 128), "splits": S}."""
     v = [ctypes.c_int() for _ in range(4)]
     _call("convrot_linear_plan", M, K, N, g, *[ctypes.byref(x) for x in v])
     return {"mfma": v[0].value, "tile": (v[1].value, v[2].value), "splits": v[3].value}

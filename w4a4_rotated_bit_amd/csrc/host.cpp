@@ -192,9 +192,9 @@ int convrot_linear_plan(int64_t M, int64_t K, int64_t N, int g, int* kind, int* 
     *tile_m = *tile_n = 0;
     *splits = 1;
     if (M == 0 || N == 0) return CONVROT_OK;
-    // M <= 32 streams the weight through the INT8 16x16x64 MFMA
+    // M <= kStreamMaxRows streams the weight through the INT8 16x16x64 MFMA
     *kind = CONVROT_MFMA_I8;
-    if (M <= 32) return CONVROT_OK;
+    if (M <= kStreamMaxRows) return CONVROT_OK;
     const GemmPlan p = gemm_plan(M, N, rotated_width(K, g), image_has_fp6(g));
     if (gemm_shape_fp6(p.shape)) *kind = CONVROT_MFMA_FP6;
     *tile_m = gemm_tile_m(p.shape);

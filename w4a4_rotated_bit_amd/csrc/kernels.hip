@@ -13,9 +13,10 @@
 //   gemm_kernel   the same on the INT8 matrix cores (v_mfma_i32_32x32x32_i8,
 //                 codes widened to INT8 x 16 in registers), two tile shapes,
 //                 one of them split along K.
-//   skinny_kernel, small_m_kernel, w4a16_kernel, small_w4a16_kernel:
-//                 the weight-streaming products of M <= 32 (one launch for
-//                 M <= 4, the rows rotated in every workgroup).
+//   skinny_kernel the weight-streaming product of M <= 128.
+//   small_m_kernel, w4a16_kernel, small_w4a16_kernel:
+//                 one-launch W4A4 for M <= 4 (the rows rotated in every
+//                 workgroup) and the weight-only variant (M <= 32).
 //   relayout kernels: lossless layout moves into the operand images.
 //
 // Method: convrot-mlx README, "What is included" (normalized Hadamard
@@ -1685,19 +1686,24 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// skinny_kernel: M <= 32 (one 32-row unit of activation codes)
+// skinny_kernel: M <= 128 (up to four 32-row units of activation codes)
 //
 // The product is a stream over the weight image.  One workgroup per
-// 16-column strip (half of a 32-row weight unit: 1 KB per 128-K unit), its
-// four waves splitting K; each strip is computed with the 16x16x64 INT8 MFMA
-// as W . X^T for MH 16-row halves of the activation unit.  Every lane loads
-// one 16-byte chunk (32 codes) of its weight row and of its activation row(s)
-// per unit straight into registers -- no reuse, so no LDS staging -- with up
-// to kSkinnyBatch units of loads in flight per wave (at K <= 3072 the whole
-// strip, so the full weight image is requested as soon as the grid is
-// resident).  With 16-column strips a 12288-column weight is 768 equal
-// workgroups, three per CU.  The chunk of lane quad q feeds k-slots q of two
-// MFMAs (its first and second 16 codes); both operands use the same
+// 16-column strip (half of a 32-row weight unit: 1 KB per 128-K unit) and
+// 32-row group of activations, its four waves splitting K; each strip is
+// computed with the 16x16x64 INT8 MFMA as W . X^T for MH 16-row blocks of
+// the group.  Every lane loads one 16-byte chunk (32 codes) of its weight
+// row and of its activation row(s) per unit straight into registers -- no
+// reuse inside the workgroup, so no LDS staging -- with kSkinnyBatch units of
+// loads in flight per wave (at K <= 3072 the whole strip, so the full weight
+// image is requested as soon as the grid is resident).  With 16-column
+// strips a 12288-column weight is 768 equal workgroups, three per CU.  With
+// more than one row group the workgroups of a strip are numbered so that
+// they run on the same XCD (workgroups go to the XCDs in turn by number) and
+// read the strip from that XCD's L2 after the first; with one group the
+// weight is read with the non-temporal hint.  The activation codes are
+// re-read from L2 by every strip.  The chunk of lane quad q feeds k-slots q
+// of two MFMAs (its first and second 16 codes); both operands use the same
 // assignment, so the sum over k is the dot product.  The four partial tiles
 // are summed through LDS and the epilogue writes the valid rows.
 // ---------------------------------------------------------------------------
@@ -1729,15 +1735,25 @@ __device__ inline void load_column_params(const GemmArgs& a, int64_t n0, float (
     }
 }
 
-template <int OUT, int MH>
+// Workgroup number -> (16-column strip, 32-row group) with the groups of a
+// strip on one XCD: b = 8 l + x runs on XCD x; l = groups * j + rg.  The
+// strips are padded to a multiple of 8; the padding workgroups do nothing.
+CONVROT_HD inline int skinny_strips_padded(int64_t N) { return (int)(((N + 15) / 16 + 7) / 8 * 8); }
+
+template <int OUT, int MH, bool NONTEMPORAL>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 {
+    constexpr int BATCH = kSkinnyBatch;
     __shared__ __attribute__((aligned(16))) int32_t red[kSkinnyWaves - 1][MH][4][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, q = lane >> 4;
-    const int strip = blockIdx.x;                   // output columns 16 strip .. 16 strip + 15
-    const int nt = strip >> 1, half = strip & 1;    // weight unit row tile and its half
+    const int groups = (int)((a.M + 31) / 32);
+    const int l = (int)(blockIdx.x >> 3);
+    const int rg = l % groups;                                    // rows 32 rg .. 32 rg + 31
+    const int strip = (l / groups) * 8 + (int)(blockIdx.x & 7);  // columns 16 strip .. 16 strip + 15
+    if ((int64_t)strip * 16 >= a.N) return;  // padding workgroup (uniform exit)
+    const int nt = strip >> 1, half = strip & 1;  // weight unit row tile and its half
     const int KB = a.KB;
     const int per = (KB + kSkinnyWaves - 1) / kSkinnyWaves;
     const int kb0 = wave * per, kb1 = min(KB, kb0 + per);
@@ -1747,17 +1763,17 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
     bool act_row[MH];
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh) {
-        const int arow = 16 * mh + r16;
-        abase[mh] = a.act + arow * 64 + ((q ^ row_swizzle(arow)) * 16);
-        act_row[mh] = arow < a.M;  // rows past M are zero in the image: not loaded
+        const int rr = 16 * mh + r16;  // row of the group's activation unit row tile
+        abase[mh] = a.act + (size_t)rg * KB * kUnitBytes + rr * 64 + ((q ^ row_swizzle(rr)) * 16);
+        act_row[mh] = 32 * rg + rr < a.M;  // rows past M are zero in the image: not loaded
     }
-    // lane's output columns (n0 .. n0 + 3) and rows (16 mh + r16) in the epilogue
+    // lane's output columns (n0 .. n0 + 3) and rows (32 rg + 16 mh + r16) in the epilogue
     const int64_t n0 = (int64_t)strip * 16 + 4 * q;
     float swv[4], bv[4], sxv[MH];
     if constexpr (OUT == GEMM_OUT_BF16) {
         load_column_params(a, n0, swv, bv);
 #pragma unroll
-        for (int mh = 0; mh < MH; ++mh) sxv[mh] = a.sx[min((int64_t)(16 * mh + r16), a.M - 1)];
+        for (int mh = 0; mh < MH; ++mh) sxv[mh] = a.sx[min((int64_t)(32 * rg + 16 * mh + r16), a.M - 1)];
         __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
     }
 
@@ -1765,19 +1781,20 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh) acc[mh] = v4i{0, 0, 0, 0};
 
-    for (int kb = kb0; kb < kb1; kb += kSkinnyBatch) {
-        uint4 wq[kSkinnyBatch], aq[kSkinnyBatch][MH];
+    for (int kb = kb0; kb < kb1; kb += BATCH) {
+        uint4 wq[BATCH], aq[BATCH][MH];
 #pragma unroll
-        for (int u = 0; u < kSkinnyBatch; ++u) {
+        for (int u = 0; u < BATCH; ++u) {
             const bool in = kb + u < kb1;
-            wq[u] = in ? load_stream16(wbase + (size_t)(kb + u) * kUnitBytes) : make_uint4(0, 0, 0, 0);
+            const uint8_t* wp = wbase + (size_t)(kb + u) * kUnitBytes;
+            wq[u] = !in ? make_uint4(0, 0, 0, 0) : NONTEMPORAL ? load_stream16(wp) : *(const uint4*)wp;
 #pragma unroll
             for (int mh = 0; mh < MH; ++mh)
                 aq[u][mh] = (in && act_row[mh]) ? *(const uint4*)(abase[mh] + (size_t)(kb + u) * kUnitBytes)
                                                 : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < kSkinnyBatch; ++u) {
+        for (int u = 0; u < BATCH; ++u) {
             if (kb + u >= kb1) break;
             const v4i w0 = widen_lo_hi(wq[u].x, wq[u].y), w1 = widen_lo_hi(wq[u].z, wq[u].w);
 #pragma unroll
@@ -1806,13 +1823,13 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(GemmArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mh][j] += red[w][mh][j][lane];
 
-    // lane holds, per half mh, output row m = 16 mh + r16 and the four
-    // consecutive columns n = n0 + (0..3)
+    // lane holds, per block mh, output row m = 32 rg + 16 mh + r16 and the
+    // four consecutive columns n = n0 + (0..3)
     if (n0 >= a.N) return;
     const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh) {
-        const int64_t m = 16 * mh + r16;
+        const int64_t m = 32 * rg + 16 * mh + r16;
         if (m >= a.M) continue;
         int32_t v[4];
 #pragma unroll
@@ -2486,6 +2503,21 @@ void launch_prep(int g, int mode, PrepArgs a, hipStream_t s)
     }
 }
 
+// one or two 16-row blocks per workgroup; the weight is read with the
+// non-temporal hint when no other workgroup reads the same strip
+template <int OUT>
+static void launch_skinny(const GemmArgs& a, hipStream_t s)
+{
+    const int groups = (int)((a.M + 31) / 32);
+    const dim3 grid((unsigned)(skinny_strips_padded(a.N) * groups)), block(kSkinnyWaves * 64);
+    if (a.M <= 16)
+        hipLaunchKernelGGL((skinny_kernel<OUT, 1, true>), grid, block, 0, s, a);
+    else if (a.M <= 32)
+        hipLaunchKernelGGL((skinny_kernel<OUT, 2, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((skinny_kernel<OUT, 2, false>), grid, block, 0, s, a);
+}
+
 template <typename G, int OUT, bool SPLIT>
 static void launch_block_tile_kernel(dim3 grid, const GemmArgs& a, hipStream_t s)
 {
@@ -2508,20 +2540,11 @@ static void launch_block_tile(int out_mode, bool split, dim3 grid, const GemmArg
 
 void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
 {
-    if (a.M <= 32) {
-        dim3 grid((unsigned)((a.N + 15) / 16)), block(kSkinnyWaves * 64);
-        const bool one = a.M <= 16;
-        if (out_mode == GEMM_OUT_I32) {
-            if (one)
-                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32, 1>), grid, block, 0, s, a);
-            else
-                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_I32, 2>), grid, block, 0, s, a);
-        } else {
-            if (one)
-                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16, 1>), grid, block, 0, s, a);
-            else
-                hipLaunchKernelGGL((skinny_kernel<GEMM_OUT_BF16, 2>), grid, block, 0, s, a);
-        }
+    if (a.M <= kStreamMaxRows) {
+        if (out_mode == GEMM_OUT_I32)
+            launch_skinny<GEMM_OUT_I32>(a, s);
+        else
+            launch_skinny<GEMM_OUT_BF16>(a, s);
         return;
     }
     if (a.splits < 1) a.splits = 1;

@@ -198,12 +198,15 @@ CONVROT_HD inline size_t w16_word_offset(int64_t m, int64_t k, int64_t K)
 // 1024 outputs per block (measured on MI355X on the FLUX shapes), one
 // prologue + epilogue (about 4 us) per round, and for a split the exchange of
 // (S - 1) 4-byte partial tiles per tile through memory (written and read back
-// at about 4 TB/s, plus 3 us).  M <= 32 goes to the weight-streaming kernels
-// and is never split.
+// at about 4 TB/s, plus 3 us).  M <= kStreamMaxRows goes to the
+// weight-streaming kernel instead (one workgroup per 16 output columns, the
+// activation codes of up to 128 rows read from L2 by every workgroup): at
+// such M the block tiles leave most compute units idle.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
 constexpr int kSplitCounters = 256;    // counter slots: a split launch has at most this many tiles
 constexpr int kMaxSplits = 8;
 constexpr int kGemmShapes = 3;
+constexpr int64_t kStreamMaxRows = 128;
 
 CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 2 ? 256 : 192; }
 CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 384 : (shape == 1 ? 192 : 256); }
@@ -241,7 +244,7 @@ CONVROT_HD inline GemmPlan gemm_plan_forced(int64_t M, int64_t N, int shape, int
 CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool fp6)
 {
     GemmPlan best{0, 1, 1, 1};
-    if (M <= 32 || M <= 0 || N <= 0) return best;
+    if (M <= kStreamMaxRows || N <= 0) return best;
     const int64_t KB = (K + kTileK - 1) / kTileK;
     int64_t best_ns = -1;
     for (int shape = 0; shape < kGemmShapes; ++shape) {
