@@ -73,14 +73,15 @@ __device__ inline void quantize_bits(const float (&r)[P], float s, bool zero_row
     constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
     const bool exact_only = !(s >= 0x1p-126f);
     const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
-    bool need = exact_only && !zero_row;
+    float dmax = 0.0f;  // the largest distance to the rounded value (one compare for all P)
 #pragma unroll
     for (int e = 0; e < P; ++e) {
         const float y = r[e] * inv;
         const float fy = y + kMagic;
-        need |= fabsf(y - (fy - kMagic)) > 0.5f - 0x1p-18f;
+        dmax = fmaxf(dmax, fabsf(y - (fy - kMagic)));
         f[e] = __float_as_uint(fy);
     }
+    const bool need = exact_only || dmax > 0.5f - 0x1p-18f;
     if (need && !zero_row) {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
@@ -579,14 +580,15 @@ __device__ inline void quantize_fma(const float (&r)[P], float s, bool zero_row,
     constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
     const bool exact_only = !(s >= 0x1p-126f);
     const float inv = exact_only ? 0.0f : __builtin_amdgcn_rcpf(s);
-    bool need = exact_only && !zero_row;
+    float dmax = 0.0f;  // the largest distance to the rounded value (one compare for all P)
 #pragma unroll
     for (int e = 0; e < P; ++e) {
         const float fy = __builtin_fmaf(r[e], inv, kMagic);
         t[e] = fy - kMagic;
-        need |= fabsf(__builtin_fmaf(r[e], inv, -t[e])) > 0.5f - 0x1p-18f;
+        dmax = fmaxf(dmax, fabsf(__builtin_fmaf(r[e], inv, -t[e])));
         f[e] = __float_as_uint(fy);
     }
+    const bool need = exact_only || dmax > 0.5f - 0x1p-18f;
     if (need && !zero_row) {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
@@ -655,7 +657,9 @@ __device__ __forceinline__ void team_row(const PrepArgs& a, uint4 (&w)[PrepShape
     const int gbase = (lane / P) * P;
     const int lo = lane % P;
     float* lf = (float*)ld;
-    team_zero_unless<P>(a, row, k0, w);
+    // a row of data whose every lane holds input values needs no zeroing
+    // (uniform test: rows of the FLUX shapes skip it)
+    if (!(row < a.rows && a.ld == a.K_pad && (int64_t)blockDim.x * P == a.K_pad)) team_zero_unless<P>(a, row, k0, w);
     // ---- phase 1: P consecutive elements, butterflies over the low bits ----
     double v[P];
 #pragma unroll
