@@ -1478,7 +1478,9 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
 //     fragments of the same stage are read into Y;
 //   barrier: the next stage has landed everywhere and every wave is done
 //     reading this stage, whose buffer then takes the copy three stages on;
-//   Y feeds 16 MFMAs while the next stage's k-step 0 fragments are read into X.
+//   Y feeds 16 MFMAs while the next stage's k-step 0 fragments are read into X
+//     (the reads interleaved with the MFMAs: a wave stalls once 15 LDS reads
+//     are outstanding).
 // Each stage so starts and ends with the same registers, and the body is
 // straight-line code.
 // ---------------------------------------------------------------------------
@@ -1674,7 +1676,9 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
             if constexpr (ISSUE) issue(lds0 + slot_kr * kStage, kb0 + kr + G::kStages);
             read(smem + ((kr + 1) % G::kStages) * kStage, 0, xa, xb);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // no scheduling fence here: the next stage's k-step 0 reads
+        // interleave with these MFMAs (issued all at once, they would exceed
+        // the 15 LDS reads a wave can have outstanding and stall its MFMAs)
         mma(ya, yb);
         hints(MORE ? 24 : 0);
         __builtin_amdgcn_sched_barrier(0);
