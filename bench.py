@@ -197,6 +197,71 @@ def summarize_profile(path: str) -> str:
     return "\n".join(out)
 
 
+def _pmc_per_kernel(path: str, counter: str):
+    """{kernel name: (dispatches, mean counter value per dispatch)} of one
+    counter in a rocprofv3 results database."""
+    import collections
+    import sqlite3
+    db = sqlite3.connect(path)
+    names = dict(db.execute("select dispatch_id, name from kernels"))
+    per = collections.defaultdict(float)
+    for d, c, v in db.execute("select dispatch_id, counter_name, counter_value from pmc_events"):
+        if c == counter:
+            per[d] += v
+    agg = collections.defaultdict(list)
+    for d, v in per.items():
+        agg[names.get(d, "?")].append(v)
+    return {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
+
+
+def traffic_summary(workload: str, fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_db: str) -> str:
+    """HBM traffic of the dominant product kernel of one workload, from
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each in its own run), scaled
+    by what the same counters read on a plain 256 MiB device copy."""
+    product = ("gemm", "skinny", "small_m", "w4a16_kernel")
+    fetch = {k: v for k, v in _pmc_per_kernel(fetch_db, "FETCH_SIZE").items() if any(p in k for p in product)}
+    write = _pmc_per_kernel(write_db, "WRITE_SIZE")
+    # the product kernel with the most dispatches is the timed one (the
+    # weight-prep and baseline launches are few)
+    kernel = max(fetch, key=lambda k: fetch[k][0])
+    n, fkib = fetch[kernel]
+    _, wkib = write[kernel]
+    cf = max(_pmc_per_kernel(copy_fetch_db, "FETCH_SIZE").values(), key=lambda t: t[1])[1]
+    cw = max(_pmc_per_kernel(copy_write_db, "WRITE_SIZE").values(), key=lambda t: t[1])[1]
+    copied_kib = 256 * 1024
+    fs, ws = copied_kib / cf, copied_kib / cw
+    fb, wb = int(fkib * 1024 * fs), int(wkib * 1024 * ws)
+    short = kernel.split("(")[0].replace("void ", "")
+    cmd = ("rocprofv3 --pmc {c} --kernel-include-regex 'gemm|skinny|small_m|prep' -d <out> -o run -- "
+           f"python3 bench.py --workload {workload} --no-per-config --no-cpu-baseline --no-baselines "
+           "--steps 20 --warmup 5")
+    lines = [
+        f"# HBM-side traffic of {short} on {workload} (per dispatch)",
+        "# counters, each in its own run:",
+        "#   " + cmd.format(c="FETCH_SIZE"),
+        "#   " + cmd.format(c="WRITE_SIZE"),
+        "# calibration, the same counters on a plain 256 MiB device copy:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <out> -o run -- python3 bench.py --copy-probe 268435456",
+        "#   (same with WRITE_SIZE)",
+        "# summary: python3 bench.py --workload " + workload +
+        " --write-traffic <fetch db> <write db> <copy fetch db> <copy write db>",
+        "# scale = copied KiB / counter KiB on the copy; traffic = counter * scale",
+        "# (L2-miss bytes toward the fabric: part may be served by the Infinity Cache)",
+        f"fetch_kib_per_dispatch = {fkib:.1f}",
+        f"write_kib_per_dispatch = {wkib:.1f}",
+        f"copy_fetch_kib = {cf:.1f}",
+        f"copy_write_kib = {cw:.1f}",
+        f"fetch_scale = {fs:.4f}",
+        f"write_scale = {ws:.4f}",
+        f"fetch_bytes_per_launch = {fb}",
+        f"write_bytes_per_launch = {wb}",
+        f"hbm_bytes_per_launch = {fb + wb}",
+        f"dispatches_sampled = {n}",
+        f"kernel_source_sha256_16 = {kernel_source_hash()}",
+    ]
+    return "\n".join(lines)
+
+
 def copy_probe(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -209,11 +274,17 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
+SPIN_CYCLES = 10_000_000  # GPU clock cycles of the spin kernel ahead of a timed replay
+
+
 def graph_times_ms(fn, n: int, warmup: int, batches: int):
     """fn(i) enqueues one unit of work.  Captures n units in a HIP graph,
     replays it once untimed, then once timed (the primary figure) and
     `batches` more times; returns (primary ms per unit, [ms per unit of each
-    batch])."""
+    batch]).  Between the synchronize that opens the timed region and its
+    start event the stream runs a spin kernel of a few milliseconds, so that
+    the timed replay starts on a busy GPU at its working clock (after an idle
+    synchronize the first milliseconds of a replay otherwise run slower)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -225,6 +296,7 @@ def graph_times_ms(fn, n: int, warmup: int, batches: int):
     graph.replay()  # first-touch costs of the graph
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 2)]
+    torch.cuda._sleep(SPIN_CYCLES)
     ev[0].record()
     graph.replay()
     ev[1].record()
@@ -239,13 +311,15 @@ def graph_times_ms(fn, n: int, warmup: int, batches: int):
 
 
 def eager_times_ms(fn, n: int, warmup: int):
-    """Average ms per call of n eager launches of fn between two events (for
-    vendor kernels long enough that launch latency is hidden)."""
+    """Average ms per call of n eager launches of fn between two events.  A
+    spin kernel ahead of the start event holds the stream while the host
+    enqueues the n launches, so host launch latency is not timed."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES)
     e0.record()
     for _ in range(n):
         fn()
@@ -375,6 +449,13 @@ def baselines(steps: int):
     out["copy_256MiB_us"] = round(copy_ms * 1e3, 1)
     out["copy_gbs_read_plus_write"] = round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)
     del src, dst
+    # a plain streaming read of the decode weight stream's size (12288 x 3072
+    # INT4 codes, 18.9 MB): a row-wise integer sum that writes 18 KB
+    rd = torch.ones(12288 * 3072 // 8, dtype=torch.int32, device="cuda").view(4608, 1024)
+    read_ms = eager_times_ms(lambda: rd.sum(dim=1, dtype=torch.int32), 50, 5)
+    out["stream_read_18.9MB_us"] = round(read_ms * 1e3, 2)
+    out["stream_read_gbs"] = round(rd.numel() * 4 / (read_ms * 1e-3) / 1e9, 1)
+    del rd
     M, K, N = 1536, 3072, 9216
     a = torch.randint(-7, 8, (M, K), dtype=torch.int8, device="cuda")
     b = torch.randint(-7, 8, (K, N), dtype=torch.int8, device="cuda")
@@ -405,6 +486,10 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
     ap.add_argument("--summarize-profile", metavar="DB", help="print per-kernel statistics of a rocprofv3 "
                     "results database and exit (no GPU needed)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="print the HBM traffic summary of --workload's dominant kernel from four rocprofv3 "
+                    "counter databases and exit (no GPU needed)")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the floor and vendor baselines")
     ap.add_argument("--path", choices=("w4a4", "w4a16"), default="w4a4",
                     help="w4a16: weight-only INT4 with bf16 rotated activations (M <= 32)")
     ap.add_argument("--rotation", choices=("sylvester", "regular"), default="sylvester",
@@ -413,6 +498,9 @@ def main():
 
     if args.summarize_profile:
         print(summarize_profile(args.summarize_profile))
+        return
+    if args.write_traffic:
+        print(traffic_summary(args.workload, *args.write_traffic))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -444,7 +532,7 @@ def main():
                 continue
             per_config[name] = measure(name, min(args.steps, 100), args.warmup, args.cold_bytes)
             log(f"{name}: {per_config[name]['median_ms'] * 1e3:.2f} us/step (median)")
-    base = baselines(min(args.steps, 100))
+    base = None if args.no_baselines else baselines(min(args.steps, 100))
     cpu = None
     single = None
     if not args.no_cpu_baseline:

@@ -4,26 +4,32 @@ For each workload, runs ``convrot_linear`` on the GPU with the Sylvester and
 with the regular Hadamard rotation, and compares Y with the dense
 Y_ref = X W^T + bias (binary64, from the bf16 inputs) on a sample of rows.
 As a point of reference it also reports rowwise absmax INT4 quantization of
-X and W without any rotation (computed here with numpy, same rounding rule:
-codes clamp(rint(v / s), -7, 7), s = absmax / 7).
+X and W without any rotation, quantized by the oracle's quantizer (the same
+rule: s = absmax / 7, codes clamp(rint(v / s), -7, 7)).  A measurement
+script beside the tests (it reads the oracle, so it stays out of the
+package).
 
-Usage: python -m w4a4_rotated_bit_amd.quant_error [workload ...]
+Usage: python tests/quant_error.py [workload ...]
 Prints one JSON line per workload.
 """
 from __future__ import annotations
 
 import json
+import os
 import sys
 
 import numpy as np
 
-from . import binding, synth
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import oracle  # noqa: E402
+from w4a4_rotated_bit_amd import binding, synth  # noqa: E402
 
 
 def _rowwise_int4(a: np.ndarray):
-    s = np.abs(a).max(axis=1, keepdims=True) / 7.0
-    s[s == 0] = 1.0
-    return np.clip(np.rint(a / s), -7, 7), s
+    """Rowwise absmax INT4 codes and scales of binary32 rows, by the oracle."""
+    q, s = oracle.quantize_rows(a.astype(np.float32))
+    return q.astype(np.float64), s.astype(np.float64)[:, None]
 
 
 def _errors(y: np.ndarray, ref: np.ndarray) -> dict:
