@@ -274,17 +274,17 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
-SPIN_CYCLES = 10_000_000  # GPU clock cycles of the spin kernel ahead of a timed replay
+SPIN_CYCLES = 10_000_000  # GPU clock cycles of the spin kernel ahead of timed eager launches
 
 
 def graph_times_ms(fn, n: int, warmup: int, batches: int):
     """fn(i) enqueues one unit of work.  Captures n units in a HIP graph,
     replays it once untimed, then once timed (the primary figure) and
     `batches` more times; returns (primary ms per unit, [ms per unit of each
-    batch]).  Between the synchronize that opens the timed region and its
-    start event the stream runs a spin kernel of a few milliseconds, so that
-    the timed replay starts on a busy GPU at its working clock (after an idle
-    synchronize the first milliseconds of a replay otherwise run slower)."""
+    batch]).  The primary replay starts right after a synchronize, on a GPU
+    that has just gone idle: on the compute-bound shapes its first
+    milliseconds run at a lower clock, so it is several percent slower than
+    the back-to-back batches that follow (both are reported)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -296,7 +296,6 @@ def graph_times_ms(fn, n: int, warmup: int, batches: int):
     graph.replay()  # first-touch costs of the graph
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 2)]
-    torch.cuda._sleep(SPIN_CYCLES)
     ev[0].record()
     graph.replay()
     ev[1].record()
