@@ -434,9 +434,10 @@ def measure(name: str, steps: int, warmup: int, cold_bytes: float, rotation: str
 
 
 def baselines(steps: int):
-    """Empty-dispatch floor, a plain device copy, and at the QKV shape the
-    vendor INT8 GEMM (int8 operands, int32 out, no rotation, quantization or
-    epilogue) and the dense bf16 linear."""
+    """Empty-dispatch floor, a plain device copy, a plain streaming read of
+    the decode weight size, the matrix-core rate of an MFMA-only loop (FP6
+    and INT8), and at the QKV shape the vendor INT8 GEMM (int8 operands, int32
+    out, no rotation, quantization or epilogue) and the dense bf16 linear."""
     import torch
     out = {}
     empty_ms, _ = graph_times_ms(lambda i: torch.cuda._sleep(0), steps, 5, 1)
@@ -455,6 +456,15 @@ def baselines(steps: int):
     out["stream_read_18.9MB_us"] = round(read_ms * 1e3, 2)
     out["stream_read_gbs"] = round(rd.numel() * 4 / (read_ms * 1e-3) / 1e9, 1)
     del rd
+    # the MFMA-only loop of the library's probe: the rate the matrix cores
+    # sustain here (the practical denominator beside the published peak)
+    from w4a4_rotated_bit_amd import binding
+    for label, kind in (("fp6", binding.CONVROT_PROBE_FP6), ("int8", binding.CONVROT_PROBE_INT8)):
+        count, buf = binding.convrot_matrix_core_probe(kind, 100)
+        ms = eager_times_ms(lambda: binding.convrot_matrix_core_probe(kind, 4000, out=buf), 3, 1)
+        count, _ = binding.convrot_matrix_core_probe(kind, 4000, out=buf)
+        out[f"{label}_mfma_loop_tops"] = round(count * binding.PROBE_OPS_PER_MFMA[kind] / (ms * 1e-3) / 1e12, 1)
+    torch.cuda.synchronize()
     M, K, N = 1536, 3072, 9216
     a = torch.randint(-7, 8, (M, K), dtype=torch.int8, device="cuda")
     b = torch.randint(-7, 8, (K, N), dtype=torch.int8, device="cuda")
@@ -475,7 +485,10 @@ def baselines(steps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    # 1000 steps: long enough that the primary replay's start, on a GPU that
+    # has just idled, is a small part of it (at 200 steps it was 2-11% slower
+    # than the back-to-back batches on the compute-bound shapes)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="headline workload (name, optionally +int4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -529,7 +542,7 @@ def main():
         for name in PER_CONFIG:
             if name == args.workload:
                 continue
-            per_config[name] = measure(name, min(args.steps, 100), args.warmup, args.cold_bytes)
+            per_config[name] = measure(name, min(args.steps, 500), args.warmup, args.cold_bytes)
             log(f"{name}: {per_config[name]['median_ms'] * 1e3:.2f} us/step (median)")
     base = None if args.no_baselines else baselines(min(args.steps, 100))
     cpu = None

@@ -323,6 +323,25 @@ int convrot_gemm_i32_tiled(const int8_t* qx_dev, int64_t M, int64_t K, const voi
 int convrot_split_k_extent(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits,
                            size_t* partial_end_host, int* counters_used_host, size_t* lds_end_host);
 
+/* ---- measurement hook ---------------------------------------------------- */
+/* The rate the matrix cores sustain on an MFMA-only loop -- operands in
+ * registers, no memory traffic, two waves per SIMD as in the block tiles --
+ * the practical denominator beside the published dense peak (under sustained
+ * matrix-core load the clock stays below the peak figure's 2.4 GHz).  kind:
+ * CONVROT_PROBE_FP6 (32x32x64 MFMA on FP6 e2m3 operands, 131072 ops each) or
+ * CONVROT_PROBE_INT8 (32x32x32 INT8, 65536 ops each).  Each wave runs
+ * `iterations` (1 .. 2^24) rounds of four independent MFMAs; out_dev receives
+ * one float per thread (a checksum; its value carries no meaning) and must
+ * hold *bytes from convrot_matrix_core_probe_bytes; *mfma_count_host = the
+ * MFMA instructions the launch runs.  The caller times the launch on its
+ * stream.  CONVROT_EINVAL for a bad kind, count or pointer, CONVROT_EWORKSPACE
+ * for a short buffer. */
+#define CONVROT_PROBE_FP6 1
+#define CONVROT_PROBE_INT8 2
+int convrot_matrix_core_probe_bytes(size_t* bytes_host);
+int convrot_matrix_core_probe(int kind, int iterations, float* out_dev, size_t out_bytes, int64_t* mfma_count_host,
+                              void* stream);
+
 /* ---- host layout tools (host memory, no HIP call) ----------------------- */
 
 /* int8 codes [N][K] <-> N x packed-K uint8 [N][K/2] (low nibble = even k). */

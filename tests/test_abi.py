@@ -43,6 +43,24 @@ def test_regular_flag_matches_header():
     assert m and int(m.group(1), 16) == B.CONVROT_REGULAR_HADAMARD
 
 
+def test_matrix_core_probe_constants_and_argument_checks():
+    """The probe kinds match the header, and bad arguments are refused before
+    any device call (so the check runs without a GPU)."""
+    import ctypes
+    text = open(HEADER).read()
+    for name in ("CONVROT_PROBE_FP6", "CONVROT_PROBE_INT8"):
+        m = re.search(rf"#define\s+{name}\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name)
+    lib = B.load()
+    count = ctypes.c_int64(0)
+    buf = ctypes.create_string_buffer(16)
+    for kind, iters in ((0, 10), (3, 10), (B.CONVROT_PROBE_FP6, 0), (B.CONVROT_PROBE_INT8, (1 << 24) + 1)):
+        rc = lib.convrot_matrix_core_probe(kind, iters, ctypes.cast(buf, ctypes.c_void_p), 16, ctypes.byref(count), None)
+        assert rc == B.CONVROT_EINVAL, (kind, iters, rc)
+    assert lib.convrot_matrix_core_probe(1, 10, None, 16, ctypes.byref(count), None) == B.CONVROT_EINVAL
+    assert lib.convrot_matrix_core_probe(1, 10, ctypes.cast(buf, ctypes.c_void_p), 16, None, None) == B.CONVROT_EINVAL
+
+
 def test_image_flag_status_word_and_test_flag_match_header():
     text = open(HEADER).read()
     m = re.search(r"#define\s+CONVROT_INT4_IMAGE\s+(0x[0-9a-fA-F]+)", text)

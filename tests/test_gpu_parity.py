@@ -480,6 +480,20 @@ def test_single_kernel_paths_match_two_kernel_paths(gpu, K, N, g):
     assert np.array_equal(_w16_rows(ws4, 4, Kr), _w16_rows(ws5, 5, Kr)[:4])
 
 
+@pytest.mark.parametrize("kind", [1, 2])
+def test_matrix_core_probe_runs(gpu, kind):
+    """The measurement hook: the MFMA count it reports follows its launch
+    shape (two four-wave workgroups per CU), and it ends normally."""
+    import torch
+    count, out = gpu.convrot_matrix_core_probe(kind, 8)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert count == 2 * cus * 4 * 8 * 4
+    assert out.numel() == 2 * cus * 256
+    with pytest.raises(gpu.ConvRotError):
+        gpu.convrot_matrix_core_probe(kind, 8, out=out[:16])
+
+
 FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_mlp_down_m1536_k12288_n3072",
         "decode_m1_k3072_n12288", "decode_m4_k3072_n12288", "decode_m16_k3072_n12288", "stress_m4096_k3072_n3072"]
 

@@ -86,6 +86,8 @@ _SIGNATURES = {
     "convrot_gemm_i32_tiled": ([_P, _I64, _I64, _P, _I64, _P, _I, _I, _I, _I, _P, _SZ, _P], _I),
     "convrot_split_k_extent": ([_I64, _I64, _I64, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_I),
                                 ctypes.POINTER(_SZ)], _I),
+    "convrot_matrix_core_probe_bytes": ([ctypes.POINTER(_SZ)], _I),
+    "convrot_matrix_core_probe": ([_I, _I, _P, _SZ, ctypes.POINTER(_I64), _P], _I),
     "convrot_host_pack_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_unpack_nk": ([_P, _I64, _I64, _P], _I),
     "convrot_host_nk_to_kn": ([_P, _I64, _I64, _P], _I),
@@ -349,6 +351,25 @@ def convrot_split_k_extent(M: int, K: int, N: int, tile, splits: int) -> dict:
     _call("convrot_split_k_extent", M, K, N, tile[0], tile[1], splits, ctypes.byref(pe), ctypes.byref(cu),
           ctypes.byref(le))
     return {"partial_end": pe.value, "counters_used": cu.value, "lds_end": le.value}
+
+
+CONVROT_PROBE_FP6 = 1
+CONVROT_PROBE_INT8 = 2
+PROBE_OPS_PER_MFMA = {CONVROT_PROBE_FP6: 2 * 32 * 32 * 64, CONVROT_PROBE_INT8: 2 * 32 * 32 * 32}
+
+
+def convrot_matrix_core_probe(kind: int, iterations: int, out=None, stream=None):
+    """Enqueue the MFMA-only rate loop; returns (MFMA instructions it runs, out).
+    The caller times it on the stream."""
+    import torch
+    if out is None:
+        nbytes = _SZ(0)
+        _call("convrot_matrix_core_probe_bytes", ctypes.byref(nbytes))
+        out = torch.empty(nbytes.value // 4, dtype=torch.float32, device="cuda")
+    count = _I64(0)
+    _call("convrot_matrix_core_probe", kind, iterations, _dev(out, torch.float32, "out"), out.numel() * 4,
+          ctypes.byref(count), _stream(stream))
+    return count.value, out
 
 
 def workspace_status(workspace) -> int:

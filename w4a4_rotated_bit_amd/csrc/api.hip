@@ -194,6 +194,31 @@ int convrot_quantize_weight(const void* W, int64_t N, int64_t K, int g, uint8_t*
     return launched();
 }
 
+static_assert(CONVROT_PROBE_FP6 == kProbeFp6 && CONVROT_PROBE_INT8 == kProbeInt8, "probe kinds of the header");
+
+int convrot_matrix_core_probe_bytes(size_t* bytes_host)
+{
+    if (!bytes_host) return CONVROT_EINVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    *bytes_host = (size_t)probe_grid() * kProbeThreads * sizeof(float);
+    return CONVROT_OK;
+}
+
+int convrot_matrix_core_probe(int kind, int iterations, float* out, size_t out_bytes, int64_t* mfma_count_host,
+                              void* stream)
+{
+    if ((kind != kProbeFp6 && kind != kProbeInt8) || iterations < 1 || iterations > (1 << 24) || !mfma_count_host ||
+        !out || !aligned(out, 4))
+        return CONVROT_EINVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    if (out_bytes < (size_t)probe_grid() * kProbeThreads * sizeof(float)) return CONVROT_EWORKSPACE;
+    *mfma_count_host = probe_grid() * (kProbeThreads / 64) * (int64_t)iterations * 4;
+    launch_mfma_probe(kind, iterations, out, as_stream(stream));
+    return launched();
+}
+
 int convrot_repack_nk_to_image(const uint8_t* qweight_nk, int64_t N, int64_t K, int g, void* image, void* stream)
 {
     int rc = check_shape(N, K, g);

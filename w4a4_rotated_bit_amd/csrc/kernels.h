@@ -62,4 +62,11 @@ void launch_act_relayout(const int8_t* codes, int64_t M, int64_t K, uint8_t* ima
                          int zero_count, hipStream_t s);
 void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, uint8_t* image6, hipStream_t s);
 
+// Matrix-core rate probe: kind kProbeFp6 (32x32x64 FP6 e2m3) or kProbeInt8
+// (32x32x32 INT8); probe_grid() workgroups of kProbeThreads threads, each
+// wave running iters x 4 MFMAs; out holds one float per thread.
+constexpr int kProbeFp6 = 1, kProbeInt8 = 2, kProbeThreads = 256;
+int64_t probe_grid();
+void launch_mfma_probe(int kind, int iters, float* out, hipStream_t s);
+
 }  // namespace convrot

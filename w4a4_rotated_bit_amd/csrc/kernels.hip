@@ -2646,4 +2646,62 @@ void launch_repack_nk(const uint8_t* nk, int64_t N, int64_t K, uint8_t* image, u
                        image, image6);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core rate probe (a measurement hook): each wave runs `iters` rounds
+// of four independent MFMA chains on operands held in registers -- no memory
+// traffic in the loop -- and stores one value per lane at the end.  Two
+// workgroups of four waves per CU: two waves per SIMD, as the block tiles.
+// The rate it reaches is the practical denominator beside the published peak
+// (the clock under sustained matrix-core load is below the 2.4 GHz of the
+// peak figure).
+// ---------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(kProbeThreads) void mfma_rate_kernel(float* out, int iters, int seed)
+{
+    const int lane = threadIdx.x & 63;
+    v8i a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = seed * (lane + i);
+        b[i] = seed ^ (lane * 3 + i);
+    }
+    v16f acc[4];
+    v16i iacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[t][r] = 0.0f;
+            iacc[t][r] = 0;
+        }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (KIND == kProbeFp6) {
+                acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[t], 2, 2, 0, 127, 0, 127);
+            } else {
+                const v4i a4 = {a[0], a[1], a[2], a[3]}, b4 = {b[0], b[1], b[2], b[3]};
+                iacc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a4, b4, iacc[t], 0, 0, 0);
+            }
+        }
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[t][r] + (float)iacc[t][r];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+int64_t probe_grid() { return 2 * (int64_t)device_cus(); }
+
+void launch_mfma_probe(int kind, int iters, float* out, hipStream_t s)
+{
+    const dim3 grid((unsigned)probe_grid()), block(kProbeThreads);
+    if (kind == kProbeFp6)
+        hipLaunchKernelGGL((mfma_rate_kernel<kProbeFp6>), grid, block, 0, s, out, iters, 3);
+    else
+        hipLaunchKernelGGL((mfma_rate_kernel<kProbeInt8>), grid, block, 0, s, out, iters, 3);
+}
+
 }  // namespace convrot
