@@ -14,6 +14,22 @@ TIE_BAND = 1e-4
 MISMATCH_FRACTION = 1e-5
 
 
+def w16_word_index(M: int, Kr: int) -> np.ndarray:
+    """Index of the 16-byte word (8 bf16 values) holding rotated values
+    k .. k + 7 of row m in a W4A16 workspace, as [M][Kr / 8], by the layout
+    include/convrot.h states for it: words ordered by 16-row block, 128-K
+    unit, step j, quarter q, row.  The GPU tests read the kernel's output
+    through it (so a kernel that wrote elsewhere would fail them) and a CPU
+    test checks that it is one-to-one inside the size the query returns."""
+    KB = -(-Kr // 128)
+    m = np.arange(M)[:, None]
+    k = np.arange(0, Kr, 8)[None, :]
+    kl = k % 128
+    j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1)
+    q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1)
+    return ((((m // 16) * KB + k // 128) * 4 + j) * 4 + q) * 16 + m % 16
+
+
 def bf16_to_f64(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

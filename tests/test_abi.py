@@ -13,6 +13,8 @@ import pytest
 import oracle
 from w4a4_rotated_bit_amd import binding as B
 
+from ._parity import w16_word_index
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "convrot.h")
 
@@ -307,13 +309,7 @@ def test_w4a16_row_layout_fits_the_workspace():
     inside the size the query returns, for ragged M and for K_rot % 128 == 64."""
     for M, K, g in [(1, 3072, 256), (5, 192, 64), (17, 1000, 256), (32, 2048, 256), (31, 4160, 64)]:
         Kr = -(-K // g) * g
-        KB = -(-Kr // 128)
-        m = np.arange(M)[:, None]
-        k = np.arange(0, Kr, 8)[None, :]
-        kl = k % 128
-        j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1)
-        q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1)
-        w = ((((m // 16) * KB + k // 128) * 4 + j) * 4 + q) * 16 + m % 16
+        w = w16_word_index(M, Kr)   # the decoder the GPU parity tests read the kernel's rows with
         assert len(np.unique(w)) == w.size, (M, K, g)
         assert w.max() * 16 + 16 <= B.convrot_w4a16_workspace_bytes(M, K, g), (M, K, g)
 

@@ -14,7 +14,7 @@ import pytest
 import oracle
 from w4a4_rotated_bit_amd import synth
 
-from ._parity import compare_codes, compare_rotated, compare_y
+from ._parity import compare_codes, compare_rotated, compare_y, w16_word_index
 
 pytestmark = pytest.mark.gpu
 
@@ -32,14 +32,7 @@ def _w16_rows(ws, M, Kr):
     layout that include/convrot.h states for it (16-byte words in the order
     of 16-row blocks, 128-K units, steps j, quarters q, rows)."""
     words = ws.cpu().numpy().view(np.uint16).reshape(-1, 8)
-    KB = -(-Kr // 128)
-    m = np.arange(M)[:, None]
-    k = np.arange(0, Kr, 8)[None, :]
-    kl = k % 128
-    j = 2 * ((kl >> 5) & 1) + ((kl >> 3) & 1)
-    q = 2 * ((kl >> 6) & 1) + ((kl >> 4) & 1)
-    w = ((((m // 16) * KB + k // 128) * 4 + j) * 4 + q) * 16 + m % 16
-    return words[w].reshape(M, Kr)
+    return words[w16_word_index(M, Kr)].reshape(M, Kr)
 
 
 def _host_bits(t):
