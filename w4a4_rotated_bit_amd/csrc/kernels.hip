@@ -772,14 +772,16 @@ __device__ __forceinline__ void team_row(const PrepArgs& a, uint4 (&w)[PrepShape
     }
 }
 
+constexpr int kOneRowWavesPerSimd = 6;
 // Occupancy targets of the team kernel: as prep_kernel's, one wave fewer
 // for the g = 256 instance that writes both images (weights), which spills
 // at five.
-template <int G, bool REG, bool BOTH>
-constexpr int kPrepTeamWavesPerSimd = (G == 256 && BOTH && !REG) ? 4 : kPrepWavesPerSimd<G, REG>;
+template <int G, bool REG, bool BOTH, bool ONE_ROW>
+constexpr int kPrepTeamWavesPerSimd =
+    ONE_ROW ? kOneRowWavesPerSimd : ((G == 256 && BOTH && !REG) ? 4 : kPrepWavesPerSimd<G, REG>);
 
-template <int G, bool REG, bool OUT4, bool OUT6>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepTeamWavesPerSimd<G, REG, OUT4 && OUT6>))) void
+template <int G, bool REG, bool OUT4, bool OUT6, bool ONE_ROW>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepTeamWavesPerSimd<G, REG, OUT4 && OUT6, ONE_ROW>))) void
 prep_team_kernel(PrepArgs a)
 {
     using S = PrepShape<G>;
@@ -802,6 +804,14 @@ prep_team_kernel(PrepArgs a)
     // FP6: unit kb, block ks (swizzled at the store), in-block byte 6 P / 8 (kl % 32 / P)
     const uint32_t off6 = (kb * kUnit6Bytes) << 7 | (ks << 5) | ((6 * P / 8) * ((kl % 32) / P));
     double* ld = (double*)(prep_lds + wave * S::kWaveLdsBytes);
+    if constexpr (ONE_ROW) {
+        // every row has a workgroup of its own: no next row to prefetch
+        const int64_t row = blockIdx.x;
+        uint4 w[P / 8];
+        team_load<P>(a, row, k0, w);
+        team_row<G, REG, OUT4, OUT6>(a, w, row, k0, off4, off6, lane, wave, nw, ld, red, 0);
+        return;
+    }
     int64_t row = blockIdx.x;
     const int64_t step = gridDim.x;
     uint4 wa[P / 8], wb[P / 8];
@@ -2444,21 +2454,34 @@ static int resident_per_cu(KernelPtr kernel, int block, size_t lds, std::atomic<
     return per_cu;
 }
 
-template <int G, bool REG, bool OUT4, bool OUT6>
-static void launch_prep_team(const PrepArgs& a, int team, hipStream_t s)
+template <int G, bool REG, bool OUT4, bool OUT6, bool ONE_ROW>
+static int prep_team_resident(int team, size_t lds)
 {
-    const size_t lds = (size_t)(team / 64) * PrepShape<G>::kWaveLdsBytes;
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)&prep_team_kernel<G, REG, OUT4, OUT6>,
+        (void)hipFuncSetAttribute((const void*)&prep_team_kernel<G, REG, OUT4, OUT6, ONE_ROW>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * PrepShape<G>::kWaveLdsBytes);
         attr_set = true;
     }
     static std::atomic<int> cache[17];
-    const int per_cu = resident_per_cu(&prep_team_kernel<G, REG, OUT4, OUT6>, team, lds, cache);
-    const int64_t resident = (int64_t)device_cus() * per_cu;
+    return device_cus() * resident_per_cu(&prep_team_kernel<G, REG, OUT4, OUT6, ONE_ROW>, team, lds, cache);
+}
+
+// When the resident grid of the one-row instance covers every row, each row
+// gets a workgroup of its own (no prefetch registers, more waves per SIMD);
+// otherwise one resident grid's worth of workgroups walks the rows.
+template <int G, bool REG, bool OUT4, bool OUT6>
+static void launch_prep_team(const PrepArgs& a, int team, hipStream_t s)
+{
+    const size_t lds = (size_t)(team / 64) * PrepShape<G>::kWaveLdsBytes;
+    if (a.rows_pad <= prep_team_resident<G, REG, OUT4, OUT6, true>(team, lds)) {
+        hipLaunchKernelGGL((prep_team_kernel<G, REG, OUT4, OUT6, true>), dim3((unsigned)a.rows_pad), dim3(team), lds,
+                           s, a);
+        return;
+    }
+    const int64_t resident = prep_team_resident<G, REG, OUT4, OUT6, false>(team, lds);
     const unsigned grid = (unsigned)(a.rows_pad < resident ? a.rows_pad : resident);
-    hipLaunchKernelGGL((prep_team_kernel<G, REG, OUT4, OUT6>), dim3(grid), dim3(team), lds, s, a);
+    hipLaunchKernelGGL((prep_team_kernel<G, REG, OUT4, OUT6, false>), dim3(grid), dim3(team), lds, s, a);
 }
 
 template <int G, bool REG>
