@@ -562,7 +562,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepWaves
 // fused multiply-add and keeps prep_row's near-tie fallback to the IEEE
 // division; the FP6 fields reuse the rounded codes.  OUT4 / OUT6: write the
 // INT4 image / the FP6 image (a linear whose plan reads only one of them
-// writes only that one).
+// writes only that one).  ONE_ROW: the grid has a workgroup for every row
+// (launched so when the resident grid covers all rows), so there is no row
+// loop at all.
 // ---------------------------------------------------------------------------
 
 // clamp(rint(fl32(r / s)), -7, 7) for P values, as the bit patterns f of
@@ -772,13 +774,14 @@ __device__ __forceinline__ void team_row(const PrepArgs& a, uint4 (&w)[PrepShape
     }
 }
 
-constexpr int kOneRowWavesPerSimd = 6;
-// Occupancy targets of the team kernel: as prep_kernel's, one wave fewer
-// for the g = 256 instance that writes both images (weights), which spills
-// at five.
+// Occupancy target of the team kernel: six waves per SIMD (every instance
+// stays within 80 VGPRs without spilling, 55-78 in practice), so that two
+// 12-wave workgroups of a 12288-value row fit on a CU.  Against the
+// previous loop, which prefetched the next row into a second register
+// buffer at 85-100 VGPRs and five waves: down-projection rows (12288 values)
+// 22.2 -> 19.6 us, the 4096-row stress shape 15.0 -> 13.8 us.
 template <int G, bool REG, bool BOTH, bool ONE_ROW>
-constexpr int kPrepTeamWavesPerSimd =
-    ONE_ROW ? kOneRowWavesPerSimd : ((G == 256 && BOTH && !REG) ? 4 : kPrepWavesPerSimd<G, REG>);
+constexpr int kPrepTeamWavesPerSimd = 6;
 
 template <int G, bool REG, bool OUT4, bool OUT6, bool ONE_ROW>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kPrepTeamWavesPerSimd<G, REG, OUT4 && OUT6, ONE_ROW>))) void
@@ -812,20 +815,16 @@ prep_team_kernel(PrepArgs a)
         team_row<G, REG, OUT4, OUT6>(a, w, row, k0, off4, off6, lane, wave, nw, ld, red, 0);
         return;
     }
-    int64_t row = blockIdx.x;
-    const int64_t step = gridDim.x;
-    uint4 wa[P / 8], wb[P / 8];
-    team_load<P>(a, row, k0, wa);
-    for (int parity = 0; row < a.rows_pad; parity ^= 1) {
-        const int64_t nx = row + step;
-        if (parity == 0) {
-            team_load<P>(a, nx, k0, wb);
-            team_row<G, REG, OUT4, OUT6>(a, wa, row, k0, off4, off6, lane, wave, nw, ld, red, 0);
-        } else {
-            team_load<P>(a, nx, k0, wa);
-            team_row<G, REG, OUT4, OUT6>(a, wb, row, k0, off4, off6, lane, wave, nw, ld, red, 1);
-        }
-        row = nx;
+    // rows with a stride of the grid; a row's load is not overlapped with the
+    // previous row inside the workgroup (a prefetch buffer cost 25-35 VGPRs
+    // and halved the workgroups per CU): other workgroups on the CU fill the
+    // wait
+    int parity = 0;
+    for (int64_t row = blockIdx.x; row < a.rows_pad; row += gridDim.x) {
+        uint4 w[P / 8];
+        team_load<P>(a, row, k0, w);
+        team_row<G, REG, OUT4, OUT6>(a, w, row, k0, off4, off6, lane, wave, nw, ld, red, parity);
+        parity ^= 1;
     }
 }
 
