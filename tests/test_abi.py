@@ -193,10 +193,11 @@ def test_split_k_exchange_stays_inside_its_workspace(M, K, N, tile, splits):
     """Every address of the split-K exchange, enumerated on the host through the
     kernels' own address functions: the partial-tile stores and copies end
     exactly at (S - 1) slots per tile, which is the room the same plan's
-    workspace size sets aside after its other parts; counters and LDS stay in
-    their arrays."""
+    workspace size sets aside after its other parts; the two counters of every
+    (tile, sub-block) stay in the 512 counter words, and the finalizer's
+    copies of a sub-block's pairs stay in the LDS ring."""
     tiles = _ceil(M, tile[0]) * _ceil(N, tile[1])
-    if splits > 1 and tiles > 256:
+    if splits > 1 and tiles * splits > 256:
         with pytest.raises(B.ConvRotError):
             B.convrot_split_k_extent(M, K, N, tile, splits)
         return
@@ -206,8 +207,12 @@ def test_split_k_exchange_stays_inside_its_workspace(M, K, N, tile, splits):
     ws = B.convrot_workspace_bytes_tiled(M, K, N, tile, splits)
     assert ws - B.convrot_workspace_bytes_tiled(M, K, N, tile, 1) == ext["partial_end"]
     if splits > 1:
-        assert ext["counters_used"] == 256 + tiles <= 512
-        assert ext["lds_end"] == slot // 2 <= _RING[tile]
+        assert ext["counters_used"] == 256 + tiles * splits <= 512
+        threads = 256 if tile == (192, 192) else 512
+        pair = 64 * threads                      # one MFMA tile's sums of every thread
+        pairs = slot // pair                     # MFMA tiles per wave
+        most = -(-pairs // splits)               # pairs of the largest sub-block
+        assert ext["lds_end"] == min(most, _RING[tile] // pair) * pair <= _RING[tile]
     else:
         assert ext == {"partial_end": 0, "counters_used": 0, "lds_end": 0}
 

@@ -138,6 +138,9 @@ GemmArgs gemm_args(const void* ws, int64_t M, int64_t K, const void* image, cons
 
 int enqueue_gemm(int out_mode, const GemmArgs& a, hipStream_t s)
 {
+    // the split-K exchange has two counters per (tile, sub-block) in the
+    // workspace's 2 kSplitCounters counter words; every plan stays inside
+    if (a.splits > 1 && (int64_t)a.tiles_m * a.tiles_n * a.splits > kSplitCounters) return CONVROT_EINVAL;
     launch_gemm(out_mode, a, s);
     return launched();
 }

@@ -73,7 +73,7 @@ int check_forced_plan(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, i
     const int64_t KB = round_up(K, kTileK) / kTileK;
     if (splits < 1 || splits > kMaxSplits || splits > KB) return CONVROT_EINVAL;
     const GemmPlan p = gemm_plan_forced(M, N, shape, splits);
-    if (splits > 1 && (int64_t)p.tiles_m * p.tiles_n > kSplitCounters) return CONVROT_EINVAL;
+    if (splits > 1 && (int64_t)p.tiles_m * p.tiles_n * splits > kSplitCounters) return CONVROT_EINVAL;
     *plan = p;
     return CONVROT_OK;
 }
@@ -139,32 +139,39 @@ int convrot_split_k_extent(int64_t M, int64_t K, int64_t N, int tile_m, int tile
     const int shape = p.shape;
     const int tiles = p.tiles_m * p.tiles_n;
     const int threads = gemm_threads(shape), words = split_words_per_thread(shape);
-    const int chunks = (int)(split_slot_bytes(shape) / 2 / 1024);  // 1 KB copies per half slot
+    const int pairs = split_pairs(shape), chunks = split_pair_bytes(shape) / 1024;  // 1 KB copies per pair
     size_t pend = 0, lend = 0;
     int cmax = -1;
     if (splits > 1) {
         // every address the exchange touches, through the kernels' own geometry
         for (int tile = 0; tile < tiles; ++tile) {
-            cmax = tile + kSplitCounters > cmax ? tile + kSplitCounters : cmax;  // tickets[tile], finished[tile]
+            for (int sub = 0; sub < splits; ++sub) {
+                // tickets and finished writers of sub-block `sub`
+                const int c = split_counter(tile, splits, sub) + kSplitCounters;
+                cmax = c > cmax ? c : cmax;
+            }
             for (int ticket = 0; ticket < splits - 1; ++ticket)
                 for (int u = 0; u < words; ++u)
                     for (int t = 0; t < threads; ++t) {
                         const size_t end = split_store_offset(shape, tile, splits, ticket, u, t) + 8;
                         pend = end > pend ? end : pend;
                     }
+            // the finalizer's copies: pair pr of every slot, into ring position
+            // (m mod split_pairs_per_copy) for the m-th pair of its sub-block
             for (int sl = 0; sl < splits - 1; ++sl)
-                for (int half = 0; half < 2; ++half)
+                for (int pr = 0; pr < pairs; ++pr)
                     for (int c = 0; c < chunks; ++c)
                         for (int lane = 0; lane < 64; ++lane) {
-                            const size_t end = split_copy_offset(shape, tile, splits, sl, half, c, lane) + 16;
+                            const size_t end = split_copy_offset(shape, tile, splits, sl, pr, c, lane) + 16;
                             pend = end > pend ? end : pend;
-                            const size_t lds = (size_t)c * 1024 + (size_t)lane * 16 + 16;  // LDS ring offset
+                            const int i = pr % gemm_wave_tiles_m(shape), j = pr / gemm_wave_tiles_m(shape);
+                            const int m = i * gemm_wave_tiles_n(shape) + j -
+                                          split_sub_first(shape, splits, split_sub_of(shape, splits, i, j));
+                            const size_t lds = (size_t)(m % split_pairs_per_copy(shape)) * split_pair_bytes(shape) +
+                                               (size_t)c * 1024 + (size_t)lane * 16 + 16;
                             lend = lds > lend ? lds : lend;
                         }
         }
-        // the finalizer's reads of the ring: word u2 < words / 2 of thread t
-        const size_t reads = ((size_t)(words / 2 - 1) * threads + (threads - 1)) * 8 + 8;
-        lend = reads > lend ? reads : lend;
     }
     *partial_end = pend;
     *counters_used = cmax + 1;

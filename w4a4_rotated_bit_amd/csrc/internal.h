@@ -27,8 +27,8 @@ size_t workspace_bytes_for(int64_t M, int64_t K, bool fp6, const GemmPlan& p);  
 // Words cleared by every activation step: the counters and the status word.
 constexpr int kZeroWords = 2 * kSplitCounters + 1;
 // Checks of a plan given from outside (test hooks): a known block tile, M > 32,
-// 1 <= splits <= min(kMaxSplits, 128-K blocks), at most kSplitCounters tiles
-// when split, and the FP6 tile only with fp6.  Fills *plan.
+// 1 <= splits <= min(kMaxSplits, 128-K blocks), tiles x splits at most
+// kSplitCounters when split, and the FP6 tile only with fp6.  Fills *plan.
 int check_forced_plan(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits, bool fp6, GemmPlan* plan);
 
 }  // namespace convrot

@@ -1037,27 +1037,7 @@ __device__ inline void interleave_mfma_valu(int lds_reads)
 }
 
 // ---------------------------------------------------------------------------
-// Split-K exchange.  Every workgroup of a split tile takes a ticket from the
-// tile's counter.  The first S - 1 ticket holders store their partial tile
-// (4-byte sums) into the slots laid out by split_store_offset (layout.h) with
-// device-coherent stores, wait until the stores have completed, and count
-// themselves finished.  The last ticket holder waits until S - 1 writers have
-// finished -- each of them already holds a ticket, so it is running and
-// finishes without waiting on anyone -- then pulls each slot into LDS half by
-// half with device-coherent global -> LDS copies (all in flight at once), adds
-// it to its own tile (exact integer sums, any order) and goes on to the
-// epilogue; it also returns both counters to zero for the next launch.
-// The wait is bounded (a.spin_limit sleeps).  If it runs out, the finalizer
-// sets the workspace's status word to kStatusSplitTimeout, adds no slot (their
-// contents are not known to be written), leaves the counters as they are
-// (the next activation step clears them and the status word), and still runs
-// the epilogue, so the kernel ends normally and the caller can see the
-// failure.  a.extra_wait makes the finalizer wait for that many writers more
-// than exist (a test of this path: the wait then always runs out).
-// Device-coherent (agent-scope, sc1) accesses go to the level of the memory
-// system that every compute unit sees, so no cache-wide write-back or
-// invalidation is needed.  Returns true for the workgroup that finishes the
-// tile.
+// Helpers of the split-K exchange (split_k_finish, after the epilogue).
 // ---------------------------------------------------------------------------
 
 // lds_copy16 with a device-coherent global read
@@ -1090,90 +1070,6 @@ struct AccOps<v16f> {
     __device__ static void add(v16f& a, int r, uint32_t w) { a[r] += __uint_as_float(w); }  // exact: integers < 2^24
 };
 
-template <typename G, typename ACC>
-__device__ inline bool split_k_exchange(const GemmArgs& a, int tile, int tid, int wave, int lane, uint32_t lds0,
-                                        const uint8_t* smem, ACC (&acc)[G::BJ][G::BI])
-{
-    constexpr int BI = G::BI, BJ = G::BJ;
-    constexpr int SHAPE = G::SHAPE;
-    constexpr int kThreads = G::NW * 64;
-    constexpr int kWords = BJ * BI * 8;                // 8-byte words per thread
-    constexpr int kHalf = (int)split_slot_bytes(SHAPE) / 2;
-    static_assert(kThreads == gemm_threads(SHAPE) && kWords == split_words_per_thread(SHAPE),
-                  "slot geometry of layout.h");
-    static_assert(kHalf <= G::kLdsBytes, "half a partial tile must fit in LDS");
-    __shared__ int ticket_sh;
-    __shared__ int done_sh;
-    uint32_t* tickets = a.counters + tile;
-    uint32_t* finished = a.counters + kSplitCounters + tile;
-    if (tid == 0) ticket_sh = (int)__hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();  // also: every wave is done with the stage ring
-    const int ticket = ticket_sh;
-    const int S = a.splits;
-    uint8_t* part = (uint8_t*)a.partial;
-    if (ticket < S - 1) {
-#pragma unroll
-        for (int j = 0; j < BJ; ++j)
-#pragma unroll
-            for (int i = 0; i < BI; ++i)
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int u = (j * BI + i) * 8 + q;  // 8-byte word u of this thread: registers 2q, 2q + 1
-                    const uint64_t v = (uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q) |
-                                       ((uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q + 1) << 32);
-                    __hip_atomic_store((uint64_t*)(part + split_store_offset(SHAPE, tile, S, ticket, u, tid)), v,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-        __builtin_amdgcn_s_waitcnt(0);  // every store of this wave has completed
-        __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
-    }
-    if (tid == 0) {
-        // bounded: the writers are running and never wait
-        const uint32_t need = (uint32_t)(S - 1 + a.extra_wait);
-        int done = 0;
-        for (int spin = 0; spin < a.spin_limit; ++spin) {
-            if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) {
-                done = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (done) {
-            __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            __hip_atomic_store(a.status, kStatusSplitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        done_sh = done;
-    }
-    __syncthreads();
-    if (!done_sh) return true;  // flagged in the status word; the epilogue still runs
-    constexpr int kChunksPerWave = kHalf / 1024 / G::NW;  // 1 KB per copy instruction
-    static_assert(kChunksPerWave * 1024 * G::NW == kHalf, "copies divide evenly over the waves");
-    for (int sl = 0; sl < S - 1; ++sl) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int c = 0; c < kChunksPerWave; ++c) {
-                const int chunk = wave * kChunksPerWave + c;
-                lds_copy16_coherent(part + split_copy_offset(SHAPE, tile, S, sl, half, chunk, lane), lds0 + chunk * 1024);
-            }
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-            for (int u2 = 0; u2 < kWords / 2; ++u2) {
-                const int u = half * (kWords / 2) + u2;
-                const int j = u / (BI * 8), i = (u / 8) % BI, q = u % 8;
-                const uint2 w = *(const uint2*)(smem + ((size_t)u2 * kThreads + tid) * 8);
-                AccOps<ACC>::add(acc[j][i], 2 * q, w.x);
-                AccOps<ACC>::add(acc[j][i], 2 * q + 1, w.y);
-            }
-            __syncthreads();  // every read of this half is done before the next copy
-        }
-    }
-    return true;
-}
 
 // 8 when the epilogue staging row r has its 8-byte halves exchanged, else 0
 __device__ inline int half_swap(int r) { return (((r >> 3) ^ (r >> 4)) & 1) * 8; }
@@ -1238,13 +1134,19 @@ __device__ inline void issue_epilogue_params(const GemmArgs& a, int tm, int tn, 
 
 // Epilogue of a block tile: int32 stores (parity hook) or scale + bias to bf16
 // through LDS (every copy has landed and every wave is past its last LDS
-// read of the K loop when this runs).
-template <typename G, int OUT, typename ACC>
+// read of the K loop when this runs).  MASKED: only the MFMA tiles (j, i)
+// whose sub-block split_sub_of(nsub, i, j) has its bit set in `subs` (the
+// sub-blocks of a split-K exchange that this workgroup finished).
+template <typename G, int OUT, bool MASKED = false, typename ACC>
 __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, int wn, int tid, int wave, int lane,
-                                     uint8_t* smem, const float* params, const ACC (&acc)[G::BJ][G::BI])
+                                     uint8_t* smem, const float* params, const ACC (&acc)[G::BJ][G::BI],
+                                     uint32_t subs = ~0u, int nsub = 1)
 {
     constexpr int NW = G::NW, BI = G::BI, BJ = G::BJ, WN = G::WN;
     const int r32 = lane & 31, h = lane >> 5;
+    auto member = [&](int j, int i) __attribute__((always_inline)) {
+        return !MASKED || ((subs >> split_sub_of(G::SHAPE, nsub, i, j)) & 1u) != 0;
+    };
     const int64_t m_base = (int64_t)tm * G::BM + wm * (32 * BI);
     const int64_t n_base = (int64_t)tn * G::BN + wn * WN;
 
@@ -1259,7 +1161,8 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
             const int64_t m = m_base + 32 * i + r32;
             if (m >= a.M) continue;
 #pragma unroll
-            for (int j = 0; j < BJ; ++j)
+            for (int j = 0; j < BJ; ++j) {
+                if (!member(j, i)) continue;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int64_t n0 = n_base + 32 * j + 8 * t + 4 * h;
@@ -1274,6 +1177,7 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
                         for (int u = 0; u < 4 && n0 + u < a.N; ++u) dst[u] = v[u];
                     }
                 }
+            }
         }
     } else {
         // The block's column scales, biases and row scales are in params
@@ -1299,9 +1203,14 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
         const bool vec8 = (a.N % 8) == 0;
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
+            bool any = false;
+#pragma unroll
+            for (int j = 0; j < BJ; ++j) any = any || member(j, i);
+            if (!any) continue;
             const float sxm = p_sx[wm * (32 * BI) + 32 * i + r32];
 #pragma unroll
-            for (int j = 0; j < BJ; ++j)
+            for (int j = 0; j < BJ; ++j) {
+                if (!member(j, i)) continue;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int nl = 32 * j + 8 * t + 4 * h;  // column within the wave tile
@@ -1320,6 +1229,7 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
                     *(uint2*)(tile_lds + r32 * kPitch + ((nl * 2) ^ half_swap(r32))) =
                         make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
                 }
+            }
             // read back row segments: lane l takes the 16-byte chunks l + 64 s
             // of the tile row block (row rho = chunk / kChunks)
 #pragma unroll
@@ -1327,6 +1237,7 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
                 const int idx = lane + 64 * sr;
                 const int rho = idx / kChunks;
                 const int c = idx % kChunks;
+                if (!member(c / 4, i)) continue;  // chunk c: columns 8c .. 8c + 7, in MFMA tile j = c / 4
                 uint4 w = *(const uint4*)(tile_lds + rho * kPitch + c * 16);
                 if (half_swap(rho)) w = make_uint4(w.z, w.w, w.x, w.y);
                 const int64_t m = m_base + 32 * i + rho;
@@ -1344,6 +1255,143 @@ __device__ inline void gemm_epilogue(const GemmArgs& a, int tm, int tn, int wm, 
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K exchange, spread over the S workgroups of a split tile.  The tile's
+// MFMA tiles (j, i) of every wave ("pairs") form S sub-blocks of consecutive
+// pairs in row-major order (split_sub_of, layout.h).  Each workgroup visits the S
+// sub-blocks in turn, starting at its own split index, and takes a ticket
+// from the sub-block's counter (split_counter, layout.h).  The first S - 1
+// ticket holders store their partial sums of the sub-block (4-byte words)
+// into slot `ticket` of the tile (split_store_offset) with device-coherent
+// stores, wait until the stores have completed and count themselves finished.
+// The last ticket holder waits until S - 1 writers have finished -- each of
+// them holds a ticket, so it is running, and between taking a ticket and
+// counting itself finished a workgroup never waits -- then copies the
+// sub-block's pairs of every slot into its LDS ring with device-coherent
+// global -> LDS copies, adds them (exact integer sums, any order) and returns
+// the sub-block's two counters to zero for the next launch.  One epilogue at
+// the end writes the sub-blocks the workgroup finished.  The workgroups of a
+// tile usually reach the
+// exchange together, so with the rotated visiting order each of them
+// finishes one sub-block: a workgroup stores, loads and outputs about 1/S of
+// a tile instead of one workgroup loading S - 1 tiles and writing all of Y
+// (a compute unit moves device-coherent data at only some 20-30 GB/s).
+// The wait is bounded (a.spin_limit sleeps).  If it runs out, the finalizer
+// sets the workspace's status word to kStatusSplitTimeout, adds no slot
+// (their contents are not known to be written), leaves the counters as they
+// are (the next activation step clears them and the status word), and still
+// runs the epilogue, so the kernel ends normally and the caller can see the
+// failure.  a.extra_wait makes a finalizer wait for that many writers more
+// than exist (a test of this path: the wait then always runs out).
+// Device-coherent (agent-scope, sc1) accesses go to the level of the memory
+// system that every compute unit sees, so no cache-wide write-back or
+// invalidation is needed.
+// ---------------------------------------------------------------------------
+template <typename G, int OUT, typename ACC>
+__device__ inline void split_k_finish(const GemmArgs& a, int tile, int split, int tm, int tn, int wm, int wn, int tid,
+                                      int wave, int lane, uint32_t lds0, uint8_t* smem, const float* params,
+                                      ACC (&acc)[G::BJ][G::BI])
+{
+    constexpr int BI = G::BI, BJ = G::BJ;
+    constexpr int SHAPE = G::SHAPE;
+    constexpr int kThreads = G::NW * 64;
+    constexpr int kPairs = BI * BJ;
+    constexpr int kPairBytes = split_pair_bytes(SHAPE);
+    constexpr int kPairChunks = kPairBytes / 1024 / G::NW;  // 1 KB copies per wave and pair
+    constexpr int kRingPairs = split_pairs_per_copy(SHAPE);  // pairs the ring holds at once
+    static_assert(kThreads == gemm_threads(SHAPE) && kPairs * 8 == split_words_per_thread(SHAPE),
+                  "slot geometry of layout.h");
+    static_assert(kPairChunks * 1024 * G::NW == kPairBytes && kRingPairs >= 1, "pair copies fit the ring");
+    static_assert(BI == gemm_wave_tiles_m(SHAPE) && BJ == gemm_wave_tiles_n(SHAPE), "pair geometry of layout.h");
+    __shared__ int ticket_sh;
+    __shared__ int done_sh;
+    const int S = a.splits;
+    uint8_t* part = (uint8_t*)a.partial;
+    uint32_t mine = 0;  // the sub-blocks this workgroup finishes
+    for (int k = 0; k < S; ++k) {
+        const int b = (split + k) % S;
+        uint32_t* tickets = a.counters + split_counter(tile, S, b);
+        uint32_t* finished = tickets + kSplitCounters;
+        if (tid == 0) ticket_sh = (int)__hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();  // on the first visit also: every wave is done with the stage ring
+        const int ticket = ticket_sh;
+        if (ticket < S - 1) {
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) {
+                const int j = p / BI, i = p % BI;
+                if (split_sub_of(SHAPE, S, i, j) != b) continue;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    // 8-byte word 8 p + q of this thread: registers 2q, 2q + 1
+                    const uint64_t v = (uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q) |
+                                       ((uint64_t)AccOps<ACC>::bits(acc[j][i], 2 * q + 1) << 32);
+                    __hip_atomic_store((uint64_t*)(part + split_store_offset(SHAPE, tile, S, ticket, 8 * p + q, tid)), v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // every store of this wave has completed
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            continue;
+        }
+        if (tid == 0) {
+            // bounded: the writers are running and never wait
+            const uint32_t need = (uint32_t)(S - 1 + a.extra_wait);
+            int done = 0;
+            for (int spin = 0; spin < a.spin_limit; ++spin) {
+                if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) {
+                    done = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (done) {
+                __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                __hip_atomic_store(a.status, kStatusSplitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            done_sh = done;
+        }
+        __syncthreads();
+        mine |= 1u << b;
+        if (done_sh) {
+            // the sub-block's pairs are row-major numbers first + m,
+            // m = 0 .. members - 1; the ring takes kRingPairs of them per round
+            const int first = split_sub_first(SHAPE, S, b);
+            const int members = split_sub_first(SHAPE, S, b + 1) - first;
+            for (int sl = 0; sl < S - 1; ++sl)
+                for (int m0 = 0; m0 < members; m0 += kRingPairs) {
+                    const int m1 = min(members, m0 + kRingPairs);
+                    for (int m = m0; m < m1; ++m)
+#pragma unroll
+                        for (int c = 0; c < kPairChunks; ++c) {
+                            const int chunk = wave * kPairChunks + c;
+                            lds_copy16_coherent(
+                                part + split_copy_offset(SHAPE, tile, S, sl, split_pair_of(SHAPE, first + m), chunk, lane),
+                                lds0 + (m - m0) * kPairBytes + chunk * 1024);
+                        }
+                    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+                    for (int p = 0; p < kPairs; ++p) {
+                        const int j = p / BI, i = p % BI;
+                        const int m = i * BJ + j - first;
+                        if (m < m0 || m >= m1) continue;
+                        const uint8_t* src = smem + (m - m0) * kPairBytes;
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const uint2 w = *(const uint2*)(src + ((size_t)q * kThreads + tid) * 8);
+                            AccOps<ACC>::add(acc[j][i], 2 * q, w.x);
+                            AccOps<ACC>::add(acc[j][i], 2 * q + 1, w.y);
+                        }
+                    }
+                    __syncthreads();  // every read of the ring is done before the next copies
+                }
+        }
+    }
+    if (mine) gemm_epilogue<G, OUT, true>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc, mine, S);
 }
 
 // SPLIT: the instance that takes part in a split-K exchange (launched only
@@ -1467,8 +1515,9 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
     if constexpr (SPLIT)
-        if (!split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
-    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
+        split_k_finish<G, OUT>(a, tile, split, tm, tn, wm, wn, tid, wave, lane, lds0, smem, params, acc);
+    else
+        gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1698,8 +1747,9 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
     if constexpr (SPLIT)
-        if (!split_k_exchange<G>(a, tile, tid, wave, lane, lds0, smem, acc)) return;
-    gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
+        split_k_finish<G, OUT>(a, tile, split, tm, tn, wm, wn, tid, wave, lane, lds0, smem, params, acc);
+    else
+        gemm_epilogue<G, OUT>(a, tm, tn, wm, wn, tid, wave, lane, smem, params, acc);
 }
 
 // ---------------------------------------------------------------------------

@@ -203,7 +203,8 @@ CONVROT_HD inline size_t w16_word_offset(int64_t m, int64_t k, int64_t K)
 // activation codes of up to 128 rows read from L2 by every workgroup): at
 // such M the block tiles leave most compute units idle.
 constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an MI355X
-constexpr int kSplitCounters = 256;    // counter slots: a split launch has at most this many tiles
+constexpr int kSplitCounters = 256;    // counter slots: a split launch has at most this many tiles x splits
+static_assert(kSplitTargetWGs <= kSplitCounters, "a plan's tiles x splits fit the counters");
 constexpr int kMaxSplits = 8;
 constexpr int kGemmShapes = 3;
 constexpr int64_t kStreamMaxRows = 128;
@@ -267,14 +268,39 @@ CONVROT_HD inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool fp6)
 }
 
 // ---- split-K exchange geometry -----------------------------------------------
-// The S - 1 first workgroups (tickets) of a split tile each store their partial
-// tile of 4-byte sums into a slot of the workspace's partial area; the last
-// one copies every slot back into its LDS ring, half a slot at a time, and
-// adds it.  Slot (tile, ticket) is slot number tile (S - 1) + ticket; inside
-// it, 8-byte word u of thread t sits at (u threads + t) 8, so that one store
-// instruction of a wave covers 512 contiguous bytes.  The kernels and the
-// host-side footprint check (convrot_split_k_extent) address it through
-// these functions only.
+// The tile's 4-byte sums are exchanged in S sub-blocks.  A wave owns BI x BJ
+// MFMA tiles of 32 x 32 ("pairs"); pair (j, i) has row-major number
+// r = i BJ + j, and sub-block b holds the pairs with r in [first(b),
+// first(b + 1)), first(b) = ceil(b P / S) for P = BI BJ pairs: contiguous
+// runs, so that whole 32-row blocks of Y go to one workgroup where S allows.
+// For each sub-block, the S - 1 first workgroups (tickets) of a split tile
+// store their partial sums of it into slot `ticket` of the tile's partial
+// area; the last one copies the sub-block's part of every slot into its LDS
+// ring, pair by pair, and adds it.  Slot (tile, ticket) is slot number
+// tile (S - 1) + ticket; inside it, 8-byte word u of thread t sits at
+// (u threads + t) 8, so that one store instruction of a wave covers 512
+// contiguous bytes; pair (j, i) holds words 8 p .. 8 p + 7, p = j BI + i, of
+// every thread, one contiguous run.  Sub-block b of tile `tile` has its own
+// two counters (tickets, finished writers): counter words split_counter and
+// split_counter + kSplitCounters.  The kernels and the host-side footprint
+// check (convrot_split_k_extent) address all of this through these functions
+// only.
+CONVROT_HD constexpr int gemm_wave_tiles_m(int shape) { return shape == 2 ? 4 : 3; }  // BI
+CONVROT_HD constexpr int gemm_wave_tiles_n(int shape) { return shape == 2 ? 2 : 3; }  // BJ
+CONVROT_HD constexpr int split_pairs(int shape) { return gemm_wave_tiles_m(shape) * gemm_wave_tiles_n(shape); }
+CONVROT_HD constexpr int split_sub_first(int shape, int splits, int sub)
+{
+    return (sub * split_pairs(shape) + splits - 1) / splits;
+}
+CONVROT_HD constexpr int split_sub_of(int shape, int splits, int i, int j)
+{
+    return (i * gemm_wave_tiles_n(shape) + j) * splits / split_pairs(shape);
+}
+// slot pair index p = j BI + i of row-major pair number r
+CONVROT_HD constexpr int split_pair_of(int shape, int r)
+{
+    return (r % gemm_wave_tiles_n(shape)) * gemm_wave_tiles_m(shape) + r / gemm_wave_tiles_n(shape);
+}
 CONVROT_HD constexpr size_t split_slot_bytes(int shape) { return (size_t)gemm_tile_m(shape) * gemm_tile_n(shape) * 4; }
 CONVROT_HD constexpr int split_words_per_thread(int shape)
 {
@@ -285,12 +311,15 @@ CONVROT_HD inline size_t split_store_offset(int shape, int tile, int splits, int
     return ((size_t)tile * (splits - 1) + ticket) * split_slot_bytes(shape) +
            ((size_t)word * gemm_threads(shape) + thread) * 8;
 }
-// 16-byte piece `lane` of 1 KB chunk `chunk` of half `half` of slot `slot`
-CONVROT_HD inline size_t split_copy_offset(int shape, int tile, int splits, int slot, int half, int chunk, int lane)
+// bytes of one pair's sums in a slot, and how many pairs the LDS ring holds
+CONVROT_HD constexpr int split_pair_bytes(int shape) { return 8 * gemm_threads(shape) * 8; }
+CONVROT_HD constexpr int split_pairs_per_copy(int shape) { return gemm_ring_bytes(shape) / split_pair_bytes(shape); }
+// 16-byte piece `lane` of 1 KB chunk `chunk` of pair `pair` of slot `slot`
+CONVROT_HD inline size_t split_copy_offset(int shape, int tile, int splits, int slot, int pair, int chunk, int lane)
 {
-    return ((size_t)tile * (splits - 1) + slot) * split_slot_bytes(shape) + (size_t)half * (split_slot_bytes(shape) / 2) +
-           (size_t)chunk * 1024 + (size_t)lane * 16;
+    return split_store_offset(shape, tile, splits, slot, 8 * pair, 0) + (size_t)chunk * 1024 + (size_t)lane * 16;
 }
+CONVROT_HD constexpr int split_counter(int tile, int splits, int sub) { return tile * splits + sub; }
 // The workspace's status word (at a fixed offset, cleared by every activation
 // step): kStatusSplitTimeout when a split-K finalizer stopped waiting.
 constexpr uint32_t kStatusSplitTimeout = 1;
