@@ -294,9 +294,10 @@ int convrot_gemm_i32(const int8_t* qx_dev, int64_t M, int64_t K, const void* ima
 
 /* The same with the block-tile plan given instead of the library's choice
  * (M > 32): tile_m x tile_n one of 192 x 384 and 192 x 192 (INT8 matrix
- * cores, INT4 image part) or 256 x 256 (FP6 matrix cores, FP6 image part),
- * and `splits` workgroups sharing each tile's K range (1 .. min(8, K_pad /
- * 128); a split launch may have at most 256 tiles).  Lets a test reach every
+ * cores, INT4 image part), 256 x 256 or 192 x (384 | CONVROT_TILE_FP6) (FP6
+ * matrix cores, FP6 image part), and `splits` workgroups sharing each tile's
+ * K range (1 .. min(8, K_pad / 128); a split launch may have at most 256
+ * tiles x splits).  Lets a test reach every
  * block tile, with and without the split-K exchange, at any shape.  The
  * workspace must hold convrot_workspace_bytes_tiled(M, K, N, tile_m, tile_n,
  * splits) bytes -- sized from the same plan, so the exchange's partial tiles
@@ -305,6 +306,7 @@ int convrot_gemm_i32(const int8_t* qx_dev, int64_t M, int64_t K, const void* ima
  * tiny bound on the wait (it runs out, sets the status word and still ends
  * normally; the test of that report).  CONVROT_EINVAL for any other value. */
 #define CONVROT_TEST_SPLIT_TIMEOUT 1
+#define CONVROT_TILE_FP6 0x10000 /* or-ed into tile_n: the FP6 tile where both kinds have that size */
 int convrot_workspace_bytes_tiled(int64_t M, int64_t K, int64_t N, int tile_m, int tile_n, int splits,
                                   size_t* bytes_host);
 int convrot_gemm_i32_tiled(const int8_t* qx_dev, int64_t M, int64_t K, const void* image_dev, int64_t N,

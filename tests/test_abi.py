@@ -111,13 +111,14 @@ def test_weight_image_bytes(N, K, g, int4):
 
 def test_plan_of_the_flux_shapes():
     """The block tile each FLUX-shaped linear gets (measured choices on MI355X:
-    the FP6 tile where its 256 x 256 tiles fill one round, 192 x 384 INT8 where
-    256 x 256 would need two rounds, the split 192 x 192 INT8 tile for the long
-    reduction of the down-projection)."""
+    the FP6 256 x 256 tile where its tiles fill one round, the FP6 192 x 384
+    tile where 256 x 256 would need two rounds and 192 x 384 fills the chip
+    exactly, the split 192 x 192 INT8 tile for the long reduction of the
+    down-projection)."""
     FP6, I8 = B.CONVROT_MFMA_FP6, B.CONVROT_MFMA_I8
     assert B.convrot_linear_plan(1536, 3072, 9216, 256) == {"mfma": FP6, "tile": (256, 256), "splits": 1}
     assert B.convrot_linear_plan(4096, 3072, 3072, 256) == {"mfma": FP6, "tile": (256, 256), "splits": 1}
-    assert B.convrot_linear_plan(1536, 3072, 12288, 256) == {"mfma": I8, "tile": (192, 384), "splits": 1}
+    assert B.convrot_linear_plan(1536, 3072, 12288, 256) == {"mfma": FP6, "tile": (192, 384), "splits": 1}
     assert B.convrot_linear_plan(1536, 12288, 3072, 256) == {"mfma": I8, "tile": (192, 192), "splits": 2}
     assert B.convrot_linear_plan(16, 3072, 12288, 256) == {"mfma": I8, "tile": (0, 0), "splits": 1}
     # up to 128 rows the weight is streamed; from 129 on, block tiles
@@ -183,11 +184,13 @@ def _ceil(a, b):
     return -(-a // b)
 
 
-_RING = {(192, 384): 4 * 18 * 2048, (192, 192): 4 * 12 * 2048, (256, 256): 3 * 16 * 3072}
+_F6 = B.CONVROT_TILE_FP6
+_RING = {(192, 384): 4 * 18 * 2048, (192, 192): 4 * 12 * 2048, (256, 256): 3 * 16 * 3072,
+         (192, 384 | _F6): 2 * 18 * 3072}
 
 
 @pytest.mark.parametrize("M,K,N", [(1536, 12288, 3072), (1500, 12000, 3000), (256, 4096, 256), (64, 16384, 64)])
-@pytest.mark.parametrize("tile", [(192, 384), (192, 192), (256, 256)])
+@pytest.mark.parametrize("tile", [(192, 384), (192, 192), (256, 256), (192, 384 | _F6)])
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 def test_split_k_exchange_stays_inside_its_workspace(M, K, N, tile, splits):
     """Every address of the split-K exchange, enumerated on the host through the
@@ -196,13 +199,14 @@ def test_split_k_exchange_stays_inside_its_workspace(M, K, N, tile, splits):
     workspace size sets aside after its other parts; the two counters of every
     (tile, sub-block) stay in the 512 counter words, and the finalizer's
     copies of a sub-block's pairs stay in the LDS ring."""
-    tiles = _ceil(M, tile[0]) * _ceil(N, tile[1])
+    tm, tn = tile[0], tile[1] & ~_F6
+    tiles = _ceil(M, tm) * _ceil(N, tn)
     if splits > 1 and tiles * splits > 256:
         with pytest.raises(B.ConvRotError):
             B.convrot_split_k_extent(M, K, N, tile, splits)
         return
     ext = B.convrot_split_k_extent(M, K, N, tile, splits)
-    slot = tile[0] * tile[1] * 4
+    slot = tm * tn * 4
     assert ext["partial_end"] == tiles * (splits - 1) * slot
     ws = B.convrot_workspace_bytes_tiled(M, K, N, tile, splits)
     assert ws - B.convrot_workspace_bytes_tiled(M, K, N, tile, 1) == ext["partial_end"]
@@ -247,7 +251,9 @@ def test_gemm_i32_tiled_checks():
     # the plan-sized workspace is too small for the forced split
     assert _gemm_i32_tiled_status(M, K, N, (256, 256), 3, B.convrot_workspace_bytes(M, K, N, 256)) == \
         B.CONVROT_EWORKSPACE
-    for tile, splits in [((128, 128), 1), ((192, 384), 0), ((192, 384), 9), ((256, 256), -1)]:
+    F6 = B.CONVROT_TILE_FP6
+    for tile, splits in [((128, 128), 1), ((192, 384), 0), ((192, 384), 9), ((256, 256), -1), ((192, 192 | F6), 1),
+                         ((192 | F6, 384), 1), ((192, 384 | F6 | 1), 1)]:
         assert _gemm_i32_tiled_status(M, K, N, tile, splits, 1 << 40) == B.CONVROT_EINVAL, (tile, splits)
     assert _gemm_i32_tiled_status(32, K, N, (192, 192), 1, 1 << 40) == B.CONVROT_EINVAL       # M <= 32
     assert _gemm_i32_tiled_status(M, 256, N, (192, 192), 3, 1 << 40) == B.CONVROT_EINVAL      # S > K blocks
@@ -255,6 +261,13 @@ def test_gemm_i32_tiled_checks():
     assert _gemm_i32_tiled_status(M, K, N, (192, 192), 2, 1 << 40, flags=2) == B.CONVROT_EINVAL
     with pytest.raises(B.ConvRotError):
         B.convrot_workspace_bytes_tiled(M, K, N, (192, 96), 1)
+    # the FP6 192 x 384 tile reads the FP6 copy of the codes, so its workspace
+    # holds the FP6 activation image the INT8 tile of the same size does not
+    fp6_part = B.convrot_workspace_bytes_tiled(M, K, N, (192, 384 | F6), 1) - \
+        B.convrot_workspace_bytes_tiled(M, K, N, (192, 384), 1)
+    assert fp6_part >= M * K * 3 // 4
+    assert B.convrot_workspace_bytes_tiled(M, K, N, (256, 256 | F6), 1) == \
+        B.convrot_workspace_bytes_tiled(M, K, N, (256, 256), 1)
 
 
 @pytest.mark.parametrize("M,K,N,g,want", [(1, 3072, 12288, 256, 1), (4, 4096, 64, 256, 1), (5, 3072, 64, 256, 2),

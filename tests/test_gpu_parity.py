@@ -14,6 +14,7 @@ import pytest
 import oracle
 from w4a4_rotated_bit_amd import synth
 
+from w4a4_rotated_bit_amd.binding import CONVROT_TILE_FP6
 from ._parity import compare_codes, compare_rotated, compare_y, w16_word_index
 
 pytestmark = pytest.mark.gpu
@@ -132,15 +133,15 @@ def test_weight_image_and_nk_parity(gpu, N, K, g):
 GEMM_SHAPES = [(1, 32, 128), (37, 70, 384), (256, 256, 1024), (300, 520, 1152), (64, 1024, 3072),
                (513, 257, 256), (17, 33, 12288), (5, 100, 2560), (32, 64, 640), (3, 4000, 3072),
                (256, 512, 8192), (100, 300, 6144), (20, 9000, 1024), (7, 17000, 256),
-               # FP6 256 x 256 block tiles (216 and 192 of them, also ragged), INT8 192 x 384
+               # FP6 256 x 256 block tiles (216 and 192 of them, also ragged), FP6 192 x 384
                # (256 of them, also ragged), INT8 192 x 192 split 2 ways along K, and
                # 192 x 192 split 8 ways (256 workgroups, also ragged): the shapes the plan
                # picks here (convrot_linear_plan)
                (1536, 9216, 128), (1500, 9000, 256), (1536, 12288, 128), (1500, 12000, 384),
                (1536, 3072, 8192), (4096, 3072, 128), (4000, 3000, 256), (256, 3072, 16384),
                (200, 3011, 16384),
-               # the FP6 and 192 x 384 tiles with at least eight 128-K blocks, so that their
-               # K loops run the steady state of the stage ring (aligned and ragged)
+               # the two FP6 tiles with at least eight 128-K blocks, so that their K loops
+               # run the steady state of the stage ring (aligned and ragged)
                (1536, 9216, 1024), (1500, 9000, 1152), (1536, 12288, 1024), (1500, 12000, 1408),
                # the weight stream with 2, 3 and 4 groups of 32 rows (M <= 128; strips padded
                # to a multiple of 8), and the first M past it (block tiles)
@@ -171,7 +172,11 @@ def test_gemm_i32_integer_edges(gpu):
 
 # (tile, splits, M, N, K): every block tile at shapes the plan would not give
 # it, unsplit and (192 x 192) split
+F6 = CONVROT_TILE_FP6  # or-ed into tile_n: the FP6 tile of size 192 x 384
 TILED = [((256, 256), 1, 300, 520, 1152), ((256, 256), 1, 33, 1000, 2048), ((256, 256), 1, 700, 300, 5120),
+         # the FP6 192 x 384 tile and its two-stage ring: 1, 2, 3 and many K blocks, ragged
+         ((192, 384 | F6), 1, 300, 700, 128), ((192, 384 | F6), 1, 200, 500, 256), ((192, 384 | F6), 1, 40, 3000, 384),
+         ((192, 384 | F6), 1, 1000, 400, 6144), ((192, 384 | F6), 1, 385, 769, 1152),
          ((192, 384), 1, 300, 700, 2048), ((192, 384), 1, 1000, 400, 6144), ((192, 384), 1, 40, 3000, 1024),
          ((192, 192), 1, 1536, 9216, 1024), ((192, 192), 3, 256, 600, 6144), ((192, 192), 8, 200, 3011, 16384),
          ((192, 192), 5, 500, 260, 8192)]
@@ -188,7 +193,8 @@ def test_gemm_i32_every_block_tile(gpu, tile, splits, M, N, K):
     assert gpu.workspace_status(ws) == 0
 
 
-@pytest.mark.parametrize("tile,splits", [((256, 256), 1), ((192, 384), 1), ((192, 192), 8), ((192, 192), 1)])
+@pytest.mark.parametrize("tile,splits", [((256, 256), 1), ((192, 384), 1), ((192, 192), 8), ((192, 192), 1),
+                                         ((192, 384 | F6), 1)])
 def test_gemm_i32_saturated_codes_on_every_block_tile(gpu, tile, splits):
     """Integer edges at the longest rows: every code +-7 and K = 16384, so that
     |acc| reaches 49 K = 802,816 -- through each block tile (on the FP6 tile the
@@ -208,9 +214,11 @@ def test_gemm_i32_saturated_codes_on_every_block_tile(gpu, tile, splits):
 
 
 @pytest.mark.parametrize("tile,splits,M,N,K", [((256, 256), 2, 300, 520, 4096), ((192, 384), 2, 300, 700, 4096),
-                                               ((256, 256), 3, 1536, 3072, 12288), ((192, 384), 4, 1536, 3072, 12288)])
+                                               ((256, 256), 3, 1536, 3072, 12288), ((192, 384), 4, 1536, 3072, 12288),
+                                               ((192, 384 | F6), 2, 300, 700, 4096),
+                                               ((192, 384 | F6), 3, 1536, 3072, 12288)])
 def test_gemm_i32_split_k_on_the_eight_wave_tiles(gpu, tile, splits, M, N, K):
-    """The split-K exchange on the two eight-wave block tiles, which the plan
+    """The split-K exchange on the eight-wave block tiles, which the plan
     itself never splits, including the down-projection shape with the splits
     a timing probe once forced there when the GPU faulted.  Such a split needs
     more partial-tile room than a workspace sized by the library's own plan
@@ -346,8 +354,8 @@ def test_linear_ragged_shapes(gpu, M, N, K, g):
 
 
 @pytest.mark.parametrize("M,N,K,g,bias", [
-    # the FP6 256 x 256 tile and the INT8 192 x 384 tile through the whole linear, ragged
-    # M and N (N % 8 != 0: the epilogue's partial 16-byte stores), with and without bias
+    # the FP6 256 x 256 and 192 x 384 tiles through the whole linear, ragged M and N
+    # (N % 8 != 0: the epilogue's partial 16-byte stores), with and without bias
     (1500, 9000, 3072, 256, True), (1501, 9004, 3072, 256, False), (1500, 12000, 3072, 256, True),
     (1499, 12004, 3072, 256, False), (300, 700, 1152, 256, False),
     # INT4-only weight images: every product on the INT8 matrix cores, including the

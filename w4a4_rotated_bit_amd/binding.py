@@ -35,6 +35,7 @@ WORKSPACE_STATUS_OFFSET = 2048
 CONVROT_STATUS_SPLIT_TIMEOUT = 1
 # test flag of convrot_gemm_i32_tiled
 CONVROT_TEST_SPLIT_TIMEOUT = 1
+CONVROT_TILE_FP6 = 0x10000  # or-ed into tile_n of the tiled hooks: the FP6 tile of that size (192 x 384)
 MAX_K = 16384           # largest rotated width K_rot
 MAX_ROWS = 16777216     # largest M or N
 

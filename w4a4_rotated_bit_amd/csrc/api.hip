@@ -76,8 +76,14 @@ int validate_rows_out(const void* X, int64_t rows, int64_t K, int g)
 // the GEMM that follows is unknown; otherwise the one its plan reads).  The
 // FP6 copy exists only when act_has_fp6(M, image_has_fp6(g)).  Clears the
 // split-K counters and the status word.
+// x_stream: read X with non-temporal loads.  The linear asks for it when a
+// block tile other than the FP6 256 x 256 one follows: X (9.4 MB at the
+// FLUX shapes, 37.7 MB for the down-projection) then does not stay in the
+// caches, which otherwise slowed the GEMM launched right after (its weight
+// stream's latency went up: the FP6 192 x 384 tile, whose two-stage ring
+// looks ahead one stage only, took 44 instead of 36 us at 1536 x 12288).
 int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void* ws, bool want4, bool want6,
-                                hipStream_t s)
+                                hipStream_t s, bool x_stream = false)
 {
     const int64_t Kr = rotated_width(K, g);
     const bool fp6 = image_has_fp6(g);
@@ -94,6 +100,7 @@ int enqueue_prepare_activations(const void* X, int64_t M, int64_t K, int g, void
     a.rotated = nullptr;
     a.zero = (uint32_t*)ws;
     a.zero_count = kZeroWords;
+    a.x_stream = x_stream ? 1 : 0;
     launch_prep(g, OUT_IMAGE, a, s);
     return launched();
 }
@@ -282,7 +289,8 @@ static int enqueue_linear(const void* X, int64_t M, int64_t K, const void* image
     }
     const GemmPlan plan = gemm_plan(M, N, Kr, fp6);
     const bool fp6_plan = gemm_shape_fp6(plan.shape);  // the GEMM reads only the FP6 copy, else only the INT4 image
-    int rc = enqueue_prepare_activations(X, M, K, g, ws, !fp6_plan, fp6_plan, s);
+    const bool x_stream = M > kStreamMaxRows && plan.shape != 2;
+    int rc = enqueue_prepare_activations(X, M, K, g, ws, !fp6_plan, fp6_plan, s, x_stream);
     if (rc) return rc;
     return enqueue_gemm(GEMM_OUT_BF16, gemm_args(ws, M, Kr, image, sw, bias, N, Y, fp6, plan), s);
 }
@@ -401,7 +409,7 @@ int convrot_gemm_i32_tiled(const int8_t* qx, int64_t M, int64_t K, const void* i
     if (rc || M == 0 || N == 0) return rc;
     if (test_flags & ~CONVROT_TEST_SPLIT_TIMEOUT) return CONVROT_EINVAL;
     GemmPlan plan;
-    const bool fp6 = gemm_shape_of(tile_m, tile_n) == 2;
+    const bool fp6 = gemm_shape_fp6(gemm_shape_of(tile_m, tile_n));
     if ((rc = check_forced_plan(M, K, N, tile_m, tile_n, splits, fp6, &plan))) return rc;
     if (ws_bytes < workspace_bytes_for(M, K, fp6, plan)) return CONVROT_EWORKSPACE;
     if ((rc = check_device())) return rc;

@@ -13,6 +13,7 @@ static_assert(CONVROT_REGULAR_HADAMARD == kRegularHadamard, "header and library 
 static_assert(CONVROT_INT4_IMAGE == kInt4Image, "header and library agree on the image flag");
 static_assert(CONVROT_STATUS_SPLIT_TIMEOUT == (int)kStatusSplitTimeout, "header and library agree on the status");
 static_assert(CONVROT_WORKSPACE_STATUS_OFFSET == 4 * 2 * kSplitCounters, "status word right after the counters");
+static_assert(CONVROT_TILE_FP6 == kTileFp6, "tile flag of the test hooks");
 static_assert(CONVROT_WORKSPACE_IMAGE_OFFSET >= CONVROT_WORKSPACE_STATUS_OFFSET + 4 &&
                   CONVROT_WORKSPACE_IMAGE_OFFSET % 256 == 0,
               "activation image after the status word");
@@ -122,7 +123,7 @@ int convrot_workspace_bytes_tiled(int64_t M, int64_t K, int64_t N, int tile_m, i
     if (rc) return rc;
     if (N < 0 || N > kMaxRows) return CONVROT_EINVAL;
     GemmPlan p;
-    const bool fp6 = gemm_shape_of(tile_m, tile_n) == 2;
+    const bool fp6 = gemm_shape_fp6(gemm_shape_of(tile_m, tile_n));
     if ((rc = check_forced_plan(M, K, N, tile_m, tile_n, splits, fp6, &p))) return rc;
     *bytes = workspace_bytes_for(M, K, fp6, p);
     return CONVROT_OK;

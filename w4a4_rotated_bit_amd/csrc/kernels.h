@@ -21,6 +21,7 @@ struct PrepArgs {
     uint32_t* zero;      // words cleared by workgroup 0 (split-K counters) or nullptr
     int zero_count;
     int team;            // lanes per row (set by launch_prep)
+    int x_stream;        // team kernel: read X with non-temporal loads (keeps it out of the caches)
 };
 
 struct GemmArgs {

@@ -636,7 +636,13 @@ __device__ inline void team_load(const PrepArgs& a, int64_t row, uint32_t k0, ui
 #pragma unroll
     for (int c = 0; c < P / 8; ++c) {
         const uint32_t k = k0 + 8 * c;
-        w[c] = *(const uint4*)(xr + (has_row && k < (uint32_t)a.ld ? k : 0u));
+        const uint16_t* src = xr + (has_row && k < (uint32_t)a.ld ? k : 0u);
+        if (a.x_stream) {
+            const v4i v = __builtin_nontemporal_load((const v4i*)src);
+            w[c] = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+        } else {
+            w[c] = *(const uint4*)src;
+        }
     }
 }
 
@@ -1542,7 +1548,7 @@ __global__ __launch_bounds__(GemmShape<SHAPE>::NW * 64, 1) void gemm_kernel(Gemm
 // Each stage so starts and ends with the same registers, and the body is
 // straight-line code.
 // ---------------------------------------------------------------------------
-template <int NW_, int NWM_, int BI_, int BJ_, int SHAPE_>
+template <int NW_, int NWM_, int BI_, int BJ_, int SHAPE_, int STAGES_ = 3>
 struct Gemm6Geom {
     static constexpr int NW = NW_, NWM = NWM_, BI = BI_, BJ = BJ_, SHAPE = SHAPE_;
     static constexpr int NWN = NW / NWM;
@@ -1550,11 +1556,11 @@ struct Gemm6Geom {
     static constexpr int UA = BM / 32, UB = BN / 32;
     static constexpr int kStageA = UA * kUnit6Bytes;
     static constexpr int kStage = (UA + UB) * kUnit6Bytes;
-    static constexpr int kStages = 3;
+    static constexpr int kStages = STAGES_;
     static constexpr int kLdsBytes = kStages * kStage;
-    static constexpr int UPW = (UA + UB) / NW;          // units copied per wave per stage
-    static constexpr int COPIES = 3 * UPW;              // 1 KB copies per wave per stage
-    static_assert(UPW * NW == UA + UB && UA % UPW == 0, "a wave copies whole units of one operand");
+    static constexpr int kChunks = 3 * (UA + UB);                 // 1 KB copies per stage
+    static constexpr int COPIES = (kChunks + NW - 1) / NW;        // per wave (the last ones may repeat)
+    static_assert(kStages == 2 || kStages == 3, "the stage loop is written for two or three stages");
     static_assert(BM == gemm_tile_m(SHAPE) && BN == gemm_tile_n(SHAPE), "host plan and kernel agree");
     static_assert(NW * 64 == gemm_threads(SHAPE) && kLdsBytes == gemm_ring_bytes(SHAPE), "host geometry agrees");
 };
@@ -1563,6 +1569,9 @@ struct Gemm6Geom {
 // every LDS wait stalls the matrix core: measured 14% slower on 1536 x 3072 x
 // 9216, and its epilogue has twice the work per wave.)
 using Gemm6W8 = Gemm6Geom<8, 2, 4, 2, 2>;
+// Shape 3: 192 x 384, eight waves of 96 x 96 (3 x 3 MFMA tiles); a stage is
+// 54 KB, so the ring holds two.
+using Gemm6Wide = Gemm6Geom<8, 2, 3, 3, 3, 2>;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
@@ -1622,27 +1631,29 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-    // Copies: wave w moves units UPW w .. UPW (w + 1) - 1 of each stage
-    // (activation units 0 .. UA - 1, then the weight units), three 1 KB runs
-    // per unit.  Units past the end of the matrix re-read the last valid unit
-    // (their products land in rows / columns that are never stored).
+    // Copies: a stage is 3 (UA + UB) runs of 1 KB (activation units 0 ..
+    // UA - 1, then the weight units, three runs each); wave w moves runs
+    // COPIES w .. COPIES (w + 1) - 1, and where they do not divide evenly the
+    // last wave repeats the final run (same bytes to the same place), so that
+    // every wave waits for the same count.  Units past the end of the matrix
+    // re-read the last valid unit (their products land in rows / columns
+    // that are never stored).
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
-    const bool copies_a = wave * G::UPW < G::UA;
-    const uint8_t* copy_src[G::UPW];
+    const uint8_t* copy_src[G::COPIES];
+    uint32_t copy_dst[G::COPIES];
 #pragma unroll
-    for (int u = 0; u < G::UPW; ++u) {
-        const int ug = wave * G::UPW + u;
-        const int row_tile = copies_a ? min(tm * G::UA + ug, a.MT - 1) : min(tn * G::UB + ug - G::UA, a.NT - 1);
-        copy_src[u] = (copies_a ? a.act6 : a.wgt6) + (size_t)row_tile * a.KB * kUnit6Bytes;
+    for (int i = 0; i < G::COPIES; ++i) {
+        const int c = min(wave * G::COPIES + i, G::kChunks - 1);
+        const int ug = c / 3, part = c % 3;
+        const bool is_a = ug < G::UA;
+        const int row_tile = is_a ? min(tm * G::UA + ug, a.MT - 1) : min(tn * G::UB + ug - G::UA, a.NT - 1);
+        copy_src[i] = (is_a ? a.act6 : a.wgt6) + (size_t)row_tile * a.KB * kUnit6Bytes + part * 1024;
+        copy_dst[i] = (uint32_t)(ug * kUnit6Bytes + part * 1024);
     }
     auto issue = [&](uint32_t stage, int kb) __attribute__((always_inline)) {
         const uint32_t voff = (uint32_t)kb * kUnit6Bytes + lane * 16;
 #pragma unroll
-        for (int u = 0; u < G::UPW; ++u)
-#pragma unroll
-            for (int part = 0; part < 3; ++part)
-                lds_copy16(copy_src[u] + part * 1024, voff,
-                           stage + (G::UPW * wave + u) * kUnit6Bytes + part * 1024);
+        for (int i = 0; i < G::COPIES; ++i) lds_copy16(copy_src[i], voff, stage + copy_dst[i]);
     };
 
     // Fragments: lane (r32, h) reads row r32 of its tiles' units, block
@@ -1687,15 +1698,18 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
                 acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(rb[j]), fp6_operand(ra[i]),
                                                                             acc[j][i], 2, 2, 0, 127, 0, 127);
     };
-    // each MFMA followed by its share of the 24 fragment reads of a phase
+    // each MFMA followed by its share of the phase's fragment reads (two
+    // read instructions per fragment: ds_read2_b64 + ds_read_b64)
     auto hints = [&](int reads) __attribute__((always_inline)) {
+        constexpr int NM = BI * BJ, NR = 2 * (BI + BJ);
 #pragma unroll
-        for (int m = 0; m < BI * BJ; ++m) {
+        for (int m = 0; m < NM; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            const int share = ((m + 1) * NR + NM - 1) / NM - (m * NR + NM - 1) / NM;  // 2, 1, ...
             if (reads > 0) {
-                if (m % 2 == 0)
+                if (share == 2)
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                else
+                else if (share == 1)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
@@ -1708,9 +1722,9 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
                                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)params));
     const int first = KC < G::kStages ? KC : G::kStages;
     for (int st = 0; st < first; ++st) issue(lds0 + st * kStage, kb0 + st);
-    if (first >= 3)
+    if (G::kStages == 3 && first >= 3)
         wait6_and_barrier<G::COPIES, 2>();
-    else if (first == 2)
+    else if (first >= 2)
         wait6_and_barrier<G::COPIES, 1>();
     else
         wait6_and_barrier<G::COPIES, 0>();
@@ -1741,8 +1755,14 @@ __global__ __launch_bounds__(G::NW * 64, 1) void gemm6_kernel(GemmArgs a)
         hints(MORE ? 24 : 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int kr = 0; kr < KC - G::kStages; ++kr) step(kr, Const<1>{}, Const<1>{}, Const<1>{});
-    if (KC >= 3) step(KC - 3, Const<0>{}, Const<1>{}, Const<1>{});
+    if constexpr (G::kStages == 3) {
+        for (int kr = 0; kr < KC - 3; ++kr) step(kr, Const<1>{}, Const<1>{}, Const<1>{});
+        if (KC >= 3) step(KC - 3, Const<0>{}, Const<1>{}, Const<1>{});
+    } else {
+        // two stages: at stage kr's barrier only stage kr + 1 is in flight,
+        // and it must have landed; the copy of kr + 2 is issued after it
+        for (int kr = 0; kr < KC - 2; ++kr) step(kr, Const<1>{}, Const<0>{}, Const<1>{});
+    }
     if (KC >= 2) step(KC - 2, Const<0>{}, Const<0>{}, Const<1>{});
     step(KC - 1, Const<0>{}, Const<0>{}, Const<0>{});
 
@@ -2595,7 +2615,7 @@ static void launch_skinny(const GemmArgs& a, hipStream_t s)
 template <typename G, int OUT, bool SPLIT>
 static void launch_block_tile_kernel(dim3 grid, const GemmArgs& a, hipStream_t s)
 {
-    if constexpr (G::SHAPE == 2)
+    if constexpr (gemm_shape_fp6(G::SHAPE))
         hipLaunchKernelGGL((gemm6_kernel<OUT, G, SPLIT>), grid, dim3(G::NW * 64), 0, s, a);
     else
         hipLaunchKernelGGL((gemm_kernel<OUT, G::SHAPE, SPLIT>), grid, dim3(G::NW * 64), 0, s, a);
@@ -2626,6 +2646,8 @@ void launch_gemm(int out_mode, GemmArgs a, hipStream_t s)
     const bool split = a.splits > 1;
     if (a.shape == 2)
         launch_block_tile<Gemm6W8>(out_mode, split, grid, a, s);
+    else if (a.shape == 3)
+        launch_block_tile<Gemm6Wide>(out_mode, split, grid, a, s);
     else if (a.shape == 0)
         launch_block_tile<GemmGeom<0>>(out_mode, split, grid, a, s);
     else

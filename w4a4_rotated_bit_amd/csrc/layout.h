@@ -182,16 +182,18 @@ CONVROT_HD inline size_t w16_word_offset(int64_t m, int64_t k, int64_t K)
 }
 
 // ---- GEMM plan -------------------------------------------------------------
-// The GEMM covers the output with one of three block tiles.  Shapes 0 and 1
+// The GEMM covers the output with one of four block tiles.  Shapes 0 and 1
 // run on the INT8 matrix cores from the INT4 image: shape 0 is 192 x 384,
-// shape 1 is 192 x 192.  Shape 2 is 256 x 256 on the FP6 matrix cores from
-// the FP6 image (twice the INT8 rate; bound by LDS bandwidth rather than by
-// the matrix cores), the fastest per output where its tiles fill the chip;
-// it is not a candidate when the weight image is INT4 only.
+// shape 1 is 192 x 192.  Shapes 2 and 3 run on the FP6 matrix cores from the
+// FP6 image (twice the INT8 rate; bound by their LDS reads rather than by
+// the matrix cores), the fastest per output where their tiles fill the chip:
+// shape 2 is 256 x 256 with a three-stage ring, shape 3 is 192 x 384, whose
+// 54 KB stages leave room for two (it fills the chip at 1536 x 12288).  The
+// FP6 shapes are not candidates when the weight image is INT4 only.
 // When there are too few tiles to fill the chip, the 192 x 192 tile's K range
 // is split over S workgroups (the integer partial sums are exact in any
 // order): S is the largest value <= 8 with S * tiles <= kSplitTargetWGs and
-// >= 16 128-K blocks per split.  The plan never splits the other two shapes;
+// >= 16 128-K blocks per split.  The plan never splits the other shapes;
 // a plan given from outside (gemm_plan_forced, a test hook) may.  Of the
 // shapes the plan takes the one with the smallest estimated time: rounds of
 // workgroups x 128-K blocks per workgroup x tile area at gemm_shape_ns per
@@ -206,12 +208,12 @@ constexpr int kSplitTargetWGs = 256;   // one workgroup per compute unit of an M
 constexpr int kSplitCounters = 256;    // counter slots: a split launch has at most this many tiles x splits
 static_assert(kSplitTargetWGs <= kSplitCounters, "a plan's tiles x splits fit the counters");
 constexpr int kMaxSplits = 8;
-constexpr int kGemmShapes = 3;
+constexpr int kGemmShapes = 4;
 constexpr int64_t kStreamMaxRows = 128;
 
 CONVROT_HD constexpr int gemm_tile_m(int shape) { return shape == 2 ? 256 : 192; }
-CONVROT_HD constexpr int gemm_tile_n(int shape) { return shape == 0 ? 384 : (shape == 1 ? 192 : 256); }
-CONVROT_HD constexpr bool gemm_shape_fp6(int shape) { return shape == 2; }
+CONVROT_HD constexpr int gemm_tile_n(int shape) { return (shape == 0 || shape == 3) ? 384 : (shape == 1 ? 192 : 256); }
+CONVROT_HD constexpr bool gemm_shape_fp6(int shape) { return shape >= 2; }
 // nanoseconds per 1024 outputs per 128-K block, by shape (MI355X, FLUX shapes)
 CONVROT_HD constexpr int gemm_shape_ns(int shape) { return shape == 0 ? 28 : (shape == 1 ? 30 : 19); }
 // the shapes whose K range the plan splits
@@ -220,14 +222,21 @@ CONVROT_HD constexpr bool gemm_shape_splits(int shape) { return shape == 1; }
 CONVROT_HD constexpr int gemm_threads(int shape) { return shape == 1 ? 256 : 512; }
 CONVROT_HD constexpr int gemm_ring_bytes(int shape)
 {
-    return shape == 2 ? 3 * (256 / 32 + 256 / 32) * kUnit6Bytes
-                      : 4 * (gemm_tile_m(shape) / 32 + gemm_tile_n(shape) / 32) * kUnitBytes;
+    return shape == 2   ? 3 * (256 / 32 + 256 / 32) * kUnit6Bytes
+           : shape == 3 ? 2 * (192 / 32 + 384 / 32) * kUnit6Bytes
+                        : 4 * (gemm_tile_m(shape) / 32 + gemm_tile_n(shape) / 32) * kUnitBytes;
 }
-// the block tile of (tile_m, tile_n), or -1
+// the block tile of (tile_m, tile_n), or -1; kTileFp6 or-ed into tile_n
+// picks the FP6 tile where both kinds have that size (192 x 384)
+constexpr int kTileFp6 = 0x10000;
 CONVROT_HD constexpr int gemm_shape_of(int tile_m, int tile_n)
 {
-    return (tile_m == 192 && tile_n == 384) ? 0 : (tile_m == 192 && tile_n == 192) ? 1
-                                                 : (tile_m == 256 && tile_n == 256) ? 2 : -1;
+    return (tile_m == 192 && tile_n == 384)              ? 0
+           : (tile_m == 192 && tile_n == 192)            ? 1
+           : (tile_m == 256 && tile_n == 256)            ? 2
+           : (tile_m == 256 && tile_n == (256 | kTileFp6)) ? 2
+           : (tile_m == 192 && tile_n == (384 | kTileFp6)) ? 3
+                                                         : -1;
 }
 
 struct GemmPlan {
