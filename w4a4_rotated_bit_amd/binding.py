@@ -331,7 +331,8 @@ def convrot_workspace_bytes_tiled(M: int, K: int, N: int, tile, splits: int) -> 
 
 
 def convrot_gemm_i32_tiled(qx, image, N: int, tile, splits: int, test_flags: int = 0, workspace=None, stream=None):
-    """convrot_gemm_i32 with the block tile (tile_m, tile_n) and the K split given.
+    """convrot_gemm_i32 with the block tile (tile_m, tile_n) and the K split given
+    (tile_n | CONVROT_TILE_FP6 picks the FP6 192 x 384 tile over the INT8 one).
     Returns (acc int32 [M, N], workspace)."""
     import torch
     M, K = qx.shape
