@@ -408,7 +408,9 @@ def measure(name: str, steps: int, warmup: int, cold_bytes: float, rotation: str
         ach = kernel_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None if w4a16 or variant else read_traffic(base)
+    # the counters of the GEMM this workload runs (the rotation changes only the
+    # prep; the INT4-only image has its own summary)
+    roof["traffic"] = None if w4a16 else read_traffic(name)
     med = float(np.median(batch_ms))
     rec = {
         "workload": name, "M": M, "K": K, "N": N, "group": wl.g, "rotation": rotation, "path": path,
