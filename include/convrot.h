@@ -20,7 +20,9 @@
  *     16-bit storage.
  *   - Pointers named *_dev are device pointers; pointers named *_host are host
  *     pointers.  The library never allocates, frees or retains device memory
- *     and keeps no state between calls: the caller owns every buffer.
+ *     and keeps no state between calls: the caller owns every buffer (the one
+ *     exception is the fixed device workspace of convrot_linear_noalloc,
+ *     below, which lives as long as the process).
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Device
  *     entry points only enqueue work on it and return; nothing is synchronised.
  *   - Device buffers must be 16-byte aligned except sw/sx/bias (4/4/2 bytes).
