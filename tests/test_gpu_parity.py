@@ -501,20 +501,25 @@ FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_ml
 
 @pytest.mark.parametrize("name", FULL + ["flux_qkv_m1536_k3072_n9216+regular", "flux_qkv_m1536_k3072_n9216+zero_rows",
                                          "decode_m4_k3072_n12288+zero_rows", "flux_qkv_m1536_k3072_n9216+int4",
-                                         "flux_mlp_down_m1536_k12288_n3072+regular"])
+                                         "flux_mlp_down_m1536_k12288_n3072+regular",
+                                         # the FP6 192 x 384 tile behind the other prep instances, and
+                                         # the INT8 192 x 384 tile (with the streamed X reads) at full size
+                                         "flux_mlp_up_m1536_k3072_n12288+regular", "flux_mlp_up_m1536_k3072_n12288+g64",
+                                         "flux_mlp_up_m1536_k3072_n12288+int4"])
 def test_linear_full_size(gpu, name):
     """Full shapes, in the launch configuration the benchmark times, against
     the oracle on every output: all activation and weight codes, the scales,
     and Y element by element.  "+regular": the same inputs rotated with the
     regular Hadamard matrix.  "+zero_rows": a few rows of X set to zero, whose
     scale and codes must be zero and whose output must be the bias exactly.
-    "+int4": an INT4-only weight image (INT8 matrix cores)."""
+    "+int4": an INT4-only weight image (INT8 matrix cores).  "+g64": the same
+    inputs with groups of 64."""
     import torch
     base, _, variant = name.partition("+")
     inp = synth.make(base)
     wl = inp["workload"]
     M, N, K = wl.M, wl.N, wl.K
-    g = wl.g | (REG if variant == "regular" else 0) | (INT4 if variant == "int4" else 0)
+    g = (64 if variant == "g64" else wl.g) | (REG if variant == "regular" else 0) | (INT4 if variant == "int4" else 0)
     zero_rows = np.array(sorted({1 % M, M // 2, M - 1})) if variant == "zero_rows" else np.array([], int)
     if zero_rows.size:
         inp["x"] = inp["x"].copy()
