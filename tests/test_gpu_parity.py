@@ -505,7 +505,11 @@ FULL = ["flux_qkv_m1536_k3072_n9216", "flux_mlp_up_m1536_k3072_n12288", "flux_ml
                                          # the FP6 192 x 384 tile behind the other prep instances, and
                                          # the INT8 192 x 384 tile (with the streamed X reads) at full size
                                          "flux_mlp_up_m1536_k3072_n12288+regular", "flux_mlp_up_m1536_k3072_n12288+g64",
-                                         "flux_mlp_up_m1536_k3072_n12288+int4"])
+                                         "flux_mlp_up_m1536_k3072_n12288+int4",
+                                         # 4096 rows on INT8 192 x 384 tiles: a ragged last row of tiles
+                                         "stress_m4096_k3072_n3072+int4",
+                                         # the weight stream behind the group-64 prep
+                                         "decode_m16_k3072_n12288+g64"])
 def test_linear_full_size(gpu, name):
     """Full shapes, in the launch configuration the benchmark times, against
     the oracle on every output: all activation and weight codes, the scales,
